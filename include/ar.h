@@ -1,0 +1,189 @@
+/*
+ * ar.h -- C ABI of libar: ring and double-binary-tree all-reduce (sum),
+ * reduce-scatter and all-gather over R logical ranks that all live in one
+ * MI355X's HBM.
+ *
+ * Every rank's buffer is a row of one rank-major device array: rank q's
+ * elements start at base + q * row_elems * elem_size.  One call covers all R
+ * logical ranks (in a multi-process library each rank would make the call;
+ * here the R ranks of one communicator are emulated by one process).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named send/recv/dev are DEVICE pointers allocated by the caller
+ *    (hipMalloc or torch); the library never frees them.  `stream` is a
+ *    hipStream_t passed as void* (NULL = the default stream).
+ *  - Collective calls are asynchronous on `stream`, as the NCCL host call
+ *    pattern is: enqueue, then the caller synchronizes the stream ("NCCL and
+ *    NVSHMEM -- two GPU communication models, side by side", the NCCL host
+ *    code listing).  Argument errors are reported synchronously by the return
+ *    code and nothing is enqueued.
+ *  - One collective in flight per communicator: two calls on the same comm
+ *    must be ordered on one stream (a team's internal resources cannot be
+ *    shared by two concurrent collectives -- "Demystifying NVSHMEM ..."
+ *    summary, paragraph on fence/quiet and teams).  All ranks of the comm take
+ *    part in every call with the same count and dtype ("NCCL, NIXL, and
+ *    Distributed GPU Communication", section on communication types).
+ *  - Create a communicator once and reuse it; creation is the expensive part
+ *    ("NCCL, NIXL, and Distributed GPU Communication", performance checklist:
+ *    never create the communicator inside the loop).
+ *  - Return value: AR_SUCCESS (0) or one of the ar_status_t codes below.
+ *    count == 0 is a successful no-op.
+ */
+#ifndef AR_H_
+#define AR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ar_comm* ar_comm_t;
+
+/* Element type of send/recv.  AR_BF16 elements are 16-bit bfloat16 bit
+ * patterns; they are added in float32 and rounded once (nearest-even) by the
+ * rank that owns the element. */
+typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
+
+/* AR_RING: 2(R-1) steps around the ring q -> q+1, R-1 reduce-and-pass steps
+ * then R-1 copy-and-pass steps ("GPU MODE lecture 68 notes", section 05,
+ * "SHARP -- in-network reduction": the ring takes 2(N-1) steps).
+ * AR_TREE: double binary tree -- two complementary binary trees working at
+ * once, each reducing and broadcasting half of the elements ("NCCL and
+ * NVSHMEM -- two GPU communication models, side by side", section "double
+ * binary tree").  AR_AUTO picks by message size: tree for small messages,
+ * ring for large ones (same page: tree for small messages, ring for large,
+ * chosen automatically). */
+typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
+
+/* AR_SIMPLE: bulk data, then a release, then a ready flag (or a kernel
+ * boundary between steps).  AR_LL: data and its arrival flag packed in one
+ * 8-byte store -- 4 bytes of data, 4 bytes of flag -- that the consumer polls
+ * ("Demystifying NVSHMEM ..." summary, paragraph on collectives). */
+typedef enum { AR_SIMPLE = 0, AR_LL = 1 } ar_proto_t;
+
+typedef enum {
+    AR_SUCCESS = 0,
+    AR_ERR_INVALID_ARG = 1,   /* R out of range, NULL pointer, count above capacity, misaligned */
+    AR_ERR_INVALID_USAGE = 2, /* in-place call, missing workspace, comm in error state */
+    AR_ERR_UNSUPPORTED = 3,   /* combination not provided (e.g. tree reduce-scatter) */
+    AR_ERR_HIP = 4,           /* a HIP runtime call failed; see ar_last_hip_error */
+    AR_ERR_TIMEOUT = 5,       /* a kernel's bounded wait expired (watchdog) */
+    AR_ERR_INTERNAL = 6
+} ar_status_t;
+
+/* How the ring's steps are launched.
+ * AR_LAUNCH_STEP: one kernel per ring step covering all R ranks; the kernel
+ *   boundary orders the steps.
+ * AR_LAUNCH_FUSED: one persistent kernel; each workgroup carries its chunks
+ *   of a segment through all 2(R-1) steps in order, every step still reading
+ *   the predecessor rank's buffer and writing the rank's own buffer.
+ * AR_LAUNCH_PIPELINED: one persistent kernel in which each logical rank has
+ *   its own workgroups; a chunk passes from rank q-1 to rank q through a
+ *   per-chunk ready flag (agent-scope release by the producer, acquire by
+ *   the consumer) -- the simple protocol.
+ * AR_LAUNCH_AUTO: the library's choice (the default). */
+typedef enum {
+    AR_LAUNCH_AUTO = 0,
+    AR_LAUNCH_STEP = 1,
+    AR_LAUNCH_FUSED = 2,
+    AR_LAUNCH_PIPELINED = 3
+} ar_launch_t;
+
+/* Tunables for ar_set_option / ar_get_option. */
+typedef enum {
+    AR_OPT_CHUNK_BYTES = 0,   /* ring slice ("chunk") size in bytes of T; 0 = whole segment */
+    AR_OPT_LAUNCH = 1,        /* an ar_launch_t */
+    AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default */
+    AR_OPT_TIMEOUT_SPINS = 3, /* poll iterations before a bounded wait gives up */
+    AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
+    AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
+    AR_OPT_PROTO = 6,         /* an ar_proto_t, overriding the one given to ar_init */
+    AR_OPT_TREE_MAX_BYTES = 7 /* AR_AUTO: largest per-rank message sent by tree */
+} ar_option_t;
+
+/* Create a communicator for R logical ranks (2 <= R <= 64) and up to
+ * `count` elements per rank for all-reduce (reduce-scatter input / all-gather
+ * output rows may be up to `count` long).  Builds the ring step table and
+ * the two trees on the host and sizes the workspace; allocates no device
+ * memory.  `*out` receives the handle; on error it is set to NULL.
+ * Mirrors ncclCommInitRank(&comm, nranks, id, rank). */
+int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t algo,
+            ar_proto_t proto);
+
+/* Release the host state of a communicator.  Does not free caller memory.
+ * NULL is a no-op. */
+int ar_destroy(ar_comm_t comm);
+
+/* Bytes of device workspace this communicator needs: float32 partial sums
+ * when T is not float32/int32 or when reducing into a shard, LL staging
+ * lines for the tree and the ring-LL path, per-chunk ready flags, and a
+ * small control block (LL epoch, error word).  The caller allocates at
+ * least this many bytes (any 256-byte aligned device allocation). */
+size_t ar_workspace_bytes(ar_comm_t comm);
+
+/* Hand the workspace to the communicator and clear its control block and
+ * LL lines (enqueued on `stream`; ordered before any later call on the same
+ * stream).  The memory stays owned by the caller and must outlive every
+ * collective issued on this comm.  Returns AR_ERR_INVALID_ARG when `bytes`
+ * is smaller than ar_workspace_bytes or `dev` is NULL or misaligned. */
+int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
+
+/* All-reduce (sum).  send and recv are [R][count] rank-major device arrays
+ * of the comm's dtype, distinct (in-place is AR_ERR_INVALID_USAGE).  On
+ * completion every row of recv holds the element-wise sum over the R rows
+ * of send ("NCCL, NIXL, and Distributed GPU Communication", section
+ * "All-reduce").  Floating-point sums are added in the order the schedule
+ * implies: ring -- a left fold from the owner's successor round to the owner;
+ * tree -- each node's own value, then its children's subtree sums in
+ * ascending rank order. */
+int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, void* stream);
+
+/* Reduce-scatter (sum), ring only.  send is [R][R*recvcount], recv is
+ * [R][recvcount]: row q of recv receives segment q of the sum ("NCCL, NIXL,
+ * and Distributed GPU Communication", section "Reduce-scatter").  The values
+ * are bit-identical to the same segment of ar_allreduce's result. */
+int ar_reduce_scatter(ar_comm_t comm, const void* send, void* recv, size_t recvcount,
+                      void* stream);
+
+/* All-gather, ring only.  send is [R][sendcount], recv is [R][R*sendcount]:
+ * every row of recv becomes [send_0, send_1, ..., send_{R-1}] ("NCCL, NIXL,
+ * and Distributed GPU Communication", section "All-gather").  A pure copy;
+ * reduce-scatter followed by all-gather equals all-reduce bit for bit. */
+int ar_all_gather(ar_comm_t comm, const void* send, void* recv, size_t sendcount,
+                  void* stream);
+
+/* Synchronize the comm's last stream and report its device error word:
+ * AR_ERR_TIMEOUT when a bounded wait expired in an earlier call, else
+ * AR_SUCCESS.  Clears the word. */
+int ar_check(ar_comm_t comm);
+
+/* Set / read one tunable (ar_option_t).  Unknown options or out-of-range
+ * values give AR_ERR_INVALID_ARG. */
+int ar_set_option(ar_comm_t comm, int option, int64_t value);
+int ar_get_option(ar_comm_t comm, int option, int64_t* value);
+
+/* Resolved algorithm, protocol and launch that a call with `count` elements
+ * per rank would use (values of ar_algo_t, ar_proto_t, ar_launch_t). */
+int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
+
+/* Host-side views of the schedule, for checking and tooling.
+ * ar_ring_segment: [*lo, *hi) element range of segment c for a count of
+ *   `count` elements; rank c owns it.
+ * ar_tree_parent: parent of rank r in tree 0 (A) or tree 1 (B), -1 at the
+ *   root; returns -2 for invalid arguments. */
+int ar_ring_segment(ar_comm_t comm, size_t count, int c, size_t* lo, size_t* hi);
+int ar_tree_parent(ar_comm_t comm, int tree, int r);
+
+/* Message for a status code (static storage). */
+const char* ar_status_string(int status);
+
+/* Last hipError_t seen by this comm (0 if none). */
+int ar_last_hip_error(ar_comm_t comm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H_ */

@@ -1,0 +1,390 @@
+/*
+ * oracle.c -- plain CPU oracle for ring and double-binary-tree all-reduce
+ * (sum), reduce-scatter and all-gather over R logical ranks.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct reference
+ * the GPU library is checked against.  Only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg may load it; the product path never
+ * does.  It shares no code, header, table or helper with the GPU library,
+ * and includes nothing from it.
+ *
+ * Parity status: every function here is pinned by CPU tests (closed forms,
+ * brute force, hand-computed rounding-order cases, a library conversion
+ * routine, and the pages' worked examples); none is "parity unpinned".
+ *
+ * Buffers are rank-major: row q of R rows holds logical rank q's elements
+ * contiguously.  Element types: 0 = int32, 1 = float32, 2 = bfloat16 (stored
+ * as uint16 bit patterns).  The accumulator is uint32 wrap-around arithmetic
+ * for int32 and IEEE float32 (round-to-nearest-even) for float32 and
+ * bfloat16 inputs; a bfloat16 result is rounded once, to nearest-even, by
+ * the rank that owns the element.
+ *
+ * What is computed, and where the pages say so:
+ *  - all-reduce: every rank ends with the element-wise sum of all ranks'
+ *    inputs ("NCCL, NIXL, and Distributed GPU Communication", section
+ *    "All-reduce", the four-GPU g0+g1+g2+g3 example);
+ *  - reduce-scatter: rank r receives shard r of that sum (same page,
+ *    "Reduce-scatter"); all-gather: every rank receives [x0, x1, ..., x_{k-1}]
+ *    (same page, "All-gather"); all-reduce = reduce-scatter + all-gather
+ *    (same page, "Reduce-scatter");
+ *  - ring: 2(N-1) steps ("GPU MODE lecture 68 notes", section 05, "SHARP --
+ *    in-network reduction"), read as R-1 reduce-and-pass steps followed by
+ *    R-1 copy-and-pass steps around the ring q -> q+1;
+ *  - double binary tree: two complementary binary trees working at once,
+ *    each on different links ("NCCL and NVSHMEM -- two GPU communication
+ *    models, side by side", section "double binary tree"), read as the
+ *    two-tree scheme: tree A is the in-order binary tree on ranks 0..R-1,
+ *    tree B its mirror image (even R) or its shift by one (odd R), and each
+ *    tree reduces and broadcasts one half of the elements.
+ * Floating-point sums depend on the order of the additions, so the oracle
+ * replays exactly the order the schedule implies (see each function).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_INT32 = 0, ORC_FLOAT32 = 1, ORC_BF16 = 2 };
+enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_ENOMEM = 2 };
+
+/* One accumulator value: uint32 for int32 inputs, float for the others. */
+typedef union {
+    uint32_t u;
+    float f;
+} acc_t;
+
+static int mod(int a, int m) { return ((a % m) + m) % m; }
+
+static int elem_size(int dtype) { return dtype == ORC_BF16 ? 2 : 4; }
+
+/* ---- bfloat16 -------------------------------------------------------- */
+
+/* float32 -> bfloat16, round to nearest, ties to even.  The top 16 bits are
+ * kept; the dropped low 16 bits decide: above half round up, below half
+ * round down, exactly half round to the even neighbour.  A carry out of the
+ * mantissa moves into the exponent, which is the correct result (and yields
+ * infinity above the largest finite bfloat16).  NaN stays NaN (quiet). */
+uint16_t orc_bf16_from_f32(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t hi = u >> 16;
+    uint32_t lo = u & 0xffffu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u) != 0u))
+        hi += 1u;
+    return (uint16_t)hi;
+}
+
+/* bfloat16 -> float32 is exact: the 16 bits become the top half. */
+float orc_f32_from_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+void orc_bf16_from_f32_array(const float* in, uint16_t* out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_from_f32(in[i]);
+}
+
+/* ---- LL line --------------------------------------------------------- */
+
+/* The LL protocol puts data and its arrival flag into one 8-byte write
+ * ("Demystifying NVSHMEM ..." summary, paragraph on collectives: LL/LL128
+ * pack data and an arrival flag into one atomic write).  Reading: data bits
+ * in the low 32 bits, flag in the high 32 bits. */
+uint64_t orc_ll_pack(uint32_t data_bits, uint32_t flag)
+{
+    return ((uint64_t)flag << 32) | (uint64_t)data_bits;
+}
+uint32_t orc_ll_data(uint64_t line) { return (uint32_t)(line & 0xffffffffu); }
+uint32_t orc_ll_flag(uint64_t line) { return (uint32_t)(line >> 32); }
+
+/* ---- element access -------------------------------------------------- */
+
+/* Widen element i of a T-typed buffer into the accumulator type. */
+static acc_t widen(int dtype, const void* buf, size_t i)
+{
+    acc_t a;
+    if (dtype == ORC_INT32) {
+        int32_t v;
+        memcpy(&v, (const char*)buf + 4 * i, 4);
+        a.u = (uint32_t)v;
+    } else if (dtype == ORC_FLOAT32) {
+        memcpy(&a.f, (const char*)buf + 4 * i, 4);
+    } else {
+        uint16_t h;
+        memcpy(&h, (const char*)buf + 2 * i, 2);
+        a.f = orc_f32_from_bf16(h);
+    }
+    return a;
+}
+
+/* Narrow an accumulator into element i of a T-typed buffer. */
+static void narrow(int dtype, void* buf, size_t i, acc_t a)
+{
+    if (dtype == ORC_INT32) {
+        int32_t v = (int32_t)a.u;
+        memcpy((char*)buf + 4 * i, &v, 4);
+    } else if (dtype == ORC_FLOAT32) {
+        memcpy((char*)buf + 4 * i, &a.f, 4);
+    } else {
+        uint16_t h = orc_bf16_from_f32(a.f);
+        memcpy((char*)buf + 2 * i, &h, 2);
+    }
+}
+
+/* One addition in the accumulator type: int32 wraps modulo 2^32, floats are
+ * IEEE single additions (this file is built without fast-math or FMA
+ * contraction, so the compiler may not reassociate or fuse them). */
+static acc_t acc_add(int dtype, acc_t a, acc_t b)
+{
+    acc_t r;
+    if (dtype == ORC_INT32)
+        r.u = a.u + b.u;
+    else
+        r.f = a.f + b.f;
+    return r;
+}
+
+/* ---- ring ------------------------------------------------------------ */
+
+/* Segment c of a rank's N elements: [min(c*S, N), min((c+1)*S, N)) with
+ * S = ceil(N/R).  Rank c owns segment c, matching "rank r receives shard r"
+ * of reduce-scatter.  Trailing segments may be shorter or empty. */
+static size_t seg_lo(size_t N, int R, int c)
+{
+    size_t S = (N + (size_t)R - 1) / (size_t)R;
+    size_t b = (size_t)c * S;
+    return b < N ? b : N;
+}
+static size_t seg_hi(size_t N, int R, int c) { return seg_lo(N, R, c + 1); }
+
+/* Ring reduce phase, replayed step by step.  At step s (0..R-2) every rank
+ * q works on segment c = (q - s - 2) mod R: it adds the partial sum that its
+ * predecessor q-1 holds for that segment (at step 0 the predecessor's own
+ * input) to its own input.  Before the last step the result is the partial
+ * rank q holds; at the last step q == c, the owner, and the result is final.
+ * The owner's final value is narrowed to T and written by `emit`.  So for
+ * e in segment c the sum is the left fold along the ring that starts at the
+ * owner's successor c+1 and ends at the owner c. */
+typedef void (*emit_fn)(void* ctx, int q, size_t e, acc_t v);
+
+static int ring_reduce_phase(int R, size_t N, int dtype, const void* send,
+                             emit_fn emit, void* ctx)
+{
+    acc_t* part = NULL; /* part[q*N + e]: the partial rank q holds */
+    if (R > 2) {
+        part = (acc_t*)malloc(sizeof(acc_t) * (size_t)R * (N ? N : 1));
+        if (!part)
+            return ORC_ENOMEM;
+    }
+    for (int s = 0; s <= R - 2; ++s) {
+        for (int q = 0; q < R; ++q) {
+            int c = mod(q - s - 2, R);
+            int p = mod(q - 1, R);
+            size_t lo = seg_lo(N, R, c), hi = seg_hi(N, R, c);
+            for (size_t e = lo; e < hi; ++e) {
+                acc_t in = (s == 0) ? widen(dtype, send, (size_t)p * N + e)
+                                    : part[(size_t)p * N + e];
+                acc_t v = acc_add(dtype, in, widen(dtype, send, (size_t)q * N + e));
+                if (s < R - 2)
+                    part[(size_t)q * N + e] = v;
+                else
+                    emit(ctx, q, e, v); /* here q == c */
+            }
+        }
+    }
+    free(part);
+    return ORC_OK;
+}
+
+/* Ring copy phase: at step s (0..R-2) every rank q copies segment
+ * c = (q - 1 - s) mod R from its predecessor's output into its own.
+ * Rows of y are `row` elements long; segment c of the logical N-element
+ * vector sits at the same offset in every row. */
+static void ring_gather_phase(int R, size_t N, int dtype, void* y, size_t row)
+{
+    int es = elem_size(dtype);
+    for (int s = 0; s <= R - 2; ++s) {
+        for (int q = 0; q < R; ++q) {
+            int c = mod(q - 1 - s, R);
+            int p = mod(q - 1, R);
+            size_t lo = seg_lo(N, R, c), hi = seg_hi(N, R, c);
+            memcpy((char*)y + ((size_t)q * row + lo) * es,
+                   (const char*)y + ((size_t)p * row + lo) * es, (hi - lo) * es);
+        }
+    }
+}
+
+struct emit_ctx {
+    int dtype;
+    void* out;
+    size_t row; /* elements per output row */
+    int R;
+    size_t N;
+};
+
+static void emit_full(void* vctx, int q, size_t e, acc_t v)
+{
+    struct emit_ctx* x = (struct emit_ctx*)vctx;
+    narrow(x->dtype, x->out, (size_t)q * x->row + e, v);
+}
+
+static void emit_shard(void* vctx, int q, size_t e, acc_t v)
+{
+    struct emit_ctx* x = (struct emit_ctx*)vctx;
+    narrow(x->dtype, x->out, (size_t)q * x->row + (e - seg_lo(x->N, x->R, q)), v);
+}
+
+static int check_args(int R, int dtype, const void* a, const void* b)
+{
+    if (R < 2 || R > 4096 || dtype < 0 || dtype > 2 || !a || !b)
+        return ORC_EINVAL;
+    return ORC_OK;
+}
+
+/* All-reduce by ring: reduce phase, the owner writes its final segment into
+ * its own output row, then the copy phase spreads every segment round the
+ * ring.  send and recv are [R][N]. */
+int orc_ring_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    int rc = check_args(R, dtype, send, recv);
+    if (rc)
+        return rc;
+    struct emit_ctx ctx = {dtype, recv, N, R, N};
+    rc = ring_reduce_phase(R, N, dtype, send, emit_full, &ctx);
+    if (rc)
+        return rc;
+    ring_gather_phase(R, N, dtype, recv, N);
+    return ORC_OK;
+}
+
+/* Reduce-scatter by ring: the reduce phase only; rank q's output is its own
+ * segment q, of length N/R.  send is [R][N], recv is [R][N/R]. */
+int orc_ring_reduce_scatter(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    int rc = check_args(R, dtype, send, recv);
+    if (rc)
+        return rc;
+    if (N % (size_t)R != 0)
+        return ORC_EINVAL;
+    struct emit_ctx ctx = {dtype, recv, N / (size_t)R, R, N};
+    return ring_reduce_phase(R, N, dtype, send, emit_shard, &ctx);
+}
+
+/* All-gather by ring: rank q first places its own shard at position q of its
+ * output, then the copy phase runs.  send is [R][n], recv is [R][R*n]. */
+int orc_ring_all_gather(int R, size_t n, int dtype, const void* send, void* recv)
+{
+    int rc = check_args(R, dtype, send, recv);
+    if (rc)
+        return rc;
+    int es = elem_size(dtype);
+    size_t N = n * (size_t)R;
+    for (int q = 0; q < R; ++q)
+        memcpy((char*)recv + ((size_t)q * N + (size_t)q * n) * es,
+               (const char*)send + (size_t)q * n * es, n * es);
+    ring_gather_phase(R, N, dtype, recv, N);
+    return ORC_OK;
+}
+
+/* ---- double binary tree ---------------------------------------------- */
+
+/* Tree A: the in-order binary tree on 0..R-1 rooted at 0.  For r >= 1 with
+ * lowest set bit b, r's parent is r-b when bit 2b of r is set, else r+b when
+ * that is a rank, else r-b.  Rank 0's only child is the largest power of two
+ * below R; odd ranks are leaves. */
+static int tree_a_parent(int R, int r)
+{
+    if (r == 0)
+        return -1;
+    int b = r & -r;
+    if (r & (2 * b))
+        return r - b;
+    if (r + b < R)
+        return r + b;
+    return r - b;
+}
+
+/* Parent of rank r in tree 0 (A) or tree 1 (B); -1 for the root.  Tree B is
+ * tree A relabelled by r -> R-1-r (even R) or r -> (r+1) mod R (odd R). */
+int orc_tree_parent(int R, int tree, int r)
+{
+    if (R < 2 || r < 0 || r >= R || tree < 0 || tree > 1)
+        return -2;
+    if (tree == 0)
+        return tree_a_parent(R, r);
+    if (R % 2 == 0) {
+        int p = tree_a_parent(R, R - 1 - r);
+        return p < 0 ? -1 : R - 1 - p;
+    }
+    int p = tree_a_parent(R, mod(r - 1, R));
+    return p < 0 ? -1 : mod(p + 1, R);
+}
+
+/* Subtree sum of v for element e: own input first, then each child's
+ * subtree sum in ascending rank order. */
+static acc_t tree_fold(int R, const int* parent, int dtype, const void* send,
+                       size_t N, int v, size_t e)
+{
+    acc_t p = widen(dtype, send, (size_t)v * N + e);
+    for (int ch = 0; ch < R; ++ch)
+        if (parent[ch] == v)
+            p = acc_add(dtype, p, tree_fold(R, parent, dtype, send, N, ch, e));
+    return p;
+}
+
+/* All-reduce by double binary tree: elements [0, H) go up tree A and back
+ * down, elements [H, N) go through tree B, H = ceil(N/2).  Every rank's
+ * output is the root's sum narrowed to T (the broadcast down is a copy). */
+int orc_tree_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    int rc = check_args(R, dtype, send, recv);
+    if (rc)
+        return rc;
+    int* parent = (int*)malloc(sizeof(int) * 2 * (size_t)R);
+    if (!parent)
+        return ORC_ENOMEM;
+    int root[2] = {-1, -1};
+    for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < R; ++r) {
+            parent[t * R + r] = orc_tree_parent(R, t, r);
+            if (parent[t * R + r] == -1)
+                root[t] = r;
+        }
+    size_t H = (N + 1) / 2;
+    for (size_t e = 0; e < N; ++e) {
+        int t = e < H ? 0 : 1;
+        acc_t sum = tree_fold(R, parent + t * R, dtype, send, N, root[t], e);
+        for (int q = 0; q < R; ++q)
+            narrow(dtype, recv, (size_t)q * N + e, sum);
+    }
+    free(parent);
+    return ORC_OK;
+}
+
+/* ---- plain definition, in double ------------------------------------- */
+
+/* out[e] = sum over ranks of x_r[e], added in float64 in rank order.  For
+ * R <= 4096 float32 inputs this is the exact sum to far better than the
+ * 1e-6 relative tolerance it is used with (and exact for int32). */
+int orc_exact_sum(int R, size_t N, int dtype, const void* send, double* out)
+{
+    int rc = check_args(R, dtype, send, out);
+    if (rc)
+        return rc;
+    for (size_t e = 0; e < N; ++e) {
+        double s = 0.0;
+        for (int r = 0; r < R; ++r) {
+            acc_t a = widen(dtype, send, (size_t)r * N + e);
+            s += dtype == ORC_INT32 ? (double)(int32_t)a.u : (double)a.f;
+        }
+        out[e] = s;
+    }
+    return ORC_OK;
+}
