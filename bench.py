@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring all-reduce over R logical ranks in one MI355X's HBM.
+
+Default run (one JSON line on stdout): ring all-reduce (sum), R = 8 logical
+ranks, float32, 16,777,216 elements (64 MiB) per rank, N(0,1) inputs from
+seed 2, simple protocol, 512 KiB chunks.  One step = one all-reduce of the
+whole [8, 16M] buffer, inputs resident in HBM before the timed region.
+
+  value  = busBW = algBW * 2(R-1)/R,  algBW = per-rank bytes / time
+  roofline.achieved = algorithmic HBM bytes 5(R-1) N s / kernel time
+
+Other modes (--mode): sweep (8 B .. 1 GiB per rank, alpha-beta fit),
+tree-vs-ring (8 B .. 256 KiB), buckets (R = 16 bf16 reduce-scatter then
+all-gather, 40 x 25 MiB), stream (c = a + b and copy reference kernels).
+They write JSON lines to --out and a summary line to stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "all-reduce busBW GB/s + HBM GB/s vs peak, R=8 fp32 64 MiB/rank, 1 GPU"
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["collective_communication_ring_amd/csrc/ar_ring.hip",
+                  "collective_communication_ring_amd/csrc/ar_elem.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(key)
+    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, torch):
+    """Run fn warmup times, then time `steps` back-to-back calls with events
+    on the current stream.  Returns (per-call ms list, total ms, wall s)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[steps]), wall
+
+
+def cpu_baseline(x, R, N, s, target_s=12.0):
+    """The oracle, as it is, on the host: repeat the full all-reduce until
+    about target_s seconds of CPU work; report its busBW."""
+    import oracle
+    ts = []
+    y = None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        y = oracle.ring_allreduce(x)
+        ts.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > target_s or len(ts) >= 20:
+            break
+    t = sum(ts) / len(ts)
+    algbw = N * s / t / 1e9
+    return y, dict(value=round(algbw * 2 * (R - 1) / R, 3), unit="GB/s", cores=1, kind="oracle",
+                   sample="the full workload (8 ranks x 64 MiB), %d call(s), %.2f s each; "
+                          "single-threaded C replay of the same ring order" % (len(ts), t))
+
+
+def headline(args):
+    import numpy as np
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+
+    R, N, s = 8, 16_777_216, 4
+    dev = torch.device("cuda:0")
+    x = inputs.host_inputs("ring_f32_r8_64MiB")
+    send = torch.from_numpy(x).to(dev)
+    recv = torch.empty_like(send)
+    comm = api.Comm(R, N, "float32", "ring", "simple", device=dev, launch=args.launch,
+                    chunk_bytes=512 * 1024, grid=args.grid)
+    _, _, launch = comm.plan(N)
+    launch_name = {v: k for k, v in api.LAUNCHES.items()}[launch]
+    per, total_ms, wall = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
+                                     torch)
+    assert comm.check() == api.AR_SUCCESS
+    ms = total_ms / args.steps
+    t = ms / 1e3
+    algbw = N * s / t / 1e9
+    busbw = algbw * measure.busbw_factor("allreduce", R)
+    b_alg = measure.allreduce_alg_bytes(R, N, s)
+    kernel_ms = sum(per) / len(per)
+    achieved = b_alg / (kernel_ms / 1e3) / 1e9
+    kernel = {"fused": "k_ring_fused<float32, 16-byte slots, all-reduce>",
+              "step": "k_ring_reduce_step + k_ring_copy_step (2(R-1) launches)"}[launch_name]
+    traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name)
+    line = {
+        "metric": METRIC,
+        "value": round(busbw, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "ring all-reduce (sum), R=8 logical ranks, fp32, 16,777,216 "
+                               "elements (64 MiB) per rank, N(0,1) seed 2, simple protocol, "
+                               "512 KiB chunks",
+                   "R": R, "count_per_rank": N, "launch": launch_name},
+        "algbw_GBps": round(algbw, 3),
+        "busbw_GBps": round(busbw, 3),
+        "hbm_alg_GBps": round(b_alg / t / 1e9, 3),
+        "hbm_alg_frac_of_peak": round(b_alg / t / 1e9 / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": b_alg
+                     if launch_name == "fused" else None},
+        "wall_s_timed": round(wall, 4),
+    }
+    y = None
+    if not args.no_cpu_baseline:
+        y, line["cpu_baseline"] = cpu_baseline(x, R, N, s)
+    else:
+        line["cpu_baseline"] = None
+    if y is not None:
+        got = recv.cpu().numpy()
+        line["verified_vs_oracle"] = bool(got.tobytes() == y.tobytes())
+        if not line["verified_vs_oracle"]:
+            log("ERROR: GPU result differs from the oracle")
+    print(json.dumps(line), flush=True)
+    return 0 if line.get("verified_vs_oracle", True) else 1
+
+
+def mode_sweep(args):
+    """Config 3: ring all-reduce, R = 8, fp32, 8 B .. 1 GiB per rank in powers
+    of two, 5 warm-up + 20 timed calls each; alpha-beta fit."""
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+    R, s = 8, 4
+    dev = torch.device("cuda:0")
+    max_bytes = args.max_bytes
+    counts = inputs.sweep_counts(8, max_bytes, s)
+    Nmax = counts[-1]
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    # flat buffers: the first R*N elements viewed as [R, N] are rank-major
+    send_flat = torch.randn(R * Nmax, generator=g, device=dev, dtype=torch.float32)
+    recv_flat = torch.empty_like(send_flat)
+    comm = api.Comm(R, Nmax, "float32", "ring", "simple", device=dev, launch=args.launch,
+                    chunk_bytes=512 * 1024, grid=args.grid)
+    rows = []
+    out = open(args.out, "w") if args.out else None
+    for N in counts:
+        sv = send_flat[:R * N].view(R, N)
+        rv = recv_flat[:R * N].view(R, N)
+        per, total_ms, _ = time_calls(lambda: comm.allreduce(sv, rv), 20, 5, torch)
+        t = total_ms / 20 / 1e3
+        row = dict(mode="sweep", bytes_per_rank=N * s, count=N, t_us=t * 1e6,
+                   algbw_GBps=N * s / t / 1e9,
+                   busbw_GBps=N * s / t / 1e9 * measure.busbw_factor("allreduce", R),
+                   hbm_alg_GBps=measure.allreduce_alg_bytes(R, N, s) / t / 1e9,
+                   launch=args.launch)
+        rows.append(row)
+        log("sweep %10d B/rank  %10.2f us  busBW %8.2f GB/s" % (N * s, t * 1e6, row["busbw_GBps"]))
+        if out:
+            out.write(json.dumps(row) + "\n")
+            out.flush()
+        del sv, rv
+    assert comm.check() == api.AR_SUCCESS
+    fit = measure.fit_alpha_beta([r["bytes_per_rank"] for r in rows], [r["t_us"] / 1e6 for r in rows])
+    small = [r["t_us"] for r in rows if r["bytes_per_rank"] <= 4096]
+    large = [r for r in rows if r["bytes_per_rank"] >= 64 << 20]
+    cross = {}
+    if small:
+        cross["alpha_median_small_us"] = sorted(small)[len(small) // 2]
+    if len(large) >= 2:
+        a, b = large[0], large[-1]
+        cross["inv_beta_large_GBps"] = (b["bytes_per_rank"] - a["bytes_per_rank"]) / (
+            (b["t_us"] - a["t_us"]) / 1e6) / 1e9
+    summary = dict(mode="sweep_fit", R=R, dtype="f32", launch=args.launch, **fit,
+                   bus_rate_GBps=fit["inv_beta_GBps"] * measure.busbw_factor("allreduce", R),
+                   **cross)
+    if out:
+        out.write(json.dumps(summary) + "\n")
+        out.close()
+    print(json.dumps(summary), flush=True)
+    return 0
+
+
+def mode_tree_vs_ring(args):
+    """Config 4: R = 8, fp32 U[-1,1), 8 B .. 256 KiB per rank; tree + LL
+    against ring (fused and step) at the same sizes."""
+    import torch
+    from collective_communication_ring_amd import api, inputs
+    R, s = 8, 4
+    dev = torch.device("cuda:0")
+    counts = inputs.sweep_counts(8, 256 * 1024, s)
+    Nmax = counts[-1]
+    x = inputs.draw("uniform_pm1", R, Nmax, seed=4)
+    send_flat = torch.from_numpy(x).to(dev).reshape(-1)
+    recv_flat = torch.empty_like(send_flat)
+    variants = [("tree-ll", dict(algo="tree", proto="ll")),
+                ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
+                ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
+    comms = {name: api.Comm(R, Nmax, "float32", device=dev, **kw) for name, kw in variants}
+    out = open(args.out, "w") if args.out else None
+    res = {}
+    for N in counts:
+        sv = send_flat[:R * N].view(R, N)
+        rv = recv_flat[:R * N].view(R, N)
+        for name, _ in variants:
+            c = comms[name]
+            _, total_ms, _ = time_calls(lambda: c.allreduce(sv, rv), 20, 5, torch)
+            t_us = total_ms / 20 * 1e3
+            res.setdefault(name, []).append(t_us)
+            row = dict(mode="tree_vs_ring", variant=name, bytes_per_rank=N * s, t_us=t_us)
+            log("%-10s %8d B/rank %9.2f us" % (name, N * s, t_us))
+            if out:
+                out.write(json.dumps(row) + "\n")
+    for c in comms.values():
+        assert c.check() == api.AR_SUCCESS
+    summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res)
+    if out:
+        out.write(json.dumps(summary) + "\n")
+        out.close()
+    print(json.dumps(summary), flush=True)
+    return 0
+
+
+def mode_buckets(args):
+    """Config 5: R = 16 bf16 N(0, 0.02), 40 buckets x 13,107,200 elements per
+    rank, reduce-scatter then all-gather per bucket (and all-reduce)."""
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+    w = inputs.WORKLOADS["buckets_bf16_r16"]
+    R, N, B, s = w["R"], w["count"], args.buckets or w["buckets"], 2
+    n = N // R
+    dev = torch.device("cuda:0")
+    xs = [inputs.device_bucket_bf16(R, N, w["seed"], b, dev) for b in range(B)]
+    shards = [torch.empty((R, n), dtype=torch.bfloat16, device=dev) for _ in range(B)]
+    full = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+    comm = api.Comm(R, N, "bf16", "ring", device=dev, launch=args.launch, grid=args.grid)
+
+    def rs_all():
+        for b in range(B):
+            comm.reduce_scatter(xs[b], shards[b])
+
+    def ag_all():
+        for b in range(B):
+            comm.all_gather(shards[b], full)
+
+    def ar_all():
+        for b in range(B):
+            comm.allreduce(xs[b], full)
+
+    rep = {}
+    for name, fn, op, alg in (("reduce_scatter", rs_all, "rs", measure.reduce_scatter_alg_bytes(R, N, s)),
+                              ("all_gather", ag_all, "ag", measure.all_gather_alg_bytes(R, N, s)),
+                              ("allreduce", ar_all, "ar", None)):
+        _, total_ms, _ = time_calls(fn, args.steps, 1, torch)
+        t = total_ms / args.steps / B / 1e3  # per bucket
+        algbw = N * s / t / 1e9
+        f = measure.busbw_factor("allreduce" if op == "ar" else op, R)
+        rep[name] = dict(t_us_per_bucket=t * 1e6, algbw_GBps=algbw, busbw_GBps=algbw * f,
+                         hbm_alg_GBps=(alg / t / 1e9) if alg else None)
+        log(name, rep[name])
+    assert comm.check() == api.AR_SUCCESS
+    summary = dict(mode="buckets", R=R, dtype="bf16", buckets=B, count_per_rank=N, **rep)
+    print(json.dumps(summary), flush=True)
+    return 0
+
+
+def mode_stream(args):
+    """Reference kernels: c = a + b over float32 (the access mix of one reduce
+    step) and a plain copy, each on 512 MiB arrays (larger than the 256 MB
+    infinity cache)."""
+    import torch
+    from collective_communication_ring_amd import api
+    dev = torch.device("cuda:0")
+    n = (512 << 20) // 4
+    a = torch.randn(n, device=dev)
+    b = torch.randn(n, device=dev)
+    c = torch.empty_like(a)
+    st = torch.cuda.current_stream().cuda_stream
+    _, ms, _ = time_calls(lambda: api.ar_stream_add(a.data_ptr(), b.data_ptr(), c.data_ptr(), n, st),
+                          args.steps, args.warmup, torch)
+    add_gbps = 3 * n * 4 / (ms / args.steps / 1e3) / 1e9
+    _, ms2, _ = time_calls(lambda: api.ar_stream_copy(a.data_ptr(), c.data_ptr(), n * 4, st),
+                           args.steps, args.warmup, torch)
+    copy_gbps = 2 * n * 4 / (ms2 / args.steps / 1e3) / 1e9
+    torch.cuda.synchronize()
+    ok = torch.equal(c, a)
+    summary = dict(mode="stream", bytes_per_array=n * 4, add_GBps=add_gbps,
+                   add_frac=add_gbps / PEAK_HBM_GBPS, copy_GBps=copy_gbps,
+                   copy_frac=copy_gbps / PEAK_HBM_GBPS, copy_ok=ok)
+    print(json.dumps(summary), flush=True)
+    return 0
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--launch", default="auto", choices=["auto", "fused", "step", "pipelined"])
+    ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
+    ap.add_argument("--mode", default="headline",
+                    choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream"])
+    ap.add_argument("--max-bytes", type=int, default=1 << 30)
+    ap.add_argument("--buckets", type=int, default=0)
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the R logical ranks of the ring all live in one "
+              "MI355X's HBM, so --gpus must be 1 (got --gpus %d, WORLD_SIZE %d)."
+              % (args.gpus, world), file=sys.stderr)
+        return 2
+    fn = {"headline": headline, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
+          "buckets": mode_buckets, "stream": mode_stream}[args.mode]
+    return fn(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

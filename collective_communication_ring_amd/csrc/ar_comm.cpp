@@ -1,0 +1,636 @@
+// ar_comm.cpp -- host side of libar: communicator, schedule tables,
+// workspace layout, argument checking and dispatch to the HIP kernels.
+//
+// The communicator mirrors NCCL's host pattern: create once, then enqueue
+// collectives on a stream and let the caller synchronize ("NCCL and NVSHMEM
+// -- two GPU communication models, side by side", NCCL host code listing;
+// "NCCL, NIXL, and Distributed GPU Communication", performance checklist on
+// not creating communicators inside loops).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "ar.h"
+#include "ar_internal.h"
+
+using namespace ar;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kDefaultChunkBytes = 512 * 1024;
+constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
+constexpr int64_t kDefaultTreeMaxBytes = 64 * 1024;  // AR_AUTO: tree up to this per rank
+constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int elem_size(int dtype) { return dtype == AR_BF16 ? 2 : 4; }
+
+const char* dtype_name(int d)
+{
+    return d == AR_INT32 ? "int32" : d == AR_FLOAT32 ? "float32" : d == AR_BF16 ? "bf16" : "?";
+}
+const char* launch_name(int l)
+{
+    return l == AR_LAUNCH_STEP ? "step" : l == AR_LAUNCH_FUSED ? "fused"
+         : l == AR_LAUNCH_PIPELINED ? "pipelined" : "auto";
+}
+
+// Tree A: the in-order binary tree on 0..R-1 rooted at 0.  For r >= 1 with
+// lowest set bit b: parent r-b if bit 2b of r is set, else r+b if that is a
+// rank, else r-b.  Tree B is tree A relabelled r -> R-1-r (even R) or
+// r -> (r+1) mod R (odd R), so that the two trees use complementary links
+// ("NCCL and NVSHMEM -- two GPU communication models, side by side", section
+// "double binary tree").
+int tree_a_parent(int R, int r)
+{
+    if (r == 0)
+        return -1;
+    const int b = r & -r;
+    if (r & (2 * b))
+        return r - b;
+    if (r + b < R)
+        return r + b;
+    return r - b;
+}
+
+int tree_parent_of(int R, int tree, int r)
+{
+    if (tree == 0)
+        return tree_a_parent(R, r);
+    if (R % 2 == 0) {
+        const int p = tree_a_parent(R, R - 1 - r);
+        return p < 0 ? -1 : R - 1 - p;
+    }
+    const int p = tree_a_parent(R, (r - 1 + R) % R);
+    return p < 0 ? -1 : (p + 1) % R;
+}
+
+void build_trees(int R, TreeTable* tt)
+{
+    std::memset(tt, 0, sizeof *tt);
+    for (int t = 0; t < 2; ++t) {
+        for (int r = 0; r < R; ++r) {
+            const int p = tree_parent_of(R, t, r);
+            tt->parent[t][r] = (int8_t)p;
+            if (p < 0)
+                tt->root[t] = (int8_t)r;
+        }
+        // children in ascending rank order
+        for (int r = 0; r < R; ++r) {
+            const int p = tt->parent[t][r];
+            if (p >= 0)
+                tt->child[t][p][tt->nchild[t][p]++] = (int8_t)r;
+        }
+    }
+}
+
+int64_t env_int(const char* name, int64_t dflt)
+{
+    const char* s = std::getenv(name);
+    if (!s || !*s)
+        return dflt;
+    return std::strtoll(s, nullptr, 0);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct ar_comm {
+    int R = 0;
+    size_t cap = 0;  // elements per rank row
+    int dtype = AR_FLOAT32;
+    int algo = AR_RING;
+    int proto = AR_SIMPLE;
+    // options
+    int64_t chunk_bytes = kDefaultChunkBytes;
+    int launch = AR_LAUNCH_AUTO;
+    int64_t grid = 0;
+    int64_t timeout_us = kDefaultTimeoutUs;
+    int64_t debug = 0;
+    int64_t tree_max_bytes = kDefaultTreeMaxBytes;
+    // schedule
+    TreeTable tt{};
+    // workspace layout
+    size_t off_part = 0, off_up = 0, off_down = 0, off_flags = 0, ws_need = 0;
+    uint64_t tree_lines = 0;  // lines per (tree, rank)
+    size_t nflags = 0;
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    // device facts, read on first use
+    bool dev_ready = false;
+    int ncu = 0;
+    double ticks_per_us = 100.0;
+    int resident_fused[3][2] = {};
+    int resident_tree[3] = {};
+    // last call
+    hipStream_t last_stream = nullptr;
+    int last_hip = 0;
+};
+
+namespace {
+
+int fail_hip(ar_comm* c, hipError_t e)
+{
+    c->last_hip = (int)e;
+    return AR_ERR_HIP;
+}
+
+int device_ready(ar_comm* c)
+{
+    if (c->dev_ready)
+        return AR_SUCCESS;
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    if (khz > 0)
+        c->ticks_per_us = khz / 1000.0;
+    for (int d = 0; d < 3; ++d) {
+        c->resident_fused[d][0] = resident_ring_fused(d, false);
+        c->resident_fused[d][1] = resident_ring_fused(d, true);
+        c->resident_tree[d] = resident_tree_ll(d);
+        if (c->resident_fused[d][0] <= 0 || c->resident_fused[d][1] <= 0 || c->resident_tree[d] <= 0)
+            return fail_hip(c, hipErrorInvalidDeviceFunction);
+    }
+    c->dev_ready = true;
+    return AR_SUCCESS;
+}
+
+uint64_t timeout_ticks(const ar_comm* c)
+{
+    return (uint64_t)((double)c->timeout_us * c->ticks_per_us);
+}
+
+int resolve_algo(const ar_comm* c, size_t count)
+{
+    if (c->algo != AR_AUTO)
+        return c->algo;
+    return (int64_t)(count * (size_t)elem_size(c->dtype)) <= c->tree_max_bytes ? AR_TREE : AR_RING;
+}
+
+int resolve_launch(const ar_comm* c)
+{
+    if (c->launch != AR_LAUNCH_AUTO)
+        return c->launch;
+    return AR_LAUNCH_FUSED;
+}
+
+// Do the 16-byte vector kernels apply?  Every row start and every segment
+// start must be 16-byte aligned in both T and accumulator units.
+bool vector_ok(const ar_comm* c, const void* send, const void* part, const void* out,
+               uint64_t N, uint64_t S, uint64_t send_row, uint64_t out_row)
+{
+    const uint64_t es = (uint64_t)elem_size(c->dtype);
+    return aligned16(send) && aligned16(part) && aligned16(out) && (N * es) % 16 == 0 &&
+           (S * es) % 16 == 0 && (send_row * es) % 16 == 0 && (out_row * es) % 16 == 0 &&
+           (N * 4) % 16 == 0 && (S * 4) % 16 == 0;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int ring_grid_x(const ar_comm* c, uint64_t S, bool vec)
+{
+    const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
+    const uint64_t slots = (S + V - 1) / V;
+    const uint64_t per_wg = (uint64_t)kBlock * kUnroll;
+    uint64_t need = (slots + per_wg - 1) / per_wg;
+    const int64_t total = c->grid > 0 ? c->grid : (int64_t)c->ncu * 8;
+    uint64_t cap = (uint64_t)std::max<int64_t>(1, total / c->R);
+    need = std::max<uint64_t>(1, std::min(need, cap));
+    return (int)std::min<uint64_t>(need, 65535);
+}
+
+int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
+{
+    const bool vec = vector_ok(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row);
+    const int launch = resolve_launch(c);
+    hipError_t e = hipSuccess;
+    int grid = 0;
+    if (launch == AR_LAUNCH_STEP) {
+        const int gx = ring_grid_x(c, a.S, vec);
+        grid = gx * a.R;
+        int nsteps = 0;
+        if (a.op == kOpAllGather) {
+            e = launch_ring_placement(c->dtype, vec, a, gx, st);
+            nsteps = a.R - 1;
+        } else {
+            nsteps = (a.op == kOpAllReduce) ? 2 * (a.R - 1) : a.R - 1;
+        }
+        for (int s = 0; s < nsteps && e == hipSuccess; ++s) {
+            a.step = s;
+            e = launch_ring_step(c->dtype, vec, a, gx, st);
+        }
+    } else if (launch == AR_LAUNCH_FUSED) {
+        const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
+        const uint64_t tile = (uint64_t)kBlock * kUnroll;
+        const uint64_t tiles = ((a.S + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
+        const int64_t res = c->resident_fused[c->dtype][vec ? 1 : 0];
+        const int64_t want = c->grid > 0 ? c->grid : res;
+        grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
+        e = launch_ring_fused(c->dtype, vec, a, grid, st);
+    } else {
+        return AR_ERR_UNSUPPORTED;
+    }
+    if (c->debug)
+        std::fprintf(stderr,
+                     "ar: ring op=%d R=%d N=%llu dtype=%s launch=%s vec=%d grid=%d\n", a.op, a.R,
+                     (unsigned long long)a.N, dtype_name(c->dtype), launch_name(launch), (int)vec,
+                     grid);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    return AR_SUCCESS;
+}
+
+int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t st)
+{
+    TreeArgs a{};
+    a.send = send;
+    a.out = recv;
+    a.up = reinterpret_cast<uint64_t*>(c->ws + c->off_up);
+    a.down = reinterpret_cast<uint64_t*>(c->ws + c->off_down);
+    a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
+    a.N = N;
+    a.H = (N + 1) / 2;
+    a.R = c->R;
+    a.line_stride = c->tree_lines;
+    a.timeout_ticks = timeout_ticks(c);
+    a.tt = c->tt;
+    // every workgroup must be resident at once: cap the piece accordingly
+    const uint64_t per_wg = (uint64_t)kBlock * kTreeEPT;
+    const int64_t res = c->resident_tree[c->dtype];
+    const int64_t bpr_max = std::max<int64_t>(1, res / (2 * c->R));
+    const uint64_t piece_max = std::min<uint64_t>(c->tree_lines, (uint64_t)bpr_max * per_wg);
+    const uint64_t half = a.H;  // the larger half
+    const uint64_t piece = std::min<uint64_t>(piece_max, std::max<uint64_t>(half, 1));
+    int launches = 0;
+    for (uint64_t lo = 0; lo < half; lo += piece) {
+        a.piece_lo = lo;
+        a.piece_len = piece;
+        const uint64_t plen = std::min<uint64_t>(piece, half - lo);
+        a.blocks_per_rank = (int)((plen + per_wg - 1) / per_wg);
+        const int grid = 2 * c->R * a.blocks_per_rank;
+        if (grid > res)
+            return AR_ERR_INTERNAL;
+        hipError_t e = launch_tree_ll(c->dtype, a, grid, st);
+        if (e != hipSuccess)
+            return fail_hip(c, e);
+        ++launches;
+    }
+    if (c->debug)
+        std::fprintf(stderr, "ar: tree-LL R=%d N=%llu dtype=%s piece=%llu launches=%d\n", c->R,
+                     (unsigned long long)N, dtype_name(c->dtype), (unsigned long long)piece,
+                     launches);
+    return AR_SUCCESS;
+}
+
+// Checks shared by the collectives.  A zero-element call is a successful
+// no-op whatever its pointers (an empty tensor may have a NULL data pointer);
+// it returns AR_SUCCESS through *noop.
+int common_checks(ar_comm* c, const void* send, void* recv, size_t n, bool* noop)
+{
+    *noop = false;
+    if (!c)
+        return AR_ERR_INVALID_ARG;
+    if (!c->ws)
+        return AR_ERR_INVALID_USAGE;
+    if (n == 0) {
+        *noop = true;
+        return AR_SUCCESS;
+    }
+    if (!send || !recv)
+        return AR_ERR_INVALID_ARG;
+    return device_ready(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t algo,
+            ar_proto_t proto)
+{
+    if (!out)
+        return AR_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (R < 2 || R > kMaxRanks)
+        return AR_ERR_INVALID_ARG;
+    if (dtype != AR_INT32 && dtype != AR_FLOAT32 && dtype != AR_BF16)
+        return AR_ERR_INVALID_ARG;
+    if (algo != AR_RING && algo != AR_TREE && algo != AR_AUTO)
+        return AR_ERR_INVALID_ARG;
+    if (proto != AR_SIMPLE && proto != AR_LL)
+        return AR_ERR_INVALID_ARG;
+    if (count > ((size_t)1 << 40))
+        return AR_ERR_INVALID_ARG;
+    ar_comm* c = new (std::nothrow) ar_comm();
+    if (!c)
+        return AR_ERR_INTERNAL;
+    c->R = R;
+    c->cap = count;
+    c->dtype = dtype;
+    c->algo = algo;
+    c->proto = proto;
+    c->chunk_bytes = env_int("AR_CHUNK_BYTES", kDefaultChunkBytes);
+    c->timeout_us = env_int("AR_TIMEOUT_US", kDefaultTimeoutUs);
+    c->debug = env_int("AR_DEBUG", 0);
+    const char* l = std::getenv("AR_LAUNCH");
+    if (l && !std::strcmp(l, "step"))
+        c->launch = AR_LAUNCH_STEP;
+    else if (l && !std::strcmp(l, "fused"))
+        c->launch = AR_LAUNCH_FUSED;
+    else if (l && !std::strcmp(l, "pipelined"))
+        c->launch = AR_LAUNCH_PIPELINED;
+    build_trees(R, &c->tt);
+    // workspace: control block | partial sums [R][cap] (A) | tree LL up | down
+    const size_t cap1 = count ? count : 1;
+    c->tree_lines = std::min<uint64_t>((cap1 + 1) / 2, kTreeLinesCap);
+    size_t off = kAlign;  // control block
+    c->off_part = off;
+    off = align_up(off + (size_t)R * cap1 * 4, kAlign);
+    c->off_up = off;
+    off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
+    c->off_down = off;
+    off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
+    c->off_flags = off;
+    c->nflags = 0;
+    c->ws_need = off;
+    *out = c;
+    return AR_SUCCESS;
+}
+
+int ar_destroy(ar_comm_t c)
+{
+    delete c;
+    return AR_SUCCESS;
+}
+
+size_t ar_workspace_bytes(ar_comm_t c) { return c ? c->ws_need : 0; }
+
+int ar_set_workspace(ar_comm_t c, void* dev, size_t bytes, void* stream)
+{
+    if (!c || !dev || bytes < c->ws_need || ((uintptr_t)dev % kAlign) != 0)
+        return AR_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->ws = static_cast<char*>(dev);
+    c->ws_bytes = bytes;
+    // clear the control block and every LL line (flag 0 never matches an epoch)
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws), 0u, kCtrlWords, st);
+    if (e == hipSuccess)
+        e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,
+                            (c->off_flags - c->off_up) / sizeof(uint64_t), st);
+    if (e != hipSuccess) {
+        c->ws = nullptr;
+        return fail_hip(c, e);
+    }
+    c->last_stream = st;
+    return AR_SUCCESS;
+}
+
+int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* stream)
+{
+    bool noop = false;
+    int rc = common_checks(c, send, recv, count, &noop);
+    if (rc || noop)
+        return rc;
+    if (count > c->cap)
+        return AR_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)c->R * count * elem_size(c->dtype);
+    if (count && overlaps(send, bytes, recv, bytes))
+        return AR_ERR_INVALID_USAGE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    if (count == 0)
+        return AR_SUCCESS;
+    const int algo = resolve_algo(c, count);
+    if (algo == AR_TREE)
+        return run_tree(c, send, recv, count, st);
+    if (c->proto == AR_LL)
+        return AR_ERR_UNSUPPORTED;
+    RingArgs a{};
+    a.send = send;
+    // partial sums live in recv when the accumulator is the element type
+    a.part = (c->dtype == AR_BF16) ? (void*)(c->ws + c->off_part) : recv;
+    a.out = recv;
+    a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
+    a.N = count;
+    a.S = (count + c->R - 1) / c->R;
+    a.send_row = count;
+    a.out_row = count;
+    a.R = c->R;
+    a.op = kOpAllReduce;
+    a.timeout_ticks = timeout_ticks(c);
+    return run_ring(c, a, st);
+}
+
+int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcount, void* stream)
+{
+    bool noop = false;
+    int rc = common_checks(c, send, recv, recvcount, &noop);
+    if (rc || noop)
+        return rc;
+    const size_t N = recvcount * (size_t)c->R;
+    if (N > c->cap)
+        return AR_ERR_INVALID_ARG;
+    const size_t es = elem_size(c->dtype);
+    if (N && overlaps(send, (size_t)c->R * N * es, recv, N * es))
+        return AR_ERR_INVALID_USAGE;
+    if (c->algo == AR_TREE || c->proto == AR_LL)
+        return AR_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    if (N == 0)
+        return AR_SUCCESS;
+    RingArgs a{};
+    a.send = send;
+    a.part = c->ws + c->off_part;
+    a.out = recv;
+    a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
+    a.N = N;
+    a.S = recvcount;
+    a.send_row = N;
+    a.out_row = recvcount;
+    a.R = c->R;
+    a.op = kOpReduceScatter;
+    a.timeout_ticks = timeout_ticks(c);
+    return run_ring(c, a, st);
+}
+
+int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, void* stream)
+{
+    bool noop = false;
+    int rc = common_checks(c, send, recv, sendcount, &noop);
+    if (rc || noop)
+        return rc;
+    const size_t N = sendcount * (size_t)c->R;
+    if (N > c->cap)
+        return AR_ERR_INVALID_ARG;
+    const size_t es = elem_size(c->dtype);
+    if (N && overlaps(send, N * es, recv, (size_t)c->R * N * es))
+        return AR_ERR_INVALID_USAGE;
+    if (c->algo == AR_TREE || c->proto == AR_LL)
+        return AR_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    if (N == 0)
+        return AR_SUCCESS;
+    RingArgs a{};
+    a.send = send;
+    a.part = c->ws + c->off_part;  // unused by copies; keeps the alignment check uniform
+    a.out = recv;
+    a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
+    a.N = N;
+    a.S = sendcount;
+    a.send_row = sendcount;
+    a.out_row = N;
+    a.R = c->R;
+    a.op = kOpAllGather;
+    a.timeout_ticks = timeout_ticks(c);
+    return run_ring(c, a, st);
+}
+
+int ar_check(ar_comm_t c)
+{
+    if (!c)
+        return AR_ERR_INVALID_ARG;
+    if (!c->ws)
+        return AR_SUCCESS;
+    hipError_t e = hipStreamSynchronize(c->last_stream);
+    uint32_t word = 0;
+    if (e == hipSuccess)
+        e = hipMemcpy(&word, c->ws + kCtrlError * sizeof(uint32_t), sizeof word,
+                      hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    if (word == 0)
+        return AR_SUCCESS;
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws) + kCtrlError, 0u, 1, c->last_stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(c->last_stream);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    return AR_ERR_TIMEOUT;
+}
+
+int ar_set_option(ar_comm_t c, int option, int64_t v)
+{
+    if (!c)
+        return AR_ERR_INVALID_ARG;
+    switch (option) {
+    case AR_OPT_CHUNK_BYTES:
+        if (v < 0)
+            return AR_ERR_INVALID_ARG;
+        c->chunk_bytes = v;
+        return AR_SUCCESS;
+    case AR_OPT_LAUNCH:
+        if (v < AR_LAUNCH_AUTO || v > AR_LAUNCH_PIPELINED)
+            return AR_ERR_INVALID_ARG;
+        c->launch = (int)v;
+        return AR_SUCCESS;
+    case AR_OPT_GRID:
+        if (v < 0 || v > (1 << 20))
+            return AR_ERR_INVALID_ARG;
+        c->grid = v;
+        return AR_SUCCESS;
+    case AR_OPT_TIMEOUT_US:
+        if (v <= 0)
+            return AR_ERR_INVALID_ARG;
+        c->timeout_us = v;
+        return AR_SUCCESS;
+    case AR_OPT_DEBUG:
+        c->debug = v;
+        return AR_SUCCESS;
+    case AR_OPT_ALGO:
+        if (v != AR_RING && v != AR_TREE && v != AR_AUTO)
+            return AR_ERR_INVALID_ARG;
+        c->algo = (int)v;
+        return AR_SUCCESS;
+    case AR_OPT_PROTO:
+        if (v != AR_SIMPLE && v != AR_LL)
+            return AR_ERR_INVALID_ARG;
+        c->proto = (int)v;
+        return AR_SUCCESS;
+    case AR_OPT_TREE_MAX_BYTES:
+        if (v < 0)
+            return AR_ERR_INVALID_ARG;
+        c->tree_max_bytes = v;
+        return AR_SUCCESS;
+    }
+    return AR_ERR_INVALID_ARG;
+}
+
+int ar_get_option(ar_comm_t c, int option, int64_t* v)
+{
+    if (!c || !v)
+        return AR_ERR_INVALID_ARG;
+    switch (option) {
+    case AR_OPT_CHUNK_BYTES: *v = c->chunk_bytes; return AR_SUCCESS;
+    case AR_OPT_LAUNCH: *v = c->launch; return AR_SUCCESS;
+    case AR_OPT_GRID: *v = c->grid; return AR_SUCCESS;
+    case AR_OPT_TIMEOUT_US: *v = c->timeout_us; return AR_SUCCESS;
+    case AR_OPT_DEBUG: *v = c->debug; return AR_SUCCESS;
+    case AR_OPT_ALGO: *v = c->algo; return AR_SUCCESS;
+    case AR_OPT_PROTO: *v = c->proto; return AR_SUCCESS;
+    case AR_OPT_TREE_MAX_BYTES: *v = c->tree_max_bytes; return AR_SUCCESS;
+    }
+    return AR_ERR_INVALID_ARG;
+}
+
+int ar_plan(ar_comm_t c, size_t count, int* algo, int* proto, int* launch)
+{
+    if (!c || !algo || !proto || !launch)
+        return AR_ERR_INVALID_ARG;
+    *algo = resolve_algo(c, count);
+    *proto = (*algo == AR_TREE) ? AR_LL : c->proto;
+    *launch = (*algo == AR_TREE) ? AR_LAUNCH_AUTO : resolve_launch(c);
+    return AR_SUCCESS;
+}
+
+int ar_ring_segment(ar_comm_t c, size_t count, int seg, size_t* lo, size_t* hi)
+{
+    if (!c || !lo || !hi || seg < 0 || seg >= c->R)
+        return AR_ERR_INVALID_ARG;
+    const size_t S = (count + c->R - 1) / c->R;
+    *lo = std::min(count, (size_t)seg * S);
+    *hi = std::min(count, (size_t)(seg + 1) * S);
+    return AR_SUCCESS;
+}
+
+int ar_tree_parent(ar_comm_t c, int tree, int r)
+{
+    if (!c || tree < 0 || tree > 1 || r < 0 || r >= c->R)
+        return -2;
+    return c->tt.parent[tree][r];
+}
+
+const char* ar_status_string(int s)
+{
+    switch (s) {
+    case AR_SUCCESS: return "success";
+    case AR_ERR_INVALID_ARG: return "invalid argument";
+    case AR_ERR_INVALID_USAGE: return "invalid usage";
+    case AR_ERR_UNSUPPORTED: return "unsupported";
+    case AR_ERR_HIP: return "HIP runtime error";
+    case AR_ERR_TIMEOUT: return "timeout (a bounded wait expired)";
+    case AR_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+int ar_last_hip_error(ar_comm_t c) { return c ? c->last_hip : 0; }
+
+}  // extern "C"

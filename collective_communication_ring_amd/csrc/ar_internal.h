@@ -1,0 +1,102 @@
+// ar_internal.h -- definitions shared by the host side (ar_comm.cpp) and the
+// HIP kernels (ar_ring.hip, ar_tree.hip) of libar.  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace ar {
+
+constexpr int kMaxRanks = 64;
+
+// Words of the control block at the start of the workspace (uint32 each).
+enum CtrlWord {
+    kCtrlTreeEpoch = 0,   // LL flag value of the last completed tree call
+    kCtrlError = 1,       // non-zero: a bounded wait expired (watchdog)
+    kCtrlTreeDone = 2,    // workgroups of the running tree call that finished
+    kCtrlPipeBase = 3,    // pipelined ring: flag value every chunk holds between calls
+    kCtrlPipeDone = 4,    // workgroups of the running pipelined call that finished
+    kCtrlRingLLEpoch = 5, // LL flag value of the last completed ring-LL call
+    kCtrlRingLLDone = 6,
+    kCtrlWords = 64       // 256 bytes
+};
+
+enum ErrorBits : uint32_t {
+    kErrTimeout = 1u,
+};
+
+enum Op { kOpAllReduce = 0, kOpReduceScatter = 1, kOpAllGather = 2 };
+
+// Double binary tree: per tree, per rank, the parent and up to two children
+// (ascending), plus the root.  Built on the host, passed by value.
+struct TreeTable {
+    int8_t parent[2][kMaxRanks];
+    int8_t child[2][kMaxRanks][2];
+    int8_t nchild[2][kMaxRanks];
+    int8_t root[2];
+};
+
+// Arguments of one ring collective, shared by every ring launch mode.
+//   send : [R][send_row] elements of T
+//   part : [R][N] accumulators (A); equals recv when A == T for all-reduce
+//   out  : [R][out_row] elements of T
+// Segment c of the N-element vector is [min(c*S, N), min((c+1)*S, N)).
+struct RingArgs {
+    const void* send;
+    void* part;
+    void* out;
+    uint32_t* ctrl;   // control block
+    uint32_t* flags;  // pipelined ring: one flag per chunk
+    uint64_t N;       // logical elements per rank (all-reduce count; RS input row; AG output row)
+    uint64_t S;       // segment length, ceil(N / R)
+    uint64_t send_row;
+    uint64_t out_row;
+    uint64_t chunk;   // pipelined ring: elements per chunk (multiple of the vector width)
+    uint64_t nchunks; // pipelined ring: chunks per segment
+    int R;
+    int op;           // Op
+    int step;         // step-per-launch mode: the step this launch runs
+    int per_rank_wg;  // pipelined ring: workgroups per logical rank
+    uint64_t timeout_ticks;
+};
+
+struct TreeArgs {
+    const void* send;
+    void* out;
+    uint64_t* up;     // [2 trees][R][piece_half] LL lines, child -> parent
+    uint64_t* down;   // [2 trees][R][piece_half] LL lines, parent -> child
+    uint32_t* ctrl;
+    uint64_t N;
+    uint64_t H;       // tree A's half: [0, H); tree B: [H, N)
+    uint64_t piece_lo;   // this launch covers [piece_lo, piece_lo + piece_len) of each half
+    uint64_t piece_len;
+    uint64_t line_stride; // lines per (tree, rank) in up/down
+    int R;
+    int blocks_per_rank;  // workgroups per (tree, rank)
+    uint64_t timeout_ticks;
+    TreeTable tt;
+};
+
+// Launchers (ar_ring.hip / ar_tree.hip).  Return hipSuccess or the error.
+hipError_t launch_ring_step(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
+hipError_t launch_ring_pipelined(int dtype, bool vec, const RingArgs& a, hipStream_t s);
+hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
+
+// Largest number of workgroups of each persistent kernel that can be
+// resident at once on the current device (0 on error).
+int resident_ring_fused(int dtype, bool vec);
+int resident_ring_pipelined(int dtype, bool vec);
+int resident_tree_ll(int dtype);
+
+constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
+constexpr int kUnroll = 4;       // 16-byte vectors per thread per pass
+constexpr int kTreeEPT = 4;      // LL lines per thread per tree kernel pass
+
+}  // namespace ar

@@ -1,0 +1,458 @@
+// ar_ring.hip -- ring all-reduce / reduce-scatter / all-gather kernels for
+// gfx950 (MI355X).
+//
+// The ring takes 2(R-1) steps ("GPU MODE lecture 68 notes", section 05,
+// "SHARP -- in-network reduction").  Reading used here: R-1 reduce steps,
+// then R-1 copy steps, around the ring q -> q+1.  Rank c owns segment c.
+//   reduce step s (0..R-2), rank q, segment c = (q-s-2) mod R:
+//       acc_q = (s == 0 ? x_{q-1} : acc_{q-1}) + x_q   over segment c;
+//       at s = R-2 (q == c) the result is final and is written as T.
+//   copy step s (0..R-2), rank q, segment c = (q-1-s) mod R:
+//       y_q = y_{q-1} over segment c.
+// So an element of segment c is the left fold x_{c+1} + x_{c+2} + ... + x_c.
+//
+// All R logical ranks live in one HBM: rank q's buffers are row q of
+// rank-major arrays, and "receiving from q-1" is reading row q-1 in place
+// (the symmetric-heap idea of a remote address being a base plus the local
+// offset: "Demystifying NVSHMEM ..." summary, paragraph on the symmetric
+// heap).  Every step is a reduce-copy of two 16-byte vector loads and one
+// 16-byte store per slot (a copy step: one load, one store); there is no
+// MFMA because nothing here is a contraction.
+//
+// Two launch forms live in this file:
+//   step  -- one launch per step over all R ranks; the kernel boundary
+//            orders the steps.
+//   fused -- one persistent launch; a workgroup takes a tile of a segment
+//            through all 2(R-1) steps in order.  Each thread touches the same
+//            element positions at every step, so the value it stored for rank
+//            q is the one it loads back as rank q+1's input (same-thread
+//            program order; the compiler is kept from forwarding it in
+//            registers, so every step really reads rank q's row).  Tiles of a
+//            step are independent, so there are no flags and no fences; the
+//            partial a step writes is still hot in this XCD's L2 when the
+//            next step reads it.
+#include "ar_elem.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+// Reduce kUnroll slots j0 + u*jstep (u < kUnroll) of one segment of length
+// len.  FIRST: the received value comes from the predecessor's input (T);
+// else from its accumulator row (A).  LAST: the result is final and is
+// narrowed to T; else it is this rank's accumulator.
+template <class E, int V, bool FIRST, bool LAST>
+__device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
+                                    const typename E::A* __restrict__ prevA,
+                                    const typename E::T* __restrict__ own,
+                                    typename E::A* __restrict__ dstA,
+                                    typename E::T* __restrict__ dstT, uint64_t len, uint64_t j0,
+                                    uint64_t jstep)
+{
+    using A = typename E::A;
+    A x[kUnroll][V], y[kUnroll][V];
+    if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
+        // every slot is whole: straight-line code, all loads in flight at once
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            if constexpr (FIRST)
+                load_t<E, V>(prevT + j * V, x[u]);
+            else
+                load_a<E, V>(prevA + j * V, x[u]);
+            load_t<E, V>(own + j * V, y[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                x[u][i] = E::add(x[u][i], y[u][i]);
+            if constexpr (LAST)
+                store_t<E, V>(dstT + j * V, x[u]);
+            else
+                store_a<E, V>(dstA + j * V, x[u]);
+        }
+        return;
+    }
+    // the end of a segment: whole slots, then the ragged last slot element by
+    // element
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * jstep;
+        if ((j + 1) * V <= len) {
+            if constexpr (FIRST)
+                load_t<E, V>(prevT + j * V, x[0]);
+            else
+                load_a<E, V>(prevA + j * V, x[0]);
+            load_t<E, V>(own + j * V, y[0]);
+#pragma unroll
+            for (int i = 0; i < V; ++i)
+                x[0][i] = E::add(x[0][i], y[0][i]);
+            if constexpr (LAST)
+                store_t<E, V>(dstT + j * V, x[0]);
+            else
+                store_a<E, V>(dstA + j * V, x[0]);
+        } else if (j * V < len) {
+            for (uint64_t e = j * V; e < len; ++e) {
+                A xv = FIRST ? E::widen(prevT[e]) : prevA[e];
+                A r = E::add(xv, E::widen(own[e]));
+                if constexpr (LAST)
+                    dstT[e] = E::narrow(r);
+                else
+                    dstA[e] = r;
+            }
+        }
+    }
+}
+
+// Copy kUnroll slots of T from src to dst (bit copy).
+template <class E, int V>
+__device__ inline void copy_slots(const typename E::T* __restrict__ src,
+                                  typename E::T* __restrict__ dst, uint64_t len, uint64_t j0,
+                                  uint64_t jstep)
+{
+    if constexpr (V == 1) {
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            if (j < len)
+                dst[j] = src[j];
+        }
+    } else {
+        if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
+            u32x4 r[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                r[u] = *reinterpret_cast<const u32x4*>(src + (j0 + (uint64_t)u * jstep) * V);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                *reinterpret_cast<u32x4*>(dst + (j0 + (uint64_t)u * jstep) * V) = r[u];
+            return;
+        }
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            if ((j + 1) * V <= len) {
+                *reinterpret_cast<u32x4*>(dst + j * V) = *reinterpret_cast<const u32x4*>(src + j * V);
+            } else if (j * V < len) {
+                for (uint64_t e = j * V; e < len; ++e)
+                    dst[e] = src[e];
+            }
+        }
+    }
+}
+
+// Row pointers of reduce step s for rank q, segment c = (q-s-2) mod R.
+template <class E>
+struct ReducePtrs {
+    const typename E::T* prevT;
+    const typename E::A* prevA;
+    const typename E::T* own;
+    typename E::A* dstA;
+    typename E::T* dstT;
+};
+
+template <class E>
+__device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uint64_t lo)
+{
+    using T = typename E::T;
+    using A = typename E::A;
+    const int p = mod_r(q - 1, a.R);
+    ReducePtrs<E> r;
+    const T* send = static_cast<const T*>(a.send);
+    A* part = static_cast<A*>(a.part);
+    T* out = static_cast<T*>(a.out);
+    r.prevT = send + (uint64_t)p * a.send_row + lo;
+    r.prevA = part + (uint64_t)p * a.N + lo;
+    r.own = send + (uint64_t)q * a.send_row + lo;
+    r.dstA = part + (uint64_t)q * a.N + lo;
+    // the final value (q == c): all-reduce writes it in place in the full
+    // row; reduce-scatter writes it at the start of rank c's shard row
+    r.dstT = out + (uint64_t)q * a.out_row + (a.op == kOpReduceScatter ? 0 : lo);
+    return r;
+}
+
+template <class E, int V>
+__device__ inline void reduce_step_slots(const ReducePtrs<E>& p, int s, int R, uint64_t len,
+                                         uint64_t j0, uint64_t jstep)
+{
+    const bool first = (s == 0), last = (s == R - 2);
+    if (first && last)
+        reduce_slots<E, V, true, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+    else if (first)
+        reduce_slots<E, V, true, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+    else if (last)
+        reduce_slots<E, V, false, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+    else
+        reduce_slots<E, V, false, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+}
+
+// ---- one launch per step --------------------------------------------------
+
+// grid = (gx, R): blockIdx.y is the logical rank.
+template <int DT, int V>
+__global__ __launch_bounds__(kBlock) void k_ring_reduce_step(RingArgs a)
+{
+    using E = Elem<DT>;
+    const int q = blockIdx.y;
+    const int s = a.step;
+    const int c = mod_r(q - s - 2, a.R);
+    const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+    const uint64_t len = hi - lo;
+    const uint64_t nslots = (len + V - 1) / V;
+    const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
+    for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nslots;
+         j0 += stride)
+        reduce_step_slots<E, V>(p, s, a.R, len, j0, kBlock);
+}
+
+template <int DT, int V>
+__global__ __launch_bounds__(kBlock) void k_ring_copy_step(RingArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    const int q = blockIdx.y;
+    const int s = a.step;
+    const int c = mod_r(q - 1 - s, a.R);
+    const int p = mod_r(q - 1, a.R);
+    const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+    const uint64_t len = hi - lo;
+    const uint64_t nslots = (len + V - 1) / V;
+    T* out = static_cast<T*>(a.out);
+    const T* src = out + (uint64_t)p * a.out_row + lo;
+    T* dst = out + (uint64_t)q * a.out_row + lo;
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
+    for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nslots;
+         j0 += stride)
+        copy_slots<E, V>(src, dst, len, j0, kBlock);
+}
+
+// All-gather: rank q places its own shard at segment q of its output row.
+template <int DT, int V>
+__global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    const int q = blockIdx.y;
+    const uint64_t lo = seg_lo(a.N, a.S, q), hi = seg_lo(a.N, a.S, q + 1);
+    const uint64_t len = hi - lo;
+    const uint64_t nslots = (len + V - 1) / V;
+    const T* src = static_cast<const T*>(a.send) + (uint64_t)q * a.send_row;
+    T* dst = static_cast<T*>(a.out) + (uint64_t)q * a.out_row + lo;
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
+    for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nslots;
+         j0 += stride)
+        copy_slots<E, V>(src, dst, len, j0, kBlock);
+}
+
+// ---- fused: a tile runs every step ------------------------------------------
+
+template <int DT, int V, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    const int R = a.R;
+    const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
+    const uint64_t seg_slots = (a.S + V - 1) / V;
+    const uint64_t tiles_per_seg = (seg_slots + tile_slots - 1) / tile_slots;
+    const uint64_t ntiles = tiles_per_seg * (uint64_t)R;
+    T* out = static_cast<T*>(a.out);
+
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int c = (int)(t % (uint64_t)R);
+        const uint64_t k = t / (uint64_t)R;
+        const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+        const uint64_t len = hi - lo;
+        const uint64_t j0 = k * tile_slots + threadIdx.x;
+        if (k * tile_slots * V >= len)
+            continue;  // empty tile of a short trailing segment (uniform per workgroup)
+
+        if constexpr (OP != kOpAllGather) {
+            for (int s = 0; s <= R - 2; ++s) {
+                const int q = (c + s + 2) % R;
+                const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
+                reduce_step_slots<E, V>(p, s, R, len, j0, kBlock);
+                step_boundary();
+            }
+        }
+        if constexpr (OP != kOpReduceScatter) {
+            if constexpr (OP == kOpAllGather) {
+                const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row;
+                copy_slots<E, V>(src, out + (uint64_t)c * a.out_row + lo, len, j0, kBlock);
+                step_boundary();
+            }
+            for (int s = 0; s <= R - 2; ++s) {
+                const int q = (c + 1 + s) % R;
+                const int p = (c + s) % R;
+                copy_slots<E, V>(out + (uint64_t)p * a.out_row + lo,
+                                 out + (uint64_t)q * a.out_row + lo, len, j0, kBlock);
+                step_boundary();
+            }
+        }
+    }
+}
+
+// ---- dispatch -----------------------------------------------------------------
+
+template <int DT, int V>
+hipError_t step_launch(const RingArgs& a, int gx, hipStream_t st, bool copy)
+{
+    dim3 grid(gx, a.R), block(kBlock);
+    if (copy)
+        hipLaunchKernelGGL((k_ring_copy_step<DT, V>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((k_ring_reduce_step<DT, V>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, int V>
+hipError_t fused_launch(const RingArgs& a, int grid, hipStream_t st)
+{
+    if (a.op == kOpAllReduce)
+        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+    else if (a.op == kOpReduceScatter)
+        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st,
+                           a);
+    else
+        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+int resident_fused_dt(bool vec)
+{
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    hipError_t e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                             &per_cu, k_ring_fused<DT, Elem<DT>::VEC, kOpAllReduce>, kBlock, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                             &per_cu, k_ring_fused<DT, 1, kOpAllReduce>, kBlock, 0);
+    if (e != hipSuccess)
+        return 0;
+    return per_cu * ncu;
+}
+
+}  // namespace
+
+// The step a.step of the ring: reduce steps are 0..R-2 (a.op decides where
+// the final value goes); copy steps are R-1..2R-3 of the all-reduce, or
+// 0..R-2 of an all-gather after the placement launch.
+hipError_t launch_ring_step(int dtype, bool vec, const RingArgs& a0, int gx, hipStream_t st)
+{
+    RingArgs a = a0;
+    bool copy = false;
+    if (a.op == kOpAllGather) {
+        copy = true;
+    } else if (a.step >= a.R - 1) {
+        copy = true;
+        a.step -= a.R - 1;
+    }
+    switch (dtype) {
+    case AR_INT32:
+        return vec ? step_launch<AR_INT32, 4>(a, gx, st, copy) : step_launch<AR_INT32, 1>(a, gx, st, copy);
+    case AR_FLOAT32:
+        return vec ? step_launch<AR_FLOAT32, 4>(a, gx, st, copy)
+                   : step_launch<AR_FLOAT32, 1>(a, gx, st, copy);
+    case AR_BF16:
+        return vec ? step_launch<AR_BF16, 8>(a, gx, st, copy) : step_launch<AR_BF16, 1>(a, gx, st, copy);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int gx, hipStream_t st)
+{
+    dim3 grid(gx, a.R), block(kBlock);
+    switch (dtype) {
+    case AR_INT32:
+        if (vec)
+            hipLaunchKernelGGL((k_ring_placement<AR_INT32, 4>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_ring_placement<AR_INT32, 1>), grid, block, 0, st, a);
+        break;
+    case AR_FLOAT32:
+        if (vec)
+            hipLaunchKernelGGL((k_ring_placement<AR_FLOAT32, 4>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_ring_placement<AR_FLOAT32, 1>), grid, block, 0, st, a);
+        break;
+    case AR_BF16:
+        if (vec)
+            hipLaunchKernelGGL((k_ring_placement<AR_BF16, 8>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((k_ring_placement<AR_BF16, 1>), grid, block, 0, st, a);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t st)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return vec ? fused_launch<AR_INT32, 4>(a, grid, st) : fused_launch<AR_INT32, 1>(a, grid, st);
+    case AR_FLOAT32:
+        return vec ? fused_launch<AR_FLOAT32, 4>(a, grid, st) : fused_launch<AR_FLOAT32, 1>(a, grid, st);
+    case AR_BF16:
+        return vec ? fused_launch<AR_BF16, 8>(a, grid, st) : fused_launch<AR_BF16, 1>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int resident_ring_fused(int dtype, bool vec)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return resident_fused_dt<AR_INT32>(vec);
+    case AR_FLOAT32:
+        return resident_fused_dt<AR_FLOAT32>(vec);
+    case AR_BF16:
+        return resident_fused_dt<AR_BF16>(vec);
+    }
+    return 0;
+}
+
+// ---- small fills (used instead of hipMemsetAsync so the calls stay safe
+// inside a captured graph) -----------------------------------------------------
+
+namespace {
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+__global__ void k_fill_u64(uint64_t* p, uint64_t v, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+int fill_grid(size_t n)
+{
+    size_t g = (n + 255) / 256;
+    return (int)(g < 4096 ? (g ? g : 1) : 4096);
+}
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u32, dim3(fill_grid(n)), dim3(256), 0, st, p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u64, dim3(fill_grid(n)), dim3(256), 0, st, p, v, n);
+    return hipGetLastError();
+}
+
+}  // namespace ar

@@ -1,0 +1,222 @@
+// ar_tree.hip -- double-binary-tree all-reduce with the LL protocol, for
+// gfx950 (MI355X).
+//
+// Two complementary binary trees run at once, each on different links
+// ("NCCL and NVSHMEM -- two GPU communication models, side by side", section
+// "double binary tree").  Reading used here: tree A is the in-order binary
+// tree on ranks 0..R-1 rooted at 0, tree B is its mirror image (even R) or
+// its shift by one (odd R); tree A reduces and broadcasts elements [0, H),
+// tree B elements [H, N), H = ceil(N/2).  A node's value is its own input,
+// then each child's subtree sum added in ascending rank order; the root's
+// sum comes back down unchanged and every rank writes it (narrowed to T).
+//
+// LL protocol: a value travels as one 8-byte line, 4 bytes of data (the
+// accumulator's bits) and 4 bytes of flag, written by one 64-bit atomic store
+// ("Demystifying NVSHMEM ..." summary, paragraph on collectives: LL packs data
+// and arrival flag into one atomic write).  The consumer polls the line until
+// its flag equals this call's epoch; because data and flag arrive together
+// there is no fence between them.  On gfx950 the agent-scope atomic store and
+// load of the line bypass the non-coherent per-XCD L2 state, so a line written
+// on one XCD is seen by a poller on another.
+//
+// One launch per piece: grid = 2 trees x R ranks x blocks_per_rank.  Every
+// workgroup of the grid must be resident at once (a node spins on its
+// children), which the host guarantees by capping the grid at the occupancy
+// limit; every wait is also bounded in time (the watchdog) and a timeout sets
+// the error word instead of hanging.  The epoch lives in the control block:
+// each workgroup reads it at start, and the last workgroup to finish advances
+// it, so consecutive launches on a stream use fresh flags and a replayed
+// graph does too.
+#include "ar_elem.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+__device__ inline uint64_t ll_pack(uint32_t data, uint32_t flag)
+{
+    return ((uint64_t)flag << 32) | (uint64_t)data;
+}
+
+// Poll one LL line until its flag is `epoch`.  Gives up (returns false) when
+// the deadline passes or another wave has already reported a timeout.
+__device__ inline bool ll_wait(const uint64_t* line, uint32_t epoch, uint64_t deadline,
+                               const uint32_t* err, uint32_t* data)
+{
+    for (uint32_t spin = 0;; ++spin) {
+        uint64_t v = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(v >> 32) == epoch) {
+            *data = (uint32_t)v;
+            return true;
+        }
+        if ((spin & 63u) == 63u) {
+            if ((uint64_t)wall_clock64() > deadline)
+                return false;
+            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                return false;
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+}
+
+__device__ inline void ll_put(uint64_t* line, uint32_t data, uint32_t epoch)
+{
+    __hip_atomic_store(line, ll_pack(data, epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    using A = typename E::A;
+    const int R = a.R;
+    const int bpr = a.blocks_per_rank;
+    const int t = blockIdx.x / (R * bpr);
+    const int v = (blockIdx.x / bpr) % R;
+    const int b = blockIdx.x % bpr;
+
+    __shared__ uint32_t s_epoch;
+    __shared__ uint64_t s_deadline;
+    if (threadIdx.x == 0) {
+        s_epoch = __hip_atomic_load(&a.ctrl[kCtrlTreeEpoch], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        s_deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
+    }
+    __syncthreads();
+    const uint32_t epoch = s_epoch;
+    const uint64_t deadline = s_deadline;
+    uint32_t* err = &a.ctrl[kCtrlError];
+
+    // this tree's half of the elements, and this launch's piece of it
+    const uint64_t hlo = (t == 0) ? 0 : a.H;
+    const uint64_t hlen = (t == 0) ? a.H : a.N - a.H;
+    const uint64_t plen = a.piece_lo < hlen ? min(a.piece_len, hlen - a.piece_lo) : 0;
+    const uint64_t first = hlo + a.piece_lo;  // element of line 0
+
+    const T* x = static_cast<const T*>(a.send) + (uint64_t)v * a.N + first;
+    T* y = static_cast<T*>(a.out) + (uint64_t)v * a.N + first;
+    const int parent = a.tt.parent[t][v];
+    const int nchild = a.tt.nchild[t][v];
+    uint64_t* up_mine = a.up + ((uint64_t)t * R + v) * a.line_stride;
+    uint64_t* down_mine = a.down + ((uint64_t)t * R + v) * a.line_stride;
+
+    uint64_t idx[kTreeEPT];
+    bool ok[kTreeEPT];
+    A acc[kTreeEPT];
+    bool timed_out = false;
+#pragma unroll
+    for (int k = 0; k < kTreeEPT; ++k) {
+        idx[k] = (uint64_t)b * (kBlock * kTreeEPT) + (uint64_t)k * kBlock + threadIdx.x;
+        ok[k] = idx[k] < plen;
+        if (ok[k])
+            acc[k] = E::widen(x[idx[k]]);
+    }
+    // reduce up: own value, then each child's subtree sum, ascending rank
+    for (int ci = 0; ci < nchild; ++ci) {
+        const int ch = a.tt.child[t][v][ci];
+        const uint64_t* up_ch = a.up + ((uint64_t)t * R + ch) * a.line_stride;
+#pragma unroll
+        for (int k = 0; k < kTreeEPT; ++k) {
+            if (ok[k]) {
+                uint32_t d = 0;
+                if (!ll_wait(up_ch + idx[k], epoch, deadline, err, &d))
+                    timed_out = true;
+                acc[k] = E::add(acc[k], E::from_bits(d));
+            }
+        }
+    }
+    if (parent >= 0) {
+#pragma unroll
+        for (int k = 0; k < kTreeEPT; ++k)
+            if (ok[k])
+                ll_put(up_mine + idx[k], E::to_bits(acc[k]), epoch);
+        // broadcast down: the root's sum arrives from the parent
+#pragma unroll
+        for (int k = 0; k < kTreeEPT; ++k) {
+            if (ok[k]) {
+                uint32_t d = 0;
+                if (!ll_wait(down_mine + idx[k], epoch, deadline, err, &d))
+                    timed_out = true;
+                acc[k] = E::from_bits(d);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kTreeEPT; ++k)
+        if (ok[k])
+            y[idx[k]] = E::narrow(acc[k]);
+    for (int ci = 0; ci < nchild; ++ci) {
+        const int ch = a.tt.child[t][v][ci];
+        uint64_t* down_ch = a.down + ((uint64_t)t * R + ch) * a.line_stride;
+#pragma unroll
+        for (int k = 0; k < kTreeEPT; ++k)
+            if (ok[k])
+                ll_put(down_ch + idx[k], E::to_bits(acc[k]), epoch);
+    }
+    if (timed_out)
+        __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+
+    // the last workgroup to finish publishes the epoch for the next launch
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlTreeDone], 1u, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.ctrl[kCtrlTreeDone], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kCtrlTreeEpoch], epoch, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int DT>
+int resident_tree_dt()
+{
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_ll<DT>, kBlock, 0) !=
+        hipSuccess)
+        return 0;
+    return per_cu * ncu;
+}
+
+}  // namespace
+
+hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t st)
+{
+    switch (dtype) {
+    case AR_INT32:
+        hipLaunchKernelGGL(k_tree_ll<AR_INT32>, dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_FLOAT32:
+        hipLaunchKernelGGL(k_tree_ll<AR_FLOAT32>, dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_BF16:
+        hipLaunchKernelGGL(k_tree_ll<AR_BF16>, dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+int resident_tree_ll(int dtype)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return resident_tree_dt<AR_INT32>();
+    case AR_FLOAT32:
+        return resident_tree_dt<AR_FLOAT32>();
+    case AR_BF16:
+        return resident_tree_dt<AR_BF16>();
+    }
+    return 0;
+}
+
+}  // namespace ar

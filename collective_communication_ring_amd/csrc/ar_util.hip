@@ -1,0 +1,119 @@
+// ar_util.hip -- plain streaming kernels used as measurement references:
+// c = a + b over float32 (the access mix of one reduce step) and a byte
+// copy (the access mix of one copy step, and a known-size kernel for
+// calibrating byte counters).
+#include <algorithm>
+
+#include "ar_elem.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+__global__ __launch_bounds__(kBlock) void k_stream_add(const u32x4* __restrict__ a,
+                                                       const u32x4* __restrict__ b,
+                                                       u32x4* __restrict__ c, uint64_t nvec)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
+    for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nvec;
+         j0 += stride) {
+        u32x4 x[kUnroll], y[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * kBlock;
+            if (j < nvec) {
+                x[u] = a[j];
+                y[u] = b[j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * kBlock;
+            if (j < nvec) {
+                u32x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    r[i] = __float_as_uint(__uint_as_float(x[u][i]) + __uint_as_float(y[u][i]));
+                c[j] = r;
+            }
+        }
+    }
+}
+
+__global__ void k_stream_add_tail(const float* a, const float* b, float* c, uint64_t from,
+                                  uint64_t n)
+{
+    const uint64_t i = from + threadIdx.x;
+    if (i < n)
+        c[i] = a[i] + b[i];
+}
+
+__global__ __launch_bounds__(kBlock) void k_stream_copy(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, uint64_t nvec)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
+    for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nvec;
+         j0 += stride) {
+        u32x4 r[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * kBlock;
+            if (j < nvec)
+                r[u] = src[j];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * kBlock;
+            if (j < nvec)
+                dst[j] = r[u];
+        }
+    }
+}
+
+int stream_grid(uint64_t nvec)
+{
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 256;
+    const uint64_t per = (uint64_t)kBlock * kUnroll;
+    uint64_t need = (nvec + per - 1) / per;
+    const uint64_t cap = (uint64_t)ncu * 8;
+    return (int)std::max<uint64_t>(1, std::min(need, cap));
+}
+
+}  // namespace
+}  // namespace ar
+
+extern "C" int ar_stream_add(const float* a, const float* b, float* c, size_t n, void* stream)
+{
+    using namespace ar;
+    if (!a || !b || !c || ((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & 15u)
+        return n == 0 ? AR_SUCCESS : AR_ERR_INVALID_ARG;
+    if (n == 0)
+        return AR_SUCCESS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint64_t nvec = n / 4;
+    if (nvec)
+        hipLaunchKernelGGL(k_stream_add, dim3(stream_grid(nvec)), dim3(kBlock), 0, st,
+                           reinterpret_cast<const u32x4*>(a), reinterpret_cast<const u32x4*>(b),
+                           reinterpret_cast<u32x4*>(c), nvec);
+    if (n % 4)
+        hipLaunchKernelGGL(k_stream_add_tail, dim3(1), dim3(4), 0, st, a, b, c, nvec * 4,
+                           (uint64_t)n);
+    return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
+}
+
+extern "C" int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* stream)
+{
+    using namespace ar;
+    if (nbytes == 0)
+        return AR_SUCCESS;
+    if (!src || !dst || (((uintptr_t)src | (uintptr_t)dst | nbytes) & 15u))
+        return AR_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint64_t nvec = nbytes / 16;
+    hipLaunchKernelGGL(k_stream_copy, dim3(stream_grid(nvec)), dim3(kBlock), 0, st,
+                       reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), nvec);
+    return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
+}

@@ -96,7 +96,7 @@ typedef enum {
     AR_OPT_CHUNK_BYTES = 0,   /* ring slice ("chunk") size in bytes of T; 0 = whole segment */
     AR_OPT_LAUNCH = 1,        /* an ar_launch_t */
     AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default */
-    AR_OPT_TIMEOUT_SPINS = 3, /* poll iterations before a bounded wait gives up */
+    AR_OPT_TIMEOUT_US = 3,    /* microseconds before a kernel's bounded wait gives up */
     AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
     AR_OPT_PROTO = 6,         /* an ar_proto_t, overriding the one given to ar_init */
@@ -175,6 +175,16 @@ int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
  *   root; returns -2 for invalid arguments. */
 int ar_ring_segment(ar_comm_t comm, size_t count, int c, size_t* lo, size_t* hi);
 int ar_tree_parent(ar_comm_t comm, int tree, int r);
+
+/* Measurement utilities (not collectives).  Plain streaming kernels that set
+ * the practical HBM ceiling the reduce-copy is compared with, and calibrate
+ * byte counters: ar_stream_add computes c[i] = a[i] + b[i] over n float32
+ * (two 16-byte loads, one 16-byte store per 4 elements -- the same access
+ * mix as one reduce step); ar_stream_copy copies n bytes (n a multiple of
+ * 16, pointers 16-byte aligned).  Device pointers; asynchronous on
+ * `stream`; AR_ERR_INVALID_ARG for NULL or misaligned arguments. */
+int ar_stream_add(const float* a, const float* b, float* c, size_t n, void* stream);
+int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* stream);
 
 /* Message for a status code (static storage). */
 const char* ar_status_string(int status);

@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and its host-side logic (argument checks, schedule views)
+behaves -- without any compute call (there is no GPU here)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ar.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(ar_[a-z_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def api():
+    from collective_communication_ring_amd import api
+    if not os.path.exists(api.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    api.lib()
+    return api
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("ar_init", "ar_allreduce", "ar_reduce_scatter", "ar_all_gather",
+              "ar_workspace_bytes", "ar_set_workspace", "ar_check", "ar_destroy",
+              "ar_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(api):
+    L = api.lib()
+    missing = [n for n in _declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_init_argument_checks(api):
+    import ctypes
+    L = api.lib()
+    h = ctypes.c_void_p()
+    assert L.ar_init(ctypes.byref(h), 1, 16, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
+    assert h.value is None
+    assert L.ar_init(ctypes.byref(h), 65, 16, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
+    assert L.ar_init(ctypes.byref(h), 4, 16, 7, api.AR_RING, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
+    assert L.ar_init(ctypes.byref(h), 4, 16, api.AR_FLOAT32, 9, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
+    assert L.ar_init(None, 4, 16, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
+    c = api.ar_init(8, 1024, api.AR_FLOAT32)
+    try:
+        assert api.ar_workspace_bytes(c) >= 256 + 8 * 1024 * 4
+        # no workspace yet: a collective is refused before touching the device
+        assert L.ar_allreduce(c, 16, 4096, 8, None) == api.AR_ERR_INVALID_USAGE
+        assert L.ar_set_workspace(c, None, 1 << 20, None) == api.AR_ERR_INVALID_ARG
+        assert L.ar_set_workspace(c, 257, 1 << 30, None) == api.AR_ERR_INVALID_ARG  # misaligned
+        assert L.ar_set_workspace(c, 4096, 16, None) == api.AR_ERR_INVALID_ARG      # too small
+    finally:
+        api.ar_destroy(c)
+    assert api.ar_destroy(None) == 0
+
+
+def test_options_round_trip(api):
+    c = api.ar_init(4, 100, api.AR_INT32)
+    try:
+        for opt, val in ((api.AR_OPT_CHUNK_BYTES, 4096), (api.AR_OPT_LAUNCH, api.AR_LAUNCH_STEP),
+                         (api.AR_OPT_GRID, 512), (api.AR_OPT_TIMEOUT_US, 1000),
+                         (api.AR_OPT_ALGO, api.AR_TREE), (api.AR_OPT_PROTO, api.AR_LL),
+                         (api.AR_OPT_TREE_MAX_BYTES, 1 << 20)):
+            api.ar_set_option(c, opt, val)
+            assert api.ar_get_option(c, opt) == val
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, api.AR_OPT_LAUNCH, 99)
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, 1234, 1)
+    finally:
+        api.ar_destroy(c)
+
+
+def test_plan_picks_tree_for_small_and_ring_for_large(api):
+    c = api.ar_init(8, 1 << 20, api.AR_FLOAT32, api.AR_AUTO)
+    try:
+        api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, 64 * 1024)
+        assert api.ar_plan(c, 16)[0] == api.AR_TREE
+        assert api.ar_plan(c, 16 * 1024)[0] == api.AR_TREE
+        assert api.ar_plan(c, 16 * 1024 + 1)[0] == api.AR_RING
+        assert api.ar_plan(c, 1 << 20)[0] == api.AR_RING
+    finally:
+        api.ar_destroy(c)
+
+
+@pytest.mark.parametrize("R", [2, 3, 4, 5, 7, 8, 16, 64])
+def test_library_schedule_matches_oracle(api, orc, R):
+    """The library's host scheduler and the oracle are separate code; their
+    segment bounds and tree shapes must agree."""
+    c = api.ar_init(R, 10 ** 6, api.AR_FLOAT32)
+    try:
+        for t in (0, 1):
+            assert [api.ar_tree_parent(c, t, r) for r in range(R)] == orc.tree_parents(R, t)
+        assert api.ar_tree_parent(c, 2, 0) == -2
+        for count in (0, 1, R - 1, R, 10 * R + 3, 999_983):
+            S = -(-count // R)
+            prev = 0
+            for s in range(R):
+                lo, hi = api.ar_ring_segment(c, count, s)
+                assert (lo, hi) == (min(s * S, count), min((s + 1) * S, count))
+                assert lo == prev
+                prev = hi
+            assert prev == count
+    finally:
+        api.ar_destroy(c)
+
+
+def test_status_strings(api):
+    for s in range(7):
+        assert api.ar_status_string(s)
+    assert "timeout" in api.ar_status_string(api.AR_ERR_TIMEOUT)

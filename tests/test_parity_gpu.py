@@ -1,0 +1,307 @@
+"""GPU parity: libar's HIP kernels against the CPU oracle, on the same seeded
+inputs.  The oracle replays the same ring/tree order, so every dtype is
+expected bit-exact; float32 is also held to the stated tolerance against the
+float64 sum (1e-6 relative + 1e-6*R absolute), bfloat16 to 1e-2 relative.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+LAUNCHES = ["fused", "step"]
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    from collective_communication_ring_amd import api, inputs
+    import oracle
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    api.lib()
+    return dict(torch=torch, api=api, inputs=inputs, orc=oracle, dev=torch.device("cuda:0"))
+
+
+def _np_dtype(dtype):
+    return {"int32": np.int32, "float32": np.float32, "bf16": np.uint16}[dtype]
+
+
+def to_dev(env, x, dtype):
+    torch = env["torch"]
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(env["dev"]).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(env["dev"])
+
+
+def from_dev(env, t, dtype):
+    torch = env["torch"]
+    torch.cuda.synchronize()
+    if dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def poisoned(env, shape, dtype):
+    """An output buffer full of 0xFF bytes (NaN / -1), so any element the
+    kernel fails to write is caught."""
+    torch = env["torch"]
+    tdt = {"int32": torch.int32, "float32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    t = torch.empty(shape, dtype=tdt, device=env["dev"])
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def rand_input(env, dtype, R, N, seed):
+    inputs = env["inputs"]
+    if dtype == "int32":
+        return inputs.draw("int_pm1000", R, N, seed)
+    if dtype == "float32":
+        return inputs.draw("normal", R, N, seed)
+    return inputs.to_bf16_bits(inputs.draw("normal_0.02", R, N, seed))
+
+
+def check_tolerance(env, y, x, dtype):
+    orc = env["orc"]
+    R = x.shape[0]
+    ex = orc.exact_sum(x, dtype)
+    if dtype == "float32":
+        err = np.abs(y.astype(np.float64) - ex[None, :])
+        assert (err <= 1e-6 * np.abs(ex)[None, :] + 1e-6 * R).all()
+    elif dtype == "bf16":
+        yf = orc.f32_from_bf16(y).astype(np.float64)
+        assert (np.abs(yf - ex[None, :]) <= 1e-2 * np.abs(ex)[None, :] + 1e-6 * R).all()
+
+
+def run_allreduce(env, x, dtype, algo="ring", proto="simple", launch=None, reps=1, **opts):
+    api = env["api"]
+    R, N = x.shape
+    comm = api.Comm(R, max(N, 1), dtype, algo, proto, device=env["dev"], launch=launch, **opts)
+    send = to_dev(env, x, dtype)
+    outs = []
+    for _ in range(reps):
+        recv = poisoned(env, (R, N), dtype)
+        comm.allreduce(send, recv)
+        outs.append(from_dev(env, recv, dtype))
+    assert comm.check() == api.AR_SUCCESS
+    return outs
+
+
+# ---------------------------------------------------------------- config 1
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_cfg1_ring_int32_r4(env, launch):
+    x = env["inputs"].host_inputs("ring_int32_r4")
+    R, N = x.shape
+    (y,) = run_allreduce(env, x, "int32", launch=launch, chunk_bytes=(N // R) * 4)
+    want = x.astype(np.int64).sum(axis=0).astype(np.int32)
+    assert np.array_equal(y, env["orc"].ring_allreduce(x))
+    assert (y == want[None, :]).all()
+
+
+# ---------------------------------------------------------------- config 2
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_cfg2_ring_f32_r8_64MiB(env, launch):
+    x = env["inputs"].host_inputs("ring_f32_r8_64MiB")
+    (y,) = run_allreduce(env, x, "float32", launch=launch, chunk_bytes=512 * 1024)
+    ref = env["orc"].ring_allreduce(x)
+    assert y.tobytes() == ref.tobytes()
+    check_tolerance(env, y, x, "float32")
+
+
+# ---------------------------------------------------------------- ragged sizes
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 3, 5, 8, 16])
+def test_ring_allreduce_ragged(env, launch, dtype, R):
+    orc = env["orc"]
+    for N in (1, 2, 7, 13, 64, 1000, 4097, 3 * 4096 + 5, 65536 + 40):
+        x = rand_input(env, dtype, R, N, seed=1000 * R + N)
+        (y,) = run_allreduce(env, x, dtype, launch=launch)
+        assert y.tobytes() == orc.ring_allreduce(x, dtype).tobytes(), (R, N)
+        check_tolerance(env, y, x, dtype)
+
+
+def test_ring_zero_count_is_noop(env):
+    torch, api = env["torch"], env["api"]
+    comm = api.Comm(4, 16, "float32", device=env["dev"])
+    send = torch.ones((4, 0), device=env["dev"])
+    recv = torch.ones((4, 0), device=env["dev"])
+    comm.allreduce(send, recv)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- summation order
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_ring_order_pins_in_random_data(env, launch):
+    # In segment c the ring folds x_{c+1}, x_{c+2}, ..., x_c.  With
+    # x_c = -T, x_{c+1} = T, every other rank 1 (T = 2^24) the float32 fold is
+    # T + 1 -> T (tie to even) repeatedly, then T - T = 0: result 0, exact R-2.
+    R, N = 8, 8 * 4096
+    T = np.float32(2.0 ** 24)
+    x = env["inputs"].draw("normal", R, N, seed=9)
+    S = N // R
+    for c in range(R):
+        for e in (c * S, c * S + 1, c * S + S // 2, c * S + S - 1):
+            x[:, e] = 1
+            x[c, e] = -T
+            x[(c + 1) % R, e] = T
+    (y,) = run_allreduce(env, x, "float32", launch=launch)
+    for c in range(R):
+        for e in (c * S, c * S + 1, c * S + S // 2, c * S + S - 1):
+            assert (y[:, e] == 0.0).all()
+    assert y.tobytes() == env["orc"].ring_allreduce(x).tobytes()
+
+
+# ---------------------------------------------------------------- RS / AG
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 4, 8, 16])
+def test_reduce_scatter_all_gather(env, launch, dtype, R):
+    api, orc, torch = env["api"], env["orc"], env["torch"]
+    for n in (1, 3, 8, 1000, 8192 + 8):
+        N = n * R
+        x = rand_input(env, dtype, R, N, seed=77 + n + R)
+        comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=launch)
+        send = to_dev(env, x, dtype)
+        shard = poisoned(env, (R, n), dtype)
+        comm.reduce_scatter(send, shard)
+        full = poisoned(env, (R, N), dtype)
+        comm.all_gather(shard, full)
+        ar = poisoned(env, (R, N), dtype)
+        comm.allreduce(send, ar)
+        rs, ag, y = from_dev(env, shard, dtype), from_dev(env, full, dtype), from_dev(env, ar, dtype)
+        assert rs.tobytes() == orc.ring_reduce_scatter(x, dtype).tobytes(), (R, n)
+        assert ag.tobytes() == y.tobytes(), (R, n)                      # RS o AG == AR
+        assert ag.tobytes() == orc.ring_all_gather(rs, dtype).tobytes()
+        assert y.tobytes() == orc.ring_allreduce(x, dtype).tobytes()
+        # all-gather alone on unrelated data
+        g = rand_input(env, dtype, R, n, seed=5 + n)
+        out = poisoned(env, (R, N), dtype)
+        comm.all_gather(to_dev(env, g, dtype), out)
+        assert from_dev(env, out, dtype).tobytes() == np.tile(g.reshape(-1), (R, 1)).tobytes()
+        assert comm.check() == api.AR_SUCCESS
+
+
+# ---------------------------------------------------------------- config 4: tree + LL
+
+def test_cfg4_tree_ll_sizes(env):
+    orc, inputs = env["orc"], env["inputs"]
+    for nbytes in [2 ** k for k in range(3, 19)]:
+        N = nbytes // 4
+        x = inputs.draw("uniform_pm1", 8, N, seed=4)
+        outs = run_allreduce(env, x, "float32", "tree", "ll", reps=3)
+        ref = orc.tree_allreduce(x)
+        for y in outs:  # repeated calls: the LL epoch advances each time
+            assert y.tobytes() == ref.tobytes(), nbytes
+        check_tolerance(env, outs[0], x, "float32")
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 3, 5, 8, 13, 16, 64])
+def test_tree_ll_ragged(env, dtype, R):
+    orc = env["orc"]
+    for N in (1, 2, 3, 17, 1000, 2 * 65536 + 7):
+        x = rand_input(env, dtype, R, N, seed=31 * R + N)
+        outs = run_allreduce(env, x, dtype, "tree", "ll", reps=2)
+        ref = orc.tree_allreduce(x, dtype)
+        for y in outs:
+            assert y.tobytes() == ref.tobytes(), (R, N)
+
+
+def test_tree_order_pin(env):
+    # Tree A at R = 8: P(2) = x2 + x1 + x3 = (T + 1) -> T, T - T = 0 with
+    # x2 = T, x1 = 1, x3 = -T; exact sum 1.
+    T = np.float32(2.0 ** 24)
+    x = np.zeros((8, 64), np.float32)
+    x[2, 0], x[1, 0], x[3, 0] = T, 1, -T
+    (y,) = run_allreduce(env, x, "float32", "tree", "ll")
+    assert (y[:, 0] == 0.0).all()
+
+
+def test_auto_selects_tree_then_ring(env):
+    api = env["api"]
+    x = env["inputs"].draw("normal", 8, 1 << 16, seed=12)
+    comm = api.Comm(8, 1 << 16, "float32", "auto", device=env["dev"], tree_max_bytes=4096)
+    assert comm.plan(1024)[0] == api.AR_TREE and comm.plan(1 << 16)[0] == api.AR_RING
+    for N, ref in ((1024, env["orc"].tree_allreduce(x[:, :1024].copy())),
+                   (1 << 16, env["orc"].ring_allreduce(x))):
+        send = to_dev(env, x[:, :N].copy(), "float32")
+        recv = poisoned(env, (8, N), "float32")
+        comm.allreduce(send, recv)
+        assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
+
+
+# ---------------------------------------------------------------- config 5
+
+def test_cfg5_gradient_buckets_bf16_r16(env):
+    """40 buckets x 13,107,200 bf16 per rank, R = 16: reduce-scatter then
+    all-gather equals all-reduce bit for bit on every bucket; buckets 0 and 39
+    are also replayed by the oracle."""
+    api, orc, inputs, torch = env["api"], env["orc"], env["inputs"], env["torch"]
+    w = inputs.WORKLOADS["buckets_bf16_r16"]
+    R, N, B = w["R"], w["count"], w["buckets"]
+    n = N // R
+    comm = api.Comm(R, N, "bf16", "ring", device=env["dev"])
+    shard = torch.empty((R, n), dtype=torch.bfloat16, device=env["dev"])
+    full = torch.empty((R, N), dtype=torch.bfloat16, device=env["dev"])
+    ar = torch.empty((R, N), dtype=torch.bfloat16, device=env["dev"])
+    for b in range(B):
+        x = inputs.device_bucket_bf16(R, N, w["seed"], b, env["dev"])
+        full.fill_(float("nan"))
+        comm.reduce_scatter(x, shard)
+        comm.all_gather(shard, full)
+        comm.allreduce(x, ar)
+        assert torch.equal(full.view(torch.int16), ar.view(torch.int16)), b
+        assert torch.equal(ar.view(torch.int16), ar[0:1].expand(R, N).view(torch.int16)), b
+        if b in (0, B - 1):
+            xh = from_dev(env, x, "bf16")
+            y = from_dev(env, ar, "bf16")
+            assert y.tobytes() == orc.ring_allreduce(xh, "bf16").tobytes(), b
+            assert from_dev(env, shard, "bf16").tobytes() == orc.ring_reduce_scatter(xh, "bf16").tobytes()
+            check_tolerance(env, y[:1], xh, "bf16")
+    assert comm.check() == api.AR_SUCCESS
+
+
+# ---------------------------------------------------------------- edges
+
+def test_unaligned_views_use_the_scalar_path(env):
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R, N = 8, 4099
+    x = env["inputs"].draw("normal", R, N, seed=3)
+    base = torch.zeros(R * N + 1, dtype=torch.float32, device=env["dev"])
+    send = base[1:].view(R, N)                           # 4-byte misaligned
+    send.copy_(torch.from_numpy(x).to(env["dev"]))
+    rbase = torch.full((R * N + 3,), float("nan"), device=env["dev"])
+    recv = rbase[3:].view(R, N)
+    for launch in LAUNCHES:
+        comm = api.Comm(R, N, "float32", device=env["dev"], launch=launch)
+        comm.allreduce(send, recv)
+        assert from_dev(env, recv, "float32").tobytes() == orc.ring_allreduce(x).tobytes()
+
+
+def test_argument_errors(env):
+    torch, api = env["torch"], env["api"]
+    comm = api.Comm(4, 64, "float32", device=env["dev"])
+    a = torch.zeros((4, 64), device=env["dev"])
+    with pytest.raises(api.ArError) as e:
+        comm.allreduce(a, a)
+    assert e.value.status == api.AR_ERR_INVALID_USAGE
+    big = torch.zeros((4, 65), device=env["dev"])
+    with pytest.raises(api.ArError) as e:
+        comm.allreduce(big, torch.zeros_like(big))
+    assert e.value.status == api.AR_ERR_INVALID_ARG
+    tcomm = api.Comm(4, 64, "float32", "tree", "ll", device=env["dev"])
+    with pytest.raises(api.ArError) as e:
+        tcomm.reduce_scatter(a, torch.zeros((4, 16), device=env["dev"]))
+    assert e.value.status == api.AR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_repeat_runs_bit_identical(env, launch):
+    x = env["inputs"].draw("normal", 8, 1 << 20, seed=21)
+    outs = run_allreduce(env, x, "float32", launch=launch, reps=5)
+    for y in outs[1:]:
+        assert y.tobytes() == outs[0].tobytes()
