@@ -75,6 +75,33 @@ def time_calls(fn, steps, warmup, torch):
     return per, ev[0].elapsed_time(ev[steps]), wall
 
 
+def time_graph(fn, calls, torch, reps=3):
+    """Capture `calls` back-to-back calls of fn in one HIP graph, replay it
+    once untimed, then time `reps` replays with events.  Returns ms per call.
+    Removes the host's enqueue pacing from small-message timings."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * calls)
+    del g
+    return ms
+
+
 def cpu_baseline(x, R, N, s, target_s=12.0):
     """The oracle, as it is, on the host: repeat the full all-reduce until
     about target_s seconds of CPU work; report its busBW."""
@@ -120,6 +147,7 @@ def headline(args):
     kernel_ms = sum(per) / len(per)
     achieved = b_alg / (kernel_ms / 1e3) / 1e9
     kernel = {"fused": "k_ring_fused<float32, 16-byte slots, all-reduce>",
+              "pipelined": "k_ring_pipelined<float32, 16-byte slots, all-reduce>",
               "step": "k_ring_reduce_step + k_ring_copy_step (2(R-1) launches)"}[launch_name]
     traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name)
     line = {
@@ -146,7 +174,7 @@ def headline(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": b_alg
-                     if launch_name == "fused" else None},
+                     if launch_name != "step" else None},
         "wall_s_timed": round(wall, 4),
     }
     y = None
@@ -185,8 +213,11 @@ def mode_sweep(args):
     for N in counts:
         sv = send_flat[:R * N].view(R, N)
         rv = recv_flat[:R * N].view(R, N)
-        per, total_ms, _ = time_calls(lambda: comm.allreduce(sv, rv), 20, 5, torch)
-        t = total_ms / 20 / 1e3
+        if args.eager:
+            per, total_ms, _ = time_calls(lambda: comm.allreduce(sv, rv), 20, 5, torch)
+            t = total_ms / 20 / 1e3
+        else:
+            t = time_graph(lambda: comm.allreduce(sv, rv), 20, torch) / 1e3
         row = dict(mode="sweep", bytes_per_rank=N * s, count=N, t_us=t * 1e6,
                    algbw_GBps=N * s / t / 1e9,
                    busbw_GBps=N * s / t / 1e9 * measure.busbw_factor("allreduce", R),
@@ -233,6 +264,7 @@ def mode_tree_vs_ring(args):
     recv_flat = torch.empty_like(send_flat)
     variants = [("tree-ll", dict(algo="tree", proto="ll")),
                 ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
+                ("ring-pipelined", dict(algo="ring", proto="simple", launch="pipelined")),
                 ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
     comms = {name: api.Comm(R, Nmax, "float32", device=dev, **kw) for name, kw in variants}
     out = open(args.out, "w") if args.out else None
@@ -242,8 +274,11 @@ def mode_tree_vs_ring(args):
         rv = recv_flat[:R * N].view(R, N)
         for name, _ in variants:
             c = comms[name]
-            _, total_ms, _ = time_calls(lambda: c.allreduce(sv, rv), 20, 5, torch)
-            t_us = total_ms / 20 * 1e3
+            if args.eager:
+                _, total_ms, _ = time_calls(lambda: c.allreduce(sv, rv), 20, 5, torch)
+                t_us = total_ms / 20 * 1e3
+            else:
+                t_us = time_graph(lambda: c.allreduce(sv, rv), 20, torch) * 1e3
             res.setdefault(name, []).append(t_us)
             row = dict(mode="tree_vs_ring", variant=name, bytes_per_rank=N * s, t_us=t_us)
             log("%-10s %8d B/rank %9.2f us" % (name, N * s, t_us))
@@ -329,6 +364,40 @@ def mode_stream(args):
     return 0
 
 
+def mode_counters(args):
+    """A short program for byte-counter runs (rocprofv3 --pmc): a copy of a
+    known size (the calibration), then 3 all-reduces of the headline workload
+    in each launch form, then a small tree-LL all-reduce."""
+    import torch
+    from collective_communication_ring_amd import api, inputs
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    n = (512 << 20) // 4
+    a = torch.randn(n, device=dev)
+    c = torch.empty_like(a)
+    for _ in range(3):
+        api.ar_stream_copy(a.data_ptr(), c.data_ptr(), n * 4, st)
+    torch.cuda.synchronize()
+    del a, c
+    R, N = 8, 16_777_216
+    x = inputs.host_inputs("ring_f32_r8_64MiB")
+    send = torch.from_numpy(x).to(dev)
+    recv = torch.empty_like(send)
+    for launch in ("fused", "step"):
+        comm = api.Comm(R, N, "float32", "ring", device=dev, launch=launch)
+        for _ in range(3):
+            comm.allreduce(send, recv)
+        torch.cuda.synchronize()
+    comm = api.Comm(R, 65536, "float32", "tree", "ll", device=dev)
+    small = send[:, :65536].contiguous()
+    out = torch.empty_like(small)
+    for _ in range(3):
+        comm.allreduce(small, out)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(mode="counters", copy_bytes=n * 4, allreduce_count=N)), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,11 +406,14 @@ def main():
     ap.add_argument("--launch", default="auto", choices=["auto", "fused", "step", "pipelined"])
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
-                    choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream"])
+                    choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream",
+                             "counters"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="sweep / tree-vs-ring: time host-enqueued calls instead of graph replays")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -350,7 +422,7 @@ def main():
               % (args.gpus, world), file=sys.stderr)
         return 2
     fn = {"headline": headline, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
-          "buckets": mode_buckets, "stream": mode_stream}[args.mode]
+          "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters}[args.mode]
     return fn(args)
 
 

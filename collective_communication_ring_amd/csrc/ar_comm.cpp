@@ -120,7 +120,7 @@ struct ar_comm {
     // workspace layout
     size_t off_part = 0, off_up = 0, off_down = 0, off_flags = 0, ws_need = 0;
     uint64_t tree_lines = 0;  // lines per (tree, rank)
-    size_t nflags = 0;
+    uint64_t flag_stride = 0; // pipelined ring: ready flags per segment
     char* ws = nullptr;
     size_t ws_bytes = 0;
     // device facts, read on first use
@@ -128,6 +128,7 @@ struct ar_comm {
     int ncu = 0;
     double ticks_per_us = 100.0;
     int resident_fused[3][2] = {};
+    int resident_pipe[3][2] = {};
     int resident_tree[3] = {};
     // last call
     hipStream_t last_stream = nullptr;
@@ -159,8 +160,11 @@ int device_ready(ar_comm* c)
     for (int d = 0; d < 3; ++d) {
         c->resident_fused[d][0] = resident_ring_fused(d, false);
         c->resident_fused[d][1] = resident_ring_fused(d, true);
+        c->resident_pipe[d][0] = resident_ring_pipelined(d, false);
+        c->resident_pipe[d][1] = resident_ring_pipelined(d, true);
         c->resident_tree[d] = resident_tree_ll(d);
-        if (c->resident_fused[d][0] <= 0 || c->resident_fused[d][1] <= 0 || c->resident_tree[d] <= 0)
+        if (c->resident_fused[d][0] <= 0 || c->resident_fused[d][1] <= 0 ||
+            c->resident_pipe[d][0] <= 0 || c->resident_pipe[d][1] <= 0 || c->resident_tree[d] <= 0)
             return fail_hip(c, hipErrorInvalidDeviceFunction);
     }
     c->dev_ready = true;
@@ -243,6 +247,36 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
         const int64_t want = c->grid > 0 ? c->grid : res;
         grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
         e = launch_ring_fused(c->dtype, vec, a, grid, st);
+    } else if (launch == AR_LAUNCH_PIPELINED) {
+        const int res = c->resident_pipe[c->dtype][vec ? 1 : 0];
+        int64_t gmax = res / a.R;
+        if (c->grid > 0)
+            gmax = std::min<int64_t>(gmax, c->grid / a.R);
+        if (gmax < 1)
+            return AR_ERR_UNSUPPORTED;
+        const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
+        const uint64_t tile = (uint64_t)kBlock * kUnroll * V;  // elements per workgroup pass
+        const uint64_t es = (uint64_t)elem_size(c->dtype);
+        uint64_t unit = c->chunk_bytes > 0 ? (uint64_t)c->chunk_bytes / es : a.S;
+        unit = std::max<uint64_t>(tile, unit / tile * tile);
+        uint64_t nunits = (a.S + unit - 1) / unit;
+        // the chunk is the pipelining unit; cut it finer when a segment has
+        // fewer chunks than there are workgroups per rank
+        while (nunits < (uint64_t)gmax && unit > tile) {
+            unit = std::max<uint64_t>(tile, (unit / 2 + tile - 1) / tile * tile);
+            nunits = (a.S + unit - 1) / unit;
+        }
+        uint64_t G = std::min<uint64_t>(nunits, (uint64_t)gmax);
+        G = (nunits + (nunits + G - 1) / G - 1) / ((nunits + G - 1) / G);  // balance chunks per workgroup
+        if (nunits > c->flag_stride)
+            return AR_ERR_INTERNAL;
+        a.flags = reinterpret_cast<uint64_t*>(c->ws + c->off_flags);
+        a.flag_stride = c->flag_stride;
+        a.unit = unit;
+        a.nunits = nunits;
+        a.per_rank_wg = (int)G;
+        grid = (int)G * a.R;
+        e = launch_ring_pipelined(c->dtype, vec, a, grid, st);
     } else {
         return AR_ERR_UNSUPPORTED;
     }
@@ -367,7 +401,10 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     c->off_down = off;
     off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
     c->off_flags = off;
-    c->nflags = 0;
+    // one flag per (segment, chunk); a chunk is at least one workgroup pass
+    // of the scalar path (kBlock * kUnroll elements)
+    c->flag_stride = ((cap1 + R - 1) / R + (size_t)kBlock * kUnroll - 1) / ((size_t)kBlock * kUnroll) + 1;
+    off = align_up(off + (size_t)R * c->flag_stride * 8, kAlign);
     c->ws_need = off;
     *out = c;
     return AR_SUCCESS;
@@ -392,7 +429,7 @@ int ar_set_workspace(ar_comm_t c, void* dev, size_t bytes, void* stream)
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws), 0u, kCtrlWords, st);
     if (e == hipSuccess)
         e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,
-                            (c->off_flags - c->off_up) / sizeof(uint64_t), st);
+                            (c->ws_need - c->off_up) / sizeof(uint64_t), st);
     if (e != hipSuccess) {
         c->ws = nullptr;
         return fail_hip(c, e);

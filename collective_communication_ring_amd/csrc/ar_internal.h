@@ -14,14 +14,13 @@ constexpr int kMaxRanks = 64;
 
 // Words of the control block at the start of the workspace (uint32 each).
 enum CtrlWord {
-    kCtrlTreeEpoch = 0,   // LL flag value of the last completed tree call
-    kCtrlError = 1,       // non-zero: a bounded wait expired (watchdog)
-    kCtrlTreeDone = 2,    // workgroups of the running tree call that finished
-    kCtrlPipeBase = 3,    // pipelined ring: flag value every chunk holds between calls
-    kCtrlPipeDone = 4,    // workgroups of the running pipelined call that finished
-    kCtrlRingLLEpoch = 5, // LL flag value of the last completed ring-LL call
-    kCtrlRingLLDone = 6,
-    kCtrlWords = 64       // 256 bytes
+    kCtrlTreeEpoch = 0,  // LL flag value of the last completed tree call
+    kCtrlError = 1,      // non-zero: a bounded wait expired (watchdog)
+    kCtrlTreeDone = 2,   // workgroups of the running tree call that finished
+    kCtrlPipeDone = 3,   // workgroups of the running pipelined call that finished
+    kCtrlPipeBase = 8,   // uint64 at words 8-9: the value every chunk flag holds between
+                         // pipelined calls; a call of n steps raises it by n
+    kCtrlWords = 64      // 256 bytes
 };
 
 enum ErrorBits : uint32_t {
@@ -49,13 +48,14 @@ struct RingArgs {
     void* part;
     void* out;
     uint32_t* ctrl;   // control block
-    uint32_t* flags;  // pipelined ring: one flag per chunk
+    uint64_t* flags;  // pipelined ring: one ready flag per (segment, chunk)
     uint64_t N;       // logical elements per rank (all-reduce count; RS input row; AG output row)
     uint64_t S;       // segment length, ceil(N / R)
     uint64_t send_row;
     uint64_t out_row;
-    uint64_t chunk;   // pipelined ring: elements per chunk (multiple of the vector width)
-    uint64_t nchunks; // pipelined ring: chunks per segment
+    uint64_t unit;    // pipelined ring: elements per flagged chunk (a multiple of the slot)
+    uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
+    uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
     int R;
     int op;           // Op
     int step;         // step-per-launch mode: the step this launch runs
@@ -84,7 +84,7 @@ struct TreeArgs {
 hipError_t launch_ring_step(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
-hipError_t launch_ring_pipelined(int dtype, bool vec, const RingArgs& a, hipStream_t s);
+hipError_t launch_ring_pipelined(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
 hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);

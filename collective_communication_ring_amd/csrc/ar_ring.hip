@@ -33,157 +33,10 @@
 //            next step reads it.
 #include "ar_elem.h"
 #include "ar_internal.h"
+#include "ar_slots.h"
 
 namespace ar {
 namespace {
-
-// Reduce kUnroll slots j0 + u*jstep (u < kUnroll) of one segment of length
-// len.  FIRST: the received value comes from the predecessor's input (T);
-// else from its accumulator row (A).  LAST: the result is final and is
-// narrowed to T; else it is this rank's accumulator.
-template <class E, int V, bool FIRST, bool LAST>
-__device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
-                                    const typename E::A* __restrict__ prevA,
-                                    const typename E::T* __restrict__ own,
-                                    typename E::A* __restrict__ dstA,
-                                    typename E::T* __restrict__ dstT, uint64_t len, uint64_t j0,
-                                    uint64_t jstep)
-{
-    using A = typename E::A;
-    A x[kUnroll][V], y[kUnroll][V];
-    if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
-        // every slot is whole: straight-line code, all loads in flight at once
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t j = j0 + (uint64_t)u * jstep;
-            if constexpr (FIRST)
-                load_t<E, V>(prevT + j * V, x[u]);
-            else
-                load_a<E, V>(prevA + j * V, x[u]);
-            load_t<E, V>(own + j * V, y[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t j = j0 + (uint64_t)u * jstep;
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-                x[u][i] = E::add(x[u][i], y[u][i]);
-            if constexpr (LAST)
-                store_t<E, V>(dstT + j * V, x[u]);
-            else
-                store_a<E, V>(dstA + j * V, x[u]);
-        }
-        return;
-    }
-    // the end of a segment: whole slots, then the ragged last slot element by
-    // element
-    for (int u = 0; u < kUnroll; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * jstep;
-        if ((j + 1) * V <= len) {
-            if constexpr (FIRST)
-                load_t<E, V>(prevT + j * V, x[0]);
-            else
-                load_a<E, V>(prevA + j * V, x[0]);
-            load_t<E, V>(own + j * V, y[0]);
-#pragma unroll
-            for (int i = 0; i < V; ++i)
-                x[0][i] = E::add(x[0][i], y[0][i]);
-            if constexpr (LAST)
-                store_t<E, V>(dstT + j * V, x[0]);
-            else
-                store_a<E, V>(dstA + j * V, x[0]);
-        } else if (j * V < len) {
-            for (uint64_t e = j * V; e < len; ++e) {
-                A xv = FIRST ? E::widen(prevT[e]) : prevA[e];
-                A r = E::add(xv, E::widen(own[e]));
-                if constexpr (LAST)
-                    dstT[e] = E::narrow(r);
-                else
-                    dstA[e] = r;
-            }
-        }
-    }
-}
-
-// Copy kUnroll slots of T from src to dst (bit copy).
-template <class E, int V>
-__device__ inline void copy_slots(const typename E::T* __restrict__ src,
-                                  typename E::T* __restrict__ dst, uint64_t len, uint64_t j0,
-                                  uint64_t jstep)
-{
-    if constexpr (V == 1) {
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t j = j0 + (uint64_t)u * jstep;
-            if (j < len)
-                dst[j] = src[j];
-        }
-    } else {
-        if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
-            u32x4 r[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                r[u] = *reinterpret_cast<const u32x4*>(src + (j0 + (uint64_t)u * jstep) * V);
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                *reinterpret_cast<u32x4*>(dst + (j0 + (uint64_t)u * jstep) * V) = r[u];
-            return;
-        }
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t j = j0 + (uint64_t)u * jstep;
-            if ((j + 1) * V <= len) {
-                *reinterpret_cast<u32x4*>(dst + j * V) = *reinterpret_cast<const u32x4*>(src + j * V);
-            } else if (j * V < len) {
-                for (uint64_t e = j * V; e < len; ++e)
-                    dst[e] = src[e];
-            }
-        }
-    }
-}
-
-// Row pointers of reduce step s for rank q, segment c = (q-s-2) mod R.
-template <class E>
-struct ReducePtrs {
-    const typename E::T* prevT;
-    const typename E::A* prevA;
-    const typename E::T* own;
-    typename E::A* dstA;
-    typename E::T* dstT;
-};
-
-template <class E>
-__device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uint64_t lo)
-{
-    using T = typename E::T;
-    using A = typename E::A;
-    const int p = mod_r(q - 1, a.R);
-    ReducePtrs<E> r;
-    const T* send = static_cast<const T*>(a.send);
-    A* part = static_cast<A*>(a.part);
-    T* out = static_cast<T*>(a.out);
-    r.prevT = send + (uint64_t)p * a.send_row + lo;
-    r.prevA = part + (uint64_t)p * a.N + lo;
-    r.own = send + (uint64_t)q * a.send_row + lo;
-    r.dstA = part + (uint64_t)q * a.N + lo;
-    // the final value (q == c): all-reduce writes it in place in the full
-    // row; reduce-scatter writes it at the start of rank c's shard row
-    r.dstT = out + (uint64_t)q * a.out_row + (a.op == kOpReduceScatter ? 0 : lo);
-    return r;
-}
-
-template <class E, int V>
-__device__ inline void reduce_step_slots(const ReducePtrs<E>& p, int s, int R, uint64_t len,
-                                         uint64_t j0, uint64_t jstep)
-{
-    const bool first = (s == 0), last = (s == R - 2);
-    if (first && last)
-        reduce_slots<E, V, true, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
-    else if (first)
-        reduce_slots<E, V, true, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
-    else if (last)
-        reduce_slots<E, V, false, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
-    else
-        reduce_slots<E, V, false, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
-}
 
 // ---- one launch per step --------------------------------------------------
 

@@ -8,7 +8,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-LAUNCHES = ["fused", "step"]
+LAUNCHES = ["fused", "step", "pipelined"]
 
 
 @pytest.fixture(scope="module")
@@ -305,3 +305,45 @@ def test_repeat_runs_bit_identical(env, launch):
     outs = run_allreduce(env, x, "float32", launch=launch, reps=5)
     for y in outs[1:]:
         assert y.tobytes() == outs[0].tobytes()
+
+
+# ---------------------------------------------------------------- graphs
+
+@pytest.mark.parametrize("variant", ["fused", "step", "pipelined", "tree"])
+def test_graph_replay_matches_eager(env, variant):
+    """Capture one call in a HIP graph and replay it several times with eager
+    calls and synchronizations in between; every replay must equal the eager
+    result (the tree's LL epoch and the pipelined flags' base live on the
+    device, so replays stay correct)."""
+    torch, api = env["torch"], env["api"]
+    R, N = 8, 40_000
+    x = env["inputs"].draw("normal", R, N, seed=17)
+    if variant == "tree":
+        comm = api.Comm(R, N, "float32", "tree", "ll", device=env["dev"])
+        ref = env["orc"].tree_allreduce(x)
+    else:
+        comm = api.Comm(R, N, "float32", "ring", device=env["dev"], launch=variant)
+        ref = env["orc"].ring_allreduce(x)
+    send = to_dev(env, x, "float32")
+    eager = poisoned(env, (R, N), "float32")
+    comm.allreduce(send, eager)
+    assert from_dev(env, eager, "float32").tobytes() == ref.tobytes()
+    out = poisoned(env, (R, N), "float32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        comm.allreduce(send, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        comm.allreduce(send, out)
+    for i in range(4):
+        out.view(torch.uint8).fill_(0xFF)
+        comm.allreduce(send, eager)          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert from_dev(env, out, "float32").tobytes() == ref.tobytes(), i
+        assert from_dev(env, eager, "float32").tobytes() == ref.tobytes(), i
+    assert comm.check() == api.AR_SUCCESS
