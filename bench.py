@@ -28,6 +28,8 @@ METRIC = "all-reduce busBW GB/s + HBM GB/s vs peak, R=8 fp32 64 MiB/rank, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["collective_communication_ring_amd/csrc/ar_ring.hip",
+                  "collective_communication_ring_amd/csrc/ar_pipe.hip",
+                  "collective_communication_ring_amd/csrc/ar_slots.h",
                   "collective_communication_ring_amd/csrc/ar_elem.h"]
 
 
@@ -383,7 +385,7 @@ def mode_counters(args):
     x = inputs.host_inputs("ring_f32_r8_64MiB")
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
-    for launch in ("fused", "step"):
+    for launch in ("fused", "step", "pipelined"):
         comm = api.Comm(R, N, "float32", "ring", device=dev, launch=launch)
         for _ in range(3):
             comm.allreduce(send, recv)

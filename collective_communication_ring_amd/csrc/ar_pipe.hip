@@ -8,13 +8,14 @@
 // same workgroup index g = k mod G of whichever rank holds it, so a chunk
 // passes point to point from workgroup (q-1, g) to workgroup (q, g).
 //
-// Simple protocol per chunk: the producer's threads store the chunk, every
-// wave issues an agent-scope release fence (on gfx950: write back the L2 and
-// wait for its own stores), the workgroup meets at a barrier, and one thread
-// stores the chunk's ready flag coherently; the consumer's thread polls the
-// flag with relaxed agent-scope loads, takes one agent-scope acquire fence
-// when it matches (invalidating stale L1/L2 lines), and the workgroup meets
-// at a barrier before reading the chunk.
+// Simple protocol per chunk: the producer's threads store the chunk with
+// device-scope (write-through) stores, every wave waits for its own stores
+// to complete, the workgroup meets at a barrier, and one thread stores the
+// chunk's ready flag coherently; the consumer's thread polls the flag with
+// relaxed agent-scope loads, the workgroup meets at a barrier, and the chunk
+// is read with device-scope loads.  Nothing is left dirty in an XCD's L2 for
+// another XCD to miss, so no whole-cache writeback or invalidation is needed
+// per chunk.
 // The ordering rules follow the fence/quiet distinction ("Demystifying
 // NVSHMEM ..." summary: a fence orders, only a completed release makes data
 // visible to the target).
@@ -35,21 +36,232 @@
 
 #include "ar_elem.h"
 #include "ar_internal.h"
-#include "ar_slots.h"
 
 namespace ar {
 namespace {
 
-// Poll a ready flag with relaxed agent-scope loads; one acquire fence once it
-// has the wanted value (so the cache invalidation happens once, not per poll).
+// ---- device-scope coherent accesses ----------------------------------------
+// Data that one logical rank writes and another reads inside this kernel goes
+// through buffer instructions with the sc1 cache policy (device scope): a
+// store is written through the XCD's L2 to the device's coherence point and
+// is complete, for s_waitcnt, only once it is there; a load is served from
+// the coherence point, never from a stale line of another XCD's L2.  So the
+// producer needs only to wait for its own stores before the flag, and the
+// consumer needs no cache invalidation -- no whole-L2 writeback per chunk.
+// Each buffer resource covers exactly the chunk it addresses, so an access
+// past the chunk is dropped by the hardware rather than reaching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kCoherent = 16;  // sc1
+constexpr int kPlain = 0;
+
+__device__ inline rsrc_t make_rsrc(const void* p, uint64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                             (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull),
+                                             0x00020000);
+}
+
+// Wait until every memory access this wave issued has completed (stores
+// included: on gfx950 they count in vmcnt).  Also a compiler barrier, so no
+// store is moved past it.
+__device__ inline void wait_own_stores() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <class E, int V, int POL>
+__device__ inline void cload_t(rsrc_t r, uint32_t elem, typename E::A (&o)[V])
+{
+    using T = typename E::T;
+    const uint32_t off = elem * (uint32_t)sizeof(T);
+    if constexpr (V == 1) {
+        if constexpr (sizeof(T) == 4)
+            o[0] = E::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL));
+        else
+            o[0] = E::widen((T)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POL));
+    } else {
+        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = E::from_bits(w[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[2 * i] = E::widen((T)(w[i] & 0xffffu));
+                o[2 * i + 1] = E::widen((T)(w[i] >> 16));
+            }
+        }
+    }
+}
+
+template <class E, int V, int POL>
+__device__ inline void cstore_t(rsrc_t r, uint32_t elem, const typename E::A (&v)[V])
+{
+    using T = typename E::T;
+    const uint32_t off = elem * (uint32_t)sizeof(T);
+    if constexpr (V == 1) {
+        if constexpr (sizeof(T) == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(E::to_bits(v[0]), r, off, 0, POL);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)E::narrow(v[0]), r, off, 0, POL);
+    } else {
+        u32x4 w;
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = E::to_bits(v[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = (uint32_t)E::narrow(v[2 * i]) | ((uint32_t)E::narrow(v[2 * i + 1]) << 16);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, POL);
+    }
+}
+
+template <class E, int V, int POL>
+__device__ inline void cload_a(rsrc_t r, uint32_t elem, typename E::A (&o)[V])
+{
+    const uint32_t off = elem * 4u;
+    if constexpr (V == 1) {
+        o[0] = E::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL));
+    } else {
+#pragma unroll
+        for (int h = 0; h < V / 4; ++h) {
+            u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * h, 0, POL);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[4 * h + i] = E::from_bits(w[i]);
+        }
+    }
+}
+
+template <class E, int V, int POL>
+__device__ inline void cstore_a(rsrc_t r, uint32_t elem, const typename E::A (&v)[V])
+{
+    const uint32_t off = elem * 4u;
+    if constexpr (V == 1) {
+        __builtin_amdgcn_raw_buffer_store_b32(E::to_bits(v[0]), r, off, 0, POL);
+    } else {
+#pragma unroll
+        for (int h = 0; h < V / 4; ++h) {
+            u32x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                w[i] = E::to_bits(v[4 * h + i]);
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, off + 16u * h, 0, POL);
+        }
+    }
+}
+
+// Reduce one chunk of ulen elements: dst = prev + own.  prev is the
+// predecessor's input (FIRST) or its accumulator row; dst is this rank's
+// accumulator row or, at the last reduce step, its output (LAST).  Whole
+// slots move as 16-byte vectors; the ragged end element by element.
+template <class E, int V, bool FIRST, bool LAST>
+__device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_t ulen)
+{
+    using A = typename E::A;
+    constexpr int PREV_POL = FIRST ? kPlain : kCoherent;  // inputs predate the kernel
+    const uint32_t nfull = (uint32_t)(ulen / V);
+    for (uint32_t j0 = threadIdx.x; j0 < nfull; j0 += kBlock * kUnroll) {
+        A x[kUnroll][V], y[kUnroll][V];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t j = j0 + u * kBlock;
+            if (j < nfull) {
+                if constexpr (FIRST)
+                    cload_t<E, V, PREV_POL>(prev, j * V, x[u]);
+                else
+                    cload_a<E, V, PREV_POL>(prev, j * V, x[u]);
+                cload_t<E, V, kPlain>(own, j * V, y[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t j = j0 + u * kBlock;
+            if (j < nfull) {
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    x[u][i] = E::add(x[u][i], y[u][i]);
+                if constexpr (LAST)
+                    cstore_t<E, V, kCoherent>(dst, j * V, x[u]);
+                else
+                    cstore_a<E, V, kCoherent>(dst, j * V, x[u]);
+            }
+        }
+    }
+    const uint32_t e = nfull * V + threadIdx.x;
+    if (e < ulen) {
+        A x[1], y[1];
+        if constexpr (FIRST)
+            cload_t<E, 1, PREV_POL>(prev, e, x);
+        else
+            cload_a<E, 1, PREV_POL>(prev, e, x);
+        cload_t<E, 1, kPlain>(own, e, y);
+        x[0] = E::add(x[0], y[0]);
+        if constexpr (LAST)
+            cstore_t<E, 1, kCoherent>(dst, e, x);
+        else
+            cstore_a<E, 1, kCoherent>(dst, e, x);
+    }
+}
+
+// Copy one chunk of T (SRC_POL: kPlain when the source predates the kernel).
+template <class E, int V, int SRC_POL>
+__device__ inline void chunk_copy(rsrc_t src, rsrc_t dst, uint64_t ulen)
+{
+    using T = typename E::T;
+    const uint32_t nfull = (uint32_t)(ulen / V);
+    for (uint32_t j0 = threadIdx.x; j0 < nfull; j0 += kBlock * kUnroll) {
+        u32x4 w[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t j = j0 + u * kBlock;
+            if (j < nfull)
+                w[u] = __builtin_amdgcn_raw_buffer_load_b128(src, j * 16u, 0, SRC_POL);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t j = j0 + u * kBlock;
+            if (j < nfull)
+                __builtin_amdgcn_raw_buffer_store_b128(w[u], dst, j * 16u, 0, kCoherent);
+        }
+    }
+    const uint32_t e = nfull * V + threadIdx.x;
+    if (V > 1 && e < ulen) {
+        if constexpr (sizeof(T) == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_amdgcn_raw_buffer_load_b32(src, e * 4u, 0, SRC_POL), dst, e * 4u, 0, kCoherent);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_amdgcn_raw_buffer_load_b16(src, e * 2u, 0, SRC_POL), dst, e * 2u, 0, kCoherent);
+    }
+}
+
+template <class E, int V>
+__device__ inline void chunk_copy_scalar(rsrc_t src, rsrc_t dst, uint64_t ulen, bool src_coherent)
+{
+    using T = typename E::T;
+    for (uint32_t e = threadIdx.x; e < ulen; e += kBlock) {
+        if constexpr (sizeof(T) == 4) {
+            uint32_t v = src_coherent ? __builtin_amdgcn_raw_buffer_load_b32(src, e * 4u, 0, kCoherent)
+                                      : __builtin_amdgcn_raw_buffer_load_b32(src, e * 4u, 0, kPlain);
+            __builtin_amdgcn_raw_buffer_store_b32(v, dst, e * 4u, 0, kCoherent);
+        } else {
+            uint16_t v = src_coherent ? __builtin_amdgcn_raw_buffer_load_b16(src, e * 2u, 0, kCoherent)
+                                      : __builtin_amdgcn_raw_buffer_load_b16(src, e * 2u, 0, kPlain);
+            __builtin_amdgcn_raw_buffer_store_b16(v, dst, e * 2u, 0, kCoherent);
+        }
+    }
+}
+
+// Poll a ready flag with relaxed agent-scope loads (coherent, no cache
+// invalidation).
 __device__ inline bool wait_flag(const uint64_t* flag, uint64_t want, uint64_t deadline,
                                  const uint32_t* err)
 {
     for (uint32_t spin = 0;; ++spin) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want)
             return true;
-        }
         if ((spin & 31u) == 31u) {
             if ((uint64_t)wall_clock64() > deadline)
                 return false;
@@ -65,6 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
 {
     using E = Elem<DT>;
     using T = typename E::T;
+    using A = typename E::A;
     const int R = a.R;
     const int q = blockIdx.x % R;
     const int g = blockIdx.x / R;
@@ -72,6 +285,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
     const int nsteps = (OP == kOpAllReduce) ? 2 * (R - 1) : (OP == kOpReduceScatter) ? R - 1 : R;
     uint32_t* err = &a.ctrl[kCtrlError];
     uint64_t* basep = reinterpret_cast<uint64_t*>(a.ctrl + kCtrlPipeBase);
+    const T* send = static_cast<const T*>(a.send);
+    A* part = static_cast<A*>(a.part);
+    T* out = static_cast<T*>(a.out);
 
     __shared__ uint64_t s_base, s_deadline;
     __shared__ int s_fail;
@@ -82,8 +298,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
     }
     __syncthreads();
     const uint64_t base = s_base;
-    const uint64_t slot_step = (uint64_t)kBlock * kUnroll;
-    T* out = static_cast<T*>(a.out);
+    const int p = mod_r(q - 1, R);
 
     for (int s = 0; s < nsteps; ++s) {
         const int c = (OP == kOpAllGather) ? mod_r(q - s, R) : mod_r(q - s - 2, R);
@@ -94,34 +309,48 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
             if (ulo >= len)
                 break;  // a short trailing segment has fewer chunks (same for every rank)
             const uint64_t ulen = min(a.unit, len - ulo);
+            const uint64_t e0 = lo + ulo;  // first element of the chunk in a full row
             uint64_t* flag = a.flags + (uint64_t)c * a.flag_stride + k;
             if (s > 0) {
                 if (threadIdx.x == 0 && !wait_flag(flag, base + (uint64_t)s, s_deadline, err))
                     s_fail = 1;
                 __syncthreads();
             }
-            const uint64_t nslots = (ulen + V - 1) / V;
             if (OP != kOpAllGather && s <= R - 2) {
-                ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo + ulo);
-                if (OP == kOpReduceScatter)
-                    p.dstT = static_cast<T*>(a.out) + (uint64_t)q * a.out_row + ulo;
-                for (uint64_t j0 = threadIdx.x; j0 < nslots; j0 += slot_step)
-                    reduce_step_slots<E, V>(p, s, R, ulen, j0, kBlock);
-            } else if (OP == kOpAllGather && s == 0) {
-                const T* src = static_cast<const T*>(a.send) + (uint64_t)q * a.send_row + ulo;
-                T* dst = out + (uint64_t)q * a.out_row + lo + ulo;
-                for (uint64_t j0 = threadIdx.x; j0 < nslots; j0 += slot_step)
-                    copy_slots<E, V>(src, dst, ulen, j0, kBlock);
+                const bool first = (s == 0), last = (s == R - 2);
+                const rsrc_t own = make_rsrc(send + (uint64_t)q * a.send_row + e0, ulen * sizeof(T));
+                const rsrc_t prevT = make_rsrc(send + (uint64_t)p * a.send_row + e0, ulen * sizeof(T));
+                const rsrc_t prevA = make_rsrc(part + (uint64_t)p * a.N + e0, ulen * 4);
+                const rsrc_t dstA = make_rsrc(part + (uint64_t)q * a.N + e0, ulen * 4);
+                T* dT = out + (uint64_t)q * a.out_row + (OP == kOpReduceScatter ? ulo : e0);
+                const rsrc_t dstT = make_rsrc(dT, ulen * sizeof(T));
+                if (first && last)
+                    chunk_reduce<E, V, true, true>(prevT, own, dstT, ulen);
+                else if (first)
+                    chunk_reduce<E, V, true, false>(prevT, own, dstA, ulen);
+                else if (last)
+                    chunk_reduce<E, V, false, true>(prevA, own, dstT, ulen);
+                else
+                    chunk_reduce<E, V, false, false>(prevA, own, dstA, ulen);
             } else {
-                const int p = mod_r(q - 1, R);
-                const T* src = out + (uint64_t)p * a.out_row + lo + ulo;
-                T* dst = out + (uint64_t)q * a.out_row + lo + ulo;
-                for (uint64_t j0 = threadIdx.x; j0 < nslots; j0 += slot_step)
-                    copy_slots<E, V>(src, dst, ulen, j0, kBlock);
+                // a copy step; at all-gather step 0 the source is the rank's own
+                // shard in send (written before the kernel), else the
+                // predecessor's output row (written in this kernel)
+                const bool placement = (OP == kOpAllGather && s == 0);
+                const T* srcp = placement ? send + (uint64_t)q * a.send_row + ulo
+                                          : out + (uint64_t)p * a.out_row + e0;
+                const rsrc_t src = make_rsrc(srcp, ulen * sizeof(T));
+                const rsrc_t dst = make_rsrc(out + (uint64_t)q * a.out_row + e0, ulen * sizeof(T));
+                if constexpr (V == 1)
+                    chunk_copy_scalar<E, V>(src, dst, ulen, !placement);
+                else if (placement)
+                    chunk_copy<E, V, kPlain>(src, dst, ulen);
+                else
+                    chunk_copy<E, V, kCoherent>(src, dst, ulen);
             }
-            // publish: every wave releases its own stores at agent scope, the
-            // workgroup meets, then one thread stores the flag
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            // publish: each wave waits for its own (write-through) stores, the
+            // workgroup meets, one thread stores the flag coherently
+            wait_own_stores();
             __syncthreads();
             if (threadIdx.x == 0)
                 __hip_atomic_store(flag, base + (uint64_t)s + 1, __ATOMIC_RELAXED,
