@@ -24,7 +24,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kDefaultChunkBytes = 512 * 1024;
 constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
-constexpr int64_t kDefaultTreeMaxBytes = 64 * 1024;  // AR_AUTO: tree up to this per rank
+constexpr int64_t kDefaultTreeMaxBytes = 128 * 1024; // AR_AUTO: tree up to this per rank
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -176,18 +176,26 @@ uint64_t timeout_ticks(const ar_comm* c)
     return (uint64_t)((double)c->timeout_us * c->ticks_per_us);
 }
 
-int resolve_algo(const ar_comm* c, size_t count)
-{
-    if (c->algo != AR_AUTO)
-        return c->algo;
-    return (int64_t)(count * (size_t)elem_size(c->dtype)) <= c->tree_max_bytes ? AR_TREE : AR_RING;
-}
-
 int resolve_launch(const ar_comm* c)
 {
     if (c->launch != AR_LAUNCH_AUTO)
         return c->launch;
     return AR_LAUNCH_FUSED;
+}
+
+// AR_AUTO: tree for small messages, ring for large ones ("NCCL and NVSHMEM
+// -- two GPU communication models, side by side": NCCL picks by size).  The
+// threshold is the measured crossover between the tree and the ring forms in
+// which every hop is a hand-off between ranks (step, pipelined).  The fused
+// ring has no hand-offs and is faster than the tree at every size on one
+// GPU, so with it the ring is kept.
+int resolve_algo(const ar_comm* c, size_t count)
+{
+    if (c->algo != AR_AUTO)
+        return c->algo;
+    if (resolve_launch(c) == AR_LAUNCH_FUSED)
+        return AR_RING;
+    return (int64_t)(count * (size_t)elem_size(c->dtype)) <= c->tree_max_bytes ? AR_TREE : AR_RING;
 }
 
 // Do the 16-byte vector kernels apply?  Every row start and every segment

@@ -54,7 +54,10 @@ typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
  * NVSHMEM -- two GPU communication models, side by side", section "double
  * binary tree").  AR_AUTO picks by message size: tree for small messages,
  * ring for large ones (same page: tree for small messages, ring for large,
- * chosen automatically). */
+ * chosen automatically) -- when the ring would run in a form whose every
+ * step is a hand-off between ranks (AR_LAUNCH_STEP / AR_LAUNCH_PIPELINED);
+ * the default fused ring is faster than the tree at every size on one GPU
+ * and is kept. */
 typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
 
 /* AR_SIMPLE: bulk data, then a release, then a ready flag (or a kernel

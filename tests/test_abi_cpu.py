@@ -84,6 +84,10 @@ def test_options_round_trip(api):
 def test_plan_picks_tree_for_small_and_ring_for_large(api):
     c = api.ar_init(8, 1 << 20, api.AR_FLOAT32, api.AR_AUTO)
     try:
+        assert api.ar_plan(c, 16)[0] == api.AR_RING  # default fused ring: no tree
+        api.ar_set_option(c, api.AR_OPT_LAUNCH, api.AR_LAUNCH_PIPELINED)
+        assert api.ar_plan(c, 16)[0] == api.AR_TREE
+        assert api.ar_plan(c, 32 * 1024)[0] == api.AR_TREE   # 128 KiB default
         api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, 64 * 1024)
         assert api.ar_plan(c, 16)[0] == api.AR_TREE
         assert api.ar_plan(c, 16 * 1024)[0] == api.AR_TREE

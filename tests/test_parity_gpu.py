@@ -224,7 +224,8 @@ def test_tree_order_pin(env):
 def test_auto_selects_tree_then_ring(env):
     api = env["api"]
     x = env["inputs"].draw("normal", 8, 1 << 16, seed=12)
-    comm = api.Comm(8, 1 << 16, "float32", "auto", device=env["dev"], tree_max_bytes=4096)
+    comm = api.Comm(8, 1 << 16, "float32", "auto", device=env["dev"], tree_max_bytes=4096,
+                    launch="pipelined")
     assert comm.plan(1024)[0] == api.AR_TREE and comm.plan(1 << 16)[0] == api.AR_RING
     for N, ref in ((1024, env["orc"].tree_allreduce(x[:, :1024].copy())),
                    (1 << 16, env["orc"].ring_allreduce(x))):
