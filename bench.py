@@ -386,7 +386,7 @@ def mode_counters(args):
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
     for launch in ("fused", "step", "pipelined"):
-        comm = api.Comm(R, N, "float32", "ring", device=dev, launch=launch)
+        comm = api.Comm(R, N, "float32", "ring", device=dev, launch=launch, grid=args.grid)
         for _ in range(3):
             comm.allreduce(send, recv)
         torch.cuda.synchronize()
@@ -400,6 +400,33 @@ def mode_counters(args):
     return 0
 
 
+def mode_tune(args):
+    """Time the R = 8 fp32 64 MiB/rank all-reduce for a list of grid sizes
+    (workgroups per launch) in one launch form."""
+    import torch
+    from collective_communication_ring_amd import api, inputs
+    R, N, s = 8, 16_777_216, 4
+    dev = torch.device("cuda:0")
+    x = inputs.host_inputs("ring_f32_r8_64MiB")
+    send = torch.from_numpy(x).to(dev)
+    recv = torch.empty_like(send)
+    import oracle
+    ref = oracle.ring_allreduce(x)
+    res = []
+    for grid in [int(g) for g in args.grids.split(",")]:
+        comm = api.Comm(R, N, "float32", "ring", "simple", device=dev, launch=args.launch,
+                        chunk_bytes=args.chunk_bytes, grid=grid)
+        _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
+                                    torch)
+        ms = total_ms / args.steps
+        ok = recv.cpu().numpy().tobytes() == ref.tobytes()
+        res.append(dict(grid=grid, ms=ms, busbw=N * s / (ms / 1e3) / 1e9 * 1.75, exact=ok))
+        log("grid %6d  %.4f ms  busBW %.1f GB/s  exact=%s" % (grid, ms, res[-1]["busbw"], ok))
+        comm.close()
+    print(json.dumps(dict(mode="tune", launch=args.launch, results=res)), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,10 +436,12 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
                     choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream",
-                             "counters"])
+                             "counters", "tune"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--grids", default="256,512,768,1024,1280,1536,1792,2048")
+    ap.add_argument("--chunk-bytes", type=int, default=512 * 1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="sweep / tree-vs-ring: time host-enqueued calls instead of graph replays")
@@ -424,7 +453,8 @@ def main():
               % (args.gpus, world), file=sys.stderr)
         return 2
     fn = {"headline": headline, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
-          "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters}[args.mode]
+          "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
+          "tune": mode_tune}[args.mode]
     return fn(args)
 
 

@@ -25,22 +25,25 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile libar.so (to `out`); `defines` are extra -D settings such as
+    AR_BLOCK / AR_UNROLL for tuning builds."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs + ["-o", tmp]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ([HIPCC] + FLAGS + ["-D" + d for d in defines]
+           + ["-I", os.path.join(ROOT, "include"), "-I", CSRC] + srcs + ["-o", tmp])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines()
+    log = "\n".join(l for l in r.stdout.splitlines()
                     if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
     if r.returncode != 0:
-        sys.stderr.write(out + "\n")
+        sys.stderr.write(log + "\n")
         raise RuntimeError("hipcc failed building libar.so")
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -69,6 +69,14 @@ struct Elem<AR_BF16> {
 
 // ---- slot loads and stores ----------------------------------------------
 
+// 16-byte load of user input (a T row of send).  Every input element is read
+// exactly once per collective, so the load is marked non-temporal: it should
+// not displace the partial sums that the next step re-reads from L2.
+__device__ inline u32x4 load16(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 template <class E, int V>
 __device__ inline void load_t(const typename E::T* p, typename E::A (&o)[V])
 {
@@ -76,13 +84,13 @@ __device__ inline void load_t(const typename E::T* p, typename E::A (&o)[V])
         o[0] = E::widen(p[0]);
     } else if constexpr (sizeof(typename E::T) == 4) {
         static_assert(V == 4, "16-byte slot of 32-bit elements");
-        u32x4 r = *reinterpret_cast<const u32x4*>(p);
+        u32x4 r = load16(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[i] = E::from_bits(r[i]);
     } else {
         static_assert(V == 8, "16-byte slot of 16-bit elements");
-        u32x4 r = *reinterpret_cast<const u32x4*>(p);
+        u32x4 r = load16(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             o[2 * i] = E::widen((typename E::T)(r[i] & 0xffffu));

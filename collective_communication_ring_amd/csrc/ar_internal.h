@@ -95,8 +95,14 @@ int resident_ring_fused(int dtype, bool vec);
 int resident_ring_pipelined(int dtype, bool vec);
 int resident_tree_ll(int dtype);
 
-constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
-constexpr int kUnroll = 4;       // 16-byte vectors per thread per pass
+#ifndef AR_BLOCK
+#define AR_BLOCK 256
+#endif
+#ifndef AR_UNROLL
+#define AR_UNROLL 4
+#endif
+constexpr int kBlock = AR_BLOCK;   // threads per workgroup (4 wave64 by default)
+constexpr int kUnroll = AR_UNROLL; // 16-byte vectors per thread per pass
 constexpr int kTreeEPT = 4;      // LL lines per thread per tree kernel pass
 
 }  // namespace ar
