@@ -115,6 +115,7 @@ struct ar_comm {
     int64_t timeout_us = kDefaultTimeoutUs;
     int64_t debug = 0;
     int64_t tree_max_bytes = kDefaultTreeMaxBytes;
+    int64_t mute_rank = -1;  // testing the watchdog only
     // schedule
     TreeTable tt{};
     // workspace layout
@@ -229,6 +230,7 @@ int ring_grid_x(const ar_comm* c, uint64_t S, bool vec)
 
 int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
 {
+    a.mute_rank = (int)c->mute_rank;
     const bool vec = vector_ok(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row);
     const int launch = resolve_launch(c);
     hipError_t e = hipSuccess;
@@ -314,6 +316,7 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     a.R = c->R;
     a.line_stride = c->tree_lines;
     a.timeout_ticks = timeout_ticks(c);
+    a.mute_rank = (int)c->mute_rank;
     a.tt = c->tt;
     // every workgroup must be resident at once: cap the piece accordingly
     const uint64_t per_wg = (uint64_t)kBlock * kTreeEPT;
@@ -617,6 +620,11 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
             return AR_ERR_INVALID_ARG;
         c->tree_max_bytes = v;
         return AR_SUCCESS;
+    case AR_OPT_DEBUG_MUTE_RANK:
+        if (v < -1 || v >= c->R)
+            return AR_ERR_INVALID_ARG;
+        c->mute_rank = v;
+        return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }
@@ -634,6 +642,7 @@ int ar_get_option(ar_comm_t c, int option, int64_t* v)
     case AR_OPT_ALGO: *v = c->algo; return AR_SUCCESS;
     case AR_OPT_PROTO: *v = c->proto; return AR_SUCCESS;
     case AR_OPT_TREE_MAX_BYTES: *v = c->tree_max_bytes; return AR_SUCCESS;
+    case AR_OPT_DEBUG_MUTE_RANK: *v = c->mute_rank; return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }

@@ -60,6 +60,7 @@ struct RingArgs {
     int op;           // Op
     int step;         // step-per-launch mode: the step this launch runs
     int per_rank_wg;  // pipelined ring: workgroups per logical rank
+    int mute_rank;    // testing only: rank that skips publishing (-1: none)
     uint64_t timeout_ticks;
 };
 
@@ -76,6 +77,7 @@ struct TreeArgs {
     uint64_t line_stride; // lines per (tree, rank) in up/down
     int R;
     int blocks_per_rank;  // workgroups per (tree, rank)
+    int mute_rank;        // testing only: rank that skips publishing (-1: none)
     uint64_t timeout_ticks;
     TreeTable tt;
 };

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
             // workgroup meets, one thread stores the flag coherently
             wait_own_stores();
             __syncthreads();
-            if (threadIdx.x == 0)
+            if (threadIdx.x == 0 && q != a.mute_rank)
                 __hip_atomic_store(flag, base + (uint64_t)s + 1, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }

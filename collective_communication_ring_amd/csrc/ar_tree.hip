@@ -126,10 +126,11 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
             }
         }
     }
+    const bool publish = (v != a.mute_rank);
     if (parent >= 0) {
 #pragma unroll
         for (int k = 0; k < kTreeEPT; ++k)
-            if (ok[k])
+            if (ok[k] && publish)
                 ll_put(up_mine + idx[k], E::to_bits(acc[k]), epoch);
         // broadcast down: the root's sum arrives from the parent
 #pragma unroll
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
         uint64_t* down_ch = a.down + ((uint64_t)t * R + ch) * a.line_stride;
 #pragma unroll
         for (int k = 0; k < kTreeEPT; ++k)
-            if (ok[k])
+            if (ok[k] && publish)
                 ll_put(down_ch + idx[k], E::to_bits(acc[k]), epoch);
     }
     if (timed_out)

@@ -70,13 +70,16 @@ def test_options_round_trip(api):
         for opt, val in ((api.AR_OPT_CHUNK_BYTES, 4096), (api.AR_OPT_LAUNCH, api.AR_LAUNCH_STEP),
                          (api.AR_OPT_GRID, 512), (api.AR_OPT_TIMEOUT_US, 1000),
                          (api.AR_OPT_ALGO, api.AR_TREE), (api.AR_OPT_PROTO, api.AR_LL),
-                         (api.AR_OPT_TREE_MAX_BYTES, 1 << 20)):
+                         (api.AR_OPT_TREE_MAX_BYTES, 1 << 20), (api.AR_OPT_DEBUG_MUTE_RANK, 2),
+                         (api.AR_OPT_DEBUG_MUTE_RANK, -1)):
             api.ar_set_option(c, opt, val)
             assert api.ar_get_option(c, opt) == val
         with pytest.raises(api.ArError):
             api.ar_set_option(c, api.AR_OPT_LAUNCH, 99)
         with pytest.raises(api.ArError):
             api.ar_set_option(c, 1234, 1)
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, api.AR_OPT_DEBUG_MUTE_RANK, 4)  # R = 4
     finally:
         api.ar_destroy(c)
 

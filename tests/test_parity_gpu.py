@@ -348,3 +348,89 @@ def test_graph_replay_matches_eager(env, variant):
         assert from_dev(env, out, "float32").tobytes() == ref.tobytes(), i
         assert from_dev(env, eager, "float32").tobytes() == ref.tobytes(), i
     assert comm.check() == api.AR_SUCCESS
+
+
+# ---------------------------------------------------------------- config 3 at full size
+
+def _segment_samples(rng, N, R, m):
+    """m element indices from each ring segment of an N-element row, in
+    segment order, always including each segment's first and last element."""
+    S = -(-N // R)
+    idx = []
+    for c in range(R):
+        lo, hi = min(c * S, N), min((c + 1) * S, N)
+        pick = set([lo, hi - 1]) | set(rng.integers(lo, hi, size=m - 2).tolist())
+        pick = sorted(pick)
+        while len(pick) < m:  # keep exactly m per segment
+            pick.append(pick[-1])
+        idx.extend(pick[:m])
+    return np.array(idx, dtype=np.int64)
+
+
+@pytest.mark.parametrize("launch", ["auto", "step", "pipelined"])
+def test_cfg3_largest_size_sampled(env, launch):
+    """R = 8, fp32, 1 GiB per rank (the sweep's largest size) in the launch form
+    the benchmark times: sampled outputs against the oracle.  The ring's fold
+    for an element depends only on its segment, so m samples from each
+    segment, laid out as an [R, R*m] array, have the same fold order there."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R, N, m = 8, 1 << 28, 64
+    g = torch.Generator(device=env["dev"])
+    g.manual_seed(3)
+    send = torch.randn((R, N), generator=g, device=env["dev"], dtype=torch.float32)
+    recv = torch.full_like(send, float("nan"))
+    comm = api.Comm(R, N, "float32", "ring", device=env["dev"],
+                    launch=None if launch == "auto" else launch)
+    comm.allreduce(send, recv)
+    torch.cuda.synchronize()
+    assert comm.check() == api.AR_SUCCESS
+    idx = _segment_samples(np.random.default_rng(0), N, R, m)
+    ti = torch.from_numpy(idx).to(env["dev"])
+    xs = send[:, ti].cpu().numpy()
+    ys = recv[:, ti].cpu().numpy()
+    ref = orc.ring_allreduce(np.ascontiguousarray(xs))
+    assert ys.tobytes() == ref.tobytes()
+    check_tolerance(env, ys, xs, "float32")
+    # every element written: no NaN left anywhere (checked on the device)
+    assert not torch.isnan(recv).any().item()
+    del send, recv, comm
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- watchdog
+
+@pytest.mark.parametrize("variant", ["tree", "pipelined"])
+def test_watchdog_reports_timeout_and_recovers(env, variant):
+    """Forced from the host: one logical rank skips publishing, so its
+    consumers' bounded waits (5 ms here) expire.  The kernel still finishes,
+    ar_check reports AR_ERR_TIMEOUT once, and the next call is correct."""
+    import time
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R, N = 8, 4096
+    x = env["inputs"].draw("normal", R, N, seed=23)
+    if variant == "tree":
+        comm = api.Comm(R, N, "float32", "tree", "ll", device=env["dev"], timeout_us=5000)
+        ref = orc.tree_allreduce(x)
+    else:
+        comm = api.Comm(R, N, "float32", "ring", device=env["dev"], launch="pipelined",
+                        timeout_us=5000)
+        ref = orc.ring_allreduce(x)
+    send = to_dev(env, x, "float32")
+    recv = poisoned(env, (R, N), "float32")
+    comm.allreduce(send, recv)            # warm (first call initialises the device facts)
+    torch.cuda.synchronize()
+    assert comm.check() == api.AR_SUCCESS
+    comm.set_option(api.AR_OPT_DEBUG_MUTE_RANK, 3)
+    t0 = time.perf_counter()
+    comm.allreduce(send, recv)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert comm.check() == api.AR_ERR_TIMEOUT
+    assert comm.check() == api.AR_SUCCESS  # the error word was cleared
+    assert dt < 1.0, dt
+    comm.set_option(api.AR_OPT_DEBUG_MUTE_RANK, -1)
+    for _ in range(2):
+        recv = poisoned(env, (R, N), "float32")
+        comm.allreduce(send, recv)
+        assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
+    assert comm.check() == api.AR_SUCCESS
