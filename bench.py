@@ -232,6 +232,13 @@ def mode_sweep(args):
             out.flush()
         del sv, rv
     assert comm.check() == api.AR_SUCCESS
+    import oracle
+    cpu = []
+    for N in (256, 65536, 1 << 22):  # 1 KiB, 256 KiB, 16 MiB per rank
+        xs = send_flat[:R * N].view(R, N).cpu().numpy()
+        t_or, n_or = oracle_time_s(lambda: oracle.ring_allreduce(xs), 3.0)
+        cpu.append(dict(bytes_per_rank=N * s, t_us=t_or * 1e6, calls=n_or))
+        log("oracle %10d B/rank  %10.1f us" % (N * s, t_or * 1e6))
     fit = measure.fit_alpha_beta([r["bytes_per_rank"] for r in rows], [r["t_us"] / 1e6 for r in rows])
     small = [r["t_us"] for r in rows if r["bytes_per_rank"] <= 4096]
     large = [r for r in rows if r["bytes_per_rank"] >= 64 << 20]
@@ -244,12 +251,46 @@ def mode_sweep(args):
             (b["t_us"] - a["t_us"]) / 1e6) / 1e9
     summary = dict(mode="sweep_fit", R=R, dtype="f32", launch=args.launch, **fit,
                    bus_rate_GBps=fit["inv_beta_GBps"] * measure.busbw_factor("allreduce", R),
-                   **cross)
+                   **cross, cpu_baseline=dict(kind="oracle", cores=1, points=cpu))
     if out:
         out.write(json.dumps(summary) + "\n")
         out.close()
     print(json.dumps(summary), flush=True)
     return 0
+
+
+def ll_hop_latency_us(torch, iters=20000):
+    """One-way latency of an 8-byte LL line between two workgroups, on
+    different XCDs and on the same XCD (the tree's per-hop bound)."""
+    from collective_communication_ring_amd import api
+    dev = torch.device("cuda:0")
+    lines = torch.zeros(64, dtype=torch.int64, device=dev)
+    result = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, apart in (("xcd_apart", 1), ("same_xcd", 0)):
+        api.ar_ll_pingpong(lines.data_ptr(), result.data_ptr(), 100, apart, 2_000_000, st)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.ar_ll_pingpong(lines.data_ptr(), result.data_ptr(), iters, apart, 2_000_000, st)
+        e1.record()
+        torch.cuda.synchronize()
+        if int(result.item()) != 0:
+            raise RuntimeError("LL ping-pong timed out")
+        out[name] = e0.elapsed_time(e1) * 1e3 / (2 * iters)
+    return out
+
+
+def oracle_time_s(fn, target_s=3.0, max_calls=50):
+    """Average host seconds per call of an oracle function (bounded sample)."""
+    ts = []
+    t_start = time.perf_counter()
+    while not ts or (time.perf_counter() - t_start < target_s and len(ts) < max_calls):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sum(ts) / len(ts), len(ts)
 
 
 def mode_tree_vs_ring(args):
@@ -288,7 +329,18 @@ def mode_tree_vs_ring(args):
                 out.write(json.dumps(row) + "\n")
     for c in comms.values():
         assert c.check() == api.AR_SUCCESS
-    summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res)
+    hop = ll_hop_latency_us(torch)
+    log("LL one-way hop latency: %s" % hop)
+    # latency roofline of the tree: 2 * depth hops (up, then down) per call
+    import oracle
+    depth = 3 if R == 8 else None
+    t_or, n_or = oracle_time_s(lambda: oracle.tree_allreduce(x), 3.0)
+    summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res,
+                   ll_hop_us=hop, tree_depth=depth,
+                   tree_hop_bound_us=2 * depth * hop["xcd_apart"] if depth else None,
+                   cpu_baseline=dict(kind="oracle", cores=1, value_us=t_or * 1e6,
+                                     sample="tree all-reduce, %d B/rank, %d calls"
+                                            % (Nmax * s, n_or)))
     if out:
         out.write(json.dumps(summary) + "\n")
         out.close()
@@ -334,6 +386,14 @@ def mode_buckets(args):
                          hbm_alg_GBps=(alg / t / 1e9) if alg else None)
         log(name, rep[name])
     assert comm.check() == api.AR_SUCCESS
+    import numpy as np
+    import oracle
+    xh = xs[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    t_rs, _ = oracle_time_s(lambda: oracle.ring_reduce_scatter(xh, "bf16"), 0.0, 1)
+    sh = oracle.ring_reduce_scatter(xh, "bf16")
+    t_ag, _ = oracle_time_s(lambda: oracle.ring_all_gather(sh, "bf16"), 0.0, 1)
+    rep["cpu_baseline"] = dict(kind="oracle", cores=1, sample="bucket 0, one call each",
+                               reduce_scatter_us=t_rs * 1e6, all_gather_us=t_ag * 1e6)
     summary = dict(mode="buckets", R=R, dtype="bf16", buckets=B, count_per_rank=N, **rep)
     print(json.dumps(summary), flush=True)
     return 0

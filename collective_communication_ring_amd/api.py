@@ -67,6 +67,7 @@ def lib():
         "ar_last_hip_error": ([vp], i),
         "ar_stream_add": ([vp, vp, vp, sz, vp], i),
         "ar_stream_copy": ([vp, vp, sz, vp], i),
+        "ar_ll_pingpong": ([vp, vp, i, i, i64, vp], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -159,6 +160,11 @@ def ar_stream_add(a_ptr, b_ptr, c_ptr, n, stream=0):
 
 def ar_stream_copy(src_ptr, dst_ptr, nbytes, stream=0):
     _ok(lib().ar_stream_copy(src_ptr, dst_ptr, nbytes, stream), "ar_stream_copy")
+
+
+def ar_ll_pingpong(lines_ptr, result_ptr, iters, xcd_apart, timeout_us=2_000_000, stream=0):
+    _ok(lib().ar_ll_pingpong(lines_ptr, result_ptr, iters, int(bool(xcd_apart)), timeout_us, stream),
+        "ar_ll_pingpong")
 
 
 # ---- torch convenience wrapper ---------------------------------------------

@@ -117,3 +117,66 @@ extern "C" int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* s
                        reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), nvec);
     return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
 }
+
+// ---- LL hop-latency probe ---------------------------------------------------
+
+namespace ar {
+namespace {
+
+// Workgroups "a" and "b" (by position in the grid) bounce one LL line: a
+// writes round r into line 0 and waits for round r in line 1; b waits for
+// line 0 then answers in line 1.  Idle workgroups of the grid (used only to
+// place a and b on the wanted XCDs) exit at once.
+__global__ void k_ll_pingpong(uint64_t* lines, uint32_t* result, int iters, int wa, int wb,
+                              uint64_t timeout_ticks)
+{
+    const int me = blockIdx.x;
+    if ((me != wa && me != wb) || threadIdx.x != 0)
+        return;
+    const uint64_t deadline = (uint64_t)wall_clock64() + timeout_ticks;
+    uint64_t* mine = lines + (me == wa ? 0 : 16);
+    const uint64_t* theirs = lines + (me == wa ? 16 : 0);
+    for (uint32_t r = 1; r <= (uint32_t)iters; ++r) {
+        if (me == wa)
+            __hip_atomic_store(mine, ((uint64_t)r << 32) | r, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        for (uint32_t spin = 0;; ++spin) {
+            const uint64_t v = __hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(v >> 32) == r)
+                break;
+            if ((spin & 255u) == 255u && (uint64_t)wall_clock64() > deadline) {
+                __hip_atomic_store(result, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return;
+            }
+        }
+        if (me == wb)
+            __hip_atomic_store(mine, ((uint64_t)r << 32) | r, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+}  // namespace
+}  // namespace ar
+
+extern "C" int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int xcd_apart,
+                              int64_t timeout_us, void* stream)
+{
+    using namespace ar;
+    if (!lines || !result_dev || iters < 1 || timeout_us <= 0 || ((uintptr_t)lines & 255u))
+        return AR_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+        return AR_ERR_HIP;
+    const uint64_t ticks = (uint64_t)timeout_us * (uint64_t)(khz > 0 ? khz : 100000) / 1000u;
+    hipError_t e = launch_fill_u64(static_cast<uint64_t*>(lines), 0ull, 32, st);
+    if (e == hipSuccess)
+        e = launch_fill_u32(result_dev, 0u, 1, st);
+    if (e != hipSuccess)
+        return AR_ERR_HIP;
+    const int wb = xcd_apart ? 1 : 8;  // round-robin dispatch: id mod 8 is the XCD
+    hipLaunchKernelGGL(k_ll_pingpong, dim3(wb + 1), dim3(64), 0, st,
+                       static_cast<uint64_t*>(lines), result_dev, iters, 0, wb, ticks);
+    return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
+}

@@ -192,6 +192,18 @@ int ar_tree_parent(ar_comm_t comm, int tree, int r);
 int ar_stream_add(const float* a, const float* b, float* c, size_t n, void* stream);
 int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* stream);
 
+/* LL hop-latency probe (measurement utility): two workgroups pass one 8-byte
+ * LL line back and forth `iters` times -- each waits for the other's line
+ * with the current round number as flag, then answers.  `lines` is device
+ * memory of at least 256 bytes, zeroed by the call.  `xcd_apart` != 0 puts
+ * the two workgroups on different XCDs (workgroup ids 0 and 1 under the
+ * round-robin dispatch), 0 on the same XCD (ids 0 and 8).  Every wait is
+ * bounded by `timeout_us`; `*result_dev` (device uint32) receives 0 on
+ * success, 1 on a timeout.  Time the call with events: one-way latency =
+ * elapsed / (2 * iters). */
+int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int xcd_apart,
+                   int64_t timeout_us, void* stream);
+
 /* Message for a status code (static storage). */
 const char* ar_status_string(int status);
 

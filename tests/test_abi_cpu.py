@@ -126,3 +126,12 @@ def test_status_strings(api):
     for s in range(7):
         assert api.ar_status_string(s)
     assert "timeout" in api.ar_status_string(api.AR_ERR_TIMEOUT)
+
+
+def test_utilities_reject_bad_arguments(api):
+    L = api.lib()
+    assert L.ar_stream_add(None, None, None, 16, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_stream_add(None, None, None, 0, None) == api.AR_SUCCESS
+    assert L.ar_stream_copy(16, 32, 15, None) == api.AR_ERR_INVALID_ARG  # not a multiple of 16
+    assert L.ar_ll_pingpong(None, None, 10, 1, 1000, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_ll_pingpong(256, 512, 0, 1, 1000, None) == api.AR_ERR_INVALID_ARG

@@ -434,3 +434,26 @@ def test_watchdog_reports_timeout_and_recovers(env, variant):
         comm.allreduce(send, recv)
         assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
     assert comm.check() == api.AR_SUCCESS
+
+
+def test_measurement_utilities(env):
+    """The streaming references and the LL ping-pong probe run and finish."""
+    torch, api = env["torch"], env["api"]
+    st = torch.cuda.current_stream().cuda_stream
+    a = torch.randn(4099, device=env["dev"])
+    b = torch.randn(4099, device=env["dev"])
+    c = torch.empty_like(a)
+    api.ar_stream_add(a.data_ptr(), b.data_ptr(), c.data_ptr(), a.numel(), st)
+    torch.cuda.synchronize()
+    assert torch.equal(c, a + b)
+    d = torch.empty_like(a)
+    api.ar_stream_copy(a.data_ptr(), d.data_ptr(), 4096 * 4, st)
+    torch.cuda.synchronize()
+    assert torch.equal(d[:4096], a[:4096])
+    lines = torch.zeros(64, dtype=torch.int64, device=env["dev"])
+    res = torch.ones(1, dtype=torch.int32, device=env["dev"])
+    for apart in (1, 0):
+        api.ar_ll_pingpong(lines.data_ptr(), res.data_ptr(), 1000, apart, 2_000_000, st)
+        torch.cuda.synchronize()
+        assert int(res.item()) == 0
+        assert (int(lines[0].item()) >> 32) == 1000 and (int(lines[16].item()) >> 32) == 1000
