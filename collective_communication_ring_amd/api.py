@@ -22,7 +22,9 @@ AR_SUCCESS, AR_ERR_INVALID_ARG, AR_ERR_INVALID_USAGE, AR_ERR_UNSUPPORTED = 0, 1,
 AR_ERR_HIP, AR_ERR_TIMEOUT, AR_ERR_INTERNAL = 4, 5, 6
 AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 3
 (AR_OPT_CHUNK_BYTES, AR_OPT_LAUNCH, AR_OPT_GRID, AR_OPT_TIMEOUT_US, AR_OPT_DEBUG,
- AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK) = range(9)
+ AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK, AR_OPT_REDOP) = range(10)
+AR_SUM, AR_MAX, AR_MIN, AR_AVG = 0, 1, 2, 3
+REDOPS = {"sum": AR_SUM, "max": AR_MAX, "min": AR_MIN, "avg": AR_AVG}
 
 DTYPES = {"int32": AR_INT32, "float32": AR_FLOAT32, "bf16": AR_BF16}
 ALGOS = {"ring": AR_RING, "tree": AR_TREE, "auto": AR_AUTO}
@@ -194,6 +196,8 @@ class Comm:
         if launch is not None:
             self.set_option(AR_OPT_LAUNCH, LAUNCHES[launch] if isinstance(launch, str) else launch)
         for k, v in options.items():
+            if k == "redop" and isinstance(v, str):
+                v = REDOPS[v]
             self.set_option(globals()["AR_OPT_" + k.upper()], v)
         nbytes = ar_workspace_bytes(self.handle)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)

@@ -116,6 +116,7 @@ struct ar_comm {
     int64_t debug = 0;
     int64_t tree_max_bytes = kDefaultTreeMaxBytes;
     int64_t mute_rank = -1;  // testing the watchdog only
+    int64_t redop = AR_SUM;
     // schedule
     TreeTable tt{};
     // workspace layout
@@ -231,6 +232,7 @@ int ring_grid_x(const ar_comm* c, uint64_t S, bool vec)
 int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
 {
     a.mute_rank = (int)c->mute_rank;
+    a.redop = (int)c->redop;
     const bool vec = vector_ok(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row);
     const int launch = resolve_launch(c);
     hipError_t e = hipSuccess;
@@ -317,6 +319,7 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     a.line_stride = c->tree_lines;
     a.timeout_ticks = timeout_ticks(c);
     a.mute_rank = (int)c->mute_rank;
+    a.redop = (int)c->redop;
     a.tt = c->tt;
     // every workgroup must be resident at once: cap the piece accordingly
     const uint64_t per_wg = (uint64_t)kBlock * kTreeEPT;
@@ -461,7 +464,10 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
     if (count > c->cap)
         return AR_ERR_INVALID_ARG;
     const size_t bytes = (size_t)c->R * count * elem_size(c->dtype);
-    if (count && overlaps(send, bytes, recv, bytes))
+    // in place (send == recv) is allowed: every schedule reads an element of
+    // a rank's input before that rank's row is written at the same position
+    // (same thread, or ordered by the step hand-off); partial overlap is not
+    if (send != recv && overlaps(send, bytes, recv, bytes))
         return AR_ERR_INVALID_USAGE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
@@ -625,6 +631,11 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
             return AR_ERR_INVALID_ARG;
         c->mute_rank = v;
         return AR_SUCCESS;
+    case AR_OPT_REDOP:
+        if (v < AR_SUM || v > AR_AVG || (v == AR_AVG && c->dtype == AR_INT32))
+            return AR_ERR_INVALID_ARG;
+        c->redop = v;
+        return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }
@@ -643,6 +654,7 @@ int ar_get_option(ar_comm_t c, int option, int64_t* v)
     case AR_OPT_PROTO: *v = c->proto; return AR_SUCCESS;
     case AR_OPT_TREE_MAX_BYTES: *v = c->tree_max_bytes; return AR_SUCCESS;
     case AR_OPT_DEBUG_MUTE_RANK: *v = c->mute_rank; return AR_SUCCESS;
+    case AR_OPT_REDOP: *v = c->redop; return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }

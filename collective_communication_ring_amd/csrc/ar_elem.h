@@ -67,6 +67,37 @@ struct Elem<AR_BF16> {
     __device__ static uint32_t to_bits(A a) { return __float_as_uint(a); }
 };
 
+// ---- reduction operators ------------------------------------------------
+
+// One step of the fold, a = running value, b = next value.  Sum and average
+// add; max / min keep a only when it is strictly larger / smaller.  The
+// integer compare is signed (the accumulator holds int32 bits).
+template <class E, int RED>
+__device__ inline typename E::A combine(typename E::A a, typename E::A b)
+{
+    if constexpr (RED == AR_MAX || RED == AR_MIN) {
+        bool a_wins;
+        if constexpr (sizeof(typename E::T) == 4 && !__is_same(typename E::A, float))
+            a_wins = RED == AR_MAX ? (int32_t)a > (int32_t)b : (int32_t)a < (int32_t)b;
+        else
+            a_wins = RED == AR_MAX ? a > b : a < b;
+        return a_wins ? a : b;
+    } else {
+        return E::add(a, b);
+    }
+}
+
+// The value the owner (or the tree's root) keeps: an average divides the
+// sum by R once (IEEE division, correctly rounded).
+template <class E, int RED>
+__device__ inline typename E::A finalize(typename E::A a, float R)
+{
+    if constexpr (RED == AR_AVG)
+        return a / R;
+    else
+        return a;
+}
+
 // ---- slot loads and stores ----------------------------------------------
 
 // 16-byte load of user input (a T row of send).  Every input element is read

@@ -61,6 +61,7 @@ struct RingArgs {
     int step;         // step-per-launch mode: the step this launch runs
     int per_rank_wg;  // pipelined ring: workgroups per logical rank
     int mute_rank;    // testing only: rank that skips publishing (-1: none)
+    int redop;        // ar_redop_t
     uint64_t timeout_ticks;
 };
 
@@ -78,6 +79,7 @@ struct TreeArgs {
     int R;
     int blocks_per_rank;  // workgroups per (tree, rank)
     int mute_rank;        // testing only: rank that skips publishing (-1: none)
+    int redop;            // ar_redop_t
     uint64_t timeout_ticks;
     TreeTable tt;
 };

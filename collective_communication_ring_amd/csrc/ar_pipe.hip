@@ -156,8 +156,8 @@ __device__ inline void cstore_a(rsrc_t r, uint32_t elem, const typename E::A (&v
 // predecessor's input (FIRST) or its accumulator row; dst is this rank's
 // accumulator row or, at the last reduce step, its output (LAST).  Whole
 // slots move as 16-byte vectors; the ragged end element by element.
-template <class E, int V, bool FIRST, bool LAST>
-__device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_t ulen)
+template <class E, int V, bool FIRST, bool LAST, int RED>
+__device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_t ulen, float R)
 {
     using A = typename E::A;
     constexpr int PREV_POL = FIRST ? kPlain : kCoherent;  // inputs predate the kernel
@@ -180,8 +180,11 @@ __device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_
             const uint32_t j = j0 + u * kBlock;
             if (j < nfull) {
 #pragma unroll
-                for (int i = 0; i < V; ++i)
-                    x[u][i] = E::add(x[u][i], y[u][i]);
+                for (int i = 0; i < V; ++i) {
+                    x[u][i] = combine<E, RED>(x[u][i], y[u][i]);
+                    if constexpr (LAST)
+                        x[u][i] = finalize<E, RED>(x[u][i], R);
+                }
                 if constexpr (LAST)
                     cstore_t<E, V, kCoherent>(dst, j * V, x[u]);
                 else
@@ -197,12 +200,29 @@ __device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_
         else
             cload_a<E, 1, PREV_POL>(prev, e, x);
         cload_t<E, 1, kPlain>(own, e, y);
-        x[0] = E::add(x[0], y[0]);
-        if constexpr (LAST)
+        x[0] = combine<E, RED>(x[0], y[0]);
+        if constexpr (LAST) {
+            x[0] = finalize<E, RED>(x[0], R);
             cstore_t<E, 1, kCoherent>(dst, e, x);
-        else
+        } else {
             cstore_a<E, 1, kCoherent>(dst, e, x);
+        }
     }
+}
+
+template <class E, int V, int RED>
+__device__ inline void chunk_reduce_step(bool first, bool last, rsrc_t prevT, rsrc_t prevA,
+                                         rsrc_t own, rsrc_t dstA, rsrc_t dstT, uint64_t ulen,
+                                         float R)
+{
+    if (first && last)
+        chunk_reduce<E, V, true, true, RED>(prevT, own, dstT, ulen, R);
+    else if (first)
+        chunk_reduce<E, V, true, false, RED>(prevT, own, dstA, ulen, R);
+    else if (last)
+        chunk_reduce<E, V, false, true, RED>(prevA, own, dstT, ulen, R);
+    else
+        chunk_reduce<E, V, false, false, RED>(prevA, own, dstA, ulen, R);
 }
 
 // Copy one chunk of T (SRC_POL: kPlain when the source predates the kernel).
@@ -324,14 +344,21 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
                 const rsrc_t dstA = make_rsrc(part + (uint64_t)q * a.N + e0, ulen * 4);
                 T* dT = out + (uint64_t)q * a.out_row + (OP == kOpReduceScatter ? ulo : e0);
                 const rsrc_t dstT = make_rsrc(dT, ulen * sizeof(T));
-                if (first && last)
-                    chunk_reduce<E, V, true, true>(prevT, own, dstT, ulen);
-                else if (first)
-                    chunk_reduce<E, V, true, false>(prevT, own, dstA, ulen);
-                else if (last)
-                    chunk_reduce<E, V, false, true>(prevA, own, dstT, ulen);
-                else
-                    chunk_reduce<E, V, false, false>(prevA, own, dstA, ulen);
+                const float fr = (float)R;
+                switch (a.redop) {
+                case AR_MAX:
+                    chunk_reduce_step<E, V, AR_MAX>(first, last, prevT, prevA, own, dstA, dstT, ulen, fr);
+                    break;
+                case AR_MIN:
+                    chunk_reduce_step<E, V, AR_MIN>(first, last, prevT, prevA, own, dstA, dstT, ulen, fr);
+                    break;
+                case AR_AVG:
+                    chunk_reduce_step<E, V, AR_AVG>(first, last, prevT, prevA, own, dstA, dstT, ulen, fr);
+                    break;
+                default:
+                    chunk_reduce_step<E, V, AR_SUM>(first, last, prevT, prevA, own, dstA, dstT, ulen, fr);
+                    break;
+                }
             } else {
                 // a copy step; at all-gather step 0 the source is the rank's own
                 // shard in send (written before the kernel), else the

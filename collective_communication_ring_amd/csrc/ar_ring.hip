@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_reduce_step(RingArgs a)
     const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
     for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nslots;
          j0 += stride)
-        reduce_step_slots<E, V>(p, s, a.R, len, j0, kBlock);
+        reduce_step_slots<E, V>(p, s, a.R, a.redop, len, j0, kBlock);
 }
 
 template <int DT, int V>
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
             for (int s = 0; s <= R - 2; ++s) {
                 const int q = (c + s + 2) % R;
                 const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
-                reduce_step_slots<E, V>(p, s, R, len, j0, kBlock);
+                reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, kBlock);
                 step_boundary();
             }
         }

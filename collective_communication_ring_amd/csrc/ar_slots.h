@@ -11,13 +11,13 @@ namespace ar {
 // len.  FIRST: the received value comes from the predecessor's input (T);
 // else from its accumulator row (A).  LAST: the result is final and is
 // narrowed to T; else it is this rank's accumulator.
-template <class E, int V, bool FIRST, bool LAST>
+template <class E, int V, bool FIRST, bool LAST, int RED>
 __device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
                                     const typename E::A* __restrict__ prevA,
                                     const typename E::T* __restrict__ own,
                                     typename E::A* __restrict__ dstA,
                                     typename E::T* __restrict__ dstT, uint64_t len, uint64_t j0,
-                                    uint64_t jstep)
+                                    uint64_t jstep, float R)
 {
     using A = typename E::A;
     A x[kUnroll][V], y[kUnroll][V];
@@ -36,8 +36,11 @@ __device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t j = j0 + (uint64_t)u * jstep;
 #pragma unroll
-            for (int i = 0; i < V; ++i)
-                x[u][i] = E::add(x[u][i], y[u][i]);
+            for (int i = 0; i < V; ++i) {
+                x[u][i] = combine<E, RED>(x[u][i], y[u][i]);
+                if constexpr (LAST)
+                    x[u][i] = finalize<E, RED>(x[u][i], R);
+            }
             if constexpr (LAST)
                 store_t<E, V>(dstT + j * V, x[u]);
             else
@@ -56,8 +59,11 @@ __device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
                 load_a<E, V>(prevA + j * V, x[0]);
             load_t<E, V>(own + j * V, y[0]);
 #pragma unroll
-            for (int i = 0; i < V; ++i)
-                x[0][i] = E::add(x[0][i], y[0][i]);
+            for (int i = 0; i < V; ++i) {
+                x[0][i] = combine<E, RED>(x[0][i], y[0][i]);
+                if constexpr (LAST)
+                    x[0][i] = finalize<E, RED>(x[0][i], R);
+            }
             if constexpr (LAST)
                 store_t<E, V>(dstT + j * V, x[0]);
             else
@@ -65,9 +71,9 @@ __device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
         } else if (j * V < len) {
             for (uint64_t e = j * V; e < len; ++e) {
                 A xv = FIRST ? E::widen(prevT[e]) : prevA[e];
-                A r = E::add(xv, E::widen(own[e]));
+                A r = combine<E, RED>(xv, E::widen(own[e]));
                 if constexpr (LAST)
-                    dstT[e] = E::narrow(r);
+                    dstT[e] = E::narrow(finalize<E, RED>(r, R));
                 else
                     dstA[e] = r;
             }
@@ -140,19 +146,42 @@ __device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uin
     return r;
 }
 
-template <class E, int V>
-__device__ inline void reduce_step_slots(const ReducePtrs<E>& p, int s, int R, uint64_t len,
-                                         uint64_t j0, uint64_t jstep)
+template <class E, int V, int RED>
+__device__ inline void reduce_step_slots_op(const ReducePtrs<E>& p, int s, int R, uint64_t len,
+                                            uint64_t j0, uint64_t jstep)
 {
     const bool first = (s == 0), last = (s == R - 2);
+    const float fr = (float)R;
     if (first && last)
-        reduce_slots<E, V, true, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+        reduce_slots<E, V, true, true, RED>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep, fr);
     else if (first)
-        reduce_slots<E, V, true, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+        reduce_slots<E, V, true, false, RED>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep, fr);
     else if (last)
-        reduce_slots<E, V, false, true>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+        reduce_slots<E, V, false, true, RED>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep, fr);
     else
-        reduce_slots<E, V, false, false>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep);
+        reduce_slots<E, V, false, false, RED>(p.prevT, p.prevA, p.own, p.dstA, p.dstT, len, j0, jstep, fr);
+}
+
+// The reduction operator is uniform per launch: one branch per step picks
+// the code path.
+template <class E, int V>
+__device__ inline void reduce_step_slots(const ReducePtrs<E>& p, int s, int R, int redop,
+                                         uint64_t len, uint64_t j0, uint64_t jstep)
+{
+    switch (redop) {
+    case AR_MAX:
+        reduce_step_slots_op<E, V, AR_MAX>(p, s, R, len, j0, jstep);
+        break;
+    case AR_MIN:
+        reduce_step_slots_op<E, V, AR_MIN>(p, s, R, len, j0, jstep);
+        break;
+    case AR_AVG:
+        reduce_step_slots_op<E, V, AR_AVG>(p, s, R, len, j0, jstep);
+        break;
+    default:
+        reduce_step_slots_op<E, V, AR_SUM>(p, s, R, len, j0, jstep);
+        break;
+    }
 }
 
 }  // namespace ar

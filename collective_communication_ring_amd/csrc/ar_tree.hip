@@ -64,6 +64,21 @@ __device__ inline void ll_put(uint64_t* line, uint32_t data, uint32_t epoch)
     __hip_atomic_store(line, ll_pack(data, epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The reduction operator is uniform per launch (a runtime switch is enough
+// on this latency-bound path).
+template <class E>
+__device__ inline typename E::A combine_rt(int redop, typename E::A a, typename E::A b)
+{
+    switch (redop) {
+    case AR_MAX:
+        return combine<E, AR_MAX>(a, b);
+    case AR_MIN:
+        return combine<E, AR_MIN>(a, b);
+    default:
+        return combine<E, AR_SUM>(a, b);
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 {
@@ -122,11 +137,17 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
                 uint32_t d = 0;
                 if (!ll_wait(up_ch + idx[k], epoch, deadline, err, &d))
                     timed_out = true;
-                acc[k] = E::add(acc[k], E::from_bits(d));
+                acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d));
             }
         }
     }
     const bool publish = (v != a.mute_rank);
+    if (parent < 0 && a.redop == AR_AVG) {  // the root's sum is final: average it once
+#pragma unroll
+        for (int k = 0; k < kTreeEPT; ++k)
+            if (ok[k])
+                acc[k] = finalize<E, AR_AVG>(acc[k], (float)R);
+    }
     if (parent >= 0) {
 #pragma unroll
         for (int k = 0; k < kTreeEPT; ++k)

@@ -66,6 +66,16 @@ typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
  * ("Demystifying NVSHMEM ..." summary, paragraph on collectives). */
 typedef enum { AR_SIMPLE = 0, AR_LL = 1 } ar_proto_t;
 
+/* Reduction operator (ar_set_option(AR_OPT_REDOP, ...)); the default is the
+ * sum.  Ranks reduce with sum, min or max; an average is the sum divided by
+ * the number of ranks ("NCCL, NIXL, and Distributed GPU Communication",
+ * section "All-reduce").  Max/min fold like the sum, keeping the running
+ * value only when it is strictly larger/smaller (with equal values -- +0 and
+ * -0 -- or a NaN, the value folded later wins).  AR_AVG divides the reduced
+ * sum by R once, in float32 (IEEE division), where it is final (the ring
+ * segment's owner, the tree's root); not for AR_INT32. */
+typedef enum { AR_SUM = 0, AR_MAX = 1, AR_MIN = 2, AR_AVG = 3 } ar_redop_t;
+
 typedef enum {
     AR_SUCCESS = 0,
     AR_ERR_INVALID_ARG = 1,   /* R out of range, NULL pointer, count above capacity, misaligned */
@@ -104,9 +114,10 @@ typedef enum {
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
     AR_OPT_PROTO = 6,         /* an ar_proto_t, overriding the one given to ar_init */
     AR_OPT_TREE_MAX_BYTES = 7, /* AR_AUTO: largest per-rank message sent by tree */
-    AR_OPT_DEBUG_MUTE_RANK = 8 /* testing the watchdog only: this logical rank's workgroups
-                                  skip publishing (LL lines, ready flags), so its consumers'
-                                  bounded waits expire; -1 (default) = none */
+    AR_OPT_DEBUG_MUTE_RANK = 8, /* testing the watchdog only: this logical rank's workgroups
+                                   skip publishing (LL lines, ready flags), so its consumers'
+                                   bounded waits expire; -1 (default) = none */
+    AR_OPT_REDOP = 9            /* an ar_redop_t for ar_allreduce / ar_reduce_scatter */
 } ar_option_t;
 
 /* Create a communicator for R logical ranks (2 <= R <= 64) and up to
@@ -136,10 +147,11 @@ size_t ar_workspace_bytes(ar_comm_t comm);
  * is smaller than ar_workspace_bytes or `dev` is NULL or misaligned. */
 int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
 
-/* All-reduce (sum).  send and recv are [R][count] rank-major device arrays
- * of the comm's dtype, distinct (in-place is AR_ERR_INVALID_USAGE).  On
- * completion every row of recv holds the element-wise sum over the R rows
- * of send ("NCCL, NIXL, and Distributed GPU Communication", section
+/* All-reduce (sum, or the comm's AR_OPT_REDOP).  send and recv are
+ * [R][count] rank-major device arrays of the comm's dtype; they may be the
+ * same array (in place) but must not otherwise overlap (AR_ERR_INVALID_USAGE).
+ * On completion every row of recv holds the element-wise reduction over the
+ * R rows of send ("NCCL, NIXL, and Distributed GPU Communication", section
  * "All-reduce").  Floating-point sums are added in the order the schedule
  * implies: ring -- a left fold from the owner's successor round to the owner;
  * tree -- each node's own value, then its children's subtree sums in

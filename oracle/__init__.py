@@ -16,6 +16,7 @@ import numpy as np
 from . import build as _build
 
 _DT = {"int32": 0, "float32": 1, "bf16": 2}
+OPS = {"sum": 0, "max": 1, "min": 2, "avg": 3}
 _NP = {"int32": np.int32, "float32": np.float32, "bf16": np.uint16}
 _lib = None
 
@@ -32,6 +33,11 @@ def lib():
                      "orc_ring_all_gather", "orc_tree_allreduce"):
             f = getattr(L, name)
             f.argtypes = [i, sz, i, vp, vp]
+            f.restype = i
+        for name in ("orc_ring_allreduce_op", "orc_ring_reduce_scatter_op",
+                     "orc_tree_allreduce_op"):
+            f = getattr(L, name)
+            f.argtypes = [i, sz, i, i, vp, vp]
             f.restype = i
         L.orc_exact_sum.argtypes = [i, sz, i, vp, vp]
         L.orc_exact_sum.restype = i
@@ -78,26 +84,27 @@ def _check(rc, name):
         raise RuntimeError("%s failed with code %d" % (name, rc))
 
 
-def ring_allreduce(x, dtype=None):
-    """Ring all-reduce (sum): every row of the result is the sum over ranks,
-    added in the ring's order (left fold from the owner's successor)."""
+def ring_allreduce(x, dtype=None, op="sum"):
+    """Ring all-reduce: every row of the result is the reduction over ranks,
+    folded in the ring's order (left fold from the owner's successor); for
+    "avg" the owner divides the sum by R once."""
     x, dtype = _prep(x, dtype)
     R, N = x.shape
     y = np.empty_like(x)
-    _check(lib().orc_ring_allreduce(R, N, _DT[dtype], x.ctypes.data, y.ctypes.data),
-           "orc_ring_allreduce")
+    _check(lib().orc_ring_allreduce_op(R, N, _DT[dtype], OPS[op], x.ctypes.data, y.ctypes.data),
+           "orc_ring_allreduce_op")
     return y
 
 
-def ring_reduce_scatter(x, dtype=None):
-    """Ring reduce-scatter (sum): rank q gets segment q of the sum; [R, N/R]."""
+def ring_reduce_scatter(x, dtype=None, op="sum"):
+    """Ring reduce-scatter: rank q gets segment q of the reduction; [R, N/R]."""
     x, dtype = _prep(x, dtype)
     R, N = x.shape
     if N % R:
         raise ValueError("reduce-scatter needs N divisible by R")
     y = np.empty((R, N // R), dtype=x.dtype)
-    _check(lib().orc_ring_reduce_scatter(R, N, _DT[dtype], x.ctypes.data, y.ctypes.data),
-           "orc_ring_reduce_scatter")
+    _check(lib().orc_ring_reduce_scatter_op(R, N, _DT[dtype], OPS[op], x.ctypes.data,
+                                            y.ctypes.data), "orc_ring_reduce_scatter_op")
     return y
 
 
@@ -111,15 +118,15 @@ def ring_all_gather(shards, dtype=None):
     return y
 
 
-def tree_allreduce(x, dtype=None):
-    """Double-binary-tree all-reduce (sum): first half of the elements through
-    tree A, second half through tree B; fold = own value, then children in
-    ascending rank order."""
+def tree_allreduce(x, dtype=None, op="sum"):
+    """Double-binary-tree all-reduce: first half of the elements through tree
+    A, second half through tree B; fold = own value, then children in
+    ascending rank order; for "avg" the root divides the sum by R once."""
     x, dtype = _prep(x, dtype)
     R, N = x.shape
     y = np.empty_like(x)
-    _check(lib().orc_tree_allreduce(R, N, _DT[dtype], x.ctypes.data, y.ctypes.data),
-           "orc_tree_allreduce")
+    _check(lib().orc_tree_allreduce_op(R, N, _DT[dtype], OPS[op], x.ctypes.data, y.ctypes.data),
+           "orc_tree_allreduce_op")
     return y
 
 

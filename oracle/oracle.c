@@ -8,6 +8,9 @@
  * does.  It shares no code, header, table or helper with the GPU library,
  * and includes nothing from it.
  *
+ * Reduction operators: sum (the pages' worked examples), max, min, and
+ * average (sum / R).
+ *
  * Parity status: every function here is pinned by CPU tests (closed forms,
  * brute force, hand-computed rounding-order cases, a library conversion
  * routine, and the pages' worked examples); none is "parity unpinned".
@@ -44,6 +47,10 @@
 #include <string.h>
 
 enum { ORC_INT32 = 0, ORC_FLOAT32 = 1, ORC_BF16 = 2 };
+/* Reduction operators: sum, max, min, and average = sum / R ("NCCL, NIXL,
+ * and Distributed GPU Communication", section "All-reduce": ranks reduce with
+ * sum/min/max; DDP divides the sum by the world size to average). */
+enum { ORC_SUM = 0, ORC_MAX = 1, ORC_MIN = 2, ORC_AVG = 3 };
 enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_ENOMEM = 2 };
 
 /* One accumulator value: uint32 for int32 inputs, float for the others. */
@@ -151,6 +158,32 @@ static acc_t acc_add(int dtype, acc_t a, acc_t b)
     return r;
 }
 
+/* One step of the fold: a is what has been accumulated so far, b the next
+ * value.  max / min keep a when it is strictly larger / smaller, else take b
+ * (so with equal values, e.g. -0 and +0, or a NaN, the newer value wins);
+ * sum and average add. */
+static acc_t acc_op(int dtype, int op, acc_t a, acc_t b)
+{
+    if (op == ORC_MAX || op == ORC_MIN) {
+        int a_wins;
+        if (dtype == ORC_INT32)
+            a_wins = op == ORC_MAX ? (int32_t)a.u > (int32_t)b.u : (int32_t)a.u < (int32_t)b.u;
+        else
+            a_wins = op == ORC_MAX ? a.f > b.f : a.f < b.f;
+        return a_wins ? a : b;
+    }
+    return acc_add(dtype, a, b);
+}
+
+/* What the owner does with the fully reduced value before narrowing it:
+ * average divides the sum by R once, in float32 (IEEE division). */
+static acc_t acc_final(int op, int R, acc_t a)
+{
+    if (op == ORC_AVG)
+        a.f = a.f / (float)R;
+    return a;
+}
+
 /* ---- ring ------------------------------------------------------------ */
 
 /* Segment c of a rank's N elements: [min(c*S, N), min((c+1)*S, N)) with
@@ -174,7 +207,7 @@ static size_t seg_hi(size_t N, int R, int c) { return seg_lo(N, R, c + 1); }
  * owner's successor c+1 and ends at the owner c. */
 typedef void (*emit_fn)(void* ctx, int q, size_t e, acc_t v);
 
-static int ring_reduce_phase(int R, size_t N, int dtype, const void* send,
+static int ring_reduce_phase(int R, size_t N, int dtype, int op, const void* send,
                              emit_fn emit, void* ctx)
 {
     acc_t* part = NULL; /* part[q*N + e]: the partial rank q holds */
@@ -191,11 +224,11 @@ static int ring_reduce_phase(int R, size_t N, int dtype, const void* send,
             for (size_t e = lo; e < hi; ++e) {
                 acc_t in = (s == 0) ? widen(dtype, send, (size_t)p * N + e)
                                     : part[(size_t)p * N + e];
-                acc_t v = acc_add(dtype, in, widen(dtype, send, (size_t)q * N + e));
+                acc_t v = acc_op(dtype, op, in, widen(dtype, send, (size_t)q * N + e));
                 if (s < R - 2)
                     part[(size_t)q * N + e] = v;
                 else
-                    emit(ctx, q, e, v); /* here q == c */
+                    emit(ctx, q, e, acc_final(op, R, v)); /* here q == c */
             }
         }
     }
@@ -248,33 +281,52 @@ static int check_args(int R, int dtype, const void* a, const void* b)
     return ORC_OK;
 }
 
+static int check_op(int dtype, int op)
+{
+    if (op < ORC_SUM || op > ORC_AVG)
+        return ORC_EINVAL;
+    if (op == ORC_AVG && dtype == ORC_INT32)
+        return ORC_EINVAL; /* no integer average */
+    return ORC_OK;
+}
+
 /* All-reduce by ring: reduce phase, the owner writes its final segment into
  * its own output row, then the copy phase spreads every segment round the
  * ring.  send and recv are [R][N]. */
-int orc_ring_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+int orc_ring_allreduce_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc)
+    if (rc || (rc = check_op(dtype, op)))
         return rc;
     struct emit_ctx ctx = {dtype, recv, N, R, N};
-    rc = ring_reduce_phase(R, N, dtype, send, emit_full, &ctx);
+    rc = ring_reduce_phase(R, N, dtype, op, send, emit_full, &ctx);
     if (rc)
         return rc;
     ring_gather_phase(R, N, dtype, recv, N);
     return ORC_OK;
 }
 
+int orc_ring_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    return orc_ring_allreduce_op(R, N, dtype, ORC_SUM, send, recv);
+}
+
 /* Reduce-scatter by ring: the reduce phase only; rank q's output is its own
  * segment q, of length N/R.  send is [R][N], recv is [R][N/R]. */
-int orc_ring_reduce_scatter(int R, size_t N, int dtype, const void* send, void* recv)
+int orc_ring_reduce_scatter_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc)
+    if (rc || (rc = check_op(dtype, op)))
         return rc;
     if (N % (size_t)R != 0)
         return ORC_EINVAL;
     struct emit_ctx ctx = {dtype, recv, N / (size_t)R, R, N};
-    return ring_reduce_phase(R, N, dtype, send, emit_shard, &ctx);
+    return ring_reduce_phase(R, N, dtype, op, send, emit_shard, &ctx);
+}
+
+int orc_ring_reduce_scatter(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    return orc_ring_reduce_scatter_op(R, N, dtype, ORC_SUM, send, recv);
 }
 
 /* All-gather by ring: rank q first places its own shard at position q of its
@@ -327,25 +379,25 @@ int orc_tree_parent(int R, int tree, int r)
     return p < 0 ? -1 : mod(p + 1, R);
 }
 
-/* Subtree sum of v for element e: own input first, then each child's
- * subtree sum in ascending rank order. */
-static acc_t tree_fold(int R, const int* parent, int dtype, const void* send,
+/* Subtree reduction of v for element e: own input first, then each child's
+ * subtree value in ascending rank order. */
+static acc_t tree_fold(int R, const int* parent, int dtype, int op, const void* send,
                        size_t N, int v, size_t e)
 {
     acc_t p = widen(dtype, send, (size_t)v * N + e);
     for (int ch = 0; ch < R; ++ch)
         if (parent[ch] == v)
-            p = acc_add(dtype, p, tree_fold(R, parent, dtype, send, N, ch, e));
+            p = acc_op(dtype, op, p, tree_fold(R, parent, dtype, op, send, N, ch, e));
     return p;
 }
 
 /* All-reduce by double binary tree: elements [0, H) go up tree A and back
  * down, elements [H, N) go through tree B, H = ceil(N/2).  Every rank's
  * output is the root's sum narrowed to T (the broadcast down is a copy). */
-int orc_tree_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+int orc_tree_allreduce_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc)
+    if (rc || (rc = check_op(dtype, op)))
         return rc;
     int* parent = (int*)malloc(sizeof(int) * 2 * (size_t)R);
     if (!parent)
@@ -360,12 +412,17 @@ int orc_tree_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
     size_t H = (N + 1) / 2;
     for (size_t e = 0; e < N; ++e) {
         int t = e < H ? 0 : 1;
-        acc_t sum = tree_fold(R, parent + t * R, dtype, send, N, root[t], e);
+        acc_t v = acc_final(op, R, tree_fold(R, parent + t * R, dtype, op, send, N, root[t], e));
         for (int q = 0; q < R; ++q)
-            narrow(dtype, recv, (size_t)q * N + e, sum);
+            narrow(dtype, recv, (size_t)q * N + e, v);
     }
     free(parent);
     return ORC_OK;
+}
+
+int orc_tree_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
+{
+    return orc_tree_allreduce_op(R, N, dtype, ORC_SUM, send, recv);
 }
 
 /* ---- plain definition, in double ------------------------------------- */

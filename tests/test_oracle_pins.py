@@ -415,3 +415,70 @@ def test_ll_line_round_trip(orc):
     # float data travel as their bit pattern
     bits = int(np.array([1.5], np.float32).view(np.uint32)[0])
     assert orc.ll_unpack(orc.ll_pack(bits, 7)) == (0x3FC00000, 7)
+
+
+# ---------------------------------------------------------------- max / min / avg
+
+@pytest.mark.parametrize("R", [2, 3, 5, 8, 16])
+def test_max_min_equal_elementwise_extremes(orc, R):
+    rng = np.random.default_rng(40 + R)
+    N = R * 23 + 5
+    xi = rng.integers(-(2 ** 31), 2 ** 31, size=(R, N), dtype=np.int64).astype(np.int32)
+    xf = rng.standard_normal((R, N)).astype(np.float32)
+    for x in (xi, xf):
+        for op, ref in (("max", x.max(axis=0)), ("min", x.min(axis=0))):
+            assert (orc.ring_allreduce(x, op=op) == ref[None, :]).all()
+            assert (orc.tree_allreduce(x, op=op) == ref[None, :]).all()
+    xb = orc.bf16_from_f32(xf)
+    yb = orc.ring_allreduce(xb, "bf16", op="max")[0]
+    assert (orc.f32_from_bf16(yb) == orc.f32_from_bf16(xb).max(axis=0)).all()
+    NR = (N // R) * R
+    assert (orc.ring_reduce_scatter(xi[:, :NR], op="min").reshape(-1) == xi[:, :NR].min(axis=0)).all()
+
+
+def test_max_signed_zero_follows_the_fold_order(orc):
+    # max keeps the running value only when it is strictly larger, so for
+    # {+0, -0} the value folded last wins.  R = 2, N = 2: element 0 is in
+    # segment 0 (fold x1 then x0), element 1 in segment 1 (fold x0 then x1).
+    x = np.array([[0.0, 0.0], [-0.0, -0.0]], np.float32)
+    y = orc.ring_allreduce(x, op="max")[0]
+    assert np.signbit(y[0]) == False and np.signbit(y[1]) == True  # noqa: E712
+    y = orc.ring_allreduce(x, op="min")[0]
+    assert np.signbit(y[0]) == False and np.signbit(y[1]) == True  # noqa: E712
+
+
+@pytest.mark.parametrize("R", [2, 3, 8, 16])
+def test_avg_is_the_sum_divided_once(orc, R):
+    rng = np.random.default_rng(60 + R)
+    N = 1000
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    want = orc.ring_allreduce(x) / np.float32(R)          # numpy float32 division
+    assert orc.ring_allreduce(x, op="avg").tobytes() == want.astype(np.float32).tobytes()
+    want_t = orc.tree_allreduce(x) / np.float32(R)
+    assert orc.tree_allreduce(x, op="avg").tobytes() == want_t.astype(np.float32).tobytes()
+    ex = orc.exact_sum(x) / R
+    y = orc.ring_allreduce(x, op="avg")[0].astype(np.float64)
+    assert (np.abs(y - ex) <= 1e-6 * np.abs(ex) + 1e-6).all()
+    # integer multiples of R: the average is exact
+    k = rng.integers(-1000, 1001, size=(R, N))
+    xi = (k * R).astype(np.float32)
+    assert (orc.ring_allreduce(xi, op="avg")[0] == k.sum(axis=0).astype(np.float32)).all()
+
+
+def test_bf16_avg_rounds_once_after_dividing(orc):
+    import torch
+    R, N = 16, 3000
+    rng = np.random.default_rng(9)
+    xb = orc.bf16_from_f32(rng.standard_normal((R, N)).astype(np.float32) * 0.02)
+    # the same fold in float32 on the widened inputs, divided, rounded once
+    s32 = orc.ring_allreduce(orc.f32_from_bf16(xb))[0]
+    want = torch.from_numpy(s32 / np.float32(R)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (orc.ring_allreduce(xb, "bf16", op="avg")[0] == want).all()
+    assert (orc.ring_reduce_scatter(xb[:, :N - N % R], "bf16", op="avg").reshape(-1) ==
+            orc.ring_allreduce(xb[:, :N - N % R], "bf16", op="avg")[0]).all()
+
+
+def test_int32_avg_is_refused(orc):
+    x = np.ones((4, 8), np.int32)
+    with pytest.raises(RuntimeError):
+        orc.ring_allreduce(x, op="avg")

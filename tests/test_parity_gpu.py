@@ -287,9 +287,6 @@ def test_argument_errors(env):
     torch, api = env["torch"], env["api"]
     comm = api.Comm(4, 64, "float32", device=env["dev"])
     a = torch.zeros((4, 64), device=env["dev"])
-    with pytest.raises(api.ArError) as e:
-        comm.allreduce(a, a)
-    assert e.value.status == api.AR_ERR_INVALID_USAGE
     big = torch.zeros((4, 65), device=env["dev"])
     with pytest.raises(api.ArError) as e:
         comm.allreduce(big, torch.zeros_like(big))
@@ -457,3 +454,60 @@ def test_measurement_utilities(env):
         torch.cuda.synchronize()
         assert int(res.item()) == 0
         assert (int(lines[0].item()) >> 32) == 1000 and (int(lines[16].item()) >> 32) == 1000
+
+
+# ---------------------------------------------------------------- operators, in place
+
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("op", ["max", "min", "avg"])
+def test_reduction_operators(env, variant, dtype, op):
+    if op == "avg" and dtype == "int32":
+        pytest.skip("no integer average")
+    api, orc = env["api"], env["orc"]
+    for R, N in ((3, 1001), (8, 8 * 4096 + 24), (16, 16 * 5)):
+        x = rand_input(env, dtype, R, N, seed=R * 7 + N)
+        if variant == "tree":
+            (y,) = run_allreduce(env, x, dtype, "tree", "ll", redop=op)
+            ref = orc.tree_allreduce(x, dtype, op=op)
+        else:
+            (y,) = run_allreduce(env, x, dtype, launch=variant, redop=op)
+            ref = orc.ring_allreduce(x, dtype, op=op)
+        assert y.tobytes() == ref.tobytes(), (R, N)
+        if variant != "tree" and N % R == 0:
+            comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=variant, redop=op)
+            shard = poisoned(env, (R, N // R), dtype)
+            comm.reduce_scatter(to_dev(env, x, dtype), shard)
+            assert from_dev(env, shard, dtype).tobytes() == orc.ring_reduce_scatter(x, dtype, op=op).tobytes()
+
+
+def test_int32_average_is_refused(env):
+    api = env["api"]
+    comm = api.Comm(4, 64, "int32", device=env["dev"])
+    with pytest.raises(api.ArError) as e:
+        comm.set_option(api.AR_OPT_REDOP, api.AR_AVG)
+    assert e.value.status == api.AR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+def test_in_place_allreduce(env, variant, dtype):
+    api, orc, torch = env["api"], env["orc"], env["torch"]
+    for R, N in ((2, 7), (5, 1003), (8, 1 << 16), (16, 16 * 4096 + 3)):
+        x = rand_input(env, dtype, R, N, seed=31 + R + N)
+        if variant == "tree":
+            comm = api.Comm(R, N, dtype, "tree", "ll", device=env["dev"])
+            ref = orc.tree_allreduce(x, dtype)
+        else:
+            comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=variant)
+            ref = orc.ring_allreduce(x, dtype)
+        buf = to_dev(env, x, dtype)
+        comm.allreduce(buf, buf)
+        assert from_dev(env, buf, dtype).tobytes() == ref.tobytes(), (R, N)
+        assert comm.check() == api.AR_SUCCESS
+    # partial overlap is refused
+    comm = api.Comm(4, 64, "float32", device=env["dev"])
+    base = torch.zeros(4 * 64 + 64, device=env["dev"])
+    with pytest.raises(api.ArError) as e:
+        comm.allreduce(base[:256].view(4, 64), base[64:320].view(4, 64))
+    assert e.value.status == api.AR_ERR_INVALID_USAGE
