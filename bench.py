@@ -33,6 +33,13 @@ KERNEL_SOURCES = ["collective_communication_ring_amd/csrc/ar_ring.hip",
                   "collective_communication_ring_amd/csrc/ar_elem.h"]
 
 
+def ring_kw(launch):
+    """Comm keyword arguments for a --launch value ('ll' selects the LL protocol)."""
+    if launch == "ll":
+        return dict(algo="ring", proto="ll")
+    return dict(algo="ring", proto="simple", launch=launch)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -134,10 +141,10 @@ def headline(args):
     x = inputs.host_inputs("ring_f32_r8_64MiB")
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
-    comm = api.Comm(R, N, "float32", "ring", "simple", device=dev, launch=args.launch,
-                    chunk_bytes=512 * 1024, grid=args.grid)
-    _, _, launch = comm.plan(N)
-    launch_name = {v: k for k, v in api.LAUNCHES.items()}[launch]
+    comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=512 * 1024, grid=args.grid,
+                    **ring_kw(args.launch))
+    _, proto, launch = comm.plan(N)
+    launch_name = "ll" if proto == api.AR_LL else {v: k for k, v in api.LAUNCHES.items()}[launch]
     per, total_ms, wall = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                      torch)
     assert comm.check() == api.AR_SUCCESS
@@ -150,6 +157,7 @@ def headline(args):
     achieved = b_alg / (kernel_ms / 1e3) / 1e9
     kernel = {"fused": "k_ring_fused<float32, 16-byte slots, all-reduce>",
               "pipelined": "k_ring_pipelined<float32, 16-byte slots, all-reduce>",
+              "ll": "k_ring_ll<float32, all-reduce> (one launch per piece)",
               "step": "k_ring_reduce_step + k_ring_copy_step (2(R-1) launches)"}[launch_name]
     traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name)
     line = {
@@ -208,8 +216,8 @@ def mode_sweep(args):
     # flat buffers: the first R*N elements viewed as [R, N] are rank-major
     send_flat = torch.randn(R * Nmax, generator=g, device=dev, dtype=torch.float32)
     recv_flat = torch.empty_like(send_flat)
-    comm = api.Comm(R, Nmax, "float32", "ring", "simple", device=dev, launch=args.launch,
-                    chunk_bytes=512 * 1024, grid=args.grid)
+    comm = api.Comm(R, Nmax, "float32", device=dev, chunk_bytes=512 * 1024, grid=args.grid,
+                    **ring_kw(args.launch))
     rows = []
     out = open(args.out, "w") if args.out else None
     for N in counts:
@@ -306,6 +314,7 @@ def mode_tree_vs_ring(args):
     send_flat = torch.from_numpy(x).to(dev).reshape(-1)
     recv_flat = torch.empty_like(send_flat)
     variants = [("tree-ll", dict(algo="tree", proto="ll")),
+                ("ring-ll", dict(algo="ring", proto="ll")),
                 ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
                 ("ring-pipelined", dict(algo="ring", proto="simple", launch="pipelined")),
                 ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
@@ -360,7 +369,7 @@ def mode_buckets(args):
     xs = [inputs.device_bucket_bf16(R, N, w["seed"], b, dev) for b in range(B)]
     shards = [torch.empty((R, n), dtype=torch.bfloat16, device=dev) for _ in range(B)]
     full = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
-    comm = api.Comm(R, N, "bf16", "ring", device=dev, launch=args.launch, grid=args.grid)
+    comm = api.Comm(R, N, "bf16", device=dev, grid=args.grid, **ring_kw(args.launch))
 
     def rs_all():
         for b in range(B):
@@ -474,8 +483,8 @@ def mode_tune(args):
     ref = oracle.ring_allreduce(x)
     res = []
     for grid in [int(g) for g in args.grids.split(",")]:
-        comm = api.Comm(R, N, "float32", "ring", "simple", device=dev, launch=args.launch,
-                        chunk_bytes=args.chunk_bytes, grid=grid)
+        comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=args.chunk_bytes, grid=grid,
+                        **ring_kw(args.launch))
         _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                     torch)
         ms = total_ms / args.steps
@@ -492,7 +501,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--launch", default="auto", choices=["auto", "fused", "step", "pipelined"])
+    ap.add_argument("--launch", default="auto", choices=["auto", "fused", "step", "pipelined", "ll"],
+                    help="ring launch form; 'll' = the ring with the LL protocol")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
                     choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream",

@@ -123,6 +123,8 @@ struct ar_comm {
     size_t off_part = 0, off_up = 0, off_down = 0, off_flags = 0, ws_need = 0;
     uint64_t tree_lines = 0;  // lines per (tree, rank)
     uint64_t flag_stride = 0; // pipelined ring: ready flags per segment
+    size_t off_rll = 0;       // ring-LL line slots
+    uint64_t rll_cap = 0;     // ring-LL: lines per (sender, segment) per launch
     char* ws = nullptr;
     size_t ws_bytes = 0;
     // device facts, read on first use
@@ -132,6 +134,7 @@ struct ar_comm {
     int resident_fused[3][2] = {};
     int resident_pipe[3][2] = {};
     int resident_tree[3] = {};
+    int resident_rll[3] = {};
     // last call
     hipStream_t last_stream = nullptr;
     int last_hip = 0;
@@ -165,8 +168,10 @@ int device_ready(ar_comm* c)
         c->resident_pipe[d][0] = resident_ring_pipelined(d, false);
         c->resident_pipe[d][1] = resident_ring_pipelined(d, true);
         c->resident_tree[d] = resident_tree_ll(d);
+        c->resident_rll[d] = resident_ring_ll(d);
         if (c->resident_fused[d][0] <= 0 || c->resident_fused[d][1] <= 0 ||
-            c->resident_pipe[d][0] <= 0 || c->resident_pipe[d][1] <= 0 || c->resident_tree[d] <= 0)
+            c->resident_pipe[d][0] <= 0 || c->resident_pipe[d][1] <= 0 || c->resident_tree[d] <= 0 ||
+            c->resident_rll[d] <= 0)
             return fail_hip(c, hipErrorInvalidDeviceFunction);
     }
     c->dev_ready = true;
@@ -229,8 +234,61 @@ int ring_grid_x(const ar_comm* c, uint64_t S, bool vec)
     return (int)std::min<uint64_t>(need, 65535);
 }
 
+// Workgroups per rank (per tree and rank for the tree) of an LL kernel over
+// `lines` lines per rank, cut into sub-blocks of kBlock: one line per thread
+// while the whole grid stays within one workgroup per CU (the latency-best
+// shape), beyond that each thread batches up to `ept` lines (more
+// workgroups would only add polling traffic); never above the residency cap.
+uint64_t ll_grid_per_rank(uint64_t lines, int groups, int ncu, int ept, int64_t cap)
+{
+    const uint64_t nsub = (lines + kBlock - 1) / kBlock;
+    const uint64_t batched = (nsub + ept - 1) / ept;
+    const uint64_t budget = (uint64_t)std::max(1, ncu / groups);
+    uint64_t g = std::min<uint64_t>(nsub, std::max<uint64_t>(batched, budget));
+    return std::max<uint64_t>(1, std::min<uint64_t>(g, (uint64_t)cap));
+}
+
+// Ring with the LL protocol: one launch per piece of the segments.
+int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
+{
+    RingLLArgs a{};
+    a.send = r.send;
+    a.out = r.out;
+    a.lines = reinterpret_cast<uint64_t*>(c->ws + c->off_rll);
+    a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
+    a.N = r.N;
+    a.S = r.S;
+    a.send_row = r.send_row;
+    a.out_row = r.out_row;
+    a.piece_cap = c->rll_cap;
+    a.R = r.R;
+    a.op = r.op;
+    a.mute_rank = (int)c->mute_rank;
+    a.redop = (int)c->redop;
+    a.timeout_ticks = r.timeout_ticks;
+    const int64_t gmax = c->resident_rll[c->dtype] / a.R;
+    if (gmax < 1)
+        return AR_ERR_UNSUPPORTED;
+    int launches = 0;
+    for (uint64_t lo = 0; lo < a.S; lo += c->rll_cap) {
+        a.piece_lo = lo;
+        a.piece_len = std::min<uint64_t>(c->rll_cap, a.S - lo);
+        a.per_rank_wg = (int)ll_grid_per_rank(a.piece_len, a.R, c->ncu, kRingLLEPT, gmax);
+        hipError_t e = launch_ring_ll(c->dtype, a, a.per_rank_wg * a.R, st);
+        if (e != hipSuccess)
+            return fail_hip(c, e);
+        ++launches;
+    }
+    if (c->debug)
+        std::fprintf(stderr, "ar: ring-LL op=%d R=%d N=%llu dtype=%s launches=%d\n", a.op, a.R,
+                     (unsigned long long)a.N, dtype_name(c->dtype), launches);
+    return AR_SUCCESS;
+}
+
 int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
 {
+    if (c->proto == AR_LL)
+        return run_ring_ll(c, a, st);
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
     const bool vec = vector_ok(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row);
@@ -321,19 +379,20 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
     a.tt = c->tt;
-    // every workgroup must be resident at once: cap the piece accordingly
-    const uint64_t per_wg = (uint64_t)kBlock * kTreeEPT;
+    // every workgroup must be resident at once: at most res / (2R) per
+    // (tree, rank); a workgroup loops over its sub-blocks of kBlock lines
     const int64_t res = c->resident_tree[c->dtype];
-    const int64_t bpr_max = std::max<int64_t>(1, res / (2 * c->R));
-    const uint64_t piece_max = std::min<uint64_t>(c->tree_lines, (uint64_t)bpr_max * per_wg);
+    const int64_t bpr_max = res / (2 * c->R);
+    if (bpr_max < 1)
+        return AR_ERR_UNSUPPORTED;
     const uint64_t half = a.H;  // the larger half
-    const uint64_t piece = std::min<uint64_t>(piece_max, std::max<uint64_t>(half, 1));
+    const uint64_t piece = std::min<uint64_t>(c->tree_lines, std::max<uint64_t>(half, 1));
     int launches = 0;
     for (uint64_t lo = 0; lo < half; lo += piece) {
         a.piece_lo = lo;
         a.piece_len = piece;
         const uint64_t plen = std::min<uint64_t>(piece, half - lo);
-        a.blocks_per_rank = (int)((plen + per_wg - 1) / per_wg);
+        a.blocks_per_rank = (int)ll_grid_per_rank(plen, 2 * c->R, c->ncu, kTreeEPT, bpr_max);
         const int grid = 2 * c->R * a.blocks_per_rank;
         if (grid > res)
             return AR_ERR_INTERNAL;
@@ -422,6 +481,12 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     // of the scalar path (kBlock * kUnroll elements)
     c->flag_stride = ((cap1 + R - 1) / R + (size_t)kBlock * kUnroll - 1) / ((size_t)kBlock * kUnroll) + 1;
     off = align_up(off + (size_t)R * c->flag_stride * 8, kAlign);
+    // ring-LL: one line per (sender, segment, offset within a launch's piece);
+    // pieces keep the region near 16 MiB whatever R
+    c->off_rll = off;
+    c->rll_cap = std::min<uint64_t>((cap1 + R - 1) / R,
+                                    std::max<uint64_t>(64, (uint64_t)(1u << 21) / ((uint64_t)R * R)));
+    off = align_up(off + (size_t)R * R * c->rll_cap * 8, kAlign);
     c->ws_need = off;
     *out = c;
     return AR_SUCCESS;
@@ -476,8 +541,6 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
     const int algo = resolve_algo(c, count);
     if (algo == AR_TREE)
         return run_tree(c, send, recv, count, st);
-    if (c->proto == AR_LL)
-        return AR_ERR_UNSUPPORTED;
     RingArgs a{};
     a.send = send;
     // partial sums live in recv when the accumulator is the element type
@@ -506,7 +569,7 @@ int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcoun
     const size_t es = elem_size(c->dtype);
     if (N && overlaps(send, (size_t)c->R * N * es, recv, N * es))
         return AR_ERR_INVALID_USAGE;
-    if (c->algo == AR_TREE || c->proto == AR_LL)
+    if (c->algo == AR_TREE)
         return AR_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
@@ -539,7 +602,7 @@ int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, v
     const size_t es = elem_size(c->dtype);
     if (N && overlaps(send, N * es, recv, (size_t)c->R * N * es))
         return AR_ERR_INVALID_USAGE;
-    if (c->algo == AR_TREE || c->proto == AR_LL)
+    if (c->algo == AR_TREE)
         return AR_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->last_stream = st;
@@ -665,7 +728,7 @@ int ar_plan(ar_comm_t c, size_t count, int* algo, int* proto, int* launch)
         return AR_ERR_INVALID_ARG;
     *algo = resolve_algo(c, count);
     *proto = (*algo == AR_TREE) ? AR_LL : c->proto;
-    *launch = (*algo == AR_TREE) ? AR_LAUNCH_AUTO : resolve_launch(c);
+    *launch = (*algo == AR_TREE || *proto == AR_LL) ? AR_LAUNCH_AUTO : resolve_launch(c);
     return AR_SUCCESS;
 }
 

@@ -31,6 +31,8 @@ struct Elem<AR_INT32> {
     __device__ static A add(A a, A b) { return a + b; }
     __device__ static A from_bits(uint32_t u) { return u; }
     __device__ static uint32_t to_bits(A a) { return a; }
+    __device__ static uint32_t t_bits(T v) { return (uint32_t)v; }
+    __device__ static T t_from_bits(uint32_t u) { return (T)u; }
 };
 
 template <>
@@ -43,6 +45,8 @@ struct Elem<AR_FLOAT32> {
     __device__ static A add(A a, A b) { return a + b; }
     __device__ static A from_bits(uint32_t u) { return __uint_as_float(u); }
     __device__ static uint32_t to_bits(A a) { return __float_as_uint(a); }
+    __device__ static uint32_t t_bits(T v) { return __float_as_uint(v); }
+    __device__ static T t_from_bits(uint32_t u) { return __uint_as_float(u); }
 };
 
 template <>
@@ -65,6 +69,8 @@ struct Elem<AR_BF16> {
     __device__ static A add(A a, A b) { return a + b; }
     __device__ static A from_bits(uint32_t u) { return __uint_as_float(u); }
     __device__ static uint32_t to_bits(A a) { return __float_as_uint(a); }
+    __device__ static uint32_t t_bits(T v) { return (uint32_t)v; }
+    __device__ static T t_from_bits(uint32_t u) { return (T)(u & 0xffffu); }
 };
 
 // ---- reduction operators ------------------------------------------------
@@ -181,6 +187,56 @@ __device__ inline void store_a(typename E::A* p, const typename E::A (&v)[V])
             for (int i = 0; i < 4; ++i)
                 r[i] = E::to_bits(v[4 * h + i]);
             reinterpret_cast<u32x4*>(p)[h] = r;
+        }
+    }
+}
+
+// ---- LL lines ---------------------------------------------------------------
+// An LL line is 8 bytes: the data bits in the low half, the arrival flag in
+// the high half, written and read as one 64-bit agent-scope atomic.
+
+__device__ inline void ll_store(uint64_t* line, uint32_t data, uint32_t flag)
+{
+    __hip_atomic_store(line, ((uint64_t)flag << 32) | (uint64_t)data, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for K lines at once: every pass issues the loads of all lines still
+// pending, so the K waits overlap instead of adding up.  Lines with
+// pending[k] == false on entry are skipped.  Gives up (returns false) when
+// `deadline` passes or the error word is set; data[k] of a line that never
+// arrived is left 0.
+template <int K>
+__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pending)[K],
+                                     uint32_t flag, uint64_t deadline, const uint32_t* err,
+                                     uint32_t (&data)[K])
+{
+    for (uint32_t spin = 0;; ++spin) {
+        uint64_t v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (pending[k])
+                v[k] = __hip_atomic_load(line[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            if (pending[k]) {
+                if ((uint32_t)(v[k] >> 32) == flag) {
+                    data[k] = (uint32_t)v[k];
+                    pending[k] = false;
+                } else {
+                    any = true;
+                }
+            }
+        }
+        if (!any)
+            return true;
+        if ((spin & 63u) == 63u) {
+            if ((uint64_t)wall_clock64() > deadline)
+                return false;
+            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                return false;
+            __builtin_amdgcn_s_sleep(1);
         }
     }
 }

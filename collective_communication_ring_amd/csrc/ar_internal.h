@@ -18,6 +18,8 @@ enum CtrlWord {
     kCtrlError = 1,      // non-zero: a bounded wait expired (watchdog)
     kCtrlTreeDone = 2,   // workgroups of the running tree call that finished
     kCtrlPipeDone = 3,   // workgroups of the running pipelined call that finished
+    kCtrlRingLLEpoch = 4, // ring-LL: epoch of the last completed launch
+    kCtrlRingLLDone = 5,  // ring-LL: workgroups of the running launch that finished
     kCtrlPipeBase = 8,   // uint64 at words 8-9: the value every chunk flag holds between
                          // pipelined calls; a call of n steps raises it by n
     kCtrlWords = 64      // 256 bytes
@@ -84,12 +86,36 @@ struct TreeArgs {
     TreeTable tt;
 };
 
+// Ring with the LL protocol: every value a rank passes on travels as an
+// 8-byte line lines[q][c][i] (sender q, segment c, offset i within this
+// launch's piece of the segment).
+struct RingLLArgs {
+    const void* send;
+    void* out;
+    uint64_t* lines;     // [R][R][piece_cap]
+    uint32_t* ctrl;
+    uint64_t N;
+    uint64_t S;
+    uint64_t send_row;
+    uint64_t out_row;
+    uint64_t piece_lo;   // this launch covers offsets [piece_lo, piece_lo + piece_len) of every segment
+    uint64_t piece_len;
+    uint64_t piece_cap;  // lines per (sender, segment)
+    int R;
+    int op;
+    int per_rank_wg;
+    int mute_rank;
+    int redop;
+    uint64_t timeout_ticks;
+};
+
 // Launchers (ar_ring.hip / ar_tree.hip).  Return hipSuccess or the error.
 hipError_t launch_ring_step(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
 hipError_t launch_ring_pipelined(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
 hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t s);
+hipError_t launch_ring_ll(int dtype, const RingLLArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 
@@ -98,6 +124,7 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 int resident_ring_fused(int dtype, bool vec);
 int resident_ring_pipelined(int dtype, bool vec);
 int resident_tree_ll(int dtype);
+int resident_ring_ll(int dtype);
 
 #ifndef AR_BLOCK
 #define AR_BLOCK 256
@@ -108,5 +135,6 @@ int resident_tree_ll(int dtype);
 constexpr int kBlock = AR_BLOCK;   // threads per workgroup (4 wave64 by default)
 constexpr int kUnroll = AR_UNROLL; // 16-byte vectors per thread per pass
 constexpr int kTreeEPT = 4;      // LL lines per thread per tree kernel pass
+constexpr int kRingLLEPT = 4;    // LL lines per thread per ring-LL pass
 
 }  // namespace ar

@@ -1,0 +1,244 @@
+// ar_ring_ll.hip -- the ring with the LL protocol, for gfx950 (MI355X).
+//
+// Same schedule as the other ring forms (R-1 reduce steps, then R-1 copy
+// steps around q -> q+1; rank c owns segment c), but every value a rank
+// passes to its successor travels as an 8-byte LL line: 4 bytes of data (the
+// accumulator's bits, or T's bits zero-extended) and 4 bytes of flag, in one
+// 64-bit atomic store ("Demystifying NVSHMEM ..." summary, paragraph on
+// collectives: LL packs data and arrival flag into one atomic write).  No
+// chunk flags, barriers or fences: each element carries its own arrival
+// flag, and the consumer polls it.
+//
+// Line slot lines[q][c][i] is written by rank q for segment c.  In one call
+// a slot may carry two values: the reduce-phase partial (flag 2*epoch) and,
+// later, the copy-phase final (flag 2*epoch+1).  The final is only produced
+// after the whole reduce chain of the segment has run, which includes the
+// successor's read of the partial, so the overwrite never races the read.
+// Each rank has its own workgroups (workgroup w plays rank w mod R), and the
+// workgroup with index g of rank q handles the same element positions as the
+// workgroup g of every other rank, so a line passes point to point.  All
+// workgroups must be resident together (the host caps the grid); every wait
+// is bounded by the kernel-wide deadline.
+#include "ar_elem.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+template <class E>
+__device__ inline typename E::A combine_rt(int redop, typename E::A a, typename E::A b)
+{
+    switch (redop) {
+    case AR_MAX:
+        return combine<E, AR_MAX>(a, b);
+    case AR_MIN:
+        return combine<E, AR_MIN>(a, b);
+    default:
+        return combine<E, AR_SUM>(a, b);
+    }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    using A = typename E::A;
+    const int R = a.R;
+    const int q = blockIdx.x % R;
+    const int g = blockIdx.x / R;
+    const int G = a.per_rank_wg;
+    const int p = mod_r(q - 1, R);
+    const int nsteps = (OP == kOpAllReduce) ? 2 * (R - 1) : (OP == kOpReduceScatter) ? R - 1 : R;
+    uint32_t* err = &a.ctrl[kCtrlError];
+
+    __shared__ uint32_t s_epoch;
+    __shared__ uint64_t s_deadline;
+    if (threadIdx.x == 0) {
+        s_epoch = __hip_atomic_load(&a.ctrl[kCtrlRingLLEpoch], __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        s_deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
+    }
+    __syncthreads();
+    const uint32_t epoch = s_epoch;
+    const uint32_t f_red = 2u * epoch, f_copy = 2u * epoch + 1u;
+    const uint64_t deadline = s_deadline;
+    const bool publish = (q != a.mute_rank);
+    const T* send = static_cast<const T*>(a.send);
+    T* out = static_cast<T*>(a.out);
+    const float fr = (float)R;
+    bool timed_out = false;
+    constexpr int K = kRingLLEPT;
+
+    for (int s = 0; s < nsteps; ++s) {
+        const int c = (OP == kOpAllGather) ? mod_r(q - s, R) : mod_r(q - s - 2, R);
+        const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+        const uint64_t len = hi - lo;
+        const uint64_t plen = a.piece_lo < len ? min(a.piece_len, len - a.piece_lo) : 0;
+        const uint64_t e0 = lo + a.piece_lo;  // element of offset 0 in a full row
+        uint64_t* mine = a.lines + ((uint64_t)q * R + c) * a.piece_cap;
+        const uint64_t* theirs = a.lines + ((uint64_t)p * R + c) * a.piece_cap;
+        const bool reduce = (OP != kOpAllGather) && s <= R - 2;
+        const bool last_reduce = reduce && s == R - 2;
+        // the last receiver of a segment's final does not pass it on
+        const bool forward = !reduce && (mod_r(c - 1, R) != q);
+        // sub-blocks of kBlock offsets: sub-block j belongs to workgroup j mod G
+        // of every rank; a thread takes K of its workgroup's sub-blocks at once
+        const uint64_t nsub = (plen + kBlock - 1) / kBlock;
+        for (uint64_t j0 = (uint64_t)g; j0 < nsub; j0 += (uint64_t)G * K) {
+            uint64_t i[K];
+            bool ok[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                i[k] = (j0 + (uint64_t)k * G) * kBlock + threadIdx.x;
+                ok[k] = i[k] < plen;
+            }
+            if (reduce) {
+                A in[K];
+                if (s == 0) {
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        if (ok[k])
+                            in[k] = E::widen(send[(uint64_t)p * a.send_row + e0 + i[k]]);
+                } else {
+                    const uint64_t* ln[K];
+                    bool pend[K];
+                    uint32_t d[K];
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        ln[k] = theirs + (ok[k] ? i[k] : 0);
+                        pend[k] = ok[k];
+                        d[k] = 0;
+                    }
+                    if (!ll_wait_batch<K>(ln, pend, f_red, deadline, err, d))
+                        timed_out = true;
+#pragma unroll
+                    for (int k = 0; k < K; ++k)
+                        in[k] = E::from_bits(d[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if (!ok[k])
+                        continue;
+                    A v = combine_rt<E>(a.redop, in[k],
+                                        E::widen(send[(uint64_t)q * a.send_row + e0 + i[k]]));
+                    if (!last_reduce) {
+                        if (publish)
+                            ll_store(mine + i[k], E::to_bits(v), f_red);
+                    } else {
+                        if (a.redop == AR_AVG)
+                            v = finalize<E, AR_AVG>(v, fr);
+                        const uint64_t at = (OP == kOpReduceScatter) ? a.piece_lo + i[k] : e0 + i[k];
+                        out[(uint64_t)q * a.out_row + at] = E::narrow(v);
+                        if (OP == kOpAllReduce && publish)  // the owner starts the copy phase
+                            ll_store(mine + i[k], E::to_bits(v), f_copy);
+                    }
+                }
+            } else if (OP == kOpAllGather && s == 0) {
+                // place the rank's own shard and pass it on (T bits)
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if (!ok[k])
+                        continue;
+                    const T v = send[(uint64_t)q * a.send_row + a.piece_lo + i[k]];
+                    out[(uint64_t)q * a.out_row + e0 + i[k]] = v;
+                    if (publish)
+                        ll_store(mine + i[k], E::t_bits(v), f_copy);
+                }
+            } else {
+                const uint64_t* ln[K];
+                bool pend[K];
+                uint32_t d[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    ln[k] = theirs + (ok[k] ? i[k] : 0);
+                    pend[k] = ok[k];
+                    d[k] = 0;
+                }
+                if (!ll_wait_batch<K>(ln, pend, f_copy, deadline, err, d))
+                    timed_out = true;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    if (!ok[k])
+                        continue;
+                    if (OP == kOpAllGather)
+                        out[(uint64_t)q * a.out_row + e0 + i[k]] = E::t_from_bits(d[k]);
+                    else
+                        out[(uint64_t)q * a.out_row + e0 + i[k]] = E::narrow(E::from_bits(d[k]));
+                    if (forward && publish)
+                        ll_store(mine + i[k], d[k], f_copy);
+                }
+            }
+        }
+    }
+    if (timed_out)
+        __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlRingLLDone], 1u, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            __hip_atomic_store(&a.ctrl[kCtrlRingLLDone], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ctrl[kCtrlRingLLEpoch], epoch, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int DT>
+hipError_t ring_ll_launch(const RingLLArgs& a, int grid, hipStream_t st)
+{
+    if (a.op == kOpAllReduce)
+        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+    else if (a.op == kOpReduceScatter)
+        hipLaunchKernelGGL((k_ring_ll<DT, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+int resident_ring_ll_dt()
+{
+    int dev = 0, ncu = 0, a1 = 0, a2 = 0, a3 = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, k_ring_ll<DT, kOpAllReduce>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, k_ring_ll<DT, kOpReduceScatter>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a3, k_ring_ll<DT, kOpAllGather>, kBlock, 0) != hipSuccess)
+        return 0;
+    return min(a1, min(a2, a3)) * ncu;
+}
+
+}  // namespace
+
+hipError_t launch_ring_ll(int dtype, const RingLLArgs& a, int grid, hipStream_t st)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return ring_ll_launch<AR_INT32>(a, grid, st);
+    case AR_FLOAT32:
+        return ring_ll_launch<AR_FLOAT32>(a, grid, st);
+    case AR_BF16:
+        return ring_ll_launch<AR_BF16>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int resident_ring_ll(int dtype)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return resident_ring_ll_dt<AR_INT32>();
+    case AR_FLOAT32:
+        return resident_ring_ll_dt<AR_FLOAT32>();
+    case AR_BF16:
+        return resident_ring_ll_dt<AR_BF16>();
+    }
+    return 0;
+}
+
+}  // namespace ar

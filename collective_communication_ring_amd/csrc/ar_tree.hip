@@ -33,37 +33,6 @@
 namespace ar {
 namespace {
 
-__device__ inline uint64_t ll_pack(uint32_t data, uint32_t flag)
-{
-    return ((uint64_t)flag << 32) | (uint64_t)data;
-}
-
-// Poll one LL line until its flag is `epoch`.  Gives up (returns false) when
-// the deadline passes or another wave has already reported a timeout.
-__device__ inline bool ll_wait(const uint64_t* line, uint32_t epoch, uint64_t deadline,
-                               const uint32_t* err, uint32_t* data)
-{
-    for (uint32_t spin = 0;; ++spin) {
-        uint64_t v = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(v >> 32) == epoch) {
-            *data = (uint32_t)v;
-            return true;
-        }
-        if ((spin & 63u) == 63u) {
-            if ((uint64_t)wall_clock64() > deadline)
-                return false;
-            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-                return false;
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-}
-
-__device__ inline void ll_put(uint64_t* line, uint32_t data, uint32_t epoch)
-{
-    __hip_atomic_store(line, ll_pack(data, epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // The reduction operator is uniform per launch (a runtime switch is enough
 // on this latency-bound path).
 template <class E>
@@ -116,65 +85,84 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     uint64_t* up_mine = a.up + ((uint64_t)t * R + v) * a.line_stride;
     uint64_t* down_mine = a.down + ((uint64_t)t * R + v) * a.line_stride;
 
-    uint64_t idx[kTreeEPT];
-    bool ok[kTreeEPT];
-    A acc[kTreeEPT];
-    bool timed_out = false;
-#pragma unroll
-    for (int k = 0; k < kTreeEPT; ++k) {
-        idx[k] = (uint64_t)b * (kBlock * kTreeEPT) + (uint64_t)k * kBlock + threadIdx.x;
-        ok[k] = idx[k] < plen;
-        if (ok[k])
-            acc[k] = E::widen(x[idx[k]]);
-    }
-    // reduce up: own value, then each child's subtree sum, ascending rank
-    for (int ci = 0; ci < nchild; ++ci) {
-        const int ch = a.tt.child[t][v][ci];
-        const uint64_t* up_ch = a.up + ((uint64_t)t * R + ch) * a.line_stride;
-#pragma unroll
-        for (int k = 0; k < kTreeEPT; ++k) {
-            if (ok[k]) {
-                uint32_t d = 0;
-                if (!ll_wait(up_ch + idx[k], epoch, deadline, err, &d))
-                    timed_out = true;
-                acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d));
-            }
-        }
-    }
+    constexpr int K = kTreeEPT;
     const bool publish = (v != a.mute_rank);
-    if (parent < 0 && a.redop == AR_AVG) {  // the root's sum is final: average it once
+    bool timed_out = false;
+    // sub-blocks of kBlock lines: sub-block j belongs to workgroup j mod bpr of
+    // this (tree, rank); a thread takes K of its workgroup's sub-blocks at once
+    // and waits for their lines together
+    const uint64_t nsub = (plen + kBlock - 1) / kBlock;
+    for (uint64_t j0 = (uint64_t)b; j0 < nsub; j0 += (uint64_t)bpr * K) {
+        uint64_t idx[K];
+        bool ok[K];
+        A acc[K];
 #pragma unroll
-        for (int k = 0; k < kTreeEPT; ++k)
+        for (int k = 0; k < K; ++k) {
+            idx[k] = (j0 + (uint64_t)k * bpr) * kBlock + threadIdx.x;
+            ok[k] = idx[k] < plen;
             if (ok[k])
-                acc[k] = finalize<E, AR_AVG>(acc[k], (float)R);
-    }
-    if (parent >= 0) {
-#pragma unroll
-        for (int k = 0; k < kTreeEPT; ++k)
-            if (ok[k] && publish)
-                ll_put(up_mine + idx[k], E::to_bits(acc[k]), epoch);
-        // broadcast down: the root's sum arrives from the parent
-#pragma unroll
-        for (int k = 0; k < kTreeEPT; ++k) {
-            if (ok[k]) {
-                uint32_t d = 0;
-                if (!ll_wait(down_mine + idx[k], epoch, deadline, err, &d))
-                    timed_out = true;
-                acc[k] = E::from_bits(d);
-            }
+                acc[k] = E::widen(x[idx[k]]);
         }
-    }
+        // reduce up: own value, then each child's subtree value, ascending rank
+        for (int ci = 0; ci < nchild; ++ci) {
+            const int ch = a.tt.child[t][v][ci];
+            const uint64_t* up_ch = a.up + ((uint64_t)t * R + ch) * a.line_stride;
+            const uint64_t* ln[K];
+            bool pend[K];
+            uint32_t d[K];
 #pragma unroll
-    for (int k = 0; k < kTreeEPT; ++k)
-        if (ok[k])
-            y[idx[k]] = E::narrow(acc[k]);
-    for (int ci = 0; ci < nchild; ++ci) {
-        const int ch = a.tt.child[t][v][ci];
-        uint64_t* down_ch = a.down + ((uint64_t)t * R + ch) * a.line_stride;
+            for (int k = 0; k < K; ++k) {
+                ln[k] = up_ch + (ok[k] ? idx[k] : 0);
+                pend[k] = ok[k];
+                d[k] = 0;
+            }
+            if (!ll_wait_batch<K>(ln, pend, epoch, deadline, err, d))
+                timed_out = true;
 #pragma unroll
-        for (int k = 0; k < kTreeEPT; ++k)
-            if (ok[k] && publish)
-                ll_put(down_ch + idx[k], E::to_bits(acc[k]), epoch);
+            for (int k = 0; k < K; ++k)
+                if (ok[k])
+                    acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d[k]));
+        }
+        if (parent < 0 && a.redop == AR_AVG) {  // the root's sum is final: average it once
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (ok[k])
+                    acc[k] = finalize<E, AR_AVG>(acc[k], (float)R);
+        }
+        if (parent >= 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (ok[k] && publish)
+                    ll_store(up_mine + idx[k], E::to_bits(acc[k]), epoch);
+            // broadcast down: the root's value arrives from the parent
+            const uint64_t* ln[K];
+            bool pend[K];
+            uint32_t d[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                ln[k] = down_mine + (ok[k] ? idx[k] : 0);
+                pend[k] = ok[k];
+                d[k] = 0;
+            }
+            if (!ll_wait_batch<K>(ln, pend, epoch, deadline, err, d))
+                timed_out = true;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (ok[k])
+                    acc[k] = E::from_bits(d[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (ok[k])
+                y[idx[k]] = E::narrow(acc[k]);
+        for (int ci = 0; ci < nchild; ++ci) {
+            const int ch = a.tt.child[t][v][ci];
+            uint64_t* down_ch = a.down + ((uint64_t)t * R + ch) * a.line_stride;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (ok[k] && publish)
+                    ll_store(down_ch + idx[k], E::to_bits(acc[k]), epoch);
+        }
     }
     if (timed_out)
         __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,

@@ -8,7 +8,15 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-LAUNCHES = ["fused", "step", "pipelined"]
+# ring launch forms; "ll" is the ring with the LL protocol
+LAUNCHES = ["fused", "step", "pipelined", "ll"]
+
+
+def ring_opts(launch):
+    """Comm keyword arguments for a ring variant name."""
+    if launch == "ll":
+        return dict(algo="ring", proto="ll")
+    return dict(algo="ring", proto="simple", launch=launch)
 
 
 @pytest.fixture(scope="module")
@@ -74,6 +82,8 @@ def check_tolerance(env, y, x, dtype):
 def run_allreduce(env, x, dtype, algo="ring", proto="simple", launch=None, reps=1, **opts):
     api = env["api"]
     R, N = x.shape
+    if launch == "ll":
+        proto, launch = "ll", None
     comm = api.Comm(R, max(N, 1), dtype, algo, proto, device=env["dev"], launch=launch, **opts)
     send = to_dev(env, x, dtype)
     outs = []
@@ -164,7 +174,7 @@ def test_reduce_scatter_all_gather(env, launch, dtype, R):
     for n in (1, 3, 8, 1000, 8192 + 8):
         N = n * R
         x = rand_input(env, dtype, R, N, seed=77 + n + R)
-        comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=launch)
+        comm = api.Comm(R, N, dtype, device=env["dev"], **ring_opts(launch))
         send = to_dev(env, x, dtype)
         shard = poisoned(env, (R, n), dtype)
         comm.reduce_scatter(send, shard)
@@ -278,7 +288,7 @@ def test_unaligned_views_use_the_scalar_path(env):
     rbase = torch.full((R * N + 3,), float("nan"), device=env["dev"])
     recv = rbase[3:].view(R, N)
     for launch in LAUNCHES:
-        comm = api.Comm(R, N, "float32", device=env["dev"], launch=launch)
+        comm = api.Comm(R, N, "float32", device=env["dev"], **ring_opts(launch))
         comm.allreduce(send, recv)
         assert from_dev(env, recv, "float32").tobytes() == orc.ring_allreduce(x).tobytes()
 
@@ -307,7 +317,7 @@ def test_repeat_runs_bit_identical(env, launch):
 
 # ---------------------------------------------------------------- graphs
 
-@pytest.mark.parametrize("variant", ["fused", "step", "pipelined", "tree"])
+@pytest.mark.parametrize("variant", ["fused", "step", "pipelined", "ll", "tree"])
 def test_graph_replay_matches_eager(env, variant):
     """Capture one call in a HIP graph and replay it several times with eager
     calls and synchronizations in between; every replay must equal the eager
@@ -320,7 +330,7 @@ def test_graph_replay_matches_eager(env, variant):
         comm = api.Comm(R, N, "float32", "tree", "ll", device=env["dev"])
         ref = env["orc"].tree_allreduce(x)
     else:
-        comm = api.Comm(R, N, "float32", "ring", device=env["dev"], launch=variant)
+        comm = api.Comm(R, N, "float32", device=env["dev"], **ring_opts(variant))
         ref = env["orc"].ring_allreduce(x)
     send = to_dev(env, x, "float32")
     eager = poisoned(env, (R, N), "float32")
@@ -364,7 +374,7 @@ def _segment_samples(rng, N, R, m):
     return np.array(idx, dtype=np.int64)
 
 
-@pytest.mark.parametrize("launch", ["auto", "step", "pipelined"])
+@pytest.mark.parametrize("launch", ["auto", "step", "pipelined", "ll"])
 def test_cfg3_largest_size_sampled(env, launch):
     """R = 8, fp32, 1 GiB per rank (the sweep's largest size) in the launch form
     the benchmark times: sampled outputs against the oracle.  The ring's fold
@@ -376,8 +386,8 @@ def test_cfg3_largest_size_sampled(env, launch):
     g.manual_seed(3)
     send = torch.randn((R, N), generator=g, device=env["dev"], dtype=torch.float32)
     recv = torch.full_like(send, float("nan"))
-    comm = api.Comm(R, N, "float32", "ring", device=env["dev"],
-                    launch=None if launch == "auto" else launch)
+    comm = api.Comm(R, N, "float32", device=env["dev"],
+                    **(dict(algo="ring") if launch == "auto" else ring_opts(launch)))
     comm.allreduce(send, recv)
     torch.cuda.synchronize()
     assert comm.check() == api.AR_SUCCESS
@@ -396,7 +406,7 @@ def test_cfg3_largest_size_sampled(env, launch):
 
 # ---------------------------------------------------------------- watchdog
 
-@pytest.mark.parametrize("variant", ["tree", "pipelined"])
+@pytest.mark.parametrize("variant", ["tree", "pipelined", "ll"])
 def test_watchdog_reports_timeout_and_recovers(env, variant):
     """Forced from the host: one logical rank skips publishing, so its
     consumers' bounded waits (5 ms here) expire.  The kernel still finishes,
@@ -409,8 +419,7 @@ def test_watchdog_reports_timeout_and_recovers(env, variant):
         comm = api.Comm(R, N, "float32", "tree", "ll", device=env["dev"], timeout_us=5000)
         ref = orc.tree_allreduce(x)
     else:
-        comm = api.Comm(R, N, "float32", "ring", device=env["dev"], launch="pipelined",
-                        timeout_us=5000)
+        comm = api.Comm(R, N, "float32", device=env["dev"], timeout_us=5000, **ring_opts(variant))
         ref = orc.ring_allreduce(x)
     send = to_dev(env, x, "float32")
     recv = poisoned(env, (R, N), "float32")
@@ -475,7 +484,7 @@ def test_reduction_operators(env, variant, dtype, op):
             ref = orc.ring_allreduce(x, dtype, op=op)
         assert y.tobytes() == ref.tobytes(), (R, N)
         if variant != "tree" and N % R == 0:
-            comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=variant, redop=op)
+            comm = api.Comm(R, N, dtype, device=env["dev"], redop=op, **ring_opts(variant))
             shard = poisoned(env, (R, N // R), dtype)
             comm.reduce_scatter(to_dev(env, x, dtype), shard)
             assert from_dev(env, shard, dtype).tobytes() == orc.ring_reduce_scatter(x, dtype, op=op).tobytes()
@@ -499,7 +508,7 @@ def test_in_place_allreduce(env, variant, dtype):
             comm = api.Comm(R, N, dtype, "tree", "ll", device=env["dev"])
             ref = orc.tree_allreduce(x, dtype)
         else:
-            comm = api.Comm(R, N, dtype, "ring", device=env["dev"], launch=variant)
+            comm = api.Comm(R, N, dtype, device=env["dev"], **ring_opts(variant))
             ref = orc.ring_allreduce(x, dtype)
         buf = to_dev(env, x, dtype)
         comm.allreduce(buf, buf)
@@ -511,3 +520,18 @@ def test_in_place_allreduce(env, variant, dtype):
     with pytest.raises(api.ArError) as e:
         comm.allreduce(base[:256].view(4, 64), base[64:320].view(4, 64))
     assert e.value.status == api.AR_ERR_INVALID_USAGE
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 8, 64])
+def test_ring_ll_multiple_pieces(env, dtype, R):
+    """Counts whose segments exceed one launch's line capacity run as several
+    ring-LL launches (each with a fresh epoch)."""
+    orc = env["orc"]
+    cap = min(10 ** 9, max(64, (1 << 21) // (R * R)))
+    N = R * (2 * cap + 37) + 5
+    x = rand_input(env, dtype, R, N, seed=R + 91)
+    outs = run_allreduce(env, x, dtype, launch="ll", reps=2)
+    ref = orc.ring_allreduce(x, dtype)
+    for y in outs:
+        assert y.tobytes() == ref.tobytes()
