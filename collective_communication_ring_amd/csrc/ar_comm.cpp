@@ -313,11 +313,14 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
         const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
         const uint64_t tile = (uint64_t)kBlock * kUnroll;
         const uint64_t tiles = ((a.S + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
-        // One workgroup per CU by default: with more tiles in flight per XCD
-        // the partial a step writes is evicted from the XCD's L2 before the
-        // next step re-reads it (measured: 0.23 ms at 256 workgroups against
-        // 0.29 ms at the occupancy limit, R = 8 fp32 64 MiB/rank).
-        const int64_t want = c->grid > 0 ? c->grid : (int64_t)c->ncu;
+        // One workgroup per CU by default for all-reduce and all-gather: with
+        // more tiles in flight per XCD the partial a step writes is evicted
+        // from the XCD's L2 before the next step re-reads it (measured: 0.23 ms
+        // at 256 workgroups against 0.29 ms at the occupancy limit, R = 8 fp32
+        // 64 MiB/rank).  Reduce-scatter alone does better with 8 per CU
+        // (R = 16 bf16 25 MiB buckets: 367 against 397 us).
+        const int64_t dflt = (a.op == kOpReduceScatter) ? 8 * (int64_t)c->ncu : (int64_t)c->ncu;
+        const int64_t want = c->grid > 0 ? c->grid : dflt;
         grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
         e = launch_ring_fused(c->dtype, vec, a, grid, st);
     } else if (launch == AR_LAUNCH_PIPELINED) {
