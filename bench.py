@@ -435,6 +435,96 @@ def mode_stream(args):
     return 0
 
 
+def mode_overlap(args):
+    """DDP-style overlap ("NCCL, NIXL, and Distributed GPU Communication",
+    performance checklist: without overlap total = compute + communication,
+    with overlap about max(compute, communication) + a tail).  Buckets of a
+    ring all-reduce (R = 8 fp32, 25 MiB per rank each) run on a second stream
+    while bf16 GEMMs run on the first; reports compute alone, communication
+    alone, both serial and both overlapped, and the exposed communication
+    time.  Uses a launch form without cross-workgroup waits (fused by
+    default), since a concurrent kernel can hold CUs the spin-waiting forms
+    would need."""
+    import torch
+    from collective_communication_ring_amd import api
+    dev = torch.device("cuda:0")
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    raw = []
+    if args.comm_cus:
+        # CU-masked streams need hardware queues of their own (a few per
+        # process): create them before anything else takes one.  The first k
+        # CU indices (k a multiple of 8, so every XCD gets the same share)
+        # go to the collective, the rest to compute.
+        k = max(8, args.comm_cus // 8 * 8)
+        comm_cus = list(range(k))
+        comp_cus = list(range(k, ncu))
+        raw = [api.ar_stream_create_cu_masked(comm_cus, ncu),
+               api.ar_stream_create_cu_masked(comp_cus, ncu)]
+    R, N, B = 8, (25 << 20) // 4, args.buckets or 8
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    xs = [torch.randn((R, N), generator=g, device=dev) for _ in range(B)]
+    ys = [torch.empty_like(x) for x in xs]
+    launch = args.launch if args.launch in ("fused", "step") else "fused"
+    comm = api.Comm(R, N, "float32", device=dev, **ring_kw(launch))
+    M = 8192
+    a = torch.randn((M, M), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((M, M), generator=g, device=dev).to(torch.bfloat16)
+    gemms = args.gemms
+    if raw:
+        s_comm = torch.cuda.ExternalStream(raw[0], device=dev)
+        s_comp = torch.cuda.ExternalStream(raw[1], device=dev)
+        comm.set_option(api.AR_OPT_GRID, len(comm_cus) * (8 if launch == "step" else 1))
+    else:
+        s_comp = torch.cuda.current_stream()
+        s_comm = torch.cuda.Stream()
+
+    def compute():
+        with torch.cuda.stream(s_comp):
+            for _ in range(gemms):
+                torch.mm(a, b)
+
+    def communicate(stream):
+        for x, y in zip(xs, ys):
+            comm.allreduce(x, y, stream=stream)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    def serial():
+        compute()
+        s_comm.wait_stream(s_comp)
+        communicate(s_comm)
+
+    t_comp = timed(compute)
+    t_comm = timed(lambda: communicate(s_comm))
+    t_serial = timed(serial)
+
+    def overlapped():
+        communicate(s_comm)
+        compute()
+
+    t_over = timed(overlapped)
+    assert comm.check() == api.AR_SUCCESS
+    torch.cuda.synchronize()
+    for r in raw:
+        api.ar_stream_destroy(r)
+    out = dict(mode="overlap", launch=launch, comm_cus=args.comm_cus or None, buckets=B,
+               bucket_bytes_per_rank=N * 4, R=R,
+               gemms=gemms, gemm="bf16 %dx%dx%d" % (M, M, M), compute_ms=t_comp, comm_ms=t_comm,
+               serial_ms=t_serial, overlapped_ms=t_over,
+               exposed_comm_ms=t_over - t_comp,
+               ideal_overlapped_ms=max(t_comp, t_comm))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def mode_counters(args):
     """A short program for byte-counter runs (rocprofv3 --pmc): a copy of a
     known size (the calibration), then 3 all-reduces of the headline workload
@@ -506,11 +596,14 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
                     choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream",
-                             "counters", "tune"])
+                             "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
     ap.add_argument("--grids", default="256,512,768,1024,1280,1536,1792,2048")
+    ap.add_argument("--gemms", type=int, default=8, help="overlap mode: GEMMs per iteration")
+    ap.add_argument("--comm-cus", type=int, default=0,
+                    help="overlap mode: CUs reserved for the collective (0: no CU masks)")
     ap.add_argument("--chunk-bytes", type=int, default=512 * 1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
@@ -524,7 +617,7 @@ def main():
         return 2
     fn = {"headline": headline, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
           "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
-          "tune": mode_tune}[args.mode]
+          "tune": mode_tune, "overlap": mode_overlap}[args.mode]
     return fn(args)
 
 

@@ -70,6 +70,9 @@ def lib():
         "ar_stream_add": ([vp, vp, vp, sz, vp], i),
         "ar_stream_copy": ([vp, vp, sz, vp], i),
         "ar_ll_pingpong": ([vp, vp, i, i, i64, vp], i),
+        "ar_stream_create_cu_masked": ([ctypes.POINTER(vp), ctypes.c_uint32,
+                                        ctypes.POINTER(ctypes.c_uint32)], i),
+        "ar_stream_destroy": ([vp], i),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -167,6 +170,24 @@ def ar_stream_copy(src_ptr, dst_ptr, nbytes, stream=0):
 def ar_ll_pingpong(lines_ptr, result_ptr, iters, xcd_apart, timeout_us=2_000_000, stream=0):
     _ok(lib().ar_ll_pingpong(lines_ptr, result_ptr, iters, int(bool(xcd_apart)), timeout_us, stream),
         "ar_ll_pingpong")
+
+
+def ar_stream_create_cu_masked(cus, num_cus):
+    """A stream restricted to the CUs in `cus` (an iterable of CU indices);
+    returns the raw hipStream_t as an integer."""
+    words = (num_cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for c in cus:
+        mask[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = lib().ar_stream_create_cu_masked(ctypes.byref(h), words, mask)
+    if rc != AR_SUCCESS:
+        raise ArError(rc, "ar_stream_create_cu_masked (hipError %d)" % ar_last_hip_error(None))
+    return h.value
+
+
+def ar_stream_destroy(stream):
+    _ok(lib().ar_stream_destroy(stream), "ar_stream_destroy")
 
 
 # ---- torch convenience wrapper ---------------------------------------------

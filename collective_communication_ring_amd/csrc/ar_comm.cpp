@@ -766,6 +766,6 @@ const char* ar_status_string(int s)
     return "unknown status";
 }
 
-int ar_last_hip_error(ar_comm_t c) { return c ? c->last_hip : 0; }
+int ar_last_hip_error(ar_comm_t c) { return c ? c->last_hip : ar::g_util_hip_error; }
 
 }  // extern "C"

@@ -119,6 +119,9 @@ hipError_t launch_ring_ll(int dtype, const RingLLArgs& a, int grid, hipStream_t 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 
+// Last HIP error of the utility calls (ar_stream_*, ar_ll_pingpong).
+extern int g_util_hip_error;
+
 // Largest number of workgroups of each persistent kernel that can be
 // resident at once on the current device (0 on error).
 int resident_ring_fused(int dtype, bool vec);

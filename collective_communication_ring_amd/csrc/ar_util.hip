@@ -180,3 +180,31 @@ extern "C" int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int 
                        static_cast<uint64_t*>(lines), result_dev, iters, 0, wb, ticks);
     return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
 }
+
+// ---- CU-masked streams -------------------------------------------------------
+
+namespace ar {
+int g_util_hip_error = 0;  // last HIP error of the utility calls
+}
+
+extern "C" int ar_stream_create_cu_masked(void** stream, uint32_t mask_words, const uint32_t* mask)
+{
+    if (!stream || !mask || mask_words == 0)
+        return AR_ERR_INVALID_ARG;
+    *stream = nullptr;
+    hipStream_t st = nullptr;
+    const hipError_t e = hipExtStreamCreateWithCUMask(&st, mask_words, mask);
+    if (e != hipSuccess) {
+        ar::g_util_hip_error = (int)e;
+        return AR_ERR_HIP;
+    }
+    *stream = st;
+    return AR_SUCCESS;
+}
+
+extern "C" int ar_stream_destroy(void* stream)
+{
+    if (!stream)
+        return AR_SUCCESS;
+    return hipStreamDestroy(static_cast<hipStream_t>(stream)) == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
+}

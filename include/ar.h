@@ -204,6 +204,16 @@ int ar_tree_parent(ar_comm_t comm, int tree, int r);
 int ar_stream_add(const float* a, const float* b, float* c, size_t n, void* stream);
 int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* stream);
 
+/* Stream with a CU mask (runtime utility for overlapping a collective with
+ * compute, "NCCL, NIXL, and Distributed GPU Communication", performance
+ * checklist: overlap communication with computation).  On one GPU the
+ * collective and the compute share the CUs; giving each its own CUs keeps
+ * them from queueing behind each other.  `mask` has `mask_words` 32-bit
+ * words, bit i enabling CU i.  *stream receives a hipStream_t (default
+ * priority).  Destroy with ar_stream_destroy. */
+int ar_stream_create_cu_masked(void** stream, uint32_t mask_words, const uint32_t* mask);
+int ar_stream_destroy(void* stream);
+
 /* LL hop-latency probe (measurement utility): two workgroups pass one 8-byte
  * LL line back and forth `iters` times -- each waits for the other's line
  * with the current round number as flag, then answers.  `lines` is device
@@ -219,7 +229,8 @@ int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int xcd_apart,
 /* Message for a status code (static storage). */
 const char* ar_status_string(int status);
 
-/* Last hipError_t seen by this comm (0 if none). */
+/* Last hipError_t seen by this comm (0 if none); with comm == NULL, the last
+ * one seen by the utility calls (ar_stream_*, ar_ll_pingpong). */
 int ar_last_hip_error(ar_comm_t comm);
 
 #ifdef __cplusplus

@@ -535,3 +535,29 @@ def test_ring_ll_multiple_pieces(env, dtype, R):
     ref = orc.ring_allreduce(x, dtype)
     for y in outs:
         assert y.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("launch", ["fused", "step"])
+def test_concurrent_with_compute_on_another_stream(env, launch):
+    """A ring all-reduce on a second stream while GEMMs run on the first
+    (the overlap pattern) stays exact."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R, N = 8, 1 << 20
+    x = env["inputs"].draw("normal", R, N, seed=44)
+    ref = orc.ring_allreduce(x)
+    comm = api.Comm(R, N, "float32", device=env["dev"], launch=launch)
+    send = to_dev(env, x, "float32")
+    recv = poisoned(env, (R, N), "float32")
+    a = torch.randn((2048, 2048), device=env["dev"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(side):
+            comm.allreduce(send, recv)
+        c = a
+        for _ in range(4):
+            c = c @ a / 2048.0
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
+    assert comm.check() == api.AR_SUCCESS
