@@ -39,6 +39,12 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [i, sz, i, i, vp, vp]
             f.restype = i
+        for name in ("orc_ring_allreduce_ch", "orc_ring_reduce_scatter_ch"):
+            f = getattr(L, name)
+            f.argtypes = [i, sz, i, i, i, vp, vp, vp]
+            f.restype = i
+        L.orc_ring_all_gather_ch.argtypes = [i, sz, i, i, vp, vp, vp]
+        L.orc_ring_all_gather_ch.restype = i
         L.orc_exact_sum.argtypes = [i, sz, i, vp, vp]
         L.orc_exact_sum.restype = i
         L.orc_tree_parent.argtypes = [i, i, i]
@@ -84,37 +90,46 @@ def _check(rc, name):
         raise RuntimeError("%s failed with code %d" % (name, rc))
 
 
-def ring_allreduce(x, dtype=None, op="sum"):
+def _strides(strides):
+    strides = [1] if strides is None else list(strides)
+    return len(strides), (ctypes.c_int * len(strides))(*strides)
+
+
+def ring_allreduce(x, dtype=None, op="sum", strides=None):
     """Ring all-reduce: every row of the result is the reduction over ranks,
     folded in the ring's order (left fold from the owner's successor); for
-    "avg" the owner divides the sum by R once."""
+    "avg" the owner divides the sum by R once.  `strides` lists one ring
+    stride per channel (default: one channel, stride 1)."""
     x, dtype = _prep(x, dtype)
     R, N = x.shape
     y = np.empty_like(x)
-    _check(lib().orc_ring_allreduce_op(R, N, _DT[dtype], OPS[op], x.ctypes.data, y.ctypes.data),
-           "orc_ring_allreduce_op")
+    K, m = _strides(strides)
+    _check(lib().orc_ring_allreduce_ch(R, N, _DT[dtype], OPS[op], K, m, x.ctypes.data,
+                                       y.ctypes.data), "orc_ring_allreduce_ch")
     return y
 
 
-def ring_reduce_scatter(x, dtype=None, op="sum"):
+def ring_reduce_scatter(x, dtype=None, op="sum", strides=None):
     """Ring reduce-scatter: rank q gets segment q of the reduction; [R, N/R]."""
     x, dtype = _prep(x, dtype)
     R, N = x.shape
     if N % R:
         raise ValueError("reduce-scatter needs N divisible by R")
     y = np.empty((R, N // R), dtype=x.dtype)
-    _check(lib().orc_ring_reduce_scatter_op(R, N, _DT[dtype], OPS[op], x.ctypes.data,
-                                            y.ctypes.data), "orc_ring_reduce_scatter_op")
+    K, m = _strides(strides)
+    _check(lib().orc_ring_reduce_scatter_ch(R, N, _DT[dtype], OPS[op], K, m, x.ctypes.data,
+                                            y.ctypes.data), "orc_ring_reduce_scatter_ch")
     return y
 
 
-def ring_all_gather(shards, dtype=None):
+def ring_all_gather(shards, dtype=None, strides=None):
     """Ring all-gather: [R, n] shards -> [R, R*n], every row [x0, ..., x_{R-1}]."""
     x, dtype = _prep(shards, dtype)
     R, n = x.shape
     y = np.empty((R, R * n), dtype=x.dtype)
-    _check(lib().orc_ring_all_gather(R, n, _DT[dtype], x.ctypes.data, y.ctypes.data),
-           "orc_ring_all_gather")
+    K, m = _strides(strides)
+    _check(lib().orc_ring_all_gather_ch(R, n, _DT[dtype], K, m, x.ctypes.data, y.ctypes.data),
+           "orc_ring_all_gather_ch")
     return y
 
 

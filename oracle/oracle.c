@@ -197,18 +197,32 @@ static size_t seg_lo(size_t N, int R, int c)
 }
 static size_t seg_hi(size_t N, int R, int c) { return seg_lo(N, R, c + 1); }
 
-/* Ring reduce phase, replayed step by step.  At step s (0..R-2) every rank
- * q works on segment c = (q - s - 2) mod R: it adds the partial sum that its
- * predecessor q-1 holds for that segment (at step 0 the predecessor's own
- * input) to its own input.  Before the last step the result is the partial
- * rank q holds; at the last step q == c, the owner, and the result is final.
- * The owner's final value is narrowed to T and written by `emit`.  So for
- * e in segment c the sum is the left fold along the ring that starts at the
- * owner's successor c+1 and ends at the owner c. */
+/* Multi-channel rings (reading of the ring plus "channels = rails", "GPU
+ * MODE lecture 68 notes" section 06, multi-rail aggregation: one channel per
+ * rail).  With K channels every segment is cut into K sub-ranges of
+ * Sk = ceil(ceil(S/K)/8)*8 elements; channel k covers sub-range k of every
+ * segment, [c*S + k*Sk, c*S + (k+1)*Sk) clipped to the segment, and runs its
+ * own ring q -> q + m_k (mod R) with a stride m_k coprime with R.  Rank c
+ * still owns segment c.  K = 1, m = 1 is the plain ring. */
+static void sub_range(size_t N, int R, int c, size_t Sk, int k, size_t* lo, size_t* hi)
+{
+    size_t a = seg_lo(N, R, c), b = seg_hi(N, R, c);
+    size_t x = a + (size_t)k * Sk, y = x + Sk;
+    *lo = x < b ? x : b;
+    *hi = y < b ? y : b;
+}
+
+/* Ring reduce phase of one channel, replayed step by step.  At step s
+ * (0..R-2) every rank q works on segment c = (q - (s+2)m) mod R: it combines
+ * the partial its predecessor q-m holds for that segment (at step 0 the
+ * predecessor's own input) with its own input.  Before the last step the
+ * result is the partial rank q holds; at the last step q == c, the owner,
+ * and the result is final.  The owner's final value is written by `emit`.
+ * So for e in segment c the fold runs x_{c+m}, x_{c+2m}, ..., x_c. */
 typedef void (*emit_fn)(void* ctx, int q, size_t e, acc_t v);
 
-static int ring_reduce_phase(int R, size_t N, int dtype, int op, const void* send,
-                             emit_fn emit, void* ctx)
+static int ring_reduce_phase(int R, size_t N, int dtype, int op, int m, size_t Sk, int k,
+                             const void* send, emit_fn emit, void* ctx)
 {
     acc_t* part = NULL; /* part[q*N + e]: the partial rank q holds */
     if (R > 2) {
@@ -218,9 +232,10 @@ static int ring_reduce_phase(int R, size_t N, int dtype, int op, const void* sen
     }
     for (int s = 0; s <= R - 2; ++s) {
         for (int q = 0; q < R; ++q) {
-            int c = mod(q - s - 2, R);
-            int p = mod(q - 1, R);
-            size_t lo = seg_lo(N, R, c), hi = seg_hi(N, R, c);
+            int c = mod(q - (s + 2) * m, R);
+            int p = mod(q - m, R);
+            size_t lo, hi;
+            sub_range(N, R, c, Sk, k, &lo, &hi);
             for (size_t e = lo; e < hi; ++e) {
                 acc_t in = (s == 0) ? widen(dtype, send, (size_t)p * N + e)
                                     : part[(size_t)p * N + e];
@@ -236,22 +251,50 @@ static int ring_reduce_phase(int R, size_t N, int dtype, int op, const void* sen
     return ORC_OK;
 }
 
-/* Ring copy phase: at step s (0..R-2) every rank q copies segment
- * c = (q - 1 - s) mod R from its predecessor's output into its own.
- * Rows of y are `row` elements long; segment c of the logical N-element
- * vector sits at the same offset in every row. */
-static void ring_gather_phase(int R, size_t N, int dtype, void* y, size_t row)
+/* Ring copy phase of one channel: at step s (0..R-2) every rank q copies
+ * segment c = (q - (1+s)m) mod R from its predecessor q-m's output into its
+ * own.  Rows of y are `row` elements long; segment c of the logical
+ * N-element vector sits at the same offset in every row. */
+static void ring_gather_phase(int R, size_t N, int dtype, int m, size_t Sk, int k, void* y,
+                              size_t row)
 {
     int es = elem_size(dtype);
     for (int s = 0; s <= R - 2; ++s) {
         for (int q = 0; q < R; ++q) {
-            int c = mod(q - 1 - s, R);
-            int p = mod(q - 1, R);
-            size_t lo = seg_lo(N, R, c), hi = seg_hi(N, R, c);
+            int c = mod(q - (1 + s) * m, R);
+            int p = mod(q - m, R);
+            size_t lo, hi;
+            sub_range(N, R, c, Sk, k, &lo, &hi);
             memcpy((char*)y + ((size_t)q * row + lo) * es,
                    (const char*)y + ((size_t)p * row + lo) * es, (hi - lo) * es);
         }
     }
+}
+
+static size_t channel_len(size_t N, int R, int K)
+{
+    size_t S = (N + (size_t)R - 1) / (size_t)R;
+    size_t Sk = (S + (size_t)K - 1) / (size_t)K;
+    return (Sk + 7) / 8 * 8;
+}
+
+static int check_strides(int R, int K, const int* m)
+{
+    if (K < 1 || !m)
+        return ORC_EINVAL;
+    for (int k = 0; k < K; ++k) {
+        int a = mod(m[k], R), b = R;
+        if (a == 0)
+            return ORC_EINVAL;
+        while (b) { /* gcd(m, R) must be 1: the ring visits every rank */
+            int t = a % b;
+            a = b;
+            b = t;
+        }
+        if (a != 1)
+            return ORC_EINVAL;
+    }
+    return ORC_OK;
 }
 
 struct emit_ctx {
@@ -290,20 +333,31 @@ static int check_op(int dtype, int op)
     return ORC_OK;
 }
 
-/* All-reduce by ring: reduce phase, the owner writes its final segment into
- * its own output row, then the copy phase spreads every segment round the
+/* All-reduce by ring with K channels (strides m[0..K-1]): per channel, the
+ * reduce phase (the owner writes its final sub-segment into its own output
+ * row), then the copy phase spreads every sub-segment round that channel's
  * ring.  send and recv are [R][N]. */
-int orc_ring_allreduce_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
+int orc_ring_allreduce_ch(int R, size_t N, int dtype, int op, int K, const int* m,
+                          const void* send, void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc || (rc = check_op(dtype, op)))
+    if (rc || (rc = check_op(dtype, op)) || (rc = check_strides(R, K, m)))
         return rc;
+    size_t Sk = channel_len(N, R, K);
     struct emit_ctx ctx = {dtype, recv, N, R, N};
-    rc = ring_reduce_phase(R, N, dtype, op, send, emit_full, &ctx);
-    if (rc)
-        return rc;
-    ring_gather_phase(R, N, dtype, recv, N);
+    for (int k = 0; k < K; ++k) {
+        rc = ring_reduce_phase(R, N, dtype, op, m[k], Sk, k, send, emit_full, &ctx);
+        if (rc)
+            return rc;
+        ring_gather_phase(R, N, dtype, m[k], Sk, k, recv, N);
+    }
     return ORC_OK;
+}
+
+int orc_ring_allreduce_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
+{
+    const int one = 1;
+    return orc_ring_allreduce_ch(R, N, dtype, op, 1, &one, send, recv);
 }
 
 int orc_ring_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
@@ -313,15 +367,26 @@ int orc_ring_allreduce(int R, size_t N, int dtype, const void* send, void* recv)
 
 /* Reduce-scatter by ring: the reduce phase only; rank q's output is its own
  * segment q, of length N/R.  send is [R][N], recv is [R][N/R]. */
-int orc_ring_reduce_scatter_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
+int orc_ring_reduce_scatter_ch(int R, size_t N, int dtype, int op, int K, const int* m,
+                               const void* send, void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc || (rc = check_op(dtype, op)))
+    if (rc || (rc = check_op(dtype, op)) || (rc = check_strides(R, K, m)))
         return rc;
     if (N % (size_t)R != 0)
         return ORC_EINVAL;
+    size_t Sk = channel_len(N, R, K);
     struct emit_ctx ctx = {dtype, recv, N / (size_t)R, R, N};
-    return ring_reduce_phase(R, N, dtype, op, send, emit_shard, &ctx);
+    for (int k = 0; k < K; ++k)
+        if ((rc = ring_reduce_phase(R, N, dtype, op, m[k], Sk, k, send, emit_shard, &ctx)))
+            return rc;
+    return ORC_OK;
+}
+
+int orc_ring_reduce_scatter_op(int R, size_t N, int dtype, int op, const void* send, void* recv)
+{
+    const int one = 1;
+    return orc_ring_reduce_scatter_ch(R, N, dtype, op, 1, &one, send, recv);
 }
 
 int orc_ring_reduce_scatter(int R, size_t N, int dtype, const void* send, void* recv)
@@ -330,19 +395,29 @@ int orc_ring_reduce_scatter(int R, size_t N, int dtype, const void* send, void* 
 }
 
 /* All-gather by ring: rank q first places its own shard at position q of its
- * output, then the copy phase runs.  send is [R][n], recv is [R][R*n]. */
-int orc_ring_all_gather(int R, size_t n, int dtype, const void* send, void* recv)
+ * output, then each channel's copy phase runs.  send is [R][n], recv is
+ * [R][R*n]. */
+int orc_ring_all_gather_ch(int R, size_t n, int dtype, int K, const int* m, const void* send,
+                           void* recv)
 {
     int rc = check_args(R, dtype, send, recv);
-    if (rc)
+    if (rc || (rc = check_strides(R, K, m)))
         return rc;
     int es = elem_size(dtype);
     size_t N = n * (size_t)R;
     for (int q = 0; q < R; ++q)
         memcpy((char*)recv + ((size_t)q * N + (size_t)q * n) * es,
                (const char*)send + (size_t)q * n * es, n * es);
-    ring_gather_phase(R, N, dtype, recv, N);
+    size_t Sk = channel_len(N, R, K);
+    for (int k = 0; k < K; ++k)
+        ring_gather_phase(R, N, dtype, m[k], Sk, k, recv, N);
     return ORC_OK;
+}
+
+int orc_ring_all_gather(int R, size_t n, int dtype, const void* send, void* recv)
+{
+    const int one = 1;
+    return orc_ring_all_gather_ch(R, n, dtype, 1, &one, send, recv);
 }
 
 /* ---- double binary tree ---------------------------------------------- */

@@ -482,3 +482,84 @@ def test_int32_avg_is_refused(orc):
     x = np.ones((4, 8), np.int32)
     with pytest.raises(RuntimeError):
         orc.ring_allreduce(x, op="avg")
+
+
+# ---------------------------------------------------------------- multi-channel rings
+
+def _channel_bounds(N, R, K, c, k):
+    S = -(-N // R)
+    Sk = -(-(-(-S // K)) // 8) * 8
+    a, b = min(c * S, N), min((c + 1) * S, N)
+    return min(a + k * Sk, b), min(a + (k + 1) * Sk, b)
+
+
+def test_reverse_stride_folds_the_other_way(orc):
+    # Stride 3 at R = 4 is the ring q -> q-1: segment c folds x_{c+3},
+    # x_{c+2}, x_{c+1}, x_c.  With x_c = -T, x_{c+1} = T, x_{c+2} = x_{c+3} = 1:
+    #   1 + 1 = 2, 2 + T = T + 2 (exact: even), T + 2 - T = 2.
+    # Stride 1 (x_{c+1} first) gives 0, see test_ring_order_pin_r4_every_segment.
+    R, N = 4, 8
+    x = np.zeros((R, N), np.float32)
+    for c in range(R):
+        lo, hi = seg_bounds(N, R, c)
+        for e in range(lo, hi):
+            x[c, e], x[(c + 1) % R, e] = -T24, T24
+            x[(c + 2) % R, e] = x[(c + 3) % R, e] = 1
+    assert (orc.ring_allreduce(x, strides=[3]) == 2.0).all()
+    assert (orc.ring_allreduce(x, strides=[1]) == 0.0).all()
+
+
+def test_channel_split_of_each_segment(orc):
+    # R = 4, N = 64: S = 16, two channels of Sk = 8 -> channel 0 takes the
+    # first 8 elements of every segment (stride 1 -> 0.0), channel 1 the last
+    # 8 (stride 3 -> 2.0), with the pattern above in every element.
+    R, N = 4, 64
+    x = np.zeros((R, N), np.float32)
+    for c in range(R):
+        x[c, c * 16:(c + 1) * 16] = -T24
+        x[(c + 1) % R, c * 16:(c + 1) * 16] = T24
+        x[(c + 2) % R, c * 16:(c + 1) * 16] = 1
+        x[(c + 3) % R, c * 16:(c + 1) * 16] = 1
+    y = orc.ring_allreduce(x, strides=[1, 3])[0].reshape(R, 16)
+    assert (y[:, :8] == 0.0).all() and (y[:, 8:] == 2.0).all()
+
+
+def _closed_form_channels(x, strides):
+    R, N = x.shape
+    K = len(strides)
+    y = np.empty(N, np.float32)
+    for c in range(R):
+        for k, m in enumerate(strides):
+            lo, hi = _channel_bounds(N, R, K, c, k)
+            for e in range(lo, hi):
+                acc = np.float32(x[(c + m) % R, e])
+                for j in range(2, R + 1):
+                    acc = np.float32(acc + x[(c + j * m) % R, e])
+                y[e] = acc
+    return y
+
+
+@pytest.mark.parametrize("R,strides", [(4, [1, 3]), (5, [1, 4, 2, 3]), (8, [1, 7, 3, 5]),
+                                       (8, [3]), (7, [1, 6, 2])])
+def test_channels_brute_force_and_identities(orc, R, strides):
+    rng = np.random.default_rng(R + len(strides))
+    for N in (1, 5, 37, 200, 1000):
+        x = (rng.standard_normal((R, N)) * 10.0 ** rng.integers(-3, 4, size=(R, N))).astype(np.float32)
+        y = orc.ring_allreduce(x, strides=strides)
+        assert y.tobytes() == np.tile(_closed_form_channels(x, strides), (R, 1)).tobytes()
+        xi = rng.integers(-1000, 1001, size=(R, N)).astype(np.int32)
+        assert (orc.ring_allreduce(xi, strides=strides) == xi.sum(axis=0)[None, :]).all()
+    N = R * 53
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    ar = orc.ring_allreduce(x, strides=strides)
+    rs = orc.ring_reduce_scatter(x, strides=strides)
+    assert orc.ring_all_gather(rs, strides=strides).tobytes() == ar.tobytes()
+    assert orc.ring_all_gather(rs).tobytes() == ar.tobytes()  # all-gather is a copy
+
+
+def test_channel_strides_must_visit_every_rank(orc):
+    x = np.ones((4, 8), np.float32)
+    with pytest.raises(RuntimeError):
+        orc.ring_allreduce(x, strides=[2])     # gcd(2, 4) = 2
+    with pytest.raises(RuntimeError):
+        orc.ring_allreduce(x, strides=[4])
