@@ -33,11 +33,14 @@ KERNEL_SOURCES = ["collective_communication_ring_amd/csrc/ar_ring.hip",
                   "collective_communication_ring_amd/csrc/ar_elem.h"]
 
 
-def ring_kw(launch):
-    """Comm keyword arguments for a --launch value ('ll' selects the LL protocol)."""
-    if launch == "ll":
-        return dict(algo="ring", proto="ll")
-    return dict(algo="ring", proto="simple", launch=launch)
+def ring_kw(launch, channels=1):
+    """Comm keyword arguments for a --launch value ('ll' selects the LL protocol)
+    and a number of ring channels."""
+    kw = dict(algo="ring", proto="ll") if launch == "ll" else \
+        dict(algo="ring", proto="simple", launch=launch)
+    if channels > 1:
+        kw["channels"] = channels
+    return kw
 
 
 def log(*a):
@@ -111,16 +114,17 @@ def time_graph(fn, calls, torch, reps=3):
     return ms
 
 
-def cpu_baseline(x, R, N, s, target_s=12.0):
+def cpu_baseline(x, R, N, s, target_s=12.0, strides=None):
     """The oracle, as it is, on the host: repeat the full all-reduce until
-    about target_s seconds of CPU work; report its busBW."""
+    about target_s seconds of CPU work; report its busBW.  `strides` are the
+    ring channels' strides (one ring of stride 1 by default)."""
     import oracle
     ts = []
     y = None
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        y = oracle.ring_allreduce(x)
+        y = oracle.ring_allreduce(x, strides=strides)
         ts.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > target_s or len(ts) >= 20:
             break
@@ -142,7 +146,7 @@ def headline(args):
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
     comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=512 * 1024, grid=args.grid,
-                    **ring_kw(args.launch))
+                    **ring_kw(args.launch, args.channels))
     _, proto, launch = comm.plan(N)
     launch_name = "ll" if proto == api.AR_LL else {v: k for k, v in api.LAUNCHES.items()}[launch]
     per, total_ms, wall = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
@@ -159,7 +163,10 @@ def headline(args):
               "pipelined": "k_ring_pipelined<float32, 16-byte slots, all-reduce>",
               "ll": "k_ring_ll<float32, all-reduce> (one launch per piece)",
               "step": "k_ring_reduce_step + k_ring_copy_step (2(R-1) launches)"}[launch_name]
-    traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name)
+    if args.channels > 1:
+        kernel += ", one launch per channel x %d channels" % args.channels
+    traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name) \
+        if args.channels == 1 else None
     line = {
         "metric": METRIC,
         "value": round(busbw, 3),
@@ -176,7 +183,8 @@ def headline(args):
         "config": {"workload": "ring all-reduce (sum), R=8 logical ranks, fp32, 16,777,216 "
                                "elements (64 MiB) per rank, N(0,1) seed 2, simple protocol, "
                                "512 KiB chunks",
-                   "R": R, "count_per_rank": N, "launch": launch_name},
+                   "R": R, "count_per_rank": N, "launch": launch_name,
+                   "channels": args.channels},
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),
         "hbm_alg_GBps": round(b_alg / t / 1e9, 3),
@@ -189,7 +197,7 @@ def headline(args):
     }
     y = None
     if not args.no_cpu_baseline:
-        y, line["cpu_baseline"] = cpu_baseline(x, R, N, s)
+        y, line["cpu_baseline"] = cpu_baseline(x, R, N, s, strides=comm.channel_strides())
     else:
         line["cpu_baseline"] = None
     if y is not None:
@@ -217,7 +225,7 @@ def mode_sweep(args):
     send_flat = torch.randn(R * Nmax, generator=g, device=dev, dtype=torch.float32)
     recv_flat = torch.empty_like(send_flat)
     comm = api.Comm(R, Nmax, "float32", device=dev, chunk_bytes=512 * 1024, grid=args.grid,
-                    **ring_kw(args.launch))
+                    **ring_kw(args.launch, args.channels))
     rows = []
     out = open(args.out, "w") if args.out else None
     for N in counts:
@@ -369,7 +377,7 @@ def mode_buckets(args):
     xs = [inputs.device_bucket_bf16(R, N, w["seed"], b, dev) for b in range(B)]
     shards = [torch.empty((R, n), dtype=torch.bfloat16, device=dev) for _ in range(B)]
     full = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
-    comm = api.Comm(R, N, "bf16", device=dev, grid=args.grid, **ring_kw(args.launch))
+    comm = api.Comm(R, N, "bf16", device=dev, grid=args.grid, **ring_kw(args.launch, args.channels))
 
     def rs_all():
         for b in range(B):
@@ -574,7 +582,7 @@ def mode_tune(args):
     res = []
     for grid in [int(g) for g in args.grids.split(",")]:
         comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=args.chunk_bytes, grid=grid,
-                        **ring_kw(args.launch))
+                        **ring_kw(args.launch, args.channels))
         _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                     torch)
         ms = total_ms / args.steps
@@ -606,6 +614,9 @@ def main():
                     help="overlap mode: CUs reserved for the collective (0: no CU masks)")
     ap.add_argument("--chunk-bytes", type=int, default=512 * 1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--channels", type=int, default=1,
+                    help="ring channels (each its own ring stride over a sub-range of "
+                         "every segment)")
     ap.add_argument("--eager", action="store_true",
                     help="sweep / tree-vs-ring: time host-enqueued calls instead of graph replays")
     args = ap.parse_args()

@@ -22,7 +22,8 @@ AR_SUCCESS, AR_ERR_INVALID_ARG, AR_ERR_INVALID_USAGE, AR_ERR_UNSUPPORTED = 0, 1,
 AR_ERR_HIP, AR_ERR_TIMEOUT, AR_ERR_INTERNAL = 4, 5, 6
 AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 3
 (AR_OPT_CHUNK_BYTES, AR_OPT_LAUNCH, AR_OPT_GRID, AR_OPT_TIMEOUT_US, AR_OPT_DEBUG,
- AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK, AR_OPT_REDOP) = range(10)
+ AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK, AR_OPT_REDOP,
+ AR_OPT_CHANNELS) = range(11)
 AR_SUM, AR_MAX, AR_MIN, AR_AVG = 0, 1, 2, 3
 REDOPS = {"sum": AR_SUM, "max": AR_MAX, "min": AR_MIN, "avg": AR_AVG}
 
@@ -65,6 +66,7 @@ def lib():
         "ar_plan": ([vp, sz, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
         "ar_ring_segment": ([vp, sz, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
         "ar_tree_parent": ([vp, i, i], i),
+        "ar_ring_channel_stride": ([vp, i], i),
         "ar_status_string": ([i], ctypes.c_char_p),
         "ar_last_hip_error": ([vp], i),
         "ar_stream_add": ([vp, vp, vp, sz, vp], i),
@@ -149,6 +151,10 @@ def ar_ring_segment(comm, count, c):
 
 def ar_tree_parent(comm, tree, r):
     return lib().ar_tree_parent(comm, tree, r)
+
+
+def ar_ring_channel_stride(comm, k):
+    return lib().ar_ring_channel_stride(comm, k)
 
 
 def ar_status_string(status):
@@ -272,6 +278,11 @@ class Comm:
 
     def plan(self, count):
         return ar_plan(self.handle, count)
+
+    def channel_strides(self):
+        """Ring stride of each channel this comm runs."""
+        K = self.get_option(AR_OPT_CHANNELS)
+        return [ar_ring_channel_stride(self.handle, k) for k in range(K)]
 
     def close(self):
         if getattr(self, "handle", None):

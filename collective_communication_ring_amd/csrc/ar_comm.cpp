@@ -117,6 +117,9 @@ struct ar_comm {
     int64_t tree_max_bytes = kDefaultTreeMaxBytes;
     int64_t mute_rank = -1;  // testing the watchdog only
     int64_t redop = AR_SUM;
+    int64_t channels = 1;
+    int strides[kMaxRanks] = {};  // ring stride of each possible channel
+    int nstrides = 0;
     // schedule
     TreeTable tt{};
     // workspace layout
@@ -261,6 +264,9 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
     a.send_row = r.send_row;
     a.out_row = r.out_row;
     a.piece_cap = c->rll_cap;
+    a.sub_lo = r.sub_lo;
+    a.sub_len = r.sub_len;
+    a.m = r.m;
     a.R = r.R;
     a.op = r.op;
     a.mute_rank = (int)c->mute_rank;
@@ -270,9 +276,9 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
     if (gmax < 1)
         return AR_ERR_UNSUPPORTED;
     int launches = 0;
-    for (uint64_t lo = 0; lo < a.S; lo += c->rll_cap) {
+    for (uint64_t lo = 0; lo < a.sub_len; lo += c->rll_cap) {
         a.piece_lo = lo;
-        a.piece_len = std::min<uint64_t>(c->rll_cap, a.S - lo);
+        a.piece_len = std::min<uint64_t>(c->rll_cap, a.sub_len - lo);
         a.per_rank_wg = (int)ll_grid_per_rank(a.piece_len, a.R, c->ncu, kRingLLEPT, gmax);
         hipError_t e = launch_ring_ll(c->dtype, a, a.per_rank_wg * a.R, st);
         if (e != hipSuccess)
@@ -285,7 +291,28 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
     return AR_SUCCESS;
 }
 
+int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st);
+
+// One ring collective: every channel covers its own sub-range of every
+// segment with its own ring stride, launched one after the other.
 int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
+{
+    const uint64_t K = (uint64_t)c->channels;
+    const uint64_t Sk = ((a.S + K - 1) / K + 7) / 8 * 8;
+    for (uint64_t k = 0; k < K; ++k) {
+        a.m = c->strides[k];
+        a.sub_lo = k * Sk;
+        a.sub_len = Sk;
+        if (a.sub_lo >= a.S && k > 0)
+            break;  // nothing left for later channels
+        const int rc = run_ring_channel(c, a, st);
+        if (rc)
+            return rc;
+    }
+    return AR_SUCCESS;
+}
+
+int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
 {
     if (c->proto == AR_LL)
         return run_ring_ll(c, a, st);
@@ -296,7 +323,7 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
     hipError_t e = hipSuccess;
     int grid = 0;
     if (launch == AR_LAUNCH_STEP) {
-        const int gx = ring_grid_x(c, a.S, vec);
+        const int gx = ring_grid_x(c, a.sub_len, vec);
         grid = gx * a.R;
         int nsteps = 0;
         if (a.op == kOpAllGather) {
@@ -312,7 +339,7 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
     } else if (launch == AR_LAUNCH_FUSED) {
         const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
         const uint64_t tile = (uint64_t)kBlock * kUnroll;
-        const uint64_t tiles = ((a.S + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
+        const uint64_t tiles = ((a.sub_len + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
         // One workgroup per CU by default for all-reduce and all-gather: with
         // more tiles in flight per XCD the partial a step writes is evicted
         // from the XCD's L2 before the next step re-reads it (measured: 0.23 ms
@@ -333,14 +360,14 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
         const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
         const uint64_t tile = (uint64_t)kBlock * kUnroll * V;  // elements per workgroup pass
         const uint64_t es = (uint64_t)elem_size(c->dtype);
-        uint64_t unit = c->chunk_bytes > 0 ? (uint64_t)c->chunk_bytes / es : a.S;
+        uint64_t unit = c->chunk_bytes > 0 ? (uint64_t)c->chunk_bytes / es : a.sub_len;
         unit = std::max<uint64_t>(tile, unit / tile * tile);
-        uint64_t nunits = (a.S + unit - 1) / unit;
+        uint64_t nunits = (a.sub_len + unit - 1) / unit;
         // the chunk is the pipelining unit; cut it finer when a segment has
         // fewer chunks than there are workgroups per rank
         while (nunits < (uint64_t)gmax && unit > tile) {
             unit = std::max<uint64_t>(tile, (unit / 2 + tile - 1) / tile * tile);
-            nunits = (a.S + unit - 1) / unit;
+            nunits = (a.sub_len + unit - 1) / unit;
         }
         uint64_t G = std::min<uint64_t>(nunits, (uint64_t)gmax);
         G = (nunits + (nunits + G - 1) / G - 1) / ((nunits + G - 1) / G);  // balance chunks per workgroup
@@ -469,6 +496,23 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     else if (l && !std::strcmp(l, "pipelined"))
         c->launch = AR_LAUNCH_PIPELINED;
     build_trees(R, &c->tt);
+    // channel strides: 1, R-1, 3, R-3, ... coprime with R, each once
+    for (int m = 1; m < R && c->nstrides < kMaxRanks; ++m) {
+        for (int cand : {m, R - m}) {
+            int a = cand, b = R;
+            while (b) {
+                const int t = a % b;
+                a = b;
+                b = t;
+            }
+            bool seen = false;
+            for (int i = 0; i < c->nstrides; ++i)
+                seen |= (c->strides[i] == cand);
+            if (a == 1 && !seen)
+                c->strides[c->nstrides++] = cand;
+        }
+    }
+    c->channels = std::min<int64_t>(std::max<int64_t>(1, env_int("AR_CHANNELS", 1)), c->nstrides);
     // workspace: control block | partial sums [R][cap] (A) | tree LL up | down
     const size_t cap1 = count ? count : 1;
     c->tree_lines = std::min<uint64_t>((cap1 + 1) / 2, kTreeLinesCap);
@@ -702,6 +746,11 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
             return AR_ERR_INVALID_ARG;
         c->redop = v;
         return AR_SUCCESS;
+    case AR_OPT_CHANNELS:
+        if (v < 1 || v > c->nstrides)
+            return AR_ERR_INVALID_ARG;
+        c->channels = v;
+        return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }
@@ -721,6 +770,7 @@ int ar_get_option(ar_comm_t c, int option, int64_t* v)
     case AR_OPT_TREE_MAX_BYTES: *v = c->tree_max_bytes; return AR_SUCCESS;
     case AR_OPT_DEBUG_MUTE_RANK: *v = c->mute_rank; return AR_SUCCESS;
     case AR_OPT_REDOP: *v = c->redop; return AR_SUCCESS;
+    case AR_OPT_CHANNELS: *v = c->channels; return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }
@@ -743,6 +793,13 @@ int ar_ring_segment(ar_comm_t c, size_t count, int seg, size_t* lo, size_t* hi)
     *lo = std::min(count, (size_t)seg * S);
     *hi = std::min(count, (size_t)(seg + 1) * S);
     return AR_SUCCESS;
+}
+
+int ar_ring_channel_stride(ar_comm_t c, int k)
+{
+    if (!c || k < 0 || k >= c->nstrides)
+        return -1;
+    return c->strides[k];
 }
 
 int ar_tree_parent(ar_comm_t c, int tree, int r)

@@ -254,4 +254,16 @@ __device__ inline uint64_t seg_lo(uint64_t N, uint64_t S, int c)
     return b < N ? b : N;
 }
 
+// The part of segment c a channel covers: [c*S + sub_lo, c*S + sub_lo +
+// sub_len) clipped to the segment [c*S, min((c+1)*S, N)).
+__device__ inline void seg_range(uint64_t N, uint64_t S, int c, uint64_t sub_lo, uint64_t sub_len,
+                                 uint64_t* lo, uint64_t* hi)
+{
+    const uint64_t end = seg_lo(N, S, c + 1);
+    const uint64_t a = seg_lo(N, S, c) + sub_lo;
+    const uint64_t b = a + sub_len;
+    *lo = a < end ? a : end;
+    *hi = b < end ? b : end;
+}
+
 }  // namespace ar

@@ -58,6 +58,9 @@ struct RingArgs {
     uint64_t unit;    // pipelined ring: elements per flagged chunk (a multiple of the slot)
     uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
     uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
+    uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
+    uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
+    int m;            // this channel's ring stride: rank q receives from q - m
     int R;
     int op;           // Op
     int step;         // step-per-launch mode: the step this launch runs
@@ -98,9 +101,12 @@ struct RingLLArgs {
     uint64_t S;
     uint64_t send_row;
     uint64_t out_row;
-    uint64_t piece_lo;   // this launch covers offsets [piece_lo, piece_lo + piece_len) of every segment
+    uint64_t sub_lo;     // channel sub-range of every segment (see RingArgs)
+    uint64_t sub_len;
+    uint64_t piece_lo;   // this launch covers offsets [piece_lo, piece_lo + piece_len) of the sub-range
     uint64_t piece_len;
     uint64_t piece_cap;  // lines per (sender, segment)
+    int m;               // ring stride
     int R;
     int op;
     int per_rank_wg;

@@ -25,10 +25,11 @@
 // workgroup to finish raises base by n.  A step-s consumer waits for a
 // value >= base+s, which only this call's producers write.
 //
-// Step numbering: all-reduce steps s = 0 .. 2R-3 and reduce-scatter steps
-// s = 0 .. R-2 handle segment c = (q - s - 2) mod R (reduce for s <= R-2,
-// copy after); all-gather steps s = 0 .. R-1 handle segment c = (q - s) mod R
-// (step 0 places the rank's own shard, then copies).
+// Step numbering (ring stride m, 1 for a single channel): all-reduce steps
+// s = 0 .. 2R-3 and reduce-scatter steps s = 0 .. R-2 handle segment
+// c = (q - (s+2)m) mod R (reduce for s <= R-2, copy after); all-gather steps
+// s = 0 .. R-1 handle segment c = (q - s m) mod R (step 0 places the rank's
+// own shard, then copies).
 //
 // All R*G workgroups must be resident together; the host sizes the grid by
 // the occupancy limit, and every wait is bounded in time.
@@ -318,11 +319,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
     }
     __syncthreads();
     const uint64_t base = s_base;
-    const int p = mod_r(q - 1, R);
+    const int m = a.m;
+    const int p = mod_r(q - m, R);
 
     for (int s = 0; s < nsteps; ++s) {
-        const int c = (OP == kOpAllGather) ? mod_r(q - s, R) : mod_r(q - s - 2, R);
-        const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+        const int c = (OP == kOpAllGather) ? mod_r(q - s * m, R) : mod_r(q - (s + 2) * m, R);
+        uint64_t lo, hi;
+        seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
         const uint64_t len = hi - lo;
         for (uint64_t k = (uint64_t)g; k < a.nunits; k += (uint64_t)G) {
             const uint64_t ulo = k * a.unit;
@@ -342,7 +345,8 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
                 const rsrc_t prevT = make_rsrc(send + (uint64_t)p * a.send_row + e0, ulen * sizeof(T));
                 const rsrc_t prevA = make_rsrc(part + (uint64_t)p * a.N + e0, ulen * 4);
                 const rsrc_t dstA = make_rsrc(part + (uint64_t)q * a.N + e0, ulen * 4);
-                T* dT = out + (uint64_t)q * a.out_row + (OP == kOpReduceScatter ? ulo : e0);
+                T* dT = out + (uint64_t)q * a.out_row +
+                        (OP == kOpReduceScatter ? e0 - (uint64_t)c * a.S : e0);
                 const rsrc_t dstT = make_rsrc(dT, ulen * sizeof(T));
                 const float fr = (float)R;
                 switch (a.redop) {
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
                 // shard in send (written before the kernel), else the
                 // predecessor's output row (written in this kernel)
                 const bool placement = (OP == kOpAllGather && s == 0);
-                const T* srcp = placement ? send + (uint64_t)q * a.send_row + ulo
+                const T* srcp = placement ? send + (uint64_t)q * a.send_row + (e0 - (uint64_t)q * a.S)
                                           : out + (uint64_t)p * a.out_row + e0;
                 const rsrc_t src = make_rsrc(srcp, ulen * sizeof(T));
                 const rsrc_t dst = make_rsrc(out + (uint64_t)q * a.out_row + e0, ulen * sizeof(T));

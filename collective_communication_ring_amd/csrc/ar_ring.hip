@@ -10,6 +10,10 @@
 //   copy step s (0..R-2), rank q, segment c = (q-1-s) mod R:
 //       y_q = y_{q-1} over segment c.
 // So an element of segment c is the left fold x_{c+1} + x_{c+2} + ... + x_c.
+// With several channels (the multi-rail idea, "GPU MODE lecture 68 notes",
+// section 06: one channel per rail), each segment is cut into one sub-range
+// per channel and channel k runs its own ring q -> q + m_k with a stride m_k
+// coprime with R: every formula above with 1 replaced by m_k.
 //
 // All R logical ranks live in one HBM: rank q's buffers are row q of
 // rank-major arrays, and "receiving from q-1" is reading row q-1 in place
@@ -47,8 +51,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_reduce_step(RingArgs a)
     using E = Elem<DT>;
     const int q = blockIdx.y;
     const int s = a.step;
-    const int c = mod_r(q - s - 2, a.R);
-    const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+    const int c = mod_r(q - (s + 2) * a.m, a.R);
+    uint64_t lo, hi;
+    seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
     const uint64_t len = hi - lo;
     const uint64_t nslots = (len + V - 1) / V;
     const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
@@ -65,9 +70,10 @@ __global__ __launch_bounds__(kBlock) void k_ring_copy_step(RingArgs a)
     using T = typename E::T;
     const int q = blockIdx.y;
     const int s = a.step;
-    const int c = mod_r(q - 1 - s, a.R);
-    const int p = mod_r(q - 1, a.R);
-    const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+    const int c = mod_r(q - (1 + s) * a.m, a.R);
+    const int p = mod_r(q - a.m, a.R);
+    uint64_t lo, hi;
+    seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
     const uint64_t len = hi - lo;
     const uint64_t nslots = (len + V - 1) / V;
     T* out = static_cast<T*>(a.out);
@@ -86,10 +92,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
     using E = Elem<DT>;
     using T = typename E::T;
     const int q = blockIdx.y;
-    const uint64_t lo = seg_lo(a.N, a.S, q), hi = seg_lo(a.N, a.S, q + 1);
+    uint64_t lo, hi;
+    seg_range(a.N, a.S, q, a.sub_lo, a.sub_len, &lo, &hi);
     const uint64_t len = hi - lo;
     const uint64_t nslots = (len + V - 1) / V;
-    const T* src = static_cast<const T*>(a.send) + (uint64_t)q * a.send_row;
+    const T* src = static_cast<const T*>(a.send) + (uint64_t)q * a.send_row + (lo - (uint64_t)q * a.S);
     T* dst = static_cast<T*>(a.out) + (uint64_t)q * a.out_row + lo;
     const uint64_t stride = (uint64_t)gridDim.x * kBlock * kUnroll;
     for (uint64_t j0 = (uint64_t)blockIdx.x * kBlock * kUnroll + threadIdx.x; j0 < nslots;
@@ -106,15 +113,17 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     using T = typename E::T;
     const int R = a.R;
     const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
-    const uint64_t seg_slots = (a.S + V - 1) / V;
+    const uint64_t seg_slots = (a.sub_len + V - 1) / V;
     const uint64_t tiles_per_seg = (seg_slots + tile_slots - 1) / tile_slots;
     const uint64_t ntiles = tiles_per_seg * (uint64_t)R;
+    const int m = a.m;
     T* out = static_cast<T*>(a.out);
 
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         const int c = (int)(t % (uint64_t)R);
         const uint64_t k = t / (uint64_t)R;
-        const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+        uint64_t lo, hi;
+        seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
         const uint64_t len = hi - lo;
         const uint64_t j0 = k * tile_slots + threadIdx.x;
         if (k * tile_slots * V >= len)
@@ -122,7 +131,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
 
         if constexpr (OP != kOpAllGather) {
             for (int s = 0; s <= R - 2; ++s) {
-                const int q = (c + s + 2) % R;
+                const int q = mod_r(c + (s + 2) * m, R);
                 const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
                 reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, kBlock);
                 step_boundary();
@@ -130,13 +139,14 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
         }
         if constexpr (OP != kOpReduceScatter) {
             if constexpr (OP == kOpAllGather) {
-                const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row;
+                const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
+                               (lo - (uint64_t)c * a.S);
                 copy_slots<E, V>(src, out + (uint64_t)c * a.out_row + lo, len, j0, kBlock);
                 step_boundary();
             }
             for (int s = 0; s <= R - 2; ++s) {
-                const int q = (c + 1 + s) % R;
-                const int p = (c + s) % R;
+                const int q = mod_r(c + (1 + s) * m, R);
+                const int p = mod_r(c + s * m, R);
                 copy_slots<E, V>(out + (uint64_t)p * a.out_row + lo,
                                  out + (uint64_t)q * a.out_row + lo, len, j0, kBlock);
                 step_boundary();

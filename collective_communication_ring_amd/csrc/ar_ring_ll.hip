@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     const int q = blockIdx.x % R;
     const int g = blockIdx.x / R;
     const int G = a.per_rank_wg;
-    const int p = mod_r(q - 1, R);
+    const int m = a.m;
+    const int p = mod_r(q - m, R);
     const int nsteps = (OP == kOpAllReduce) ? 2 * (R - 1) : (OP == kOpReduceScatter) ? R - 1 : R;
     uint32_t* err = &a.ctrl[kCtrlError];
 
@@ -71,17 +72,19 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     constexpr int K = kRingLLEPT;
 
     for (int s = 0; s < nsteps; ++s) {
-        const int c = (OP == kOpAllGather) ? mod_r(q - s, R) : mod_r(q - s - 2, R);
-        const uint64_t lo = seg_lo(a.N, a.S, c), hi = seg_lo(a.N, a.S, c + 1);
+        const int c = (OP == kOpAllGather) ? mod_r(q - s * m, R) : mod_r(q - (s + 2) * m, R);
+        uint64_t lo, hi;
+        seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
         const uint64_t len = hi - lo;
         const uint64_t plen = a.piece_lo < len ? min(a.piece_len, len - a.piece_lo) : 0;
         const uint64_t e0 = lo + a.piece_lo;  // element of offset 0 in a full row
+        const uint64_t in_seg = e0 - (uint64_t)c * a.S;  // its offset within segment c
         uint64_t* mine = a.lines + ((uint64_t)q * R + c) * a.piece_cap;
         const uint64_t* theirs = a.lines + ((uint64_t)p * R + c) * a.piece_cap;
         const bool reduce = (OP != kOpAllGather) && s <= R - 2;
         const bool last_reduce = reduce && s == R - 2;
         // the last receiver of a segment's final does not pass it on
-        const bool forward = !reduce && (mod_r(c - 1, R) != q);
+        const bool forward = !reduce && (mod_r(c - m, R) != q);
         // sub-blocks of kBlock offsets: sub-block j belongs to workgroup j mod G
         // of every rank; a thread takes K of its workgroup's sub-blocks at once
         const uint64_t nsub = (plen + kBlock - 1) / kBlock;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                     } else {
                         if (a.redop == AR_AVG)
                             v = finalize<E, AR_AVG>(v, fr);
-                        const uint64_t at = (OP == kOpReduceScatter) ? a.piece_lo + i[k] : e0 + i[k];
+                        const uint64_t at = (OP == kOpReduceScatter) ? in_seg + i[k] : e0 + i[k];
                         out[(uint64_t)q * a.out_row + at] = E::narrow(v);
                         if (OP == kOpAllReduce && publish)  // the owner starts the copy phase
                             ll_store(mine + i[k], E::to_bits(v), f_copy);
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                 for (int k = 0; k < K; ++k) {
                     if (!ok[k])
                         continue;
-                    const T v = send[(uint64_t)q * a.send_row + a.piece_lo + i[k]];
+                    const T v = send[(uint64_t)q * a.send_row + in_seg + i[k]];
                     out[(uint64_t)q * a.out_row + e0 + i[k]] = v;
                     if (publish)
                         ll_store(mine + i[k], E::t_bits(v), f_copy);

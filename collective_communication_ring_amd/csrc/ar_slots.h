@@ -131,7 +131,7 @@ __device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uin
 {
     using T = typename E::T;
     using A = typename E::A;
-    const int p = mod_r(q - 1, a.R);
+    const int p = mod_r(q - a.m, a.R);
     ReducePtrs<E> r;
     const T* send = static_cast<const T*>(a.send);
     A* part = static_cast<A*>(a.part);
@@ -141,8 +141,8 @@ __device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uin
     r.own = send + (uint64_t)q * a.send_row + lo;
     r.dstA = part + (uint64_t)q * a.N + lo;
     // the final value (q == c): all-reduce writes it in place in the full
-    // row; reduce-scatter writes it at the start of rank c's shard row
-    r.dstT = out + (uint64_t)q * a.out_row + (a.op == kOpReduceScatter ? 0 : lo);
+    // row; reduce-scatter at the same offset within rank c's shard row
+    r.dstT = out + (uint64_t)q * a.out_row + (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
     return r;
 }
 

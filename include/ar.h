@@ -117,7 +117,12 @@ typedef enum {
     AR_OPT_DEBUG_MUTE_RANK = 8, /* testing the watchdog only: this logical rank's workgroups
                                    skip publishing (LL lines, ready flags), so its consumers'
                                    bounded waits expire; -1 (default) = none */
-    AR_OPT_REDOP = 9            /* an ar_redop_t for ar_allreduce / ar_reduce_scatter */
+    AR_OPT_REDOP = 9,           /* an ar_redop_t for ar_allreduce / ar_reduce_scatter */
+    AR_OPT_CHANNELS = 10        /* ring channels K (default 1): every segment is cut into K
+                                   sub-ranges of Sk = ceil(ceil(S/K)/8)*8 elements, and
+                                   channel k runs its own ring q -> q + m_k over sub-range k
+                                   (strides from ar_ring_channel_stride); the multi-rail /
+                                   channels idea ("GPU MODE lecture 68 notes", section 06) */
 } ar_option_t;
 
 /* Create a communicator for R logical ranks (2 <= R <= 64) and up to
@@ -193,6 +198,12 @@ int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
  *   root; returns -2 for invalid arguments. */
 int ar_ring_segment(ar_comm_t comm, size_t count, int c, size_t* lo, size_t* hi);
 int ar_tree_parent(ar_comm_t comm, int tree, int r);
+
+/* Ring stride of channel k: the integers in [1, R) coprime with R, ordered
+ * 1, R-1, 3, R-3, 5, ... (a stride and its complement are the two directions
+ * of one cycle, so the rings are edge-disjoint); -1 past the last one.  The
+ * number of strides bounds AR_OPT_CHANNELS. */
+int ar_ring_channel_stride(ar_comm_t comm, int k);
 
 /* Measurement utilities (not collectives).  Plain streaming kernels that set
  * the practical HBM ceiling the reduce-copy is compared with, and calibrate

@@ -135,3 +135,42 @@ def test_utilities_reject_bad_arguments(api):
     assert L.ar_stream_copy(16, 32, 15, None) == api.AR_ERR_INVALID_ARG  # not a multiple of 16
     assert L.ar_ll_pingpong(None, None, 10, 1, 1000, None) == api.AR_ERR_INVALID_ARG
     assert L.ar_ll_pingpong(256, 512, 0, 1, 1000, None) == api.AR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("R", [2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 30, 64])
+def test_channel_strides(api, R):
+    """Channel strides: every integer in [1, R) coprime with R, each once,
+    ordered 1, R-1, 3, R-3, ... with duplicates dropped; each stride walks a
+    Hamiltonian ring (q -> q + m visits every rank), and a stride and its
+    complement traverse the same undirected ring in opposite directions."""
+    import math
+    c = api.ar_init(R, 1024, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE)
+    try:
+        got = []
+        k = 0
+        while True:
+            m = api.ar_ring_channel_stride(c, k)
+            if m < 0:
+                break
+            got.append(m)
+            k += 1
+        assert sorted(got) == [m for m in range(1, R) if math.gcd(m, R) == 1]
+        assert got[0] == 1
+        if R > 2:
+            assert got[1] == R - 1
+        for m in got:
+            seen, q = set(), 0
+            for _ in range(R):
+                seen.add(q)
+                q = (q + m) % R
+            assert seen == set(range(R)) and q == 0
+        # the option accepts 1 .. len(strides) and nothing else
+        for K in range(1, len(got) + 1):
+            api.ar_set_option(c, api.AR_OPT_CHANNELS, K)
+            assert api.ar_get_option(c, api.AR_OPT_CHANNELS) == K
+        for bad in (0, len(got) + 1, -3):
+            with pytest.raises(api.ArError):
+                api.ar_set_option(c, api.AR_OPT_CHANNELS, bad)
+        assert api.ar_ring_channel_stride(c, -1) == -1
+    finally:
+        api.ar_destroy(c)

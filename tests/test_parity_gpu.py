@@ -537,6 +537,76 @@ def test_ring_ll_multiple_pieces(env, dtype, R):
         assert y.tobytes() == ref.tobytes()
 
 
+# ---------------------------------------------------------------- channels
+
+def _strides(api, R, K):
+    c = api.ar_init(R, 64, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE)
+    try:
+        return [api.ar_ring_channel_stride(c, k) for k in range(K)]
+    finally:
+        api.ar_destroy(c)
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R,K", [(2, 1), (5, 2), (5, 4), (8, 2), (8, 4), (16, 3), (16, 8)])
+def test_multi_channel_rings(env, launch, dtype, R, K):
+    """K channels: channel k reduces sub-range k of every segment around its
+    own ring q -> q + m_k; the fold order is the one the oracle replays with
+    the same strides."""
+    api, orc = env["api"], env["orc"]
+    strides = _strides(api, R, K)
+    for N in (1, 13, 1000, 4097, 16 * 4096 + 40):
+        x = rand_input(env, dtype, R, N, seed=3 * R + K + N)
+        (y,) = run_allreduce(env, x, dtype, launch=launch, channels=K)
+        assert y.tobytes() == orc.ring_allreduce(x, dtype, strides=strides).tobytes(), (R, K, N)
+        check_tolerance(env, y, x, dtype)
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("dtype", ["float32", "bf16"])
+def test_multi_channel_reduce_scatter_all_gather_operators(env, launch, dtype):
+    api, orc = env["api"], env["orc"]
+    R, K = 8, 4
+    strides = _strides(api, R, K)
+    for n in (3, 1000, 8192 + 8):
+        N = n * R
+        x = rand_input(env, dtype, R, N, seed=n + 401)
+        for op in ("sum", "max", "avg"):
+            comm = api.Comm(R, N, dtype, device=env["dev"], channels=K, redop=op,
+                            **ring_opts(launch))
+            assert comm.channel_strides() == strides
+            send = to_dev(env, x, dtype)
+            shard = poisoned(env, (R, n), dtype)
+            comm.reduce_scatter(send, shard)
+            rs = from_dev(env, shard, dtype)
+            assert rs.tobytes() == orc.ring_reduce_scatter(x, dtype, op=op,
+                                                           strides=strides).tobytes(), (n, op)
+            full = poisoned(env, (R, N), dtype)
+            comm.all_gather(shard, full)
+            assert from_dev(env, full, dtype).tobytes() == \
+                orc.ring_all_gather(rs, dtype, strides=strides).tobytes(), (n, op)
+            ar = poisoned(env, (R, N), dtype)
+            comm.allreduce(send, ar)
+            assert from_dev(env, ar, dtype).tobytes() == \
+                orc.ring_allreduce(x, dtype, op=op, strides=strides).tobytes(), (n, op)
+            assert comm.check() == api.AR_SUCCESS
+
+
+def test_multi_channel_full_size_order_differs_from_one_channel(env):
+    """At 64 MiB per rank, 8 ranks, float32: four channels match the oracle
+    with four strides bit for bit, and (the fold order being different) not
+    the single-ring result everywhere."""
+    api, orc = env["api"], env["orc"]
+    x = env["inputs"].host_inputs("ring_f32_r8_64MiB")
+    strides = _strides(api, 8, 4)
+    (y4,) = run_allreduce(env, x, "float32", launch="fused", channels=4)
+    assert y4.tobytes() == orc.ring_allreduce(x, strides=strides).tobytes()
+    (y1,) = run_allreduce(env, x, "float32", launch="fused")
+    assert y1.tobytes() != y4.tobytes()
+    check_tolerance(env, y4, x, "float32")
+
+
 @pytest.mark.parametrize("launch", ["fused", "step"])
 def test_concurrent_with_compute_on_another_stream(env, launch):
     """A ring all-reduce on a second stream while GEMMs run on the first
