@@ -578,11 +578,13 @@ def mode_tune(args):
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
     import oracle
-    ref = oracle.ring_allreduce(x)
+    ref = None
     res = []
     for grid in [int(g) for g in args.grids.split(",")]:
         comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=args.chunk_bytes, grid=grid,
                         **ring_kw(args.launch, args.channels))
+        if ref is None:
+            ref = oracle.ring_allreduce(x, strides=comm.channel_strides())
         _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                     torch)
         ms = total_ms / args.steps

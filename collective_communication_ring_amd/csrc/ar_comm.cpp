@@ -513,12 +513,13 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
         }
     }
     c->channels = std::min<int64_t>(std::max<int64_t>(1, env_int("AR_CHANNELS", 1)), c->nstrides);
-    // workspace: control block | partial sums [R][cap] (A) | tree LL up | down
+    // workspace: control block | hand-off accumulators [cap] (A) | tree LL up
+    // | down | pipelined flags | ring-LL lines
     const size_t cap1 = count ? count : 1;
     c->tree_lines = std::min<uint64_t>((cap1 + 1) / 2, kTreeLinesCap);
     size_t off = kAlign;  // control block
     c->off_part = off;
-    off = align_up(off + (size_t)R * cap1 * 4, kAlign);
+    off = align_up(off + cap1 * 4, kAlign);
     c->off_up = off;
     off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
     c->off_down = off;
@@ -576,9 +577,10 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
     if (count > c->cap)
         return AR_ERR_INVALID_ARG;
     const size_t bytes = (size_t)c->R * count * elem_size(c->dtype);
-    // in place (send == recv) is allowed: every schedule reads an element of
-    // a rank's input before that rank's row is written at the same position
-    // (same thread, or ordered by the step hand-off); partial overlap is not
+    // in place (send == recv) is allowed: the hand-off goes through the
+    // workspace row, and every schedule reads an element of a rank's input
+    // before that rank's row is written at the same position (same thread,
+    // or ordered by the step hand-off); partial overlap is not
     if (send != recv && overlaps(send, bytes, recv, bytes))
         return AR_ERR_INVALID_USAGE;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -590,8 +592,17 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
         return run_tree(c, send, recv, count, st);
     RingArgs a{};
     a.send = send;
-    // partial sums live in recv when the accumulator is the element type
-    a.part = (c->dtype == AR_BF16) ? (void*)(c->ws + c->off_part) : recv;
+    // A segment's running value lives in its owner's output row when the
+    // accumulator is the element type (the final value lands in the same
+    // place, so no extra row is written), else in the workspace row.  In
+    // place, the owner's row still holds its input, read at the last hop.
+    if (c->dtype != AR_BF16 && send != recv) {
+        a.part = recv;
+        a.part_seg = count;
+    } else {
+        a.part = c->ws + c->off_part;
+        a.part_seg = 0;
+    }
     a.out = recv;
     a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
     a.N = count;
@@ -624,7 +635,10 @@ int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcoun
         return AR_SUCCESS;
     RingArgs a{};
     a.send = send;
-    a.part = c->ws + c->off_part;
+    // segment c's running value in rank c's shard row (element e at
+    // recv[e], as the shards are contiguous) when A == T, else the workspace
+    a.part = (c->dtype != AR_BF16) ? recv : (void*)(c->ws + c->off_part);
+    a.part_seg = 0;
     a.out = recv;
     a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
     a.N = N;

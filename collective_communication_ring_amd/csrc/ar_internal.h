@@ -42,12 +42,16 @@ struct TreeTable {
 
 // Arguments of one ring collective, shared by every ring launch mode.
 //   send : [R][send_row] elements of T
-//   part : [R][N] accumulators (A); equals recv when A == T for all-reduce
+//   part : the hand-off accumulators (A): the running value of element e of
+//          segment c sits at part[c * part_seg + e] whichever rank holds it,
+//          so each hop overwrites the slot the previous hop wrote
 //   out  : [R][out_row] elements of T
 // Segment c of the N-element vector is [min(c*S, N), min((c+1)*S, N)).
 struct RingArgs {
     const void* send;
     void* part;
+    uint64_t part_seg; // 0: one workspace row of N accumulators; out_row: the
+                       //   owner's output row (A == T, the final lands there)
     void* out;
     uint32_t* ctrl;   // control block
     uint64_t* flags;  // pipelined ring: one ready flag per (segment, chunk)

@@ -343,8 +343,10 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
                 const bool first = (s == 0), last = (s == R - 2);
                 const rsrc_t own = make_rsrc(send + (uint64_t)q * a.send_row + e0, ulen * sizeof(T));
                 const rsrc_t prevT = make_rsrc(send + (uint64_t)p * a.send_row + e0, ulen * sizeof(T));
-                const rsrc_t prevA = make_rsrc(part + (uint64_t)p * a.N + e0, ulen * 4);
-                const rsrc_t dstA = make_rsrc(part + (uint64_t)q * a.N + e0, ulen * 4);
+                // the hand-off slot: rank p wrote it, rank q overwrites it
+                const rsrc_t accA = make_rsrc(part + (uint64_t)c * a.part_seg + e0, ulen * 4);
+                const rsrc_t& prevA = accA;
+                const rsrc_t& dstA = accA;
                 T* dT = out + (uint64_t)q * a.out_row +
                         (OP == kOpReduceScatter ? e0 - (uint64_t)c * a.S : e0);
                 const rsrc_t dstT = make_rsrc(dT, ulen * sizeof(T));

@@ -19,9 +19,13 @@
 // rank-major arrays, and "receiving from q-1" is reading row q-1 in place
 // (the symmetric-heap idea of a remote address being a base plus the local
 // offset: "Demystifying NVSHMEM ..." summary, paragraph on the symmetric
-// heap).  Every step is a reduce-copy of two 16-byte vector loads and one
-// 16-byte store per slot (a copy step: one load, one store); there is no
-// MFMA because nothing here is a contraction.
+// heap).  A reduce step hands its running value to the next rank through one
+// accumulator slot per element: rank q-1 stores it, rank q loads it, adds
+// x_q and stores over it.  The slot is the owner's output row when the
+// accumulator type is the element type (the final value then needs no extra
+// row), else a workspace row.  Every step is a reduce-copy of two 16-byte
+// vector loads and one 16-byte store per slot (a copy step: one load, one
+// store); there is no MFMA because nothing here is a contraction.
 //
 // Two launch forms live in this file:
 //   step  -- one launch per step over all R ranks; the kernel boundary
@@ -31,10 +35,10 @@
 //            element positions at every step, so the value it stored for rank
 //            q is the one it loads back as rank q+1's input (same-thread
 //            program order; the compiler is kept from forwarding it in
-//            registers, so every step really reads rank q's row).  Tiles of a
-//            step are independent, so there are no flags and no fences; the
-//            partial a step writes is still hot in this XCD's L2 when the
-//            next step reads it.
+//            registers, so every step really reads the hand-off slot).  Tiles
+//            of a step are independent, so there are no flags and no fences;
+//            the slot a step writes is still hot in this XCD's L2 when the
+//            next step reads and overwrites it.
 #include "ar_elem.h"
 #include "ar_internal.h"
 #include "ar_slots.h"
@@ -106,6 +110,145 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 
 // ---- fused: a tile runs every step ------------------------------------------
 
+// One reduce step of a whole tile (kUnroll full slots per thread) in the fused
+// form.  x holds the received value: on entry at step 0 (the predecessor's
+// input, loaded by the caller), else loaded here from the hand-off slot after
+// the previous step's store (LOADX).  With PREFETCH the input of the next
+// step's rank is loaded into `nxt` before this step's add, so its HBM latency
+// overlaps this step instead of lengthening the chain; `own` was loaded the
+// same way one step earlier.  LAST: the owner's step, written as T.
+template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
+__device__ inline void fused_step(typename E::A (&x)[kUnroll][V],
+                                  const typename E::A (&own)[kUnroll][V],
+                                  typename E::A (&nxt)[kUnroll][V], typename E::A* acc,
+                                  typename E::T* fin, const typename E::T* next_row,
+                                  uint64_t j0, float R)
+{
+    if constexpr (LOADX) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            load_a<E, V>(acc + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+    }
+    if constexpr (PREFETCH) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            load_t<E, V>(next_row + (j0 + (uint64_t)u * kBlock) * V, nxt[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            x[u][i] = combine<E, RED>(x[u][i], own[u][i]);
+            if constexpr (LAST)
+                x[u][i] = finalize<E, RED>(x[u][i], R);
+        }
+        if constexpr (LAST)
+            store_t<E, V>(fin + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+        else
+            store_a<E, V>(acc + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+    }
+    step_boundary();
+}
+
+// The two inputs step 0 of a whole tile of segment c needs: x_{c+m} (the
+// value it receives) into x and x_{c+2m} (its own) into b0.  (Loading them
+// for the next tile before this tile's copy steps measured slower: it adds
+// to the L2 footprint of the copy chain.)
+template <class E, int V>
+__device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
+                                        typename E::A (&x)[kUnroll][V],
+                                        typename E::A (&b0)[kUnroll][V])
+{
+    using T = typename E::T;
+    const T* send = static_cast<const T*>(a.send) + lo;
+    const T* first = send + (uint64_t)mod_r(c + a.m, a.R) * a.send_row;
+    const T* r0 = send + (uint64_t)mod_r(c + 2 * a.m, a.R) * a.send_row;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        load_t<E, V>(first + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+        load_t<E, V>(r0 + (j0 + (uint64_t)u * kBlock) * V, b0[u]);
+    }
+}
+
+// The R-1 reduce steps of a whole tile of segment c, with step 0's inputs
+// already in x and b0 (fused_load_first).  Step s is rank c + (s+2)m; the
+// prefetched input alternates between two register sets, so no step waits
+// for the next step's load.
+template <class E, int V, int RED>
+__device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
+                                          typename E::A (&x)[kUnroll][V],
+                                          typename E::A (&b0)[kUnroll][V])
+{
+    using T = typename E::T;
+    using A = typename E::A;
+    const int R = a.R;
+    const int m = a.m;
+    const float fr = (float)R;
+    const T* send = static_cast<const T*>(a.send) + lo;
+    A* acc = static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + lo;
+    T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
+             (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
+    auto row = [&](int s) { return send + (uint64_t)mod_r(c + (s + 2) * m, R) * a.send_row; };
+    A b1[kUnroll][V];
+    if (R == 2) {
+        fused_step<E, V, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, j0, fr);
+        return;
+    }
+    // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
+    fused_step<E, V, RED, false, true, false>(x, b0, b1, acc, fin, row(1), j0, fr);
+    int s = 1;  // the next step; its input is in b1
+    for (; s + 1 <= R - 3; s += 2) {
+        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, fr);
+        fused_step<E, V, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 2), j0, fr);
+    }
+    if (s == R - 3) {
+        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, fr);
+        fused_step<E, V, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, j0, fr);
+    } else {
+        fused_step<E, V, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, j0, fr);
+    }
+}
+
+template <class E, int V>
+__device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
+                                             typename E::A (&x)[kUnroll][V],
+                                             typename E::A (&b0)[kUnroll][V])
+{
+    switch (a.redop) {
+    case AR_MAX:
+        fused_reduce_whole<E, V, AR_MAX>(a, c, lo, j0, x, b0);
+        break;
+    case AR_MIN:
+        fused_reduce_whole<E, V, AR_MIN>(a, c, lo, j0, x, b0);
+        break;
+    case AR_AVG:
+        fused_reduce_whole<E, V, AR_AVG>(a, c, lo, j0, x, b0);
+        break;
+    default:
+        fused_reduce_whole<E, V, AR_SUM>(a, c, lo, j0, x, b0);
+        break;
+    }
+}
+
+// Tile t of a fused launch: segment c, its range [lo, lo + len) of a full
+// row, and this thread's first slot j0.  False for an empty tile of a short
+// trailing segment (uniform per workgroup).  *whole: every slot of this
+// thread is full (the prefetching path applies).
+template <int V>
+__device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_t* lo,
+                                  uint64_t* len, uint64_t* j0, bool* whole)
+{
+    const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
+    *c = (int)(t % (uint64_t)a.R);
+    const uint64_t k = t / (uint64_t)a.R;
+    uint64_t hi;
+    seg_range(a.N, a.S, *c, a.sub_lo, a.sub_len, lo, &hi);
+    *len = hi - *lo;
+    *j0 = k * tile_slots + threadIdx.x;
+    *whole = V > 1 && (*j0 + (kUnroll - 1) * kBlock + 1) * V <= *len;
+    return k * tile_slots * V < *len;
+}
+
 template <int DT, int V, int OP>
 __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
 {
@@ -119,22 +262,27 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     const int m = a.m;
     T* out = static_cast<T*>(a.out);
 
+    using A = typename E::A;
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int c = (int)(t % (uint64_t)R);
-        const uint64_t k = t / (uint64_t)R;
-        uint64_t lo, hi;
-        seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
-        const uint64_t len = hi - lo;
-        const uint64_t j0 = k * tile_slots + threadIdx.x;
-        if (k * tile_slots * V >= len)
+        int c;
+        uint64_t lo, len, j0;
+        bool whole;
+        if (!fused_tile<V>(a, t, &c, &lo, &len, &j0, &whole))
             continue;  // empty tile of a short trailing segment (uniform per workgroup)
 
         if constexpr (OP != kOpAllGather) {
-            for (int s = 0; s <= R - 2; ++s) {
-                const int q = mod_r(c + (s + 2) * m, R);
-                const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
-                reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, kBlock);
-                step_boundary();
+            if (whole) {
+                A x[kUnroll][V], b0[kUnroll][V];
+                fused_load_first<E, V>(a, c, lo, j0, x, b0);
+                fused_reduce_whole_op<E, V>(a, c, lo, j0, x, b0);
+            } else {
+                // the end of a segment, or the scalar path: step by step
+                for (int s = 0; s <= R - 2; ++s) {
+                    const int q = mod_r(c + (s + 2) * m, R);
+                    const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
+                    reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, kBlock);
+                    step_boundary();
+                }
             }
         }
         if constexpr (OP != kOpReduceScatter) {

@@ -11,12 +11,13 @@ namespace ar {
 // len.  FIRST: the received value comes from the predecessor's input (T);
 // else from its accumulator row (A).  LAST: the result is final and is
 // narrowed to T; else it is this rank's accumulator.
+// prevA and dstA are the same slots (a hop overwrites the running value in
+// place), and dstT may be too: every slot is read before it is written, by the
+// same thread, so no pointer here is restrict.
 template <class E, int V, bool FIRST, bool LAST, int RED>
-__device__ inline void reduce_slots(const typename E::T* __restrict__ prevT,
-                                    const typename E::A* __restrict__ prevA,
-                                    const typename E::T* __restrict__ own,
-                                    typename E::A* __restrict__ dstA,
-                                    typename E::T* __restrict__ dstT, uint64_t len, uint64_t j0,
+__device__ inline void reduce_slots(const typename E::T* prevT, const typename E::A* prevA,
+                                    const typename E::T* own, typename E::A* dstA,
+                                    typename E::T* dstT, uint64_t len, uint64_t j0,
                                     uint64_t jstep, float R)
 {
     using A = typename E::A;
@@ -116,7 +117,7 @@ __device__ inline void copy_slots(const typename E::T* __restrict__ src,
     }
 }
 
-// Row pointers of reduce step s for rank q, segment c = (q-s-2) mod R.
+// Row pointers of reduce step s for rank q, segment c = (q-(s+2)m) mod R.
 template <class E>
 struct ReducePtrs {
     const typename E::T* prevT;
@@ -137,9 +138,9 @@ __device__ inline ReducePtrs<E> reduce_ptrs(const RingArgs& a, int q, int c, uin
     A* part = static_cast<A*>(a.part);
     T* out = static_cast<T*>(a.out);
     r.prevT = send + (uint64_t)p * a.send_row + lo;
-    r.prevA = part + (uint64_t)p * a.N + lo;
+    r.prevA = part + (uint64_t)c * a.part_seg + lo;  // the hand-off from rank p ...
     r.own = send + (uint64_t)q * a.send_row + lo;
-    r.dstA = part + (uint64_t)q * a.N + lo;
+    r.dstA = part + (uint64_t)c * a.part_seg + lo;   // ... and to rank q + m: one slot
     // the final value (q == c): all-reduce writes it in place in the full
     // row; reduce-scatter at the same offset within rank c's shard row
     r.dstT = out + (uint64_t)q * a.out_row + (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);

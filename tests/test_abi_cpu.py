@@ -53,7 +53,7 @@ def test_init_argument_checks(api):
     assert L.ar_init(None, 4, 16, api.AR_FLOAT32, api.AR_RING, api.AR_SIMPLE) == api.AR_ERR_INVALID_ARG
     c = api.ar_init(8, 1024, api.AR_FLOAT32)
     try:
-        assert api.ar_workspace_bytes(c) >= 256 + 8 * 1024 * 4
+        assert api.ar_workspace_bytes(c) >= 256 + 1024 * 4  # one accumulator row
         # no workspace yet: a collective is refused before touching the device
         assert L.ar_allreduce(c, 16, 4096, 8, None) == api.AR_ERR_INVALID_USAGE
         assert L.ar_set_workspace(c, None, 1 << 20, None) == api.AR_ERR_INVALID_ARG
