@@ -348,12 +348,17 @@ def mode_tree_vs_ring(args):
         assert c.check() == api.AR_SUCCESS
     hop = ll_hop_latency_us(torch)
     log("LL one-way hop latency: %s" % hop)
+    # the launch floor: one single-workgroup kernel (a 16-byte copy) per call
+    st = lambda: torch.cuda.current_stream().cuda_stream
+    launch_floor = time_graph(lambda: api.ar_stream_copy(send_flat.data_ptr(), recv_flat.data_ptr(),
+                                                         16, st()), 20, torch) * 1e3
+    log("launch floor (16-byte copy kernel, graph-replayed): %.2f us" % launch_floor)
     # latency roofline of the tree: 2 * depth hops (up, then down) per call
     import oracle
     depth = 3 if R == 8 else None
     t_or, n_or = oracle_time_s(lambda: oracle.tree_allreduce(x), 3.0)
     summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res,
-                   ll_hop_us=hop, tree_depth=depth,
+                   ll_hop_us=hop, tree_depth=depth, launch_floor_us=launch_floor,
                    tree_hop_bound_us=2 * depth * hop["xcd_apart"] if depth else None,
                    cpu_baseline=dict(kind="oracle", cores=1, value_us=t_or * 1e6,
                                      sample="tree all-reduce, %d B/rank, %d calls"
