@@ -114,26 +114,32 @@ __device__ inline u32x4 load16(const void* p)
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// The V accumulator values of a 16-byte slot of T held as raw bits.
 template <class E, int V>
-__device__ inline void load_t(const typename E::T* p, typename E::A (&o)[V])
+__device__ inline void widen_slot(const u32x4& r, typename E::A (&o)[V])
 {
-    if constexpr (V == 1) {
-        o[0] = E::widen(p[0]);
-    } else if constexpr (sizeof(typename E::T) == 4) {
+    if constexpr (sizeof(typename E::T) == 4) {
         static_assert(V == 4, "16-byte slot of 32-bit elements");
-        u32x4 r = load16(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[i] = E::from_bits(r[i]);
     } else {
         static_assert(V == 8, "16-byte slot of 16-bit elements");
-        u32x4 r = load16(p);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             o[2 * i] = E::widen((typename E::T)(r[i] & 0xffffu));
             o[2 * i + 1] = E::widen((typename E::T)(r[i] >> 16));
         }
     }
+}
+
+template <class E, int V>
+__device__ inline void load_t(const typename E::T* p, typename E::A (&o)[V])
+{
+    if constexpr (V == 1)
+        o[0] = E::widen(p[0]);
+    else
+        widen_slot<E, V>(load16(p), o);
 }
 
 template <class E, int V>

@@ -116,14 +116,15 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 // the previous step's store (LOADX).  With PREFETCH the input of the next
 // step's rank is loaded into `nxt` before this step's add, so its HBM latency
 // overlaps this step instead of lengthening the chain; `own` was loaded the
-// same way one step earlier.  LAST: the owner's step, written as T.
+// same way one step earlier.  Prefetched inputs stay raw 16-byte vectors
+// until used (half the registers for bfloat16).  LAST: the owner's step,
+// written as T.
 template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
-__device__ inline void fused_step(typename E::A (&x)[kUnroll][V],
-                                  const typename E::A (&own)[kUnroll][V],
-                                  typename E::A (&nxt)[kUnroll][V], typename E::A* acc,
-                                  typename E::T* fin, const typename E::T* next_row,
-                                  uint64_t j0, float R)
+__device__ inline void fused_step(typename E::A (&x)[kUnroll][V], const u32x4 (&own)[kUnroll],
+                                  u32x4 (&nxt)[kUnroll], typename E::A* acc, typename E::T* fin,
+                                  const typename E::T* next_row, uint64_t j0, float R)
 {
+    using A = typename E::A;
     if constexpr (LOADX) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -132,13 +133,15 @@ __device__ inline void fused_step(typename E::A (&x)[kUnroll][V],
     if constexpr (PREFETCH) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            load_t<E, V>(next_row + (j0 + (uint64_t)u * kBlock) * V, nxt[u]);
+            nxt[u] = load16(next_row + (j0 + (uint64_t)u * kBlock) * V);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+        A y[V];
+        widen_slot<E, V>(own[u], y);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            x[u][i] = combine<E, RED>(x[u][i], own[u][i]);
+            x[u][i] = combine<E, RED>(x[u][i], y[i]);
             if constexpr (LAST)
                 x[u][i] = finalize<E, RED>(x[u][i], R);
         }
@@ -151,13 +154,12 @@ __device__ inline void fused_step(typename E::A (&x)[kUnroll][V],
 }
 
 // The two inputs step 0 of a whole tile of segment c needs: x_{c+m} (the
-// value it receives) into x and x_{c+2m} (its own) into b0.  (Loading them
-// for the next tile before this tile's copy steps measured slower: it adds
-// to the L2 footprint of the copy chain.)
+// value it receives) into x and x_{c+2m} (its own, raw) into b0.  (Loading
+// them for the next tile before this tile's copy steps measured slower: it
+// adds to the L2 footprint of the copy chain.)
 template <class E, int V>
 __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                        typename E::A (&x)[kUnroll][V],
-                                        typename E::A (&b0)[kUnroll][V])
+                                        typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
 {
     using T = typename E::T;
     const T* send = static_cast<const T*>(a.send) + lo;
@@ -166,7 +168,7 @@ __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, u
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         load_t<E, V>(first + (j0 + (uint64_t)u * kBlock) * V, x[u]);
-        load_t<E, V>(r0 + (j0 + (uint64_t)u * kBlock) * V, b0[u]);
+        b0[u] = load16(r0 + (j0 + (uint64_t)u * kBlock) * V);
     }
 }
 
@@ -176,8 +178,7 @@ __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, u
 // for the next step's load.
 template <class E, int V, int RED>
 __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                          typename E::A (&x)[kUnroll][V],
-                                          typename E::A (&b0)[kUnroll][V])
+                                          typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
 {
     using T = typename E::T;
     using A = typename E::A;
@@ -189,7 +190,7 @@ __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo,
     T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
              (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
     auto row = [&](int s) { return send + (uint64_t)mod_r(c + (s + 2) * m, R) * a.send_row; };
-    A b1[kUnroll][V];
+    u32x4 b1[kUnroll];
     if (R == 2) {
         fused_step<E, V, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, j0, fr);
         return;
@@ -211,8 +212,7 @@ __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo,
 
 template <class E, int V>
 __device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                             typename E::A (&x)[kUnroll][V],
-                                             typename E::A (&b0)[kUnroll][V])
+                                             typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
 {
     switch (a.redop) {
     case AR_MAX:
@@ -277,11 +277,17 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
             continue;  // empty tile of a short trailing segment (uniform per workgroup)
 
         if constexpr (OP != kOpAllGather) {
-            if (whole) {
-                A x[kUnroll][V], b0[kUnroll][V];
-                fused_load_first<E, V>(a, c, lo, j0, x, b0);
-                fused_reduce_whole_op<E, V>(a, c, lo, j0, x, b0);
-            } else {
+            bool done = false;
+            if constexpr (V > 1) {
+                if (whole) {
+                    A x[kUnroll][V];
+                    u32x4 b0[kUnroll];
+                    fused_load_first<E, V>(a, c, lo, j0, x, b0);
+                    fused_reduce_whole_op<E, V>(a, c, lo, j0, x, b0);
+                    done = true;
+                }
+            }
+            if (!done) {
                 // the end of a segment, or the scalar path: step by step
                 for (int s = 0; s <= R - 2; ++s) {
                     const int q = mod_r(c + (s + 2) * m, R);
