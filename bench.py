@@ -9,10 +9,13 @@ whole [8, 16M] buffer, inputs resident in HBM before the timed region.
   value  = busBW = algBW * 2(R-1)/R,  algBW = per-rank bytes / time
   roofline.achieved = algorithmic HBM bytes 5(R-1) N s / kernel time
 
-Other modes (--mode): sweep (8 B .. 1 GiB per rank, alpha-beta fit),
-tree-vs-ring (8 B .. 256 KiB), buckets (R = 16 bf16 reduce-scatter then
-all-gather, 40 x 25 MiB), stream (c = a + b and copy reference kernels).
-They write JSON lines to --out and a summary line to stdout.
+Other modes (--mode): config1 (R = 4 int32, 4096 per rank, every form),
+sweep (8 B .. 1 GiB per rank, alpha-beta fit), tree-vs-ring (8 B .. 256 KiB),
+buckets (R = 16 bf16 reduce-scatter then all-gather, 40 x 25 MiB), stream
+(c = a + b and copy reference kernels), counters (a short program for
+rocprofv3 --pmc runs), tune (grid sizes), overlap (buckets beside GEMMs on
+another stream).  They write a summary line to stdout (and JSON lines to
+--out where a mode has several points).
 """
 import argparse
 import hashlib
@@ -572,6 +575,40 @@ def mode_counters(args):
     return 0
 
 
+def mode_config1(args):
+    """Config 1: ring all-reduce (sum), R = 4, int32, 4096 elements per rank,
+    chunk = count / R; time per call (graph-replayed) in every form, each
+    result checked bit for bit against the oracle and the int64 sum."""
+    import numpy as np
+    import torch
+    from collective_communication_ring_amd import api, inputs
+    import oracle
+    R, N = 4, 4096
+    dev = torch.device("cuda:0")
+    x = inputs.host_inputs("ring_int32_r4")
+    ref = oracle.ring_allreduce(x)
+    exact = x.astype(np.int64).sum(axis=0).astype(np.int32)
+    send = torch.from_numpy(x).to(dev)
+    recv = torch.empty_like(send)
+    res = {}
+    for name, kw in (("fused", ring_kw("fused")), ("step", ring_kw("step")),
+                     ("pipelined", ring_kw("pipelined")), ("ll", ring_kw("ll")),
+                     ("tree-ll", dict(algo="tree", proto="ll"))):
+        comm = api.Comm(R, N, "int32", device=dev, chunk_bytes=(N // R) * 4, **kw)
+        t_us = time_graph(lambda: comm.allreduce(send, recv), 20, torch) * 1e3
+        got = recv.cpu().numpy()
+        ok = comm.check() == api.AR_SUCCESS and (got == exact[None, :]).all() and (
+            name == "tree-ll" or got.tobytes() == ref.tobytes())
+        res[name] = dict(t_us=round(t_us, 3), exact=bool(ok))
+        log("config 1 %-10s %8.2f us  exact=%s" % (name, t_us, ok))
+        comm.close()
+    t_or, n_or = oracle_time_s(lambda: oracle.ring_allreduce(x), 2.0)
+    print(json.dumps(dict(mode="config1", R=R, count_per_rank=N, dtype="int32", results=res,
+                          cpu_baseline=dict(kind="oracle", cores=1, t_us=t_or * 1e6,
+                                            sample="%d calls" % n_or))), flush=True)
+    return 0 if all(r["exact"] for r in res.values()) else 1
+
+
 def mode_tune(args):
     """Time the R = 8 fp32 64 MiB/rank all-reduce for a list of grid sizes
     (workgroups per launch) in one launch form."""
@@ -610,8 +647,8 @@ def main():
                     help="ring launch form; 'll' = the ring with the LL protocol")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
-                    choices=["headline", "sweep", "tree-vs-ring", "buckets", "stream",
-                             "counters", "tune", "overlap"])
+                    choices=["headline", "config1", "sweep", "tree-vs-ring", "buckets",
+                             "stream", "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
@@ -633,7 +670,7 @@ def main():
               "MI355X's HBM, so --gpus must be 1 (got --gpus %d, WORLD_SIZE %d)."
               % (args.gpus, world), file=sys.stderr)
         return 2
-    fn = {"headline": headline, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
+    fn = {"headline": headline, "config1": mode_config1, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
           "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
           "tune": mode_tune, "overlap": mode_overlap}[args.mode]
     return fn(args)
