@@ -396,12 +396,16 @@ __global__ __launch_bounds__(kBlock) void k_ring_pipelined(RingArgs a)
         if (s_fail)
             __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlPipeDone], 1u, __ATOMIC_ACQ_REL,
+        // Only the next launch on the stream reads the counter and the flag base, and
+        // the kernel boundary orders this launch's memory before it, so relaxed
+        // atomics suffice (acquire-release here would write back and invalidate
+        // the XCD's L2 in every workgroup).
+        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlPipeDone], 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(&a.ctrl[kCtrlPipeDone], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(basep, base + (uint64_t)nsteps, __ATOMIC_RELEASE,
+            __hip_atomic_store(basep, base + (uint64_t)nsteps, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }

@@ -179,12 +179,16 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                               __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlRingLLDone], 1u, __ATOMIC_ACQ_REL,
+        // Only the next launch on the stream reads the counter and the epoch, and
+        // the kernel boundary orders this launch's memory before it, so relaxed
+        // atomics suffice (acquire-release here would write back and invalidate
+        // the XCD's L2 in every workgroup).
+        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlRingLLDone], 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(&a.ctrl[kCtrlRingLLDone], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[kCtrlRingLLEpoch], epoch, __ATOMIC_RELEASE,
+            __hip_atomic_store(&a.ctrl[kCtrlRingLLEpoch], epoch, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }

@@ -171,12 +171,16 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     // the last workgroup to finish publishes the epoch for the next launch
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlTreeDone], 1u, __ATOMIC_ACQ_REL,
+        // Only the next launch on the stream reads the counter and the epoch, and
+        // the kernel boundary orders this launch's memory before it, so relaxed
+        // atomics suffice (acquire-release here would write back and invalidate
+        // the XCD's L2 in every workgroup).
+        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlTreeDone], 1u, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
             __hip_atomic_store(&a.ctrl[kCtrlTreeDone], 0u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[kCtrlTreeEpoch], epoch, __ATOMIC_RELEASE,
+            __hip_atomic_store(&a.ctrl[kCtrlTreeEpoch], epoch, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     }
