@@ -319,7 +319,7 @@ def mode_tree_vs_ring(args):
     from collective_communication_ring_amd import api, inputs
     R, s = 8, 4
     dev = torch.device("cuda:0")
-    counts = inputs.sweep_counts(8, 256 * 1024, s)
+    counts = inputs.sweep_counts(8, args.tvr_max_bytes, s)
     Nmax = counts[-1]
     x = inputs.draw("uniform_pm1", R, Nmax, seed=4)
     send_flat = torch.from_numpy(x).to(dev).reshape(-1)
@@ -650,6 +650,8 @@ def main():
                     choices=["headline", "config1", "sweep", "tree-vs-ring", "buckets",
                              "stream", "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
+    ap.add_argument("--tvr-max-bytes", type=int, default=256 * 1024,
+                    help="tree-vs-ring: largest per-rank size (config 4 stops at 256 KiB)")
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
     ap.add_argument("--grids", default="256,512,768,1024,1280,1536,1792,2048")

@@ -113,7 +113,8 @@ typedef enum {
     AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
     AR_OPT_PROTO = 6,         /* an ar_proto_t, overriding the one given to ar_init */
-    AR_OPT_TREE_MAX_BYTES = 7, /* AR_AUTO: largest per-rank message sent by tree */
+    AR_OPT_TREE_MAX_BYTES = 7, /* AR_AUTO: largest per-rank message sent by tree
+                                  (default 256 KiB) */
     AR_OPT_DEBUG_MUTE_RANK = 8, /* testing the watchdog only: this logical rank's workgroups
                                    skip publishing (LL lines, ready flags), so its consumers'
                                    bounded waits expire; -1 (default) = none */

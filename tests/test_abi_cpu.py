@@ -90,7 +90,8 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
         assert api.ar_plan(c, 16)[0] == api.AR_RING  # default fused ring: no tree
         api.ar_set_option(c, api.AR_OPT_LAUNCH, api.AR_LAUNCH_PIPELINED)
         assert api.ar_plan(c, 16)[0] == api.AR_TREE
-        assert api.ar_plan(c, 32 * 1024)[0] == api.AR_TREE   # 128 KiB default
+        assert api.ar_plan(c, 64 * 1024)[0] == api.AR_TREE   # 256 KiB default
+        assert api.ar_plan(c, 64 * 1024 + 1)[0] == api.AR_RING
         api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, 64 * 1024)
         assert api.ar_plan(c, 16)[0] == api.AR_TREE
         assert api.ar_plan(c, 16 * 1024)[0] == api.AR_TREE
