@@ -30,10 +30,14 @@ sys.path.insert(0, ROOT)
 METRIC = "all-reduce busBW GB/s + HBM GB/s vs peak, R=8 fp32 64 MiB/rank, 1 GPU"
 PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["collective_communication_ring_amd/csrc/ar_ring.hip",
-                  "collective_communication_ring_amd/csrc/ar_pipe.hip",
-                  "collective_communication_ring_amd/csrc/ar_slots.h",
-                  "collective_communication_ring_amd/csrc/ar_elem.h"]
+# The sources each launch form's kernels are built from: a counter figure in
+# the traffic file stays valid while these hash the same.
+_CSRC = "collective_communication_ring_amd/csrc/"
+KERNEL_SOURCES = {
+    "fused": [_CSRC + f for f in ("ar_ring.hip", "ar_slots.h", "ar_elem.h", "ar_internal.h")],
+    "step": [_CSRC + f for f in ("ar_ring.hip", "ar_slots.h", "ar_elem.h", "ar_internal.h")],
+    "pipelined": [_CSRC + f for f in ("ar_pipe.hip", "ar_elem.h", "ar_internal.h")],
+}
 
 
 def ring_kw(launch, channels=1):
@@ -50,9 +54,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(launch):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[launch]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -67,7 +71,9 @@ def measured_traffic(key):
     except (OSError, ValueError):
         return None
     ent = t.get(key)
-    if not ent or ent.get("kernel_source_sha") != kernel_source_sha():
+    launch = key.rsplit("_", 1)[-1]
+    if not ent or launch not in KERNEL_SOURCES or \
+            ent.get("kernel_source_sha") != kernel_source_sha(launch):
         return None
     return ent.get("bytes_per_launch")
 

@@ -53,17 +53,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     const int nsteps = (OP == kOpAllReduce) ? 2 * (R - 1) : (OP == kOpReduceScatter) ? R - 1 : R;
     uint32_t* err = &a.ctrl[kCtrlError];
 
-    __shared__ uint32_t s_epoch;
-    __shared__ uint64_t s_deadline;
-    if (threadIdx.x == 0) {
-        s_epoch = __hip_atomic_load(&a.ctrl[kCtrlRingLLEpoch], __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        s_deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
-    }
-    __syncthreads();
-    const uint32_t epoch = s_epoch;
+    // Every wave reads the epoch itself (no barrier), so the load overlaps the
+    // first input loads; only the last workgroup to finish writes it.
+    const uint32_t epoch = __hip_atomic_load(&a.ctrl[kCtrlRingLLEpoch], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
     const uint32_t f_red = 2u * epoch, f_copy = 2u * epoch + 1u;
-    const uint64_t deadline = s_deadline;
+    const uint64_t deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
     const bool publish = (q != a.mute_rank);
     const T* send = static_cast<const T*>(a.send);
     T* out = static_cast<T*>(a.out);

@@ -60,16 +60,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     const int v = (blockIdx.x / bpr) % R;
     const int b = blockIdx.x % bpr;
 
-    __shared__ uint32_t s_epoch;
-    __shared__ uint64_t s_deadline;
-    if (threadIdx.x == 0) {
-        s_epoch = __hip_atomic_load(&a.ctrl[kCtrlTreeEpoch], __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        s_deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
-    }
-    __syncthreads();
-    const uint32_t epoch = s_epoch;
-    const uint64_t deadline = s_deadline;
+    // Every wave reads the epoch itself (one request per wave, no barrier):
+    // the value is first needed at the first line stored or polled, so the
+    // load overlaps the input loads instead of preceding them.  It cannot
+    // change during the launch: only the last workgroup to finish writes it.
+    const uint32_t epoch = __hip_atomic_load(&a.ctrl[kCtrlTreeEpoch], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    const uint64_t deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
     uint32_t* err = &a.ctrl[kCtrlError];
 
     // this tree's half of the elements, and this launch's piece of it
