@@ -79,7 +79,7 @@ typedef enum { AR_SUM = 0, AR_MAX = 1, AR_MIN = 2, AR_AVG = 3 } ar_redop_t;
 typedef enum {
     AR_SUCCESS = 0,
     AR_ERR_INVALID_ARG = 1,   /* R out of range, NULL pointer, count above capacity, misaligned */
-    AR_ERR_INVALID_USAGE = 2, /* in-place call, missing workspace, comm in error state */
+    AR_ERR_INVALID_USAGE = 2, /* partly overlapping send/recv, missing workspace */
     AR_ERR_UNSUPPORTED = 3,   /* combination not provided (e.g. tree reduce-scatter) */
     AR_ERR_HIP = 4,           /* a HIP runtime call failed; see ar_last_hip_error */
     AR_ERR_TIMEOUT = 5,       /* a kernel's bounded wait expired (watchdog) */
@@ -139,11 +139,13 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
  * NULL is a no-op. */
 int ar_destroy(ar_comm_t comm);
 
-/* Bytes of device workspace this communicator needs: float32 partial sums
- * when T is not float32/int32 or when reducing into a shard, LL staging
- * lines for the tree and the ring-LL path, per-chunk ready flags, and a
- * small control block (LL epoch, error word).  The caller allocates at
- * least this many bytes (any 256-byte aligned device allocation). */
+/* Bytes of device workspace this communicator needs: one row of `count`
+ * 4-byte accumulators for the ring's hand-off (used by bfloat16 and by an
+ * in-place all-reduce; otherwise a segment's running value is handed on
+ * through its owner's row of recv), LL lines for the tree and the ring-LL
+ * path, per-chunk ready flags for the pipelined ring, and a small control
+ * block (LL epoch, flag base, error word).  The caller allocates at least
+ * this many bytes (any 256-byte aligned device allocation). */
 size_t ar_workspace_bytes(ar_comm_t comm);
 
 /* Hand the workspace to the communicator and clear its control block and
@@ -156,6 +158,8 @@ int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
 /* All-reduce (sum, or the comm's AR_OPT_REDOP).  send and recv are
  * [R][count] rank-major device arrays of the comm's dtype; they may be the
  * same array (in place) but must not otherwise overlap (AR_ERR_INVALID_USAGE).
+ * recv's contents are undefined until the call completes (the ring hands
+ * running values on through it).
  * On completion every row of recv holds the element-wise reduction over the
  * R rows of send ("NCCL, NIXL, and Distributed GPU Communication", section
  * "All-reduce").  Floating-point sums are added in the order the schedule
@@ -164,10 +168,11 @@ int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
  * ascending rank order. */
 int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, void* stream);
 
-/* Reduce-scatter (sum), ring only.  send is [R][R*recvcount], recv is
- * [R][recvcount]: row q of recv receives segment q of the sum ("NCCL, NIXL,
- * and Distributed GPU Communication", section "Reduce-scatter").  The values
- * are bit-identical to the same segment of ar_allreduce's result. */
+/* Reduce-scatter (sum, or the comm's AR_OPT_REDOP), ring only.  send is
+ * [R][R*recvcount], recv is [R][recvcount], not overlapping: row q of recv
+ * receives segment q of the reduction ("NCCL, NIXL, and Distributed GPU
+ * Communication", section "Reduce-scatter").  The values are bit-identical to
+ * the same segment of ar_allreduce's result. */
 int ar_reduce_scatter(ar_comm_t comm, const void* send, void* recv, size_t recvcount,
                       void* stream);
 
