@@ -1,7 +1,9 @@
 // ar_util.hip -- plain streaming kernels used as measurement references:
 // c = a + b over float32 (the access mix of one reduce step) and a byte
 // copy (the access mix of one copy step, and a known-size kernel for
-// calibrating byte counters).
+// calibrating byte counters).  Both load and store with non-temporal hints:
+// nothing they touch is reused, and that is the fastest way to stream on
+// gfx950 (a 512 MiB copy: ~6.1 TB/s, against ~5.6 TB/s with plain accesses).
 #include <algorithm>
 
 #include "ar_elem.h"
@@ -22,8 +24,8 @@ __global__ __launch_bounds__(kBlock) void k_stream_add(const u32x4* __restrict__
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t j = j0 + (uint64_t)u * kBlock;
             if (j < nvec) {
-                x[u] = a[j];
-                y[u] = b[j];
+                x[u] = __builtin_nontemporal_load(a + j);
+                y[u] = __builtin_nontemporal_load(b + j);
             }
         }
 #pragma unroll
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kBlock) void k_stream_add(const u32x4* __restrict__
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     r[i] = __float_as_uint(__uint_as_float(x[u][i]) + __uint_as_float(y[u][i]));
-                c[j] = r;
+                __builtin_nontemporal_store(r, c + j);
             }
         }
     }
@@ -59,13 +61,13 @@ __global__ __launch_bounds__(kBlock) void k_stream_copy(const u32x4* __restrict_
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t j = j0 + (uint64_t)u * kBlock;
             if (j < nvec)
-                r[u] = src[j];
+                r[u] = __builtin_nontemporal_load(src + j);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t j = j0 + (uint64_t)u * kBlock;
             if (j < nvec)
-                dst[j] = r[u];
+                __builtin_nontemporal_store(r[u], dst + j);
         }
     }
 }

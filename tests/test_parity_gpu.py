@@ -537,6 +537,81 @@ def test_ring_ll_multiple_pieces(env, dtype, R):
         assert y.tobytes() == ref.tobytes()
 
 
+# ---------------------------------------------------------------- special values
+
+def _special_f32(R, N, seed):
+    """float32 inputs mixing normal values with denormals, signed zeros,
+    infinities of both signs and NaNs, placed column by column."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    cols = rng.permutation(N)
+    q = N // 8
+    den, zer, negz, inf1, infpm, nan1, big = (cols[i * q:(i + 1) * q] for i in range(7))
+    x[:, den] *= np.float32(1e-39)               # float32 denormals (below 1.18e-38)
+    x[:, zer] = 0.0
+    x[rng.integers(0, R, len(zer)), zer] = -0.0  # one -0 among +0
+    x[:, negz] = -0.0                            # all -0: the sum stays -0
+    x[rng.integers(0, R, len(inf1)), inf1] = np.inf
+    r = rng.integers(0, R, len(infpm))
+    x[r, infpm] = np.inf
+    x[(r + 1 + rng.integers(0, R - 1, len(infpm))) % R, infpm] = -np.inf  # inf - inf = NaN
+    x[rng.integers(0, R, len(nan1)), nan1] = np.nan
+    x[:, big] = np.float32(3.0e38) * np.sign(x[:, big])  # overflow to +-inf mid-fold
+    return x
+
+
+def _assert_same_special(y, ref, dtype, what):
+    """Bit-exact except that a NaN result must be a NaN (IEEE fixes no NaN
+    payload or sign, and x86 and gfx950 differ there)."""
+    if dtype == "bf16":
+        yf, rf = y.astype(np.uint32) << 16, ref.astype(np.uint32) << 16
+        yf, rf = yf.view(np.float32), rf.view(np.float32)
+    else:
+        yf, rf = y, ref
+    nan = np.isnan(rf)
+    assert (np.isnan(yf) == nan).all(), what
+    assert y[~nan].tobytes() == ref[~nan].tobytes(), what
+
+
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("dtype", ["float32", "bf16"])
+@pytest.mark.parametrize("op", ["sum", "max", "min", "avg"])
+def test_special_values(env, variant, dtype, op):
+    """Denormals, signed zeros, infinities and NaNs go through every form and
+    operator exactly as the oracle folds them (no flush to zero, no fused or
+    reassociated adds, max/min by the same strict comparison)."""
+    orc = env["orc"]
+    for R, N in ((8, 8 * 4096 + 40), (5, 1003)):
+        x = _special_f32(R, N, seed=R * 131 + N)
+        if dtype == "bf16":
+            x = orc.bf16_from_f32(x)
+        if variant == "tree":
+            (y,) = run_allreduce(env, x, dtype, "tree", "ll", redop=op)
+            ref = orc.tree_allreduce(x, dtype, op=op)
+        else:
+            (y,) = run_allreduce(env, x, dtype, launch=variant, redop=op)
+            ref = orc.ring_allreduce(x, dtype, op=op)
+        _assert_same_special(y, ref, dtype, (variant, dtype, op, R, N))
+
+
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+def test_int32_sum_wraps(env, variant):
+    """int32 sums wrap modulo 2^32 in every form, as in the oracle and as
+    numpy's int64 sum reduced modulo 2^32."""
+    orc = env["orc"]
+    R, N = 8, 4 * 4096 + 3
+    rng = np.random.default_rng(77)
+    x = rng.integers(-2 ** 31, 2 ** 31, size=(R, N), dtype=np.int64).astype(np.int32)
+    want = (x.astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    if variant == "tree":
+        (y,) = run_allreduce(env, x, "int32", "tree", "ll")
+        assert y.tobytes() == orc.tree_allreduce(x).tobytes()
+    else:
+        (y,) = run_allreduce(env, x, "int32", launch=variant)
+        assert y.tobytes() == orc.ring_allreduce(x).tobytes()
+    assert (y == want[None, :]).all()
+
+
 # ---------------------------------------------------------------- channels
 
 def _strides(api, R, K):
