@@ -89,14 +89,22 @@ typedef enum {
 /* How the ring's steps are launched.
  * AR_LAUNCH_STEP: one kernel per ring step covering all R ranks; the kernel
  *   boundary orders the steps.
- * AR_LAUNCH_FUSED: one persistent kernel; each workgroup carries its chunks
- *   of a segment through all 2(R-1) steps in order, every step still reading
- *   the predecessor rank's buffer and writing the rank's own buffer.
+ * AR_LAUNCH_FUSED: one persistent kernel; each workgroup carries its tiles
+ *   of a segment through all 2(R-1) steps in order, every reduce step reading
+ *   the running value its predecessor rank stored and storing its own over
+ *   it, every copy step reading the predecessor rank's output row.
  * AR_LAUNCH_PIPELINED: one persistent kernel in which each logical rank has
  *   its own workgroups; a chunk passes from rank q-1 to rank q through a
- *   per-chunk ready flag (agent-scope release by the producer, acquire by
- *   the consumer) -- the simple protocol.
- * AR_LAUNCH_AUTO: the library's choice (the default). */
+ *   per-chunk ready flag (device-scope write-through stores, then the flag;
+ *   the consumer polls the flag, then reads coherently) -- the simple
+ *   protocol.
+ * AR_LAUNCH_AUTO: the library's choice (the default).
+ * The pipelined ring, the ring with AR_LL and the tree need every workgroup
+ * of a launch resident at once (the library sizes their grids to the
+ * device's occupancy).  Two such launches running at the same time on
+ * different streams can each hold part of the device and wait for each
+ * other until their bounded waits expire (AR_ERR_TIMEOUT): do not overlap
+ * them with each other.  The step and fused forms have no such waits. */
 typedef enum {
     AR_LAUNCH_AUTO = 0,
     AR_LAUNCH_STEP = 1,

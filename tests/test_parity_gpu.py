@@ -537,6 +537,58 @@ def test_ring_ll_multiple_pieces(env, dtype, R):
         assert y.tobytes() == ref.tobytes()
 
 
+# ---------------------------------------------------------------- R = 64, concurrency
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+def test_ring_largest_rank_count(env, launch, dtype):
+    """R = 64, the largest communicator, in every ring form: ragged and whole
+    segments, all-reduce and reduce-scatter."""
+    api, orc = env["api"], env["orc"]
+    R = 64
+    for N in (R * 1000 + 7, R * 4096):
+        x = rand_input(env, dtype, R, N, seed=640 + N)
+        (y,) = run_allreduce(env, x, dtype, launch=launch)
+        assert y.tobytes() == orc.ring_allreduce(x, dtype).tobytes(), N
+        check_tolerance(env, y, x, dtype)
+    n = 1024
+    x = rand_input(env, dtype, R, R * n, seed=641)
+    comm = api.Comm(R, R * n, dtype, device=env["dev"], **ring_opts(launch))
+    shard = poisoned(env, (R, n), dtype)
+    comm.reduce_scatter(to_dev(env, x, dtype), shard)
+    assert from_dev(env, shard, dtype).tobytes() == orc.ring_reduce_scatter(x, dtype).tobytes()
+    assert comm.check() == api.AR_SUCCESS
+
+
+@pytest.mark.parametrize("pair", [("fused", "fused"), ("fused", "step"), ("step", "step")])
+def test_two_comms_on_two_streams(env, pair):
+    """Two communicators, each with its own workspace, run at the same time on
+    two streams and both stay exact (the forms without cross-workgroup waits;
+    LL and pipelined launches need the whole device resident and must not
+    overlap each other)."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    xs = [env["inputs"].draw("normal", 8, 1 << 20, seed=51),
+          env["inputs"].draw("normal", 4, (1 << 20) + 13, seed=52)]
+    refs = [orc.ring_allreduce(x) for x in xs]
+    comms = [api.Comm(x.shape[0], x.shape[1], "float32", device=env["dev"], launch=l)
+             for x, l in zip(xs, pair)]
+    sends = [to_dev(env, x, "float32") for x in xs]
+    recvs = [poisoned(env, x.shape, "float32") for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        for c, s_, r, st in zip(comms, sends, recvs, streams):
+            with torch.cuda.stream(st):
+                for _ in range(2):
+                    c.allreduce(s_, r)
+        torch.cuda.synchronize()
+        for r, ref in zip(recvs, refs):
+            assert from_dev(env, r, "float32").tobytes() == ref.tobytes()
+    for c in comms:
+        assert c.check() == api.AR_SUCCESS
+
+
 # ---------------------------------------------------------------- special values
 
 def _special_f32(R, N, seed):
