@@ -343,11 +343,11 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         const uint64_t tile = (uint64_t)kBlock * kUnroll;
         const uint64_t tiles = ((a.sub_len + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
         // One workgroup per CU by default for all-reduce and all-gather: with
-        // more tiles in flight per XCD the partial a step writes is evicted
-        // from the XCD's L2 before the next step re-reads it (measured: 0.23 ms
-        // at 256 workgroups against 0.29 ms at the occupancy limit, R = 8 fp32
-        // 64 MiB/rank).  Reduce-scatter alone does better with 8 per CU
-        // (R = 16 bf16 25 MiB buckets: 367 against 397 us).
+        // more tiles in flight per XCD the rows of the copy chain are evicted
+        // from the XCD's L2 before the next step re-reads them (R = 8 fp32
+        // 64 MiB/rank: 0.22 ms at 256 workgroups, 0.24 at 512, 0.26 at
+        // 2048).  Reduce-scatter alone does better with 8 per CU (R = 16 bf16
+        // 25 MiB buckets: 173-178 against 182-184 us at 256).
         const int64_t dflt = (a.op == kOpReduceScatter) ? 8 * (int64_t)c->ncu : (int64_t)c->ncu;
         const int64_t want = c->grid > 0 ? c->grid : dflt;
         grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
@@ -572,12 +572,12 @@ int ar_set_workspace(ar_comm_t c, void* dev, size_t bytes, void* stream)
 
 int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* stream)
 {
+    if (c && count > c->cap)  // sizes first: checked without a device
+        return AR_ERR_INVALID_ARG;
     bool noop = false;
     int rc = common_checks(c, send, recv, count, &noop);
     if (rc || noop)
         return rc;
-    if (count > c->cap)
-        return AR_ERR_INVALID_ARG;
     const size_t bytes = (size_t)c->R * count * elem_size(c->dtype);
     // in place (send == recv) is allowed: the hand-off goes through the
     // workspace row, and every schedule reads an element of a rank's input
@@ -619,13 +619,15 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
 
 int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcount, void* stream)
 {
+    // sizes first (checked without a device), and before multiplying by R so
+    // that no count wraps around
+    if (c && recvcount > c->cap / (size_t)c->R)
+        return AR_ERR_INVALID_ARG;
     bool noop = false;
     int rc = common_checks(c, send, recv, recvcount, &noop);
     if (rc || noop)
         return rc;
     const size_t N = recvcount * (size_t)c->R;
-    if (N > c->cap)
-        return AR_ERR_INVALID_ARG;
     const size_t es = elem_size(c->dtype);
     if (N && overlaps(send, (size_t)c->R * N * es, recv, N * es))
         return AR_ERR_INVALID_USAGE;
@@ -655,13 +657,13 @@ int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcoun
 
 int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, void* stream)
 {
+    if (c && sendcount > c->cap / (size_t)c->R)  // as in ar_reduce_scatter
+        return AR_ERR_INVALID_ARG;
     bool noop = false;
     int rc = common_checks(c, send, recv, sendcount, &noop);
     if (rc || noop)
         return rc;
     const size_t N = sendcount * (size_t)c->R;
-    if (N > c->cap)
-        return AR_ERR_INVALID_ARG;
     const size_t es = elem_size(c->dtype);
     if (N && overlaps(send, N * es, recv, (size_t)c->R * N * es))
         return AR_ERR_INVALID_USAGE;

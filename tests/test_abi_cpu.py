@@ -175,3 +175,20 @@ def test_channel_strides(api, R):
         assert api.ar_ring_channel_stride(c, -1) == -1
     finally:
         api.ar_destroy(c)
+
+
+def test_counts_are_checked_before_the_device(api):
+    """Sizes are validated before anything touches the device, and a shard
+    count whose product with R would wrap around size_t is refused."""
+    L = api.lib()
+    c = api.ar_init(4, 64, api.AR_FLOAT32)
+    try:
+        huge = (1 << 64) // 4 + 1  # 4 * huge wraps to 4, below the capacity
+        for fn in (L.ar_reduce_scatter, L.ar_all_gather):
+            assert fn(c, 4096, 8192, huge, None) == api.AR_ERR_INVALID_ARG
+            assert fn(c, 4096, 8192, 17, None) == api.AR_ERR_INVALID_ARG   # 4 * 17 > 64
+            assert fn(c, 4096, 8192, 16, None) == api.AR_ERR_INVALID_USAGE  # fits: no workspace yet
+        assert L.ar_allreduce(c, 4096, 8192, 65, None) == api.AR_ERR_INVALID_ARG
+        assert L.ar_allreduce(c, 4096, 8192, 64, None) == api.AR_ERR_INVALID_USAGE
+    finally:
+        api.ar_destroy(c)

@@ -305,6 +305,15 @@ def test_argument_errors(env):
     with pytest.raises(api.ArError) as e:
         tcomm.reduce_scatter(a, torch.zeros((4, 16), device=env["dev"]))
     assert e.value.status == api.AR_ERR_UNSUPPORTED
+    # shard counts whose product with R wraps around size_t are refused
+    # before anything is launched (raw C calls: the pointers are never used)
+    L = api.lib()
+    huge = (1 << 64) // 4 + 1  # 4 * huge wraps to 4
+    p = a.data_ptr()
+    assert L.ar_reduce_scatter(comm.handle, p, p + 4096, huge, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_all_gather(comm.handle, p, p + 4096, huge, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_reduce_scatter(comm.handle, p, p + 4096, 17, None) == api.AR_ERR_INVALID_ARG
+    assert comm.check() == api.AR_SUCCESS
 
 
 @pytest.mark.parametrize("launch", LAUNCHES)
