@@ -28,6 +28,7 @@ constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
 // the pipelined ring at R = 8: the tree wins at 256 KiB, the ring at 512 KiB)
 constexpr int64_t kDefaultTreeMaxBytes = 256 * 1024;
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
+constexpr uint64_t kMaxChunkBytes = 1ull << 30;      // pipelined ring: largest chunk
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -363,6 +364,9 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         const uint64_t tile = (uint64_t)kBlock * kUnroll * V;  // elements per workgroup pass
         const uint64_t es = (uint64_t)elem_size(c->dtype);
         uint64_t unit = c->chunk_bytes > 0 ? (uint64_t)c->chunk_bytes / es : a.sub_len;
+        // a chunk is addressed through one buffer resource (byte offsets below
+        // 2 GiB): cap it at 1 GiB
+        unit = std::min<uint64_t>(unit, kMaxChunkBytes / es);
         unit = std::max<uint64_t>(tile, unit / tile * tile);
         uint64_t nunits = (a.sub_len + unit - 1) / unit;
         // the chunk is the pipelining unit; cut it finer when a segment has
