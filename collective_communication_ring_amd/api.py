@@ -228,12 +228,18 @@ class Comm:
             self.set_option(globals()["AR_OPT_" + k.upper()], v)
         nbytes = ar_workspace_bytes(self.handle)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self._ws_stream = torch.cuda.current_stream(self.device).cuda_stream
         ar_set_workspace(self.handle, self.workspace.data_ptr(), self.workspace.numel(),
                          self._stream(None))
 
     def _stream(self, stream):
         import torch
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if getattr(self, "workspace", None) is not None and \
+                s.cuda_stream != self._ws_stream and not torch.cuda.is_current_stream_capturing():
+            # the workspace may still be in use on this stream when the comm is
+            # dropped: keep torch's allocator from reusing it too early
+            self.workspace.record_stream(s)
         return s.cuda_stream
 
     def _check_tensor(self, t, rows, cols, what):
