@@ -9,7 +9,8 @@ whole [8, 16M] buffer, inputs resident in HBM before the timed region.
   value  = busBW = algBW * 2(R-1)/R,  algBW = per-rank bytes / time
   roofline.achieved = algorithmic HBM bytes 5(R-1) N s / kernel time
 
-Other modes (--mode): config1 (R = 4 int32, 4096 per rank, every form),
+Other modes (--mode): config1 (R = 4 int32, 4096 per rank, every form), matrix
+(fused, 64 MiB per rank, R = 2..16, every dtype),
 sweep (8 B .. 1 GiB per rank, alpha-beta fit), tree-vs-ring (8 B .. 256 KiB),
 buckets (R = 16 bf16 reduce-scatter then all-gather, 40 x 25 MiB), stream
 (c = a + b and copy reference kernels), counters (a short program for
@@ -615,6 +616,53 @@ def mode_config1(args):
     return 0 if all(r["exact"] for r in res.values()) else 1
 
 
+def mode_matrix(args):
+    """Fused ring all-reduce at 64 MiB per rank for R in {2, 4, 8, 16} and
+    every dtype: time, busBW and the algorithmic HBM fraction, each result
+    checked bit for bit against the oracle."""
+    import numpy as np
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+    import oracle
+    dev = torch.device("cuda:0")
+    rows = []
+    for dtype, s in (("float32", 4), ("int32", 4), ("bf16", 2)):
+        for R in (2, 4, 8, 16):
+            N = (64 << 20) // s
+            if dtype == "float32":
+                x = inputs.draw("normal", R, N, seed=100 + R)
+            elif dtype == "int32":
+                x = inputs.draw("int_pm1000", R, N, seed=100 + R)
+            else:
+                x = inputs.to_bf16_bits(inputs.draw("normal_0.02", R, N, seed=100 + R))
+            if dtype == "bf16":
+                send = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+            else:
+                send = torch.from_numpy(x).to(dev)
+            recv = torch.empty_like(send)
+            comm = api.Comm(R, N, dtype, device=dev, launch="fused")
+            _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps,
+                                        args.warmup, torch)
+            t = total_ms / args.steps / 1e3
+            got = recv.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" \
+                else recv.cpu().numpy()
+            exact = got.tobytes() == oracle.ring_allreduce(x, dtype).tobytes()
+            row = dict(dtype=dtype, R=R, bytes_per_rank=N * s, ms=round(t * 1e3, 4),
+                       busbw_GBps=round(N * s / t / 1e9 * measure.busbw_factor("allreduce", R), 1),
+                       alg_frac=round(measure.allreduce_alg_bytes(R, N, s) / t / 1e9 /
+                                      PEAK_HBM_GBPS, 3),
+                       compulsory_TBps=round(2 * R * N * s / t / 1e12, 2), exact=exact)
+            rows.append(row)
+            log("matrix %-7s R=%2d %.4f ms busBW %7.1f GB/s alg frac %.3f compulsory %.2f TB/s "
+                "exact=%s" % (dtype, R, row["ms"], row["busbw_GBps"], row["alg_frac"],
+                              row["compulsory_TBps"], exact))
+            comm.close()
+            del send, recv, x
+            torch.cuda.empty_cache()
+    print(json.dumps(dict(mode="matrix", launch="fused", results=rows)), flush=True)
+    return 0 if all(r["exact"] for r in rows) else 1
+
+
 def mode_tune(args):
     """Time the R = 8 fp32 64 MiB/rank all-reduce for a list of grid sizes
     (workgroups per launch) in one launch form."""
@@ -653,8 +701,8 @@ def main():
                     help="ring launch form; 'll' = the ring with the LL protocol")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
-                    choices=["headline", "config1", "sweep", "tree-vs-ring", "buckets",
-                             "stream", "counters", "tune", "overlap"])
+                    choices=["headline", "config1", "matrix", "sweep", "tree-vs-ring",
+                             "buckets", "stream", "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--tvr-max-bytes", type=int, default=256 * 1024,
                     help="tree-vs-ring: largest per-rank size (config 4 stops at 256 KiB)")
@@ -678,7 +726,8 @@ def main():
               "MI355X's HBM, so --gpus must be 1 (got --gpus %d, WORLD_SIZE %d)."
               % (args.gpus, world), file=sys.stderr)
         return 2
-    fn = {"headline": headline, "config1": mode_config1, "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
+    fn = {"headline": headline, "config1": mode_config1, "matrix": mode_matrix,
+          "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
           "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
           "tune": mode_tune, "overlap": mode_overlap}[args.mode]
     return fn(args)
