@@ -536,6 +536,11 @@ def mode_overlap(args):
     t_over = timed(overlapped)
     assert comm.check() == api.AR_SUCCESS
     torch.cuda.synchronize()
+    # the comm's workspace is recorded on s_comm: release it while that stream
+    # still exists, then destroy the CU-masked streams
+    comm.close()
+    del comm
+    torch.cuda.synchronize()
     for r in raw:
         api.ar_stream_destroy(r)
     out = dict(mode="overlap", launch=launch, comm_cus=args.comm_cus or None, buckets=B,

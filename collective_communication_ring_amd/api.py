@@ -291,9 +291,14 @@ class Comm:
         return [ar_ring_channel_stride(self.handle, k) for k in range(K)]
 
     def close(self):
+        """Destroy the communicator and release its workspace.  A comm used on
+        a stream that the caller destroys itself (ar_stream_destroy) must be
+        closed, and that stream's work finished, before the stream goes: the
+        workspace is recorded on every stream the comm ran on."""
         if getattr(self, "handle", None):
             ar_destroy(self.handle)
             self.handle = None
+        self.workspace = None
 
     def __del__(self):
         try:
