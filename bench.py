@@ -199,6 +199,12 @@ def headline(args):
         "busbw_GBps": round(busbw, 3),
         "hbm_alg_GBps": round(b_alg / t / 1e9, 3),
         "hbm_alg_frac_of_peak": round(b_alg / t / 1e9 / PEAK_HBM_GBPS, 4),
+        # the bytes the counters saw move (roofline.traffic) over the same time:
+        # the HBM rate proper, which the algorithmic rate overstates when the
+        # L2 serves the hand-off re-reads
+        "hbm_measured_GBps": round(traffic / (kernel_ms / 1e3) / 1e9, 3) if traffic else None,
+        "hbm_measured_frac_of_peak": round(traffic / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+        if traffic else None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": b_alg
