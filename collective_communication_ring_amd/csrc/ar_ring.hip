@@ -122,18 +122,18 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
 __device__ inline void fused_step(typename E::A (&x)[kUnroll][V], const u32x4 (&own)[kUnroll],
                                   u32x4 (&nxt)[kUnroll], typename E::A* acc, typename E::T* fin,
-                                  const typename E::T* next_row, uint64_t j0, float R)
+                                  const typename E::T* next_row, uint64_t j0, uint64_t js, float R)
 {
     using A = typename E::A;
     if constexpr (LOADX) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            load_a<E, V>(acc + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+            load_a<E, V>(acc + (j0 + (uint64_t)u * js) * V, x[u]);
     }
     if constexpr (PREFETCH) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            nxt[u] = load16(next_row + (j0 + (uint64_t)u * kBlock) * V);
+            nxt[u] = load16(next_row + (j0 + (uint64_t)u * js) * V);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -146,9 +146,9 @@ __device__ inline void fused_step(typename E::A (&x)[kUnroll][V], const u32x4 (&
                 x[u][i] = finalize<E, RED>(x[u][i], R);
         }
         if constexpr (LAST)
-            store_t<E, V>(fin + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+            store_t<E, V>(fin + (j0 + (uint64_t)u * js) * V, x[u]);
         else
-            store_a<E, V>(acc + (j0 + (uint64_t)u * kBlock) * V, x[u]);
+            store_a<E, V>(acc + (j0 + (uint64_t)u * js) * V, x[u]);
     }
     step_boundary();
 }
@@ -159,7 +159,8 @@ __device__ inline void fused_step(typename E::A (&x)[kUnroll][V], const u32x4 (&
 // adds to the L2 footprint of the copy chain.)
 template <class E, int V>
 __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                        typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
+                                        uint64_t js, typename E::A (&x)[kUnroll][V],
+                                        u32x4 (&b0)[kUnroll])
 {
     using T = typename E::T;
     const T* send = static_cast<const T*>(a.send) + lo;
@@ -167,8 +168,8 @@ __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, u
     const T* r0 = send + (uint64_t)mod_r(c + 2 * a.m, a.R) * a.send_row;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        load_t<E, V>(first + (j0 + (uint64_t)u * kBlock) * V, x[u]);
-        b0[u] = load16(r0 + (j0 + (uint64_t)u * kBlock) * V);
+        load_t<E, V>(first + (j0 + (uint64_t)u * js) * V, x[u]);
+        b0[u] = load16(r0 + (j0 + (uint64_t)u * js) * V);
     }
 }
 
@@ -178,7 +179,8 @@ __device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, u
 // for the next step's load.
 template <class E, int V, int RED>
 __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                          typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
+                                          uint64_t js, typename E::A (&x)[kUnroll][V],
+                                          u32x4 (&b0)[kUnroll])
 {
     using T = typename E::T;
     using A = typename E::A;
@@ -192,40 +194,41 @@ __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo,
     auto row = [&](int s) { return send + (uint64_t)mod_r(c + (s + 2) * m, R) * a.send_row; };
     u32x4 b1[kUnroll];
     if (R == 2) {
-        fused_step<E, V, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, j0, fr);
+        fused_step<E, V, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, j0, js, fr);
         return;
     }
     // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
-    fused_step<E, V, RED, false, true, false>(x, b0, b1, acc, fin, row(1), j0, fr);
+    fused_step<E, V, RED, false, true, false>(x, b0, b1, acc, fin, row(1), j0, js, fr);
     int s = 1;  // the next step; its input is in b1
     for (; s + 1 <= R - 3; s += 2) {
-        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, fr);
-        fused_step<E, V, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 2), j0, fr);
+        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, js, fr);
+        fused_step<E, V, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 2), j0, js, fr);
     }
     if (s == R - 3) {
-        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, fr);
-        fused_step<E, V, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, j0, fr);
+        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, js, fr);
+        fused_step<E, V, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, j0, js, fr);
     } else {
-        fused_step<E, V, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, j0, fr);
+        fused_step<E, V, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, j0, js, fr);
     }
 }
 
 template <class E, int V>
 __device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                             typename E::A (&x)[kUnroll][V], u32x4 (&b0)[kUnroll])
+                                             uint64_t js, typename E::A (&x)[kUnroll][V],
+                                             u32x4 (&b0)[kUnroll])
 {
     switch (a.redop) {
     case AR_MAX:
-        fused_reduce_whole<E, V, AR_MAX>(a, c, lo, j0, x, b0);
+        fused_reduce_whole<E, V, AR_MAX>(a, c, lo, j0, js, x, b0);
         break;
     case AR_MIN:
-        fused_reduce_whole<E, V, AR_MIN>(a, c, lo, j0, x, b0);
+        fused_reduce_whole<E, V, AR_MIN>(a, c, lo, j0, js, x, b0);
         break;
     case AR_AVG:
-        fused_reduce_whole<E, V, AR_AVG>(a, c, lo, j0, x, b0);
+        fused_reduce_whole<E, V, AR_AVG>(a, c, lo, j0, js, x, b0);
         break;
     default:
-        fused_reduce_whole<E, V, AR_SUM>(a, c, lo, j0, x, b0);
+        fused_reduce_whole<E, V, AR_SUM>(a, c, lo, j0, js, x, b0);
         break;
     }
 }
@@ -241,7 +244,8 @@ __device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t 
 // >= 128 MiB per rank).
 template <int V>
 __device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_t* lo,
-                                  uint64_t* len, uint64_t* j0, bool* whole)
+                                  uint64_t* len, uint64_t* j0, uint64_t* js, bool* active,
+                                  bool* whole)
 {
     const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
     const uint64_t tiles_per_seg = ((a.sub_len + V - 1) / V + tile_slots - 1) / tile_slots;
@@ -250,9 +254,21 @@ __device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_
     uint64_t hi;
     seg_range(a.N, a.S, *c, a.sub_lo, a.sub_len, lo, &hi);
     *len = hi - *lo;
-    *j0 = k * tile_slots + threadIdx.x;
-    *whole = V > 1 && (*j0 + (kUnroll - 1) * kBlock + 1) * V <= *len;
-    return k * tile_slots * V < *len;
+    const uint64_t first = k * tile_slots;
+    const uint64_t seg_slots = (*len + V - 1) / V;
+    // a tile the segment fills only in part (vector path): spread its n slots
+    // over ceil(n / kUnroll) threads, so that the active threads have whole
+    // slots and take the prefetching path.  The scalar path has no such path
+    // and keeps one slot per thread.
+    const uint64_t n = seg_slots > first ? seg_slots - first : 0;
+    uint64_t stride = kBlock;
+    if (V > 1 && n < tile_slots)
+        stride = (n + kUnroll - 1) / kUnroll;
+    *js = stride;
+    *active = threadIdx.x < stride;
+    *j0 = first + threadIdx.x;
+    *whole = V > 1 && *active && (*j0 + (kUnroll - 1) * stride + 1) * V <= *len;
+    return first * V < *len;
 }
 
 template <int DT, int V, int OP>
@@ -271,10 +287,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     using A = typename E::A;
     for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
         int c;
-        uint64_t lo, len, j0;
-        bool whole;
-        if (!fused_tile<V>(a, t, &c, &lo, &len, &j0, &whole))
+        uint64_t lo, len, j0, js;
+        bool active, whole;
+        if (!fused_tile<V>(a, t, &c, &lo, &len, &j0, &js, &active, &whole))
             continue;  // empty tile of a short trailing segment (uniform per workgroup)
+        if (!active)
+            continue;  // this thread has no slot in a part-filled tile
 
         if constexpr (OP != kOpAllGather) {
             bool done = false;
@@ -282,8 +300,8 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
                 if (whole) {
                     A x[kUnroll][V];
                     u32x4 b0[kUnroll];
-                    fused_load_first<E, V>(a, c, lo, j0, x, b0);
-                    fused_reduce_whole_op<E, V>(a, c, lo, j0, x, b0);
+                    fused_load_first<E, V>(a, c, lo, j0, js, x, b0);
+                    fused_reduce_whole_op<E, V>(a, c, lo, j0, js, x, b0);
                     done = true;
                 }
             }
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
                 for (int s = 0; s <= R - 2; ++s) {
                     const int q = mod_r(c + (s + 2) * m, R);
                     const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
-                    reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, kBlock);
+                    reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, js);
                     step_boundary();
                 }
             }
@@ -301,14 +319,14 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
             if constexpr (OP == kOpAllGather) {
                 const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
                                (lo - (uint64_t)c * a.S);
-                copy_slots<E, V>(src, out + (uint64_t)c * a.out_row + lo, len, j0, kBlock);
+                copy_slots<E, V>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
                 step_boundary();
             }
             for (int s = 0; s <= R - 2; ++s) {
                 const int q = mod_r(c + (1 + s) * m, R);
                 const int p = mod_r(c + s * m, R);
                 copy_slots<E, V>(out + (uint64_t)p * a.out_row + lo,
-                                 out + (uint64_t)q * a.out_row + lo, len, j0, kBlock);
+                                 out + (uint64_t)q * a.out_row + lo, len, j0, js);
                 step_boundary();
             }
         }
