@@ -345,8 +345,15 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         }
     } else if (launch == AR_LAUNCH_FUSED) {
         const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
-        const uint64_t tile = (uint64_t)kBlock * kUnroll;
-        const uint64_t tiles = ((a.sub_len + V - 1) / V + tile - 1) / tile * (uint64_t)a.R;
+        // tiles of kBlock * kUnroll slots; on the vector path smaller ones (down
+        // to one wave's 64 * kUnroll) while there are fewer tiles than CUs
+        uint64_t tile = (uint64_t)kBlock * kUnroll;
+        const uint64_t seg_slots = (a.sub_len + V - 1) / V;
+        while (vec && tile > 64u * kUnroll &&
+               (seg_slots + tile - 1) / tile * (uint64_t)a.R < (uint64_t)c->ncu)
+            tile /= 2;
+        a.tile_slots = tile;
+        const uint64_t tiles = (seg_slots + tile - 1) / tile * (uint64_t)a.R;
         // One workgroup per CU by default for all-reduce and all-gather: with
         // more tiles in flight per XCD the rows of the copy chain are evicted
         // from the XCD's L2 before the next step re-reads them (R = 8 fp32

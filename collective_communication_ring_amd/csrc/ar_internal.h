@@ -62,6 +62,7 @@ struct RingArgs {
     uint64_t unit;    // pipelined ring: elements per flagged chunk (a multiple of the slot)
     uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
     uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
+    uint64_t tile_slots; // fused form: slots per tile (a multiple of kUnroll, <= kBlock * kUnroll)
     uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
     uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
     int m;            // this channel's ring stride: rank q receives from q - m

@@ -247,7 +247,7 @@ __device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_
                                   uint64_t* len, uint64_t* j0, uint64_t* js, bool* active,
                                   bool* whole)
 {
-    const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
+    const uint64_t tile_slots = a.tile_slots;
     const uint64_t tiles_per_seg = ((a.sub_len + V - 1) / V + tile_slots - 1) / tile_slots;
     *c = (int)(t / tiles_per_seg);
     const uint64_t k = t % tiles_per_seg;
@@ -261,7 +261,7 @@ __device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_
     // slots and take the prefetching path.  The scalar path has no such path
     // and keeps one slot per thread.
     const uint64_t n = seg_slots > first ? seg_slots - first : 0;
-    uint64_t stride = kBlock;
+    uint64_t stride = V > 1 ? tile_slots / kUnroll : kBlock;
     if (V > 1 && n < tile_slots)
         stride = (n + kUnroll - 1) / kUnroll;
     *js = stride;
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     using E = Elem<DT>;
     using T = typename E::T;
     const int R = a.R;
-    const uint64_t tile_slots = (uint64_t)kBlock * kUnroll;
+    const uint64_t tile_slots = a.tile_slots;
     const uint64_t seg_slots = (a.sub_len + V - 1) / V;
     const uint64_t tiles_per_seg = (seg_slots + tile_slots - 1) / tile_slots;
     const uint64_t ntiles = tiles_per_seg * (uint64_t)R;
