@@ -309,9 +309,12 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
     for (uint64_t k = 0; k < K; ++k) {
         a.m = c->strides[k];
         a.sub_lo = k * Sk;
-        a.sub_len = Sk;
         if (a.sub_lo >= a.S && k > 0)
             break;  // nothing left for later channels
+        // the kernels clip the sub-range to each segment's end; clipping its
+        // length to what a full segment holds changes no range, and keeps grids
+        // and LL pieces from covering a rounded-up tail
+        a.sub_len = std::min<uint64_t>(Sk, a.S - a.sub_lo);
         const int rc = run_ring_channel(c, a, st);
         if (rc)
             return rc;
