@@ -428,7 +428,10 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     a.timeout_ticks = timeout_ticks(c);
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
-    a.tt = c->tt;
+    for (int t = 0; t < 2; ++t)
+        for (int r = 0; r < c->R; ++r)
+            a.node[t][r] = tree_node_word(c->tt.parent[t][r], c->tt.nchild[t][r],
+                                          c->tt.child[t][r][0], c->tt.child[t][r][1]);
     // every workgroup must be resident at once: at most res / (2R) per
     // (tree, rank); a workgroup loops over its sub-blocks of kBlock lines
     const int64_t res = c->resident_tree[c->dtype];

@@ -197,6 +197,10 @@ __device__ inline void store_a(typename E::A* p, const typename E::A (&v)[V])
     }
 }
 
+// s_waitcnt vmcnt(0), leaving the other counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---- LL lines ---------------------------------------------------------------
 // An LL line is 8 bytes: the data bits in the low half, the arrival flag in
 // the high half, written and read as one 64-bit agent-scope atomic.
@@ -223,6 +227,10 @@ __device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pe
         for (int k = 0; k < K; ++k)
             if (pending[k])
                 v[k] = __hip_atomic_load(line[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // every value is checked at once; saying so explicitly lets the
+        // compiler see that none of these conditional loads is still
+        // outstanding afterwards, so later stores need no wait of their own
+        wait_vmem_all();
         bool any = false;
 #pragma unroll
         for (int k = 0; k < K; ++k) {

@@ -40,6 +40,17 @@ struct TreeTable {
     int8_t root[2];
 };
 
+// The same table packed for the kernel, one 32-bit word per (tree, rank):
+// bits 0-7 parent + 1 (0 at the root), bits 8-15 the number of children,
+// bits 16-23 and 24-31 the children in ascending order.  A word is read with
+// one scalar load; a byte table is read with vector loads, whose waits also
+// wait for every store issued before them.
+__host__ __device__ inline uint32_t tree_node_word(int parent, int nchild, int child0, int child1)
+{
+    return (uint32_t)(parent + 1) | ((uint32_t)nchild << 8) | ((uint32_t)child0 << 16) |
+           ((uint32_t)child1 << 24);
+}
+
 // Arguments of one ring collective, shared by every ring launch mode.
 //   send : [R][send_row] elements of T
 //   part : the hand-off accumulators (A): the running value of element e of
@@ -91,7 +102,7 @@ struct TreeArgs {
     int mute_rank;        // testing only: rank that skips publishing (-1: none)
     int redop;            // ar_redop_t
     uint64_t timeout_ticks;
-    TreeTable tt;
+    uint32_t node[2][kMaxRanks];  // tree_node_word of every (tree, rank)
 };
 
 // Ring with the LL protocol: every value a rank passes on travels as an

@@ -91,13 +91,21 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                 i[k] = (j0 + (uint64_t)k * G) * kBlock + threadIdx.x;
                 ok[k] = i[k] < plen;
             }
+            // Loads are unconditional (a lane past the end reads offset 0 of
+            // the piece and never uses it) and all come before the first
+            // store: with conditional loads, or a load after a store, the
+            // compiler's waits would make each store wait for the ones before
+            // it (vmcnt counts loads and stores in one in-order count).
             if (reduce) {
                 A in[K];
+                T own[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    own[k] = send[(uint64_t)q * a.send_row + e0 + (ok[k] ? i[k] : 0)];
                 if (s == 0) {
 #pragma unroll
                     for (int k = 0; k < K; ++k)
-                        if (ok[k])
-                            in[k] = E::widen(send[(uint64_t)p * a.send_row + e0 + i[k]]);
+                        in[k] = E::widen(send[(uint64_t)p * a.send_row + e0 + (ok[k] ? i[k] : 0)]);
                 } else {
                     const uint64_t* ln[K];
                     bool pend[K];
@@ -114,34 +122,38 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                     for (int k = 0; k < K; ++k)
                         in[k] = E::from_bits(d[k]);
                 }
+                wait_vmem_all();  // on every path: nothing outstanding before the stores
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     if (!ok[k])
                         continue;
-                    A v = combine_rt<E>(a.redop, in[k],
-                                        E::widen(send[(uint64_t)q * a.send_row + e0 + i[k]]));
+                    A v = combine_rt<E>(a.redop, in[k], E::widen(own[k]));
                     if (!last_reduce) {
                         if (publish)
                             ll_store(mine + i[k], E::to_bits(v), f_red);
                     } else {
                         if (a.redop == AR_AVG)
                             v = finalize<E, AR_AVG>(v, fr);
-                        const uint64_t at = (OP == kOpReduceScatter) ? in_seg + i[k] : e0 + i[k];
-                        out[(uint64_t)q * a.out_row + at] = E::narrow(v);
                         if (OP == kOpAllReduce && publish)  // the owner starts the copy phase
                             ll_store(mine + i[k], E::to_bits(v), f_copy);
+                        const uint64_t at = (OP == kOpReduceScatter) ? in_seg + i[k] : e0 + i[k];
+                        out[(uint64_t)q * a.out_row + at] = E::narrow(v);
                     }
                 }
             } else if (OP == kOpAllGather && s == 0) {
                 // place the rank's own shard and pass it on (T bits)
+                T v[K];
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    v[k] = send[(uint64_t)q * a.send_row + in_seg + (ok[k] ? i[k] : 0)];
+                wait_vmem_all();
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     if (!ok[k])
                         continue;
-                    const T v = send[(uint64_t)q * a.send_row + in_seg + i[k]];
-                    out[(uint64_t)q * a.out_row + e0 + i[k]] = v;
                     if (publish)
-                        ll_store(mine + i[k], E::t_bits(v), f_copy);
+                        ll_store(mine + i[k], E::t_bits(v[k]), f_copy);
+                    out[(uint64_t)q * a.out_row + e0 + i[k]] = v[k];
                 }
             } else {
                 const uint64_t* ln[K];
@@ -159,12 +171,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                 for (int k = 0; k < K; ++k) {
                     if (!ok[k])
                         continue;
+                    if (forward && publish)  // pass it on first: the next rank waits for it
+                        ll_store(mine + i[k], d[k], f_copy);
                     if (OP == kOpAllGather)
                         out[(uint64_t)q * a.out_row + e0 + i[k]] = E::t_from_bits(d[k]);
                     else
                         out[(uint64_t)q * a.out_row + e0 + i[k]] = E::narrow(E::from_bits(d[k]));
-                    if (forward && publish)
-                        ll_store(mine + i[k], d[k], f_copy);
                 }
             }
         }

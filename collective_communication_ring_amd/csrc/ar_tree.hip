@@ -77,8 +77,12 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 
     const T* x = static_cast<const T*>(a.send) + (uint64_t)v * a.N + first;
     T* y = static_cast<T*>(a.out) + (uint64_t)v * a.N + first;
-    const int parent = a.tt.parent[t][v];
-    const int nchild = a.tt.nchild[t][v];
+    // the node's packed word (one scalar load; see tree_node_word)
+    const uint32_t node = a.node[t][v];
+    const int parent = (int)(node & 0xffu) - 1;
+    const int nchild = (int)((node >> 8) & 0xffu);
+    const int child0 = (int)((node >> 16) & 0xffu);
+    const int child1 = (int)(node >> 24);
     uint64_t* up_mine = a.up + ((uint64_t)t * R + v) * a.line_stride;
     uint64_t* down_mine = a.down + ((uint64_t)t * R + v) * a.line_stride;
 
@@ -93,32 +97,52 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
         uint64_t idx[K];
         bool ok[K];
         A acc[K];
+        // Loads are unconditional (a lane past the end reads element 0 of the
+        // piece and never uses it): with conditional loads the compiler cannot
+        // count the outstanding memory operations and waits for all of them,
+        // stores included, before each later store.
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             idx[k] = (j0 + (uint64_t)k * bpr) * kBlock + threadIdx.x;
             ok[k] = idx[k] < plen;
-            if (ok[k])
-                acc[k] = E::widen(x[idx[k]]);
+            acc[k] = E::widen(x[ok[k] ? idx[k] : 0]);
         }
-        // reduce up: own value, then each child's subtree value, ascending rank
-        for (int ci = 0; ci < nchild; ++ci) {
-            const int ch = a.tt.child[t][v][ci];
-            const uint64_t* up_ch = a.up + ((uint64_t)t * R + ch) * a.line_stride;
-            const uint64_t* ln[K];
-            bool pend[K];
-            uint32_t d[K];
+        // The inputs are needed at once (added, or stored up by a leaf).  An
+        // explicit wait here tells the compiler that no load is outstanding on
+        // any path, so the stores that forward a line later are not each made
+        // to wait for the stores before them (vmcnt counts both, in order).
+        wait_vmem_all();
+        // reduce up: own value, then each child's subtree value in ascending
+        // rank order.  The lines of both children are polled together (they
+        // arrive at about the same time), so the second child costs no round
+        // trip of its own; the adds still take the children in order.
+        if (nchild > 0) {
+            const uint64_t* up_c0 = a.up + ((uint64_t)t * R + child0) * a.line_stride;
+            const uint64_t* up_c1 = a.up + ((uint64_t)t * R + child1) * a.line_stride;
+            const uint64_t* ln[2 * K];
+            bool pend[2 * K];
+            uint32_t d[2 * K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
-                ln[k] = up_ch + (ok[k] ? idx[k] : 0);
+                ln[k] = up_c0 + (ok[k] ? idx[k] : 0);
+                ln[K + k] = up_c1 + (ok[k] ? idx[k] : 0);
                 pend[k] = ok[k];
+                pend[K + k] = ok[k] && nchild > 1;
                 d[k] = 0;
+                d[K + k] = 0;
             }
-            if (!ll_wait_batch<K>(ln, pend, epoch, deadline, err, d))
+            if (!ll_wait_batch<2 * K>(ln, pend, epoch, deadline, err, d))
                 timed_out = true;
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (ok[k])
                     acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d[k]));
+            if (nchild > 1) {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (ok[k])
+                        acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d[K + k]));
+            }
         }
         if (parent < 0 && a.redop == AR_AVG) {  // the root's sum is final: average it once
 #pragma unroll
@@ -148,18 +172,19 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
                 if (ok[k])
                     acc[k] = E::from_bits(d[k]);
         }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (ok[k])
-                y[idx[k]] = E::narrow(acc[k]);
+        // broadcast down to the children first (they are waiting), then
+        // write this rank's output
         for (int ci = 0; ci < nchild; ++ci) {
-            const int ch = a.tt.child[t][v][ci];
-            uint64_t* down_ch = a.down + ((uint64_t)t * R + ch) * a.line_stride;
+            uint64_t* down_ch = a.down + ((uint64_t)t * R + (ci == 0 ? child0 : child1)) * a.line_stride;
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (ok[k] && publish)
                     ll_store(down_ch + idx[k], E::to_bits(acc[k]), epoch);
         }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (ok[k])
+                y[idx[k]] = E::narrow(acc[k]);
     }
     if (timed_out)
         __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
