@@ -212,6 +212,129 @@ __device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo,
     }
 }
 
+// One reduce step of the scalar path (one element per slot; slot u of this
+// thread is element e[u], stored only if ok[u]).  The same structure as
+// fused_step: the hand-off is loaded after the previous step's store, the
+// next step's input is prefetched into `nxt`, and `own` was prefetched one
+// step earlier.  The empty asm takes the loaded hand-off values as operands,
+// so the compiler waits for them right there (leaving the prefetch in
+// flight) instead of moving each load into its store's branch and waiting
+// for everything outstanding.
+template <class E, int RED, bool LOADX, bool PREFETCH, bool LAST>
+__device__ inline void scalar_step(typename E::A (&x)[kUnroll], const typename E::T (&own)[kUnroll],
+                                   typename E::T (&nxt)[kUnroll], typename E::A* acc,
+                                   typename E::T* fin, const typename E::T* next_row,
+                                   const uint64_t (&e)[kUnroll], const bool (&ok)[kUnroll],
+                                   float R)
+{
+    using A = typename E::A;
+    if constexpr (LOADX) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            x[u] = acc[e[u]];
+    }
+    if constexpr (PREFETCH) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            nxt[u] = next_row[e[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+        __asm__ __volatile__("" ::"v"(x[u]));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        A v = combine<E, RED>(x[u], E::widen(own[u]));
+        if constexpr (LAST)
+            v = finalize<E, RED>(v, R);
+        if (ok[u]) {
+            if constexpr (LAST)
+                fin[e[u]] = E::narrow(v);
+            else
+                acc[e[u]] = v;
+        }
+        x[u] = v;
+    }
+    step_boundary();
+}
+
+// The R-1 reduce steps of a tile on the scalar path (segments shorter than
+// one 128-byte line).  Each active thread has the kUnroll elements j0 + u*js
+// of segment c; one past the end reads the thread's first element instead
+// and stores nothing, so every load is unconditional.  As on the vector path,
+// the input of the next step's rank is loaded before this step's store, into
+// the other of two register sets, so its HBM latency overlaps the hand-off
+// instead of adding to each step.
+template <class E, int RED>
+__device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t len,
+                                           uint64_t j0, uint64_t js)
+{
+    using T = typename E::T;
+    using A = typename E::A;
+    const int R = a.R;
+    const int m = a.m;
+    const float fr = (float)R;
+    const T* send = static_cast<const T*>(a.send) + lo;
+    A* acc = static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + lo;
+    T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
+             (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
+    // x_{c+km}: the input of the rank that adds at step k-2
+    auto row = [&](int k) { return send + (uint64_t)mod_r(c + k * m, R) * a.send_row; };
+    uint64_t e[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * js;
+        ok[u] = j < len;
+        e[u] = ok[u] ? j : j0;
+    }
+    A x[kUnroll];
+    T b0[kUnroll], b1[kUnroll];
+    const T* r1 = row(1);
+    const T* r2 = row(2);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        x[u] = E::widen(r1[e[u]]);
+        b0[u] = r2[e[u]];
+    }
+    if (R == 2) {
+        scalar_step<E, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+        return;
+    }
+    // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
+    scalar_step<E, RED, false, true, false>(x, b0, b1, acc, fin, row(3), e, ok, fr);
+    int s = 1;  // the next step; its input is in b1
+    for (; s + 1 <= R - 3; s += 2) {
+        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 3), e, ok, fr);
+        scalar_step<E, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 4), e, ok, fr);
+    }
+    if (s == R - 3) {
+        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 3), e, ok, fr);
+        scalar_step<E, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+    } else {
+        scalar_step<E, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, e, ok, fr);
+    }
+}
+
+template <class E>
+__device__ inline void fused_reduce_scalar_op(const RingArgs& a, int c, uint64_t lo, uint64_t len,
+                                              uint64_t j0, uint64_t js)
+{
+    switch (a.redop) {
+    case AR_MAX:
+        fused_reduce_scalar<E, AR_MAX>(a, c, lo, len, j0, js);
+        break;
+    case AR_MIN:
+        fused_reduce_scalar<E, AR_MIN>(a, c, lo, len, j0, js);
+        break;
+    case AR_AVG:
+        fused_reduce_scalar<E, AR_AVG>(a, c, lo, len, j0, js);
+        break;
+    default:
+        fused_reduce_scalar<E, AR_SUM>(a, c, lo, len, j0, js);
+        break;
+    }
+}
+
 template <class E, int V>
 __device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
                                              uint64_t js, typename E::A (&x)[kUnroll][V],
@@ -256,14 +379,16 @@ __device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_
     *len = hi - *lo;
     const uint64_t first = k * tile_slots;
     const uint64_t seg_slots = (*len + V - 1) / V;
-    // a tile the segment fills only in part (vector path): spread its n slots
+    // A tile the segment fills only in part.  Vector path: spread its n slots
     // over ceil(n / kUnroll) threads, so that the active threads have whole
-    // slots and take the prefetching path.  The scalar path has no such path
-    // and keeps one slot per thread.
+    // slots and take the prefetching path.  Scalar path: one element per
+    // thread (up to kBlock threads), so that a wave's elements are adjacent
+    // and each step stores them with one instruction (four elements of one
+    // thread in one cache line took four stores: 8.5 against 6 us a call).
     const uint64_t n = seg_slots > first ? seg_slots - first : 0;
-    uint64_t stride = V > 1 ? tile_slots / kUnroll : kBlock;
-    if (V > 1 && n < tile_slots)
-        stride = (n + kUnroll - 1) / kUnroll;
+    uint64_t stride = tile_slots / kUnroll;
+    if (n < tile_slots)
+        stride = V > 1 ? (n + kUnroll - 1) / kUnroll : (n < (uint64_t)kBlock ? n : (uint64_t)kBlock);
     *js = stride;
     *active = threadIdx.x < stride;
     *j0 = first + threadIdx.x;
@@ -305,8 +430,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
                     done = true;
                 }
             }
+            if constexpr (V == 1) {
+                fused_reduce_scalar_op<E>(a, c, lo, len, j0, js);
+                done = true;
+            }
             if (!done) {
-                // the end of a segment, or the scalar path: step by step
+                // the end of a segment on the vector path: step by step
                 for (int s = 0; s <= R - 2; ++s) {
                     const int q = mod_r(c + (s + 2) * m, R);
                     const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);

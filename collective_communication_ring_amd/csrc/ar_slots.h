@@ -13,7 +13,8 @@ namespace ar {
 // narrowed to T; else it is this rank's accumulator.
 // prevA and dstA are the same slots (a hop overwrites the running value in
 // place), and dstT may be too: every slot is read before it is written, by the
-// same thread, so no pointer here is restrict.
+// same thread, so no pointer here is restrict.  Callers guarantee j0 < the
+// number of slots (the thread's first slot is in range).
 template <class E, int V, bool FIRST, bool LAST, int RED>
 __device__ inline void reduce_slots(const typename E::T* prevT, const typename E::A* prevA,
                                     const typename E::T* own, typename E::A* dstA,
@@ -21,6 +22,33 @@ __device__ inline void reduce_slots(const typename E::T* prevT, const typename E
                                     uint64_t jstep, float R)
 {
     using A = typename E::A;
+    if constexpr (V == 1) {
+        // One element per slot.  Every load is unconditional (a slot past the
+        // end reads the thread's first slot again and is dropped) and all come
+        // before the first store: a conditional load, or one after a store,
+        // makes the compiler wait for every earlier store too (vmcnt counts
+        // loads and stores in one in-order count).
+        A xs[kUnroll], ys[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            const uint64_t jj = j < len ? j : j0;
+            xs[u] = FIRST ? E::widen(prevT[jj]) : prevA[jj];
+            ys[u] = E::widen(own[jj]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            if (j < len) {
+                A r = combine<E, RED>(xs[u], ys[u]);
+                if constexpr (LAST)
+                    dstT[j] = E::narrow(finalize<E, RED>(r, R));
+                else
+                    dstA[j] = r;
+            }
+        }
+        return;
+    }
     A x[kUnroll][V], y[kUnroll][V];
     if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
         // every slot is whole: straight-line code, all loads in flight at once
@@ -82,17 +110,26 @@ __device__ inline void reduce_slots(const typename E::T* prevT, const typename E
     }
 }
 
-// Copy kUnroll slots of T from src to dst (bit copy).
+// Copy kUnroll slots of T from src to dst (bit copy).  Callers guarantee j0
+// < the number of slots.
 template <class E, int V>
 __device__ inline void copy_slots(const typename E::T* __restrict__ src,
                                   typename E::T* __restrict__ dst, uint64_t len, uint64_t j0,
                                   uint64_t jstep)
 {
     if constexpr (V == 1) {
+        // loads first and unconditional (as in reduce_slots), then the stores
+        typename E::T r[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t j = j0 + (uint64_t)u * jstep;
+            r[u] = src[j < len ? j : j0];
+        }
+#pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const uint64_t j = j0 + (uint64_t)u * jstep;
             if (j < len)
-                dst[j] = src[j];
+                dst[j] = r[u];
         }
     } else {
         if ((j0 + (kUnroll - 1) * jstep + 1) * V <= len) {
