@@ -136,6 +136,7 @@ struct ar_comm {
     // device facts, read on first use
     bool dev_ready = false;
     int ncu = 0;
+    int nxcd = 1;             // XCDs (accelerator complex dies) of the device
     double ticks_per_us = 100.0;
     int resident_fused[3][2] = {};
     int resident_pipe[3][2] = {};
@@ -168,6 +169,11 @@ int device_ready(ar_comm* c)
         return fail_hip(c, e);
     if (khz > 0)
         c->ticks_per_us = khz / 1000.0;
+    int nxcd = 0;
+    if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && nxcd > 0)
+        c->nxcd = nxcd;
+    else
+        (void)hipGetLastError();  // not known: no packing; keep the error from the next launch check
     for (int d = 0; d < 3; ++d) {
         c->resident_fused[d][0] = resident_ring_fused(d, false);
         c->resident_fused[d][1] = resident_ring_fused(d, true);
@@ -366,6 +372,19 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         const int64_t dflt = (a.op == kOpReduceScatter) ? 8 * (int64_t)c->ncu : (int64_t)c->ncu;
         const int64_t want = c->grid > 0 ? c->grid : dflt;
         grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
+        // On the scalar path (segments shorter than a cache line, so lines are
+        // shared between the tiles of different segments) the tiles stay on one
+        // XCD: workgroups go to the XCDs round-robin (workgroup i to XCD i mod
+        // n), so the launch has n times the workgroups and only every n-th
+        // takes tiles.  Spread over the XCDs each shared line was written from
+        // several L2s (R = 8 fp32, 32-512 B/rank: 6.0-7.0 us a call, 5.5 us
+        // packed).  The vector path gains nothing and loses at 64-128 KiB/rank,
+        // where one XCD's CUs and L2 are too few (6.6 against 5.9 us).
+        a.xcd_pack = 1;
+        if (!vec && c->grid <= 0 && c->nxcd > 1 && tiles * (uint64_t)c->nxcd <= (uint64_t)c->ncu) {
+            a.xcd_pack = c->nxcd;
+            grid = (int)tiles * c->nxcd;
+        }
         e = launch_ring_fused(c->dtype, vec, a, grid, st);
     } else if (launch == AR_LAUNCH_PIPELINED) {
         const int res = c->resident_pipe[c->dtype][vec ? 1 : 0];

@@ -74,6 +74,8 @@ struct RingArgs {
     uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
     uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
     uint64_t tile_slots; // fused form: slots per tile (a multiple of kUnroll, <= kBlock * kUnroll)
+    int xcd_pack;     // fused form: only workgroups whose id is a multiple of this take
+                      //   tiles (the others exit at once), so that they share one XCD
     uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
     uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
     int m;            // this channel's ring stride: rank q receives from q - m

@@ -410,7 +410,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     T* out = static_cast<T*>(a.out);
 
     using A = typename E::A;
-    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    // with xcd_pack = n only every n-th workgroup works: workgroups are
+    // dispatched to the XCDs round-robin, so the working ones share an XCD
+    const uint32_t pack = a.xcd_pack > 1 ? (uint32_t)a.xcd_pack : 1u;
+    if (blockIdx.x % pack)
+        return;
+    const uint64_t wg = blockIdx.x / pack, nwg = gridDim.x / pack;
+    for (uint64_t t = wg; t < ntiles; t += nwg) {
         int c;
         uint64_t lo, len, j0, js;
         bool active, whole;
