@@ -127,7 +127,9 @@ struct ar_comm {
     TreeTable tt{};
     // workspace layout
     size_t off_part = 0, off_up = 0, off_down = 0, off_flags = 0, ws_need = 0;
+    size_t off_tree_epochs = 0;
     uint64_t tree_lines = 0;  // lines per (tree, rank)
+    uint64_t tree_groups = 0; // epoch words per tree: one per kTreeGroup lines
     uint64_t flag_stride = 0; // pipelined ring: ready flags per segment
     size_t off_rll = 0;       // ring-LL line slots
     uint64_t rll_cap = 0;     // ring-LL: lines per (sender, segment) per launch
@@ -439,6 +441,8 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     a.out = recv;
     a.up = reinterpret_cast<uint64_t*>(c->ws + c->off_up);
     a.down = reinterpret_cast<uint64_t*>(c->ws + c->off_down);
+    a.epochs = reinterpret_cast<uint32_t*>(c->ws + c->off_tree_epochs);
+    a.line_groups = c->tree_groups;
     a.ctrl = reinterpret_cast<uint32_t*>(c->ws);
     a.N = N;
     a.H = (N + 1) / 2;
@@ -556,7 +560,7 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     }
     c->channels = std::min<int64_t>(std::max<int64_t>(1, env_int("AR_CHANNELS", 1)), c->nstrides);
     // workspace: control block | hand-off accumulators [cap] (A) | tree LL up
-    // | down | pipelined flags | ring-LL lines
+    // | down | tree epochs | pipelined flags | ring-LL lines
     const size_t cap1 = count ? count : 1;
     c->tree_lines = std::min<uint64_t>((cap1 + 1) / 2, kTreeLinesCap);
     size_t off = kAlign;  // control block
@@ -566,6 +570,9 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
     c->off_down = off;
     off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
+    c->off_tree_epochs = off;
+    c->tree_groups = (c->tree_lines + kTreeGroup - 1) / kTreeGroup;
+    off = align_up(off + 2 * (size_t)c->tree_groups * 4, kAlign);
     c->off_flags = off;
     // one flag per (segment, chunk); a chunk is at least one workgroup pass
     // of the scalar path (kBlock * kUnroll elements)
@@ -597,7 +604,8 @@ int ar_set_workspace(ar_comm_t c, void* dev, size_t bytes, void* stream)
     hipStream_t st = static_cast<hipStream_t>(stream);
     c->ws = static_cast<char*>(dev);
     c->ws_bytes = bytes;
-    // clear the control block and every LL line (flag 0 never matches an epoch)
+    // clear the control block, every LL line and the tree epochs (flags start
+    // at 1, so a cleared line never matches)
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws), 0u, kCtrlWords, st);
     if (e == hipSuccess)
         e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,

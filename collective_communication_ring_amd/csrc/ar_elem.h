@@ -212,14 +212,14 @@ __device__ inline void ll_store(uint64_t* line, uint32_t data, uint32_t flag)
 }
 
 // Wait for K lines at once: every pass issues the loads of all lines still
-// pending, so the K waits overlap instead of adding up.  Lines with
-// pending[k] == false on entry are skipped.  Gives up (returns false) when
-// `deadline` passes or the error word is set; data[k] of a line that never
-// arrived is left 0.
+// pending, so the K waits overlap instead of adding up.  Line k is complete
+// when its flag half equals flag[k].  Lines with pending[k] == false on entry
+// are skipped.  Gives up (returns false) when `deadline` passes or the error
+// word is set; data[k] of a line that never arrived is left 0.
 template <int K>
-__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pending)[K],
-                                     uint32_t flag, uint64_t deadline, const uint32_t* err,
-                                     uint32_t (&data)[K])
+__device__ inline bool ll_wait_lines(const uint64_t* const (&line)[K], bool (&pending)[K],
+                                     const uint32_t (&flag)[K], uint64_t deadline,
+                                     const uint32_t* err, uint32_t (&data)[K])
 {
     for (uint32_t spin = 0;; ++spin) {
         uint64_t v[K];
@@ -235,7 +235,7 @@ __device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pe
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             if (pending[k]) {
-                if ((uint32_t)(v[k] >> 32) == flag) {
+                if ((uint32_t)(v[k] >> 32) == flag[k]) {
                     data[k] = (uint32_t)v[k];
                     pending[k] = false;
                 } else {
@@ -253,6 +253,19 @@ __device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pe
             __builtin_amdgcn_s_sleep(1);
         }
     }
+}
+
+// The same with one flag for every line.
+template <int K>
+__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pending)[K],
+                                     uint32_t flag, uint64_t deadline, const uint32_t* err,
+                                     uint32_t (&data)[K])
+{
+    uint32_t f[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        f[k] = flag;
+    return ll_wait_lines<K>(line, pending, f, deadline, err, data);
 }
 
 // Keeps the compiler from carrying a value stored by one ring step into the

@@ -14,9 +14,9 @@ constexpr int kMaxRanks = 64;
 
 // Words of the control block at the start of the workspace (uint32 each).
 enum CtrlWord {
-    kCtrlTreeEpoch = 0,  // LL flag value of the last completed tree call
+    kCtrlTreeEpoch = 0,  // unused (the tree keeps one epoch per group of lines)
     kCtrlError = 1,      // non-zero: a bounded wait expired (watchdog)
-    kCtrlTreeDone = 2,   // workgroups of the running tree call that finished
+    kCtrlTreeDone = 2,   // unused
     kCtrlPipeDone = 3,   // workgroups of the running pipelined call that finished
     kCtrlRingLLEpoch = 4, // ring-LL: epoch of the last completed launch
     kCtrlRingLLDone = 5,  // ring-LL: workgroups of the running launch that finished
@@ -93,6 +93,9 @@ struct TreeArgs {
     void* out;
     uint64_t* up;     // [2 trees][R][piece_half] LL lines, child -> parent
     uint64_t* down;   // [2 trees][R][piece_half] LL lines, parent -> child
+    uint32_t* epochs; // [2 trees][line_groups]: the flag of the last call that used each
+                      //   group of kTreeGroup lines (0: never)
+    uint64_t line_groups;
     uint32_t* ctrl;
     uint64_t N;
     uint64_t H;       // tree A's half: [0, H); tree B: [H, N)
@@ -161,6 +164,7 @@ int resident_ring_ll(int dtype);
 #endif
 constexpr int kBlock = AR_BLOCK;   // threads per workgroup (4 wave64 by default)
 constexpr int kUnroll = AR_UNROLL; // 16-byte vectors per thread per pass
+constexpr int kTreeGroup = 64;   // LL lines per tree epoch (one wave's lines of a sub-block)
 constexpr int kTreeEPT = 4;      // LL lines per thread per tree kernel pass
 constexpr int kRingLLEPT = 4;    // LL lines per thread per ring-LL pass
 

@@ -23,10 +23,20 @@
 // workgroup of the grid must be resident at once (a node spins on its
 // children), which the host guarantees by capping the grid at the occupancy
 // limit; every wait is also bounded in time (the watchdog) and a timeout sets
-// the error word instead of hanging.  The epoch lives in the control block:
-// each workgroup reads it at start, and the last workgroup to finish advances
-// it, so consecutive launches on a stream use fresh flags and a replayed
-// graph does too.
+// the error word instead of hanging.
+//
+// Epochs: every group of kTreeGroup lines (one wave's lines of a sub-block, the
+// same positions on every rank) has its own epoch word; a launch uses that
+// word plus one as the flag of the group's lines, and the root's wave stores
+// the new value when it has sent the group's result down.  By then every
+// rank's wave of the group has read the old value: each stored an up line
+// carrying it, and the root has received them all (directly or through its
+// children).  So no launch ever reuses a flag a line may still hold, a
+// replayed graph uses fresh flags too, and the launch needs no counter of
+// finished workgroups (an atomic round trip at the end of every workgroup).
+// Groups are fixed by line position, so launches with different grids share
+// them consistently; a group a launch does not touch keeps its epoch, and
+// its lines only carry flags up to it.
 #include "ar_elem.h"
 #include "ar_internal.h"
 
@@ -59,13 +69,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     const int t = blockIdx.x / (R * bpr);
     const int v = (blockIdx.x / bpr) % R;
     const int b = blockIdx.x % bpr;
-
-    // Every wave reads the epoch itself (one request per wave, no barrier):
-    // the value is first needed at the first line stored or polled, so the
-    // load overlaps the input loads instead of preceding them.  It cannot
-    // change during the launch: only the last workgroup to finish writes it.
-    const uint32_t epoch = __hip_atomic_load(&a.ctrl[kCtrlTreeEpoch], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
     const uint64_t deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
     uint32_t* err = &a.ctrl[kCtrlError];
 
@@ -85,32 +88,41 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     const int child1 = (int)(node >> 24);
     uint64_t* up_mine = a.up + ((uint64_t)t * R + v) * a.line_stride;
     uint64_t* down_mine = a.down + ((uint64_t)t * R + v) * a.line_stride;
+    uint32_t* epochs = a.epochs + (uint64_t)t * a.line_groups;
 
     constexpr int K = kTreeEPT;
     const bool publish = (v != a.mute_rank);
+    const uint64_t wave_first = threadIdx.x & ~(uint64_t)(kTreeGroup - 1);
     bool timed_out = false;
     // sub-blocks of kBlock lines: sub-block j belongs to workgroup j mod bpr of
     // this (tree, rank); a thread takes K of its workgroup's sub-blocks at once
     // and waits for their lines together
     const uint64_t nsub = (plen + kBlock - 1) / kBlock;
     for (uint64_t j0 = (uint64_t)b; j0 < nsub; j0 += (uint64_t)bpr * K) {
-        uint64_t idx[K];
-        bool ok[K];
+        uint64_t idx[K], grp[K];
+        bool ok[K], wave_ok[K];
         A acc[K];
+        uint32_t flag[K];
         // Loads are unconditional (a lane past the end reads element 0 of the
-        // piece and never uses it): with conditional loads the compiler cannot
-        // count the outstanding memory operations and waits for all of them,
-        // stores included, before each later store.
+        // piece, and a wave past the end group 0's epoch, and never uses
+        // them): with conditional loads the compiler cannot count the
+        // outstanding memory operations and waits for all of them, stores
+        // included, before each later store.
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            idx[k] = (j0 + (uint64_t)k * bpr) * kBlock + threadIdx.x;
+            const uint64_t base = (j0 + (uint64_t)k * bpr) * kBlock;
+            idx[k] = base + threadIdx.x;
             ok[k] = idx[k] < plen;
+            wave_ok[k] = base + wave_first < plen;  // the wave has lines in this sub-block
+            grp[k] = wave_ok[k] ? (base + wave_first) / kTreeGroup : 0;
             acc[k] = E::widen(x[ok[k] ? idx[k] : 0]);
+            flag[k] = __hip_atomic_load(&epochs[grp[k]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
         }
-        // The inputs are needed at once (added, or stored up by a leaf).  An
-        // explicit wait here tells the compiler that no load is outstanding on
-        // any path, so the stores that forward a line later are not each made
-        // to wait for the stores before them (vmcnt counts both, in order).
+        // The inputs and epochs are needed at once (added, or stored up by a
+        // leaf).  An explicit wait here tells the compiler that no load is
+        // outstanding on any path, so the stores that forward a line later
+        // are not each made to wait for the stores before them (vmcnt counts
+        // both, in order).
         wait_vmem_all();
         // reduce up: own value, then each child's subtree value in ascending
         // rank order.  The lines of both children are polled together (they
@@ -121,6 +133,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
             const uint64_t* up_c1 = a.up + ((uint64_t)t * R + child1) * a.line_stride;
             const uint64_t* ln[2 * K];
             bool pend[2 * K];
+            uint32_t fl[2 * K];
             uint32_t d[2 * K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
@@ -128,10 +141,12 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
                 ln[K + k] = up_c1 + (ok[k] ? idx[k] : 0);
                 pend[k] = ok[k];
                 pend[K + k] = ok[k] && nchild > 1;
+                fl[k] = flag[k];
+                fl[K + k] = flag[k];
                 d[k] = 0;
                 d[K + k] = 0;
             }
-            if (!ll_wait_batch<2 * K>(ln, pend, epoch, deadline, err, d))
+            if (!ll_wait_lines<2 * K>(ln, pend, fl, deadline, err, d))
                 timed_out = true;
 #pragma unroll
             for (int k = 0; k < K; ++k)
@@ -154,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (ok[k] && publish)
-                    ll_store(up_mine + idx[k], E::to_bits(acc[k]), epoch);
+                    ll_store(up_mine + idx[k], E::to_bits(acc[k]), flag[k]);
             // broadcast down: the root's value arrives from the parent
             const uint64_t* ln[K];
             bool pend[K];
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
                 pend[k] = ok[k];
                 d[k] = 0;
             }
-            if (!ll_wait_batch<K>(ln, pend, epoch, deadline, err, d))
+            if (!ll_wait_lines<K>(ln, pend, flag, deadline, err, d))
                 timed_out = true;
 #pragma unroll
             for (int k = 0; k < K; ++k)
@@ -179,33 +194,26 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 #pragma unroll
             for (int k = 0; k < K; ++k)
                 if (ok[k] && publish)
-                    ll_store(down_ch + idx[k], E::to_bits(acc[k]), epoch);
+                    ll_store(down_ch + idx[k], E::to_bits(acc[k]), flag[k]);
         }
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (ok[k])
                 y[idx[k]] = E::narrow(acc[k]);
+        // the root closes each group it finished: every rank's wave of the
+        // group has read its epoch (see the top of this file).  Done even by a
+        // muted root, so that a later launch never reuses this flag.
+        if (parent < 0 && (threadIdx.x & (kTreeGroup - 1)) == 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                if (wave_ok[k])
+                    __hip_atomic_store(&epochs[grp[k]], flag[k], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (timed_out)
         __hip_atomic_fetch_or(err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
-
-    // the last workgroup to finish publishes the epoch for the next launch
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        // Only the next launch on the stream reads the counter and the epoch, and
-        // the kernel boundary orders this launch's memory before it, so relaxed
-        // atomics suffice (acquire-release here would write back and invalidate
-        // the XCD's L2 in every workgroup).
-        uint32_t done = __hip_atomic_fetch_add(&a.ctrl[kCtrlTreeDone], 1u, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1) {
-            __hip_atomic_store(&a.ctrl[kCtrlTreeDone], 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ctrl[kCtrlTreeEpoch], epoch, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 template <int DT>

@@ -221,6 +221,23 @@ def test_tree_ll_ragged(env, dtype, R):
             assert y.tobytes() == ref.tobytes(), (R, N)
 
 
+def test_tree_epochs_across_sizes(env):
+    """The tree keeps one epoch per group of 64 lines.  Calls of different
+    sizes on one communicator use different grids and different sets of
+    groups (a group one call leaves alone is used again by a later one, over
+    lines that still hold older flags), and the largest takes two launches;
+    every call must match the oracle."""
+    api, orc = env["api"], env["orc"]
+    R, Nmax = 8, 2 * 65536 + 7
+    comm = api.Comm(R, Nmax, "float32", "tree", "ll", device=env["dev"])
+    for N in (Nmax, 1, 300, 40_000, 3, Nmax, 5000, 129, 40_000, 1, 70_001):
+        x = rand_input(env, "float32", R, N, seed=N + 1)
+        out = poisoned(env, (R, N), "float32")
+        comm.allreduce(to_dev(env, x, "float32"), out)
+        assert from_dev(env, out, "float32").tobytes() == orc.tree_allreduce(x).tobytes(), N
+    assert comm.check() == api.AR_SUCCESS
+
+
 def test_tree_order_pin(env):
     # Tree A at R = 8: P(2) = x2 + x1 + x3 = (T + 1) -> T, T - T = 0 with
     # x2 = T, x1 = 1, x3 = -T; exact sum 1.
@@ -415,11 +432,13 @@ def test_cfg3_largest_size_sampled(env, launch):
 
 # ---------------------------------------------------------------- watchdog
 
-@pytest.mark.parametrize("variant", ["tree", "pipelined", "ll"])
-def test_watchdog_reports_timeout_and_recovers(env, variant):
+@pytest.mark.parametrize("variant,mute", [("tree", 3), ("tree", 0), ("pipelined", 3), ("ll", 3)])
+def test_watchdog_reports_timeout_and_recovers(env, variant, mute):
     """Forced from the host: one logical rank skips publishing, so its
     consumers' bounded waits (5 ms here) expire.  The kernel still finishes,
-    ar_check reports AR_ERR_TIMEOUT once, and the next call is correct."""
+    ar_check reports AR_ERR_TIMEOUT once, and the next call is correct.  Rank
+    0 is tree A's root: muted, it sends nothing down, but must still advance
+    its line groups' epochs so that the next call uses fresh flags."""
     import time
     torch, api, orc = env["torch"], env["api"], env["orc"]
     R, N = 8, 4096
@@ -435,7 +454,7 @@ def test_watchdog_reports_timeout_and_recovers(env, variant):
     comm.allreduce(send, recv)            # warm (first call initialises the device facts)
     torch.cuda.synchronize()
     assert comm.check() == api.AR_SUCCESS
-    comm.set_option(api.AR_OPT_DEBUG_MUTE_RANK, 3)
+    comm.set_option(api.AR_OPT_DEBUG_MUTE_RANK, mute)
     t0 = time.perf_counter()
     comm.allreduce(send, recv)
     torch.cuda.synchronize()
