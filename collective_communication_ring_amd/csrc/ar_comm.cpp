@@ -295,7 +295,16 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
         a.piece_lo = lo;
         a.piece_len = std::min<uint64_t>(c->rll_cap, a.sub_len - lo);
         a.per_rank_wg = (int)ll_grid_per_rank(a.piece_len, a.R, c->ncu, kRingLLEPT, gmax);
-        hipError_t e = launch_ring_ll(c->dtype, a, a.per_rank_wg * a.R, st);
+        // sets of R workgroups on one XCD each, the grid rounded up to whole
+        // rows of sets; every workgroup must still be resident
+        a.xcd_sets = c->nxcd;
+        while (a.per_rank_wg > 1 &&
+               ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > c->resident_rll[c->dtype])
+            --a.per_rank_wg;
+        if (ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > c->resident_rll[c->dtype])
+            a.xcd_sets = 1;
+        const int64_t grid = ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R);
+        hipError_t e = launch_ring_ll(c->dtype, a, (int)grid, st);
         if (e != hipSuccess)
             return fail_hip(c, e);
         ++launches;
@@ -469,7 +478,15 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
         a.piece_len = piece;
         const uint64_t plen = std::min<uint64_t>(piece, half - lo);
         a.blocks_per_rank = (int)ll_grid_per_rank(plen, 2 * c->R, c->ncu, kTreeEPT, bpr_max);
-        const int grid = 2 * c->R * a.blocks_per_rank;
+        // sets of R workgroups on one XCD each (ll_set_of), the grid rounded
+        // up to whole rows of sets; every workgroup must still be resident
+        a.xcd_sets = c->nxcd;
+        while (a.blocks_per_rank > 1 &&
+               ll_grid_for_sets(2 * (int64_t)a.blocks_per_rank, a.xcd_sets, c->R) > res)
+            --a.blocks_per_rank;
+        if (ll_grid_for_sets(2 * (int64_t)a.blocks_per_rank, a.xcd_sets, c->R) > res)
+            a.xcd_sets = 1;
+        const int grid = (int)ll_grid_for_sets(2 * (int64_t)a.blocks_per_rank, a.xcd_sets, c->R);
         if (grid > res)
             return AR_ERR_INTERNAL;
         hipError_t e = launch_tree_ll(c->dtype, a, grid, st);

@@ -104,6 +104,7 @@ struct TreeArgs {
     uint64_t line_stride; // lines per (tree, rank) in up/down
     int R;
     int blocks_per_rank;  // workgroups per (tree, rank)
+    int xcd_sets;         // XCDs the (tree, block) sets of R workgroups are dealt to
     int mute_rank;        // testing only: rank that skips publishing (-1: none)
     int redop;            // ar_redop_t
     uint64_t timeout_ticks;
@@ -131,6 +132,7 @@ struct RingLLArgs {
     int R;
     int op;
     int per_rank_wg;
+    int xcd_sets;        // XCDs the sets of R workgroups (one per rank) are dealt to
     int mute_rank;
     int redop;
     uint64_t timeout_ticks;
@@ -164,6 +166,27 @@ int resident_ring_ll(int dtype);
 #endif
 constexpr int kBlock = AR_BLOCK;   // threads per workgroup (4 wave64 by default)
 constexpr int kUnroll = AR_UNROLL; // 16-byte vectors per thread per pass
+// LL kernels' placement: a launch is made of sets of R workgroups (one per
+// rank) that exchange lines only with each other.  Workgroups are dispatched
+// to the XCDs round-robin (workgroup x to XCD x mod n), so set j is put on
+// XCD j mod n: workgroup x plays rank (x / n) mod R of set x mod n + n *
+// ((x / n) / R), and a line then travels between CUs of one XCD (LL
+// ping-pong probe: ~0.37 us one way within an XCD, ~0.58 us between XCDs).
+// The grid is rounded up to whole rows of n sets; workgroups past the last
+// set have no work.
+__host__ __device__ inline uint32_t ll_set_of(uint32_t x, uint32_t n, uint32_t R)
+{
+    return x % n + n * ((x / n) / R);
+}
+__host__ __device__ inline uint32_t ll_rank_of(uint32_t x, uint32_t n, uint32_t R)
+{
+    return (x / n) % R;
+}
+inline int64_t ll_grid_for_sets(int64_t sets, int n, int R)
+{
+    return (int64_t)n * R * ((sets + n - 1) / n);
+}
+
 constexpr int kTreeGroup = 64;   // LL lines per tree epoch (one wave's lines of a sub-block)
 constexpr int kTreeEPT = 4;      // LL lines per thread per tree kernel pass
 constexpr int kRingLLEPT = 4;    // LL lines per thread per ring-LL pass

@@ -45,9 +45,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     using T = typename E::T;
     using A = typename E::A;
     const int R = a.R;
-    const int q = blockIdx.x % R;
-    const int g = blockIdx.x / R;
+    // set g of R workgroups (one per rank), all on one XCD (ll_set_of)
+    const uint32_t n = a.xcd_sets > 1 ? (uint32_t)a.xcd_sets : 1u;
+    const int q = (int)ll_rank_of(blockIdx.x, n, (uint32_t)R);
+    const int g = (int)ll_set_of(blockIdx.x, n, (uint32_t)R);
     const int G = a.per_rank_wg;
+    const bool idle = g >= G;  // past the last set: no lines, only the done counter
     const int m = a.m;
     const int p = mod_r(q - m, R);
     const int nsteps = (OP == kOpAllReduce) ? 2 * (R - 1) : (OP == kOpReduceScatter) ? R - 1 : R;
@@ -66,7 +69,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     bool timed_out = false;
     constexpr int K = kRingLLEPT;
 
-    for (int s = 0; s < nsteps; ++s) {
+    for (int s = 0; s < (idle ? 0 : nsteps); ++s) {
         const int c = (OP == kOpAllGather) ? mod_r(q - s * m, R) : mod_r(q - (s + 2) * m, R);
         uint64_t lo, hi;
         seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);

@@ -19,7 +19,8 @@
 // load of the line bypass the non-coherent per-XCD L2 state, so a line written
 // on one XCD is seen by a poller on another.
 //
-// One launch per piece: grid = 2 trees x R ranks x blocks_per_rank.  Every
+// One launch per piece: 2 trees x blocks_per_rank sets of R workgroups (one
+// per rank), each set on one XCD (ll_set_of).  Every
 // workgroup of the grid must be resident at once (a node spins on its
 // children), which the host guarantees by capping the grid at the occupancy
 // limit; every wait is also bounded in time (the watchdog) and a timeout sets
@@ -66,9 +67,14 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     using A = typename E::A;
     const int R = a.R;
     const int bpr = a.blocks_per_rank;
-    const int t = blockIdx.x / (R * bpr);
-    const int v = (blockIdx.x / bpr) % R;
-    const int b = blockIdx.x % bpr;
+    // set (tree t, block b) of R workgroups, all on one XCD (ll_set_of)
+    const uint32_t n = a.xcd_sets > 1 ? (uint32_t)a.xcd_sets : 1u;
+    const uint32_t set = ll_set_of(blockIdx.x, n, (uint32_t)R);
+    if (set >= 2u * (uint32_t)bpr)
+        return;  // past the last set
+    const int v = (int)ll_rank_of(blockIdx.x, n, (uint32_t)R);
+    const int t = (int)(set / (uint32_t)bpr);
+    const int b = (int)(set % (uint32_t)bpr);
     const uint64_t deadline = (uint64_t)wall_clock64() + a.timeout_ticks;
     uint32_t* err = &a.ctrl[kCtrlError];
 
