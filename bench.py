@@ -136,7 +136,7 @@ def cpu_baseline(x, R, N, s, target_s=12.0, strides=None):
         t0 = time.perf_counter()
         y = oracle.ring_allreduce(x, strides=strides)
         ts.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > target_s or len(ts) >= 20:
+        if time.perf_counter() - t_start > target_s or len(ts) >= 100:
             break
     t = sum(ts) / len(ts)
     algbw = N * s / t / 1e9
