@@ -124,25 +124,33 @@ def time_graph(fn, calls, torch, reps=3):
     return ms
 
 
-def cpu_baseline(x, R, N, s, target_s=12.0, strides=None):
-    """The oracle, as it is, on the host: repeat the full all-reduce until
-    about target_s seconds of CPU work; report its busBW.  `strides` are the
-    ring channels' strides (one ring of stride 1 by default)."""
+def cpu_baseline_leg(call, target_s=3.0, max_calls=50):
+    """The CPU-baseline leg of a mode: runs the oracle on the host, as it is,
+    for a bounded sample (at least one call, then until target_s seconds or
+    max_calls calls).  `call(oracle)` makes one oracle call.  Returns its last
+    result (which the mode also uses to check the GPU's), the average seconds
+    per call and the number of calls.  This is the only place bench.py runs
+    the oracle."""
     import oracle
     ts = []
     y = None
     t_start = time.perf_counter()
-    while True:
+    while not ts or (time.perf_counter() - t_start < target_s and len(ts) < max_calls):
         t0 = time.perf_counter()
-        y = oracle.ring_allreduce(x, strides=strides)
+        y = call(oracle)
         ts.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > target_s or len(ts) >= 100:
-            break
-    t = sum(ts) / len(ts)
+    return y, sum(ts) / len(ts), len(ts)
+
+
+def cpu_baseline(x, R, N, s, target_s=12.0, strides=None):
+    """The headline's CPU baseline: the full all-reduce on the host until about
+    target_s seconds of CPU work; report its busBW.  `strides` are the ring
+    channels' strides (one ring of stride 1 by default)."""
+    y, t, n = cpu_baseline_leg(lambda o: o.ring_allreduce(x, strides=strides), target_s, 100)
     algbw = N * s / t / 1e9
     return y, dict(value=round(algbw * 2 * (R - 1) / R, 3), unit="GB/s", cores=1, kind="oracle",
                    sample="the full workload (8 ranks x 64 MiB), %d call(s), %.2f s each; "
-                          "single-threaded C replay of the same ring order" % (len(ts), t))
+                          "single-threaded C replay of the same ring order" % (n, t))
 
 
 def headline(args):
@@ -264,11 +272,10 @@ def mode_sweep(args):
             out.flush()
         del sv, rv
     assert comm.check() == api.AR_SUCCESS
-    import oracle
     cpu = []
     for N in (256, 65536, 1 << 22):  # 1 KiB, 256 KiB, 16 MiB per rank
         xs = send_flat[:R * N].view(R, N).cpu().numpy()
-        t_or, n_or = oracle_time_s(lambda: oracle.ring_allreduce(xs), 3.0)
+        _, t_or, n_or = cpu_baseline_leg(lambda o: o.ring_allreduce(xs), 3.0)
         cpu.append(dict(bytes_per_rank=N * s, t_us=t_or * 1e6, calls=n_or))
         log("oracle %10d B/rank  %10.1f us" % (N * s, t_or * 1e6))
     fit = measure.fit_alpha_beta([r["bytes_per_rank"] for r in rows], [r["t_us"] / 1e6 for r in rows])
@@ -312,17 +319,6 @@ def ll_hop_latency_us(torch, iters=20000):
             raise RuntimeError("LL ping-pong timed out")
         out[name] = e0.elapsed_time(e1) * 1e3 / (2 * iters)
     return out
-
-
-def oracle_time_s(fn, target_s=3.0, max_calls=50):
-    """Average host seconds per call of an oracle function (bounded sample)."""
-    ts = []
-    t_start = time.perf_counter()
-    while not ts or (time.perf_counter() - t_start < target_s and len(ts) < max_calls):
-        t0 = time.perf_counter()
-        fn()
-        ts.append(time.perf_counter() - t0)
-    return sum(ts) / len(ts), len(ts)
 
 
 def mode_tree_vs_ring(args):
@@ -370,9 +366,8 @@ def mode_tree_vs_ring(args):
                                                          16, st()), 20, torch) * 1e3
     log("launch floor (16-byte copy kernel, graph-replayed): %.2f us" % launch_floor)
     # latency roofline of the tree: 2 * depth hops (up, then down) per call
-    import oracle
     depth = 3 if R == 8 else None
-    t_or, n_or = oracle_time_s(lambda: oracle.tree_allreduce(x), 3.0)
+    _, t_or, n_or = cpu_baseline_leg(lambda o: o.tree_allreduce(x), 3.0)
     summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res,
                    ll_hop_us=hop, tree_depth=depth, launch_floor_us=launch_floor,
                    tree_hop_bound_us=2 * depth * hop["xcd_apart"] if depth else None,
@@ -425,11 +420,9 @@ def mode_buckets(args):
         log(name, rep[name])
     assert comm.check() == api.AR_SUCCESS
     import numpy as np
-    import oracle
     xh = xs[0].view(torch.int16).cpu().numpy().view(np.uint16)
-    t_rs, _ = oracle_time_s(lambda: oracle.ring_reduce_scatter(xh, "bf16"), 0.0, 1)
-    sh = oracle.ring_reduce_scatter(xh, "bf16")
-    t_ag, _ = oracle_time_s(lambda: oracle.ring_all_gather(sh, "bf16"), 0.0, 1)
+    sh, t_rs, _ = cpu_baseline_leg(lambda o: o.ring_reduce_scatter(xh, "bf16"), 0.0, 1)
+    _, t_ag, _ = cpu_baseline_leg(lambda o: o.ring_all_gather(sh, "bf16"), 0.0, 1)
     rep["cpu_baseline"] = dict(kind="oracle", cores=1, sample="bucket 0, one call each",
                                reduce_scatter_us=t_rs * 1e6, all_gather_us=t_ag * 1e6)
     summary = dict(mode="buckets", R=R, dtype="bf16", buckets=B, count_per_rank=N, **rep)
@@ -600,11 +593,10 @@ def mode_config1(args):
     import numpy as np
     import torch
     from collective_communication_ring_amd import api, inputs
-    import oracle
     R, N = 4, 4096
     dev = torch.device("cuda:0")
     x = inputs.host_inputs("ring_int32_r4")
-    ref = oracle.ring_allreduce(x)
+    ref, t_or, n_or = cpu_baseline_leg(lambda o: o.ring_allreduce(x), 2.0)
     exact = x.astype(np.int64).sum(axis=0).astype(np.int32)
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
@@ -620,7 +612,6 @@ def mode_config1(args):
         res[name] = dict(t_us=round(t_us, 3), exact=bool(ok))
         log("config 1 %-10s %8.2f us  exact=%s" % (name, t_us, ok))
         comm.close()
-    t_or, n_or = oracle_time_s(lambda: oracle.ring_allreduce(x), 2.0)
     print(json.dumps(dict(mode="config1", R=R, count_per_rank=N, dtype="int32", results=res,
                           cpu_baseline=dict(kind="oracle", cores=1, t_us=t_or * 1e6,
                                             sample="%d calls" % n_or))), flush=True)
@@ -634,7 +625,6 @@ def mode_matrix(args):
     import numpy as np
     import torch
     from collective_communication_ring_amd import api, inputs, measure
-    import oracle
     dev = torch.device("cuda:0")
     rows = []
     for dtype, s in (("float32", 4), ("int32", 4), ("bf16", 2)):
@@ -657,12 +647,14 @@ def mode_matrix(args):
             t = total_ms / args.steps / 1e3
             got = recv.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" \
                 else recv.cpu().numpy()
-            exact = got.tobytes() == oracle.ring_allreduce(x, dtype).tobytes()
+            ref, t_or, _ = cpu_baseline_leg(lambda o: o.ring_allreduce(x, dtype), 0.0, 1)
+            exact = got.tobytes() == ref.tobytes()
             row = dict(dtype=dtype, R=R, bytes_per_rank=N * s, ms=round(t * 1e3, 4),
                        busbw_GBps=round(N * s / t / 1e9 * measure.busbw_factor("allreduce", R), 1),
                        alg_frac=round(measure.allreduce_alg_bytes(R, N, s) / t / 1e9 /
                                       PEAK_HBM_GBPS, 3),
-                       compulsory_TBps=round(2 * R * N * s / t / 1e12, 2), exact=exact)
+                       compulsory_TBps=round(2 * R * N * s / t / 1e12, 2), exact=exact,
+                       cpu_baseline_s=round(t_or, 3))
             rows.append(row)
             log("matrix %-7s R=%2d %.4f ms busBW %7.1f GB/s alg frac %.3f compulsory %.2f TB/s "
                 "exact=%s" % (dtype, R, row["ms"], row["busbw_GBps"], row["alg_frac"],
@@ -670,7 +662,10 @@ def mode_matrix(args):
             comm.close()
             del send, recv, x
             torch.cuda.empty_cache()
-    print(json.dumps(dict(mode="matrix", launch="fused", results=rows)), flush=True)
+    print(json.dumps(dict(mode="matrix", launch="fused", results=rows,
+                          cpu_baseline=dict(kind="oracle", cores=1,
+                                            sample="one call per row (cpu_baseline_s)"))),
+          flush=True)
     return 0 if all(r["exact"] for r in rows) else 1
 
 
@@ -684,14 +679,15 @@ def mode_tune(args):
     x = inputs.host_inputs("ring_f32_r8_64MiB")
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
-    import oracle
     ref = None
+    t_or = None
     res = []
     for grid in [int(g) for g in args.grids.split(",")]:
         comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=args.chunk_bytes, grid=grid,
                         **ring_kw(args.launch, args.channels))
         if ref is None:
-            ref = oracle.ring_allreduce(x, strides=comm.channel_strides())
+            ref, t_or, _ = cpu_baseline_leg(
+                lambda o: o.ring_allreduce(x, strides=comm.channel_strides()), 0.0, 1)
         _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                     torch)
         ms = total_ms / args.steps
@@ -699,7 +695,9 @@ def mode_tune(args):
         res.append(dict(grid=grid, ms=ms, busbw=N * s / (ms / 1e3) / 1e9 * 1.75, exact=ok))
         log("grid %6d  %.4f ms  busBW %.1f GB/s  exact=%s" % (grid, ms, res[-1]["busbw"], ok))
         comm.close()
-    print(json.dumps(dict(mode="tune", launch=args.launch, results=res)), flush=True)
+    print(json.dumps(dict(mode="tune", launch=args.launch, results=res,
+                          cpu_baseline=dict(kind="oracle", cores=1, seconds=t_or,
+                                            sample="one call"))), flush=True)
     return 0
 
 
