@@ -273,7 +273,7 @@ def mode_sweep(args):
         del sv, rv
     assert comm.check() == api.AR_SUCCESS
     cpu = []
-    for N in (256, 65536, 1 << 22):  # 1 KiB, 256 KiB, 16 MiB per rank
+    for N in [n for n in (256, 65536, 1 << 22) if n <= Nmax]:  # 1 KiB, 256 KiB, 16 MiB per rank
         xs = send_flat[:R * N].view(R, N).cpu().numpy()
         _, t_or, n_or = cpu_baseline_leg(lambda o: o.ring_allreduce(xs), 3.0)
         cpu.append(dict(bytes_per_rank=N * s, t_us=t_or * 1e6, calls=n_or))
