@@ -223,11 +223,23 @@ int resolve_algo(const ar_comm* c, size_t count)
 // start must be 16-byte aligned in both T and accumulator units.  Segments
 // shorter than one 128-byte cache line take the scalar path: measured faster
 // there (R = 8 fp32, 128-512 B per rank: 8.7 against 9.5 us fused).
+// Segments shorter than this take the scalar path (one element per lane)
+// in every ring form.  Its tiles put one element on each lane and, in the
+// fused form, stay on one XCD, so a short segment's few loads and stores per
+// step are single instructions; 16-byte slots only pay once a segment has
+// enough of them (R = 8 fp32, fused, graph-replayed: 1-8 KiB per rank 6.0 /
+// 6.1 / 5.8 / 5.9 us with the vector path from 128-byte segments, 5.3 / 5.2
+// / 5.3 / 5.5 us with this threshold; the step form 30 -> 27.5 us there; a
+// 8 KiB threshold was slower at 32 KiB per rank and at R = 4, 16 KiB).
+#ifndef AR_SCALAR_SEG_BYTES
+#define AR_SCALAR_SEG_BYTES 2048
+#endif
+
 bool vector_ok(const ar_comm* c, const void* send, const void* part, const void* out,
                uint64_t N, uint64_t S, uint64_t send_row, uint64_t out_row)
 {
     const uint64_t es = (uint64_t)elem_size(c->dtype);
-    if (S * es < 128)
+    if (S * es < AR_SCALAR_SEG_BYTES)
         return false;
     return aligned16(send) && aligned16(part) && aligned16(out) && (N * es) % 16 == 0 &&
            (S * es) % 16 == 0 && (send_row * es) % 16 == 0 && (out_row * es) % 16 == 0 &&
