@@ -195,6 +195,33 @@ def test_reduce_scatter_all_gather(env, launch, dtype, R):
         assert comm.check() == api.AR_SUCCESS
 
 
+@pytest.mark.parametrize("launch", ["fused", "step", "pipelined"])
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 8])
+def test_scalar_vector_switch_boundary(env, launch, dtype, R):
+    """Segments just under, at and over 2 KiB (where the ring forms switch
+    from one element per lane to 16-byte slots), whole and with a ragged last
+    segment: all-reduce, and reduce-scatter then all-gather, bit-exact."""
+    api, orc = env["api"], env["orc"]
+    es = 2 if dtype == "bf16" else 4
+    for seg_bytes in (2032, 2048, 2064):
+        S = seg_bytes // es
+        for N in (R * S, R * S - 1):
+            x = rand_input(env, dtype, R, N, seed=31 * seg_bytes + N)
+            (y,) = run_allreduce(env, x, dtype, launch=launch)
+            assert y.tobytes() == orc.ring_allreduce(x, dtype).tobytes(), (seg_bytes, N)
+        comm = api.Comm(R, R * S, dtype, device=env["dev"], **ring_opts(launch))
+        x = rand_input(env, dtype, R, R * S, seed=7 * seg_bytes)
+        shard = poisoned(env, (R, S), dtype)
+        comm.reduce_scatter(to_dev(env, x, dtype), shard)
+        rs = from_dev(env, shard, dtype)
+        assert rs.tobytes() == orc.ring_reduce_scatter(x, dtype).tobytes(), seg_bytes
+        full = poisoned(env, (R, R * S), dtype)
+        comm.all_gather(shard, full)
+        assert from_dev(env, full, dtype).tobytes() == orc.ring_all_gather(rs, dtype).tobytes()
+        assert comm.check() == api.AR_SUCCESS
+
+
 # ---------------------------------------------------------------- config 4: tree + LL
 
 def test_cfg4_tree_ll_sizes(env):
