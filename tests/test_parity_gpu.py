@@ -840,3 +840,59 @@ def test_concurrent_with_compute_on_another_stream(env, launch):
         torch.cuda.synchronize()
         assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
     assert comm.check() == api.AR_SUCCESS
+
+
+# ---------------------------------------------------------------- random combinations
+
+def test_random_configurations_match_oracle(env):
+    """200 seeded draws over the option space at once: ranks, ragged sizes,
+    dtype, launch form (and the tree), ring channels, reduction operator, in
+    place, and all-reduce or reduce-scatter then all-gather; each result
+    bit-exact against the oracle's replay of the same schedule."""
+    api, orc = env["api"], env["orc"]
+    rng = np.random.default_rng(20261203)
+    for case in range(200):
+        R = int(rng.integers(2, 17))
+        dtype = ["int32", "float32", "bf16"][int(rng.integers(3))]
+        variant = (LAUNCHES + ["tree"])[int(rng.integers(len(LAUNCHES) + 1))]
+        ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
+        op = ops[int(rng.integers(len(ops)))]
+        coll = "ar" if variant == "tree" else ["ar", "rs_ag"][int(rng.integers(2))]
+        K = 1 if variant == "tree" or R == 2 else int(rng.integers(1, 3))  # R = 2 has one stride
+        what = (case, R, dtype, variant, op, coll, K)
+        if coll == "ar":
+            N = int(np.exp(rng.uniform(0, np.log(300000))))
+            x = rand_input(env, dtype, R, N, seed=case)
+            if variant == "tree":
+                comm = api.Comm(R, N, dtype, "tree", "ll", device=env["dev"], redop=op)
+                ref = orc.tree_allreduce(x, dtype, op=op)
+            else:
+                comm = api.Comm(R, N, dtype, device=env["dev"], redop=op, channels=K,
+                                **ring_opts(variant))
+                ref = orc.ring_allreduce(x, dtype, op=op, strides=comm.channel_strides())
+            send = to_dev(env, x, dtype)
+            if rng.integers(2):
+                comm.allreduce(send, send)  # in place
+                got = from_dev(env, send, dtype)
+            else:
+                recv = poisoned(env, (R, N), dtype)
+                comm.allreduce(send, recv)
+                got = from_dev(env, recv, dtype)
+            assert got.tobytes() == ref.tobytes(), what + (N,)
+        else:
+            n = int(np.exp(rng.uniform(0, np.log(20000))))
+            N = n * R
+            x = rand_input(env, dtype, R, N, seed=case)
+            comm = api.Comm(R, N, dtype, device=env["dev"], redop=op, channels=K,
+                            **ring_opts(variant))
+            strides = comm.channel_strides()
+            shard = poisoned(env, (R, n), dtype)
+            comm.reduce_scatter(to_dev(env, x, dtype), shard)
+            rs = from_dev(env, shard, dtype)
+            assert rs.tobytes() == orc.ring_reduce_scatter(x, dtype, op=op,
+                                                           strides=strides).tobytes(), what + (n,)
+            full = poisoned(env, (R, N), dtype)
+            comm.all_gather(shard, full)
+            assert from_dev(env, full, dtype).tobytes() == \
+                orc.ring_all_gather(rs, dtype, strides=strides).tobytes(), what + (n,)
+        assert comm.check() == api.AR_SUCCESS, what
