@@ -127,6 +127,7 @@ struct ar_comm {
     TreeTable tt{};
     // workspace layout
     size_t off_part = 0, off_up = 0, off_down = 0, off_flags = 0, ws_need = 0;
+    size_t part_bytes = 0;    // the hand-off region at off_part
     size_t off_tree_epochs = 0;
     uint64_t tree_lines = 0;  // lines per (tree, rank)
     uint64_t tree_groups = 0; // epoch words per tree: one per kTreeGroup lines
@@ -178,7 +179,7 @@ int device_ready(ar_comm* c)
         (void)hipGetLastError();  // not known: no packing; keep the error from the next launch check
     for (int d = 0; d < 3; ++d) {
         c->resident_fused[d][0] = resident_ring_fused(d, false);
-        c->resident_fused[d][1] = resident_ring_fused(d, true);
+        c->resident_fused[d][1] = resident_ring_fused_vec(d);
         c->resident_pipe[d][0] = resident_ring_pipelined(d, false);
         c->resident_pipe[d][1] = resident_ring_pipelined(d, true);
         c->resident_tree[d] = resident_tree_ll(d);
@@ -375,15 +376,35 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
             a.step = s;
             e = launch_ring_step(c->dtype, vec, a, gx, st);
         }
+    } else if (launch == AR_LAUNCH_FUSED && vec) {
+        // wave tiles of kWaveTileSlots 16-byte slots; two workgroups (8 waves)
+        // per CU by default
+        const uint64_t V = c->dtype == AR_BF16 ? 8 : 4;
+        const uint64_t tps = ((a.sub_len + V - 1) / V + kWaveTileSlots - 1) / kWaveTileSlots;
+        const uint64_t units = tps * (uint64_t)a.R;
+        const uint64_t waves = (uint64_t)(kBlock / 64);
+        const int64_t want = c->grid > 0 ? c->grid : 2 * (int64_t)c->ncu;
+        uint64_t g = std::min<uint64_t>((units + waves - 1) / waves, (uint64_t)want);
+        a.stage_wave = 0;
+        a.max_units = 0xffffffffu;
+        if (a.op != kOpAllGather && a.part == (void*)(c->ws + c->off_part)) {
+            // the hand-off goes through each wave's staging slot in the workspace's
+            // hand-off region: at most as many waves as it holds slots take tiles
+            a.stage_wave = (uint64_t)kWaveTileSlots * V;
+            const uint64_t slots = c->part_bytes / (a.stage_wave * 4);
+            if (slots < 1)
+                return AR_ERR_INTERNAL;
+            a.max_units = (uint32_t)std::min<uint64_t>(slots, 0xffffffffu);
+            g = std::min<uint64_t>(g, (slots + waves - 1) / waves);
+        }
+        grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(g, 1u << 20));
+        e = launch_ring_fused_vec(c->dtype, a, grid, st);
     } else if (launch == AR_LAUNCH_FUSED) {
-        const uint64_t V = vec ? (c->dtype == AR_BF16 ? 8 : 4) : 1;
+        const uint64_t V = 1;
         // tiles of kBlock * kUnroll slots; on the vector path smaller ones (down
         // to one wave's 64 * kUnroll) while there are fewer tiles than CUs
         uint64_t tile = (uint64_t)kBlock * kUnroll;
         const uint64_t seg_slots = (a.sub_len + V - 1) / V;
-        while (vec && tile > 64u * kUnroll &&
-               (seg_slots + tile - 1) / tile * (uint64_t)a.R < (uint64_t)c->ncu)
-            tile /= 2;
         a.tile_slots = tile;
         const uint64_t tiles = (seg_slots + tile - 1) / tile * (uint64_t)a.R;
         // One workgroup per CU by default for all-reduce and all-gather: with
@@ -404,11 +425,11 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         // packed).  The vector path gains nothing and loses at 64-128 KiB/rank,
         // where one XCD's CUs and L2 are too few (6.6 against 5.9 us).
         a.xcd_pack = 1;
-        if (!vec && c->grid <= 0 && c->nxcd > 1 && tiles * (uint64_t)c->nxcd <= (uint64_t)c->ncu) {
+        if (c->grid <= 0 && c->nxcd > 1 && tiles * (uint64_t)c->nxcd <= (uint64_t)c->ncu) {
             a.xcd_pack = c->nxcd;
             grid = (int)tiles * c->nxcd;
         }
-        e = launch_ring_fused(c->dtype, vec, a, grid, st);
+        e = launch_ring_fused(c->dtype, false, a, grid, st);
     } else if (launch == AR_LAUNCH_PIPELINED) {
         const int res = c->resident_pipe[c->dtype][vec ? 1 : 0];
         int64_t gmax = res / a.R;
@@ -594,7 +615,12 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
     c->tree_lines = std::min<uint64_t>((cap1 + 1) / 2, kTreeLinesCap);
     size_t off = kAlign;  // control block
     c->off_part = off;
-    off = align_up(off + cap1 * 4, kAlign);
+    // one accumulator per element (the step and pipelined forms), which also
+    // holds one staging slot per wave tile of the fused form: a tile of
+    // kWaveTileSlots 16-byte slots of T stages 4 bytes per element, and the
+    // tiles of one call number at most cap / (slot elements) + R
+    c->part_bytes = align_up(cap1 * 4 + (size_t)R * kWaveTileSlots * 32, kAlign);
+    off = align_up(off + c->part_bytes, kAlign);
     c->off_up = off;
     off = align_up(off + 2 * (size_t)R * c->tree_lines * 8, kAlign);
     c->off_down = off;

@@ -1,0 +1,455 @@
+// ar_fused.hip -- the fused ring form on the 16-byte vector path, for gfx950
+// (MI355X).
+//
+// The schedule is the ring's (ar_ring.hip, header): R-1 reduce steps, then
+// R-1 copy steps around q -> q+m, rank c owning segment c, so an element of
+// segment c is the left fold x_{c+m} + x_{c+2m} + ... + x_c ("GPU MODE
+// lecture 68 notes", section 05: 2(N-1) steps).
+//
+// One persistent launch.  The unit of work is a wave tile: one wave64 takes
+// kWaveSlots 16-byte slots per lane -- 2 KiB of every rank row for 32-bit
+// elements -- of one segment, and carries it through all 2(R-1) steps in
+// order.  Every hop is a store by the rank that passes the value on and a
+// load by the rank that receives it, at the same address and by the same lane
+// (so program order makes the load see the store; an empty asm memory clobber
+// keeps the compiler from forwarding the value in registers).  Tiles are
+// independent, so there are no flags and no fences, and a hop's line is
+// still in this XCD's L2 when the next step reads it.
+//
+// Why wave tiles: the rows a tile touches are 16 streams through HBM (R
+// inputs read, R outputs written back from L2).  With one tile per wave and
+// two workgroups per CU, a wave's 2 KiB of a row is contiguous and the chain
+// of one tile never waits on another wave; each rank's input is loaded one
+// step ahead into the other of two register sets, so its HBM latency overlaps
+// the hand-off round trip instead of adding to it.  Ranks advance by adding m
+// (no division inside the chain).
+//
+// Where the running value is handed on: in the owner's output row when the
+// accumulator type is the element type (the final value lands on the same
+// lines), else in a per-wave staging slot of the workspace that the wave
+// reuses for every tile it takes, so those lines stay in L2 and never become
+// a row of write-backs.  The staging slot keeps each 16-byte half of a lane's
+// accumulator slot in its own 1 KiB run, so one store instruction writes
+// whole lines.
+//
+// Every access goes through a buffer resource that spans exactly the tile it
+// addresses: an offset past the tile is dropped by the hardware.
+#include "ar_elem.h"
+#include "ar_internal.h"
+#include "ar_slots.h"
+
+namespace ar {
+namespace {
+
+constexpr int kWaves = kBlock / 64;                      // waves per workgroup
+constexpr uint32_t kTileSlots = kWaveTileSlots;           // 16-byte slots per wave tile
+constexpr int kPolPlain = 0;
+constexpr int kPolStream = 2;  // nt: each input element is read once per collective
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Resource over `bytes` bytes from p; p must be wave-uniform.
+__device__ inline rsrc_t tile_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int POL>
+__device__ inline u32x4 bload(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POL));
+}
+
+template <int POL>
+__device__ inline void bstore(rsrc_t r, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, POL);
+}
+
+// Byte offset of slot u of `lane` in a row tile (16-byte slots of T) ...
+__device__ inline uint32_t t_off(int u, uint32_t lane) { return ((uint32_t)u * 64u + lane) * 16u; }
+// ... and of 16-byte half h of its accumulator slot (V/4 halves).
+template <int V>
+__device__ inline uint32_t a_off(int u, int h, uint32_t lane)
+{
+    return (((uint32_t)u * (V / 4) + (uint32_t)h) * 64u + lane) * 16u;
+}
+
+template <class E, int V>
+__device__ inline void a_load(rsrc_t r, uint32_t lane, int u, typename E::A (&o)[V])
+{
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const u32x4 q = bload<kPolPlain>(r, a_off<V>(u, h, lane));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[4 * h + i] = E::from_bits(q[i]);
+    }
+}
+
+template <class E, int V>
+__device__ inline void a_store(rsrc_t r, uint32_t lane, int u, const typename E::A (&v)[V])
+{
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = E::to_bits(v[4 * h + i]);
+        bstore<kPolPlain>(r, a_off<V>(u, h, lane), q);
+    }
+}
+
+// The final value of slot u as T (bfloat16: one nearest-even rounding).
+template <class E, int V>
+__device__ inline void t_store(rsrc_t r, uint32_t lane, int u, const typename E::A (&v)[V])
+{
+    u32x4 q;
+    if constexpr (sizeof(typename E::T) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = E::to_bits(v[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = (uint32_t)E::narrow(v[2 * i]) | ((uint32_t)E::narrow(v[2 * i + 1]) << 16);
+    }
+    bstore<kPolPlain>(r, t_off(u, lane), q);
+}
+
+// What one wave tile needs to know.
+struct Tile {
+    int c;              // segment
+    uint64_t lo;        // segment (channel sub-range) start, elements
+    uint64_t len;       // its length
+    uint64_t first;     // the tile's first slot within the segment
+    uint32_t lane;
+};
+
+// Rows of the tile: rank r's input and output, 2 KiB (32-bit T) each.
+template <class E, int V>
+__device__ inline rsrc_t in_tile(const RingArgs& a, const Tile& t, int r)
+{
+    const typename E::T* p = static_cast<const typename E::T*>(a.send) + (uint64_t)r * a.send_row +
+                             t.lo + t.first * V;
+    return tile_rsrc(p, kTileSlots * 16u);
+}
+template <class E, int V>
+__device__ inline rsrc_t out_tile(const RingArgs& a, const Tile& t, int r)
+{
+    typename E::T* p = static_cast<typename E::T*>(a.out) + (uint64_t)r * a.out_row + t.lo +
+                       t.first * V;
+    return tile_rsrc(p, kTileSlots * 16u);
+}
+
+// One reduce step of a whole wave tile.  x holds the received value: on entry
+// at step 0 (the predecessor's input), else loaded here from the hand-off slot
+// the previous step stored (LOADX).  With PREFETCH the input of the next
+// step's rank (*rn, advanced by m) is loaded into `nxt` after the hand-off
+// load, so a wait for the hand-off leaves it in flight; `own` was loaded the
+// same way one step earlier.  LAST: the owner's step, written as T.
+template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
+__device__ inline void wt_step(const RingArgs& a, const Tile& t, typename E::A (&x)[kWaveSlots][V],
+                               const u32x4 (&own)[kWaveSlots], u32x4 (&nxt)[kWaveSlots],
+                               rsrc_t hand, rsrc_t fin, int* rn)
+{
+    if constexpr (LOADX) {
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            a_load<E, V>(hand, t.lane, u, x[u]);
+    }
+    if constexpr (PREFETCH) {
+        const rsrc_t q = in_tile<E, V>(a, t, *rn);
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            nxt[u] = bload<kPolStream>(q, t_off(u, t.lane));
+        *rn += a.m;
+        if (*rn >= a.R)
+            *rn -= a.R;
+    }
+#pragma unroll
+    for (int u = 0; u < kWaveSlots; ++u) {
+        typename E::A y[V];
+        widen_slot<E, V>(own[u], y);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            x[u][i] = combine<E, RED>(x[u][i], y[i]);
+            if constexpr (LAST)
+                x[u][i] = finalize<E, RED>(x[u][i], (float)a.R);
+        }
+        if constexpr (LAST)
+            t_store<E, V>(fin, t.lane, u, x[u]);
+        else
+            a_store<E, V>(hand, t.lane, u, x[u]);
+    }
+    step_boundary();
+}
+
+// The R-1 reduce steps of a whole wave tile of segment c.  Step s is rank
+// c + (s+2)m; its input was loaded during step s-1 into the other of two
+// register sets.
+template <class E, int V, int RED>
+__device__ inline void wt_reduce(const RingArgs& a, const Tile& t, rsrc_t hand, rsrc_t fin)
+{
+    using A = typename E::A;
+    const int R = a.R, m = a.m;
+    int r1 = t.c + m;
+    if (r1 >= R)
+        r1 -= R;
+    int r2 = r1 + m;
+    if (r2 >= R)
+        r2 -= R;
+    A x[kWaveSlots][V];
+    u32x4 b0[kWaveSlots], b1[kWaveSlots];
+    {
+        const rsrc_t q1 = in_tile<E, V>(a, t, r1), q2 = in_tile<E, V>(a, t, r2);
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u) {
+            widen_slot<E, V>(bload<kPolStream>(q1, t_off(u, t.lane)), x[u]);
+            b0[u] = bload<kPolStream>(q2, t_off(u, t.lane));
+        }
+    }
+    int rn = r2 + m;  // the rank whose input step 1 adds
+    if (rn >= R)
+        rn -= R;
+    if (R == 2) {
+        wt_step<E, V, RED, false, false, true>(a, t, x, b0, b1, hand, fin, &rn);
+        return;
+    }
+    // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
+    wt_step<E, V, RED, false, true, false>(a, t, x, b0, b1, hand, fin, &rn);
+    int s = 1;  // the next step; its input is in b1
+    for (; s + 1 <= R - 3; s += 2) {
+        wt_step<E, V, RED, true, true, false>(a, t, x, b1, b0, hand, fin, &rn);
+        wt_step<E, V, RED, true, true, false>(a, t, x, b0, b1, hand, fin, &rn);
+    }
+    if (s == R - 3) {
+        wt_step<E, V, RED, true, true, false>(a, t, x, b1, b0, hand, fin, &rn);
+        wt_step<E, V, RED, true, false, true>(a, t, x, b0, b1, hand, fin, &rn);
+    } else {
+        wt_step<E, V, RED, true, false, true>(a, t, x, b1, b0, hand, fin, &rn);
+    }
+}
+
+// The copy steps of a whole wave tile: rank p's output is read and stored as
+// rank p+m's, starting at the owner c (all-gather: after the owner placed its
+// own shard).
+template <class E, int V, int OP>
+__device__ inline void wt_copy(const RingArgs& a, const Tile& t)
+{
+    if constexpr (OP == kOpAllGather) {
+        // send is [R][S]: the owner's shard, at the same offset within it
+        const typename E::T* src = static_cast<const typename E::T*>(a.send) +
+                                   (uint64_t)t.c * a.send_row + (t.lo - (uint64_t)t.c * a.S) +
+                                   t.first * V;
+        const rsrc_t s = tile_rsrc(src, kTileSlots * 16u), d = out_tile<E, V>(a, t, t.c);
+        u32x4 v[kWaveSlots];
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            v[u] = bload<kPolStream>(s, t_off(u, t.lane));
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            bstore<kPolPlain>(d, t_off(u, t.lane), v[u]);
+        step_boundary();
+    }
+    int p = t.c;
+    for (int s = 0; s <= a.R - 2; ++s) {
+        int q = p + a.m;
+        if (q >= a.R)
+            q -= a.R;
+        const rsrc_t src = out_tile<E, V>(a, t, p), dst = out_tile<E, V>(a, t, q);
+        u32x4 v[kWaveSlots];
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            v[u] = bload<kPolPlain>(src, t_off(u, t.lane));
+#pragma unroll
+        for (int u = 0; u < kWaveSlots; ++u)
+            bstore<kPolPlain>(dst, t_off(u, t.lane), v[u]);
+        step_boundary();
+        p = q;
+    }
+}
+
+// The last tile of a segment when the segment ends inside it: step by step
+// with the checked slot helpers.  Lane slots are j0 + u*64; the helpers'
+// slots past the tile lie past the segment's end, so they are skipped.  `acc`
+// addresses slot j's running value at acc + j*V.
+template <class E, int V, int OP>
+__device__ inline void wt_ragged(const RingArgs& a, const Tile& t, typename E::A* acc)
+{
+    using T = typename E::T;
+    const int R = a.R, m = a.m;
+    const uint64_t j0 = t.first + t.lane;
+    const T* send = static_cast<const T*>(a.send);
+    T* out = static_cast<T*>(a.out);
+    if constexpr (OP != kOpAllGather) {
+        int q = t.c + 2 * m;  // rank of step 0, and its predecessor p
+        q %= R;
+        int p = t.c + m;
+        p %= R;
+        for (int s = 0; s <= R - 2; ++s) {
+            ReducePtrs<E> rp;
+            rp.prevT = send + (uint64_t)p * a.send_row + t.lo;
+            rp.own = send + (uint64_t)q * a.send_row + t.lo;
+            rp.prevA = acc;
+            rp.dstA = acc;
+            rp.dstT = out + (uint64_t)q * a.out_row +
+                      (OP == kOpReduceScatter ? t.lo - (uint64_t)t.c * a.S : t.lo);
+            reduce_step_slots<E, V>(rp, s, R, a.redop, t.len, j0, 64);
+            step_boundary();
+            p = q;
+            q += m;
+            if (q >= R)
+                q -= R;
+        }
+    }
+    if constexpr (OP != kOpReduceScatter) {
+        if constexpr (OP == kOpAllGather) {
+            const T* src = send + (uint64_t)t.c * a.send_row + (t.lo - (uint64_t)t.c * a.S);
+            copy_slots<E, V>(src, out + (uint64_t)t.c * a.out_row + t.lo, t.len, j0, 64);
+            step_boundary();
+        }
+        int p = t.c;
+        for (int s = 0; s <= R - 2; ++s) {
+            int q = p + m;
+            if (q >= R)
+                q -= R;
+            copy_slots<E, V>(out + (uint64_t)p * a.out_row + t.lo, out + (uint64_t)q * a.out_row + t.lo,
+                             t.len, j0, 64);
+            step_boundary();
+            p = q;
+        }
+    }
+}
+
+template <int DT, int OP, int RED>
+__device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits, uint32_t lane)
+{
+    using E = Elem<DT>;
+    using T = typename E::T;
+    using A = typename E::A;
+    constexpr int V = E::VEC;
+    const uint64_t tps = ((a.sub_len + V - 1) / V + kTileSlots - 1) / kTileSlots;  // tiles per segment
+    const uint64_t ntiles = tps * (uint64_t)a.R;
+    // this wave's staging slot, or the running value in part at c*part_seg + e
+    A* stage = a.stage_wave ? static_cast<A*>(a.part) + (uint64_t)unit * a.stage_wave : nullptr;
+    int c = (int)(unit / tps);
+    uint64_t k = unit % tps;
+    for (uint64_t t = unit; t < ntiles; t += nunits) {
+        Tile tl;
+        tl.c = c;
+        tl.lane = lane;
+        uint64_t hi;
+        seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &tl.lo, &hi);
+        tl.len = hi - tl.lo;
+        tl.first = k * kTileSlots;
+        if (tl.first * V < tl.len) {  // else an empty tile of a short trailing segment
+            A* acc = stage ? stage - tl.first * V
+                           : static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + tl.lo;
+            if ((tl.first + kTileSlots) * V <= tl.len) {
+                if constexpr (OP != kOpAllGather) {
+                    const rsrc_t hand = tile_rsrc(acc + tl.first * V, kTileSlots * V * 4u);
+                    T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
+                             (OP == kOpReduceScatter ? tl.lo - (uint64_t)c * a.S : tl.lo) +
+                             tl.first * V;
+                    wt_reduce<E, V, RED>(a, tl, hand, tile_rsrc(fin, kTileSlots * 16u));
+                }
+                if constexpr (OP != kOpReduceScatter)
+                    wt_copy<E, V, OP>(a, tl);
+            } else {
+                wt_ragged<E, V, OP>(a, tl, acc);
+            }
+        }
+        k += nunits;
+        if (k >= tps) {
+            c += (int)(k / tps);
+            k %= tps;
+        }
+    }
+}
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kBlock) void k_ring_fused_vec(RingArgs a)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nunits = min(gridDim.x * (uint32_t)kWaves, a.max_units);
+    if (unit >= nunits)
+        return;
+    if constexpr (OP == kOpAllGather) {
+        wt_run<DT, OP, AR_SUM>(a, unit, nunits, lane);
+    } else {
+        switch (a.redop) {
+        case AR_MAX:
+            wt_run<DT, OP, AR_MAX>(a, unit, nunits, lane);
+            break;
+        case AR_MIN:
+            wt_run<DT, OP, AR_MIN>(a, unit, nunits, lane);
+            break;
+        case AR_AVG:
+            if constexpr (DT != AR_INT32)
+                wt_run<DT, OP, AR_AVG>(a, unit, nunits, lane);
+            break;
+        default:
+            wt_run<DT, OP, AR_SUM>(a, unit, nunits, lane);
+            break;
+        }
+    }
+}
+
+template <int DT>
+hipError_t fused_vec_launch(const RingArgs& a, int grid, hipStream_t st)
+{
+    if (a.op == kOpAllReduce)
+        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+    else if (a.op == kOpReduceScatter)
+        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st,
+                           a);
+    else
+        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+int resident_vec_dt()
+{
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring_fused_vec<DT, kOpAllReduce>,
+                                                     kBlock, 0) != hipSuccess)
+        return 0;
+    return per_cu * ncu;
+}
+
+}  // namespace
+
+hipError_t launch_ring_fused_vec(int dtype, const RingArgs& a, int grid, hipStream_t st)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return fused_vec_launch<AR_INT32>(a, grid, st);
+    case AR_FLOAT32:
+        return fused_vec_launch<AR_FLOAT32>(a, grid, st);
+    case AR_BF16:
+        return fused_vec_launch<AR_BF16>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int resident_ring_fused_vec(int dtype)
+{
+    switch (dtype) {
+    case AR_INT32:
+        return resident_vec_dt<AR_INT32>();
+    case AR_FLOAT32:
+        return resident_vec_dt<AR_FLOAT32>();
+    case AR_BF16:
+        return resident_vec_dt<AR_BF16>();
+    }
+    return 0;
+}
+
+}  // namespace ar

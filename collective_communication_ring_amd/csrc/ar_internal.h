@@ -73,9 +73,16 @@ struct RingArgs {
     uint64_t unit;    // pipelined ring: elements per flagged chunk (a multiple of the slot)
     uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
     uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
-    uint64_t tile_slots; // fused form: slots per tile (a multiple of kUnroll, <= kBlock * kUnroll)
-    int xcd_pack;     // fused form: only workgroups whose id is a multiple of this take
-                      //   tiles (the others exit at once), so that they share one XCD
+    uint64_t tile_slots; // fused form, scalar path: slots per tile (a multiple of kUnroll,
+                         //   <= kBlock * kUnroll)
+    int xcd_pack;     // fused form, scalar path: only workgroups whose id is a multiple of
+                      //   this take tiles (the others exit at once), so that they share one XCD
+    uint64_t stage_wave; // fused form, vector path: accumulator elements of `part` per wave
+                         //   (each wave's own hand-off staging slot, reused for every tile it
+                         //   takes); 0: the running value of element e of segment c sits at
+                         //   part[c * part_seg + e]
+    uint32_t max_units;  // fused form, vector path: waves that take tiles (the staging holds
+                         //   this many); waves of the grid past it exit
     uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
     uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
     int m;            // this channel's ring stride: rank q receives from q - m
@@ -142,6 +149,7 @@ struct RingLLArgs {
 hipError_t launch_ring_step(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
+hipError_t launch_ring_fused_vec(int dtype, const RingArgs& a, int grid, hipStream_t s);
 hipError_t launch_ring_pipelined(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t s);
 hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t s);
 hipError_t launch_ring_ll(int dtype, const RingLLArgs& a, int grid, hipStream_t s);
@@ -154,6 +162,7 @@ extern int g_util_hip_error;
 // Largest number of workgroups of each persistent kernel that can be
 // resident at once on the current device (0 on error).
 int resident_ring_fused(int dtype, bool vec);
+int resident_ring_fused_vec(int dtype);
 int resident_ring_pipelined(int dtype, bool vec);
 int resident_tree_ll(int dtype);
 int resident_ring_ll(int dtype);
@@ -166,6 +175,10 @@ int resident_ring_ll(int dtype);
 #endif
 constexpr int kBlock = AR_BLOCK;   // threads per workgroup (4 wave64 by default)
 constexpr int kUnroll = AR_UNROLL; // 16-byte vectors per thread per pass
+// Fused form, vector path: a wave tile is 64 lanes x kWaveSlots 16-byte slots
+// of one segment in every rank row (2 KiB of a row for 32-bit elements).
+constexpr int kWaveSlots = 2;
+constexpr uint32_t kWaveTileSlots = 64u * kWaveSlots;
 // LL kernels' placement: a launch is made of sets of R workgroups (one per
 // rank) that exchange lines only with each other.  Workgroups are dispatched
 // to the XCDs round-robin (workgroup x to XCD x mod n), so set j is put on

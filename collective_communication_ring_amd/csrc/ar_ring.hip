@@ -110,108 +110,6 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 
 // ---- fused: a tile runs every step ------------------------------------------
 
-// One reduce step of a whole tile (kUnroll full slots per thread) in the fused
-// form.  x holds the received value: on entry at step 0 (the predecessor's
-// input, loaded by the caller), else loaded here from the hand-off slot after
-// the previous step's store (LOADX).  With PREFETCH the input of the next
-// step's rank is loaded into `nxt` before this step's add, so its HBM latency
-// overlaps this step instead of lengthening the chain; `own` was loaded the
-// same way one step earlier.  Prefetched inputs stay raw 16-byte vectors
-// until used (half the registers for bfloat16).  LAST: the owner's step,
-// written as T.
-template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
-__device__ inline void fused_step(typename E::A (&x)[kUnroll][V], const u32x4 (&own)[kUnroll],
-                                  u32x4 (&nxt)[kUnroll], typename E::A* acc, typename E::T* fin,
-                                  const typename E::T* next_row, uint64_t j0, uint64_t js, float R)
-{
-    using A = typename E::A;
-    if constexpr (LOADX) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            load_a<E, V>(acc + (j0 + (uint64_t)u * js) * V, x[u]);
-    }
-    if constexpr (PREFETCH) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            nxt[u] = load16(next_row + (j0 + (uint64_t)u * js) * V);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        A y[V];
-        widen_slot<E, V>(own[u], y);
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            x[u][i] = combine<E, RED>(x[u][i], y[i]);
-            if constexpr (LAST)
-                x[u][i] = finalize<E, RED>(x[u][i], R);
-        }
-        if constexpr (LAST)
-            store_t<E, V>(fin + (j0 + (uint64_t)u * js) * V, x[u]);
-        else
-            store_a<E, V>(acc + (j0 + (uint64_t)u * js) * V, x[u]);
-    }
-    step_boundary();
-}
-
-// The two inputs step 0 of a whole tile of segment c needs: x_{c+m} (the
-// value it receives) into x and x_{c+2m} (its own, raw) into b0.  (Loading
-// them for the next tile before this tile's copy steps measured slower: it
-// adds to the L2 footprint of the copy chain.)
-template <class E, int V>
-__device__ inline void fused_load_first(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                        uint64_t js, typename E::A (&x)[kUnroll][V],
-                                        u32x4 (&b0)[kUnroll])
-{
-    using T = typename E::T;
-    const T* send = static_cast<const T*>(a.send) + lo;
-    const T* first = send + (uint64_t)mod_r(c + a.m, a.R) * a.send_row;
-    const T* r0 = send + (uint64_t)mod_r(c + 2 * a.m, a.R) * a.send_row;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        load_t<E, V>(first + (j0 + (uint64_t)u * js) * V, x[u]);
-        b0[u] = load16(r0 + (j0 + (uint64_t)u * js) * V);
-    }
-}
-
-// The R-1 reduce steps of a whole tile of segment c, with step 0's inputs
-// already in x and b0 (fused_load_first).  Step s is rank c + (s+2)m; the
-// prefetched input alternates between two register sets, so no step waits
-// for the next step's load.
-template <class E, int V, int RED>
-__device__ inline void fused_reduce_whole(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                          uint64_t js, typename E::A (&x)[kUnroll][V],
-                                          u32x4 (&b0)[kUnroll])
-{
-    using T = typename E::T;
-    using A = typename E::A;
-    const int R = a.R;
-    const int m = a.m;
-    const float fr = (float)R;
-    const T* send = static_cast<const T*>(a.send) + lo;
-    A* acc = static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + lo;
-    T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
-             (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
-    auto row = [&](int s) { return send + (uint64_t)mod_r(c + (s + 2) * m, R) * a.send_row; };
-    u32x4 b1[kUnroll];
-    if (R == 2) {
-        fused_step<E, V, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, j0, js, fr);
-        return;
-    }
-    // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
-    fused_step<E, V, RED, false, true, false>(x, b0, b1, acc, fin, row(1), j0, js, fr);
-    int s = 1;  // the next step; its input is in b1
-    for (; s + 1 <= R - 3; s += 2) {
-        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, js, fr);
-        fused_step<E, V, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 2), j0, js, fr);
-    }
-    if (s == R - 3) {
-        fused_step<E, V, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 1), j0, js, fr);
-        fused_step<E, V, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, j0, js, fr);
-    } else {
-        fused_step<E, V, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, j0, js, fr);
-    }
-}
-
 // One reduce step of the scalar path (one element per slot; slot u of this
 // thread is element e[u], stored only if ok[u]).  The same structure as
 // fused_step: the hand-off is loaded after the previous step's store, the
@@ -335,81 +233,50 @@ __device__ inline void fused_reduce_scalar_op(const RingArgs& a, int c, uint64_t
     }
 }
 
-template <class E, int V>
-__device__ inline void fused_reduce_whole_op(const RingArgs& a, int c, uint64_t lo, uint64_t j0,
-                                             uint64_t js, typename E::A (&x)[kUnroll][V],
-                                             u32x4 (&b0)[kUnroll])
-{
-    switch (a.redop) {
-    case AR_MAX:
-        fused_reduce_whole<E, V, AR_MAX>(a, c, lo, j0, js, x, b0);
-        break;
-    case AR_MIN:
-        fused_reduce_whole<E, V, AR_MIN>(a, c, lo, j0, js, x, b0);
-        break;
-    case AR_AVG:
-        fused_reduce_whole<E, V, AR_AVG>(a, c, lo, j0, js, x, b0);
-        break;
-    default:
-        fused_reduce_whole<E, V, AR_SUM>(a, c, lo, j0, js, x, b0);
-        break;
-    }
-}
-
-// Tile t of a fused launch: segment c, its range [lo, lo + len) of a full
-// row, and this thread's first slot j0.  False for an empty tile of a short
-// trailing segment (uniform per workgroup).  *whole: every slot of this
-// thread is full (the prefetching path applies).  Tiles are numbered segment
-// by segment, so the workgroups in flight at once cover one stretch of one
-// segment: each touches the same 2R rows near the same offset, and the pages
-// they address together stay few (numbering across segments first spread
-// them over every segment of every row and measured ~25 % slower at
-// >= 128 MiB per rank).
-template <int V>
-__device__ inline bool fused_tile(const RingArgs& a, uint64_t t, int* c, uint64_t* lo,
-                                  uint64_t* len, uint64_t* j0, uint64_t* js, bool* active,
-                                  bool* whole)
+// Tile t of a fused launch on the scalar path (segments shorter than
+// AR_SCALAR_SEG_BYTES, one element per slot): segment c, its range [lo, lo +
+// len) of a full row, and this thread's first element j0 (elements j0 + u*js).
+// False for an empty tile of a short trailing segment (uniform per
+// workgroup).  Tiles are numbered segment by segment.  A tile the segment
+// fills only in part puts one element on each thread (up to kBlock threads),
+// so that a wave's elements are adjacent and each step stores them with one
+// instruction (four elements of one thread in one cache line took four
+// stores: 8.5 against 6 us a call).
+__device__ inline bool scalar_tile(const RingArgs& a, uint64_t t, int* c, uint64_t* lo,
+                                   uint64_t* len, uint64_t* j0, uint64_t* js, bool* active)
 {
     const uint64_t tile_slots = a.tile_slots;
-    const uint64_t tiles_per_seg = ((a.sub_len + V - 1) / V + tile_slots - 1) / tile_slots;
+    const uint64_t tiles_per_seg = (a.sub_len + tile_slots - 1) / tile_slots;
     *c = (int)(t / tiles_per_seg);
     const uint64_t k = t % tiles_per_seg;
     uint64_t hi;
     seg_range(a.N, a.S, *c, a.sub_lo, a.sub_len, lo, &hi);
     *len = hi - *lo;
     const uint64_t first = k * tile_slots;
-    const uint64_t seg_slots = (*len + V - 1) / V;
-    // A tile the segment fills only in part.  Vector path: spread its n slots
-    // over ceil(n / kUnroll) threads, so that the active threads have whole
-    // slots and take the prefetching path.  Scalar path: one element per
-    // thread (up to kBlock threads), so that a wave's elements are adjacent
-    // and each step stores them with one instruction (four elements of one
-    // thread in one cache line took four stores: 8.5 against 6 us a call).
-    const uint64_t n = seg_slots > first ? seg_slots - first : 0;
+    const uint64_t n = *len > first ? *len - first : 0;
     uint64_t stride = tile_slots / kUnroll;
     if (n < tile_slots)
-        stride = V > 1 ? (n + kUnroll - 1) / kUnroll : (n < (uint64_t)kBlock ? n : (uint64_t)kBlock);
+        stride = n < (uint64_t)kBlock ? n : (uint64_t)kBlock;
     *js = stride;
     *active = threadIdx.x < stride;
     *j0 = first + threadIdx.x;
-    *whole = V > 1 && *active && (*j0 + (kUnroll - 1) * stride + 1) * V <= *len;
-    return first * V < *len;
+    return first < *len;
 }
 
-template <int DT, int V, int OP>
+// The fused form on the scalar path: a workgroup takes a tile of a segment
+// through all 2(R-1) steps (the vector path is k_ring_fused_vec).
+template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
 {
     using E = Elem<DT>;
     using T = typename E::T;
     const int R = a.R;
     const uint64_t tile_slots = a.tile_slots;
-    const uint64_t seg_slots = (a.sub_len + V - 1) / V;
-    const uint64_t tiles_per_seg = (seg_slots + tile_slots - 1) / tile_slots;
+    const uint64_t tiles_per_seg = (a.sub_len + tile_slots - 1) / tile_slots;
     const uint64_t ntiles = tiles_per_seg * (uint64_t)R;
     const int m = a.m;
     T* out = static_cast<T*>(a.out);
 
-    using A = typename E::A;
     // with xcd_pack = n only every n-th workgroup works: workgroups are
     // dispatched to the XCDs round-robin, so the working ones share an XCD
     const uint32_t pack = a.xcd_pack > 1 ? (uint32_t)a.xcd_pack : 1u;
@@ -419,50 +286,30 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     for (uint64_t t = wg; t < ntiles; t += nwg) {
         int c;
         uint64_t lo, len, j0, js;
-        bool active, whole;
-        if (!fused_tile<V>(a, t, &c, &lo, &len, &j0, &js, &active, &whole))
+        bool active;
+        if (!scalar_tile(a, t, &c, &lo, &len, &j0, &js, &active))
             continue;  // empty tile of a short trailing segment (uniform per workgroup)
         if (!active)
-            continue;  // this thread has no slot in a part-filled tile
+            continue;  // this thread has no element in a part-filled tile
 
-        if constexpr (OP != kOpAllGather) {
-            bool done = false;
-            if constexpr (V > 1) {
-                if (whole) {
-                    A x[kUnroll][V];
-                    u32x4 b0[kUnroll];
-                    fused_load_first<E, V>(a, c, lo, j0, js, x, b0);
-                    fused_reduce_whole_op<E, V>(a, c, lo, j0, js, x, b0);
-                    done = true;
-                }
-            }
-            if constexpr (V == 1) {
-                fused_reduce_scalar_op<E>(a, c, lo, len, j0, js);
-                done = true;
-            }
-            if (!done) {
-                // the end of a segment on the vector path: step by step
-                for (int s = 0; s <= R - 2; ++s) {
-                    const int q = mod_r(c + (s + 2) * m, R);
-                    const ReducePtrs<E> p = reduce_ptrs<E>(a, q, c, lo);
-                    reduce_step_slots<E, V>(p, s, R, a.redop, len, j0, js);
-                    step_boundary();
-                }
-            }
-        }
+        if constexpr (OP != kOpAllGather)
+            fused_reduce_scalar_op<E>(a, c, lo, len, j0, js);
         if constexpr (OP != kOpReduceScatter) {
             if constexpr (OP == kOpAllGather) {
                 const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
                                (lo - (uint64_t)c * a.S);
-                copy_slots<E, V>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
+                copy_slots<E, 1>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
                 step_boundary();
             }
+            int p = c;
             for (int s = 0; s <= R - 2; ++s) {
-                const int q = mod_r(c + (1 + s) * m, R);
-                const int p = mod_r(c + s * m, R);
-                copy_slots<E, V>(out + (uint64_t)p * a.out_row + lo,
-                                 out + (uint64_t)q * a.out_row + lo, len, j0, js);
+                int q = p + m;
+                if (q >= R)
+                    q -= R;
+                copy_slots<E, 1>(out + (uint64_t)p * a.out_row + lo, out + (uint64_t)q * a.out_row + lo,
+                                 len, j0, js);
                 step_boundary();
+                p = q;
             }
         }
     }
@@ -481,32 +328,28 @@ hipError_t step_launch(const RingArgs& a, int gx, hipStream_t st, bool copy)
     return hipGetLastError();
 }
 
-template <int DT, int V>
+template <int DT>
 hipError_t fused_launch(const RingArgs& a, int grid, hipStream_t st)
 {
     if (a.op == kOpAllReduce)
-        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_fused<DT, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
     else if (a.op == kOpReduceScatter)
-        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st,
-                           a);
+        hipLaunchKernelGGL((k_ring_fused<DT, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st, a);
     else
-        hipLaunchKernelGGL((k_ring_fused<DT, V, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_fused<DT, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 
 template <int DT>
-int resident_fused_dt(bool vec)
+int resident_fused_dt()
 {
     int dev = 0, ncu = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    hipError_t e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                             &per_cu, k_ring_fused<DT, Elem<DT>::VEC, kOpAllReduce>, kBlock, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                             &per_cu, k_ring_fused<DT, 1, kOpAllReduce>, kBlock, 0);
-    if (e != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring_fused<DT, kOpAllReduce>, kBlock,
+                                                     0) != hipSuccess)
         return 0;
     return per_cu * ncu;
 }
@@ -566,28 +409,33 @@ hipError_t launch_ring_placement(int dtype, bool vec, const RingArgs& a, int gx,
     return hipGetLastError();
 }
 
+// The fused form's scalar path; the vector path is launch_ring_fused_vec.
 hipError_t launch_ring_fused(int dtype, bool vec, const RingArgs& a, int grid, hipStream_t st)
 {
+    if (vec)
+        return launch_ring_fused_vec(dtype, a, grid, st);
     switch (dtype) {
     case AR_INT32:
-        return vec ? fused_launch<AR_INT32, 4>(a, grid, st) : fused_launch<AR_INT32, 1>(a, grid, st);
+        return fused_launch<AR_INT32>(a, grid, st);
     case AR_FLOAT32:
-        return vec ? fused_launch<AR_FLOAT32, 4>(a, grid, st) : fused_launch<AR_FLOAT32, 1>(a, grid, st);
+        return fused_launch<AR_FLOAT32>(a, grid, st);
     case AR_BF16:
-        return vec ? fused_launch<AR_BF16, 8>(a, grid, st) : fused_launch<AR_BF16, 1>(a, grid, st);
+        return fused_launch<AR_BF16>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }
 
 int resident_ring_fused(int dtype, bool vec)
 {
+    if (vec)
+        return resident_ring_fused_vec(dtype);
     switch (dtype) {
     case AR_INT32:
-        return resident_fused_dt<AR_INT32>(vec);
+        return resident_fused_dt<AR_INT32>();
     case AR_FLOAT32:
-        return resident_fused_dt<AR_FLOAT32>(vec);
+        return resident_fused_dt<AR_FLOAT32>();
     case AR_BF16:
-        return resident_fused_dt<AR_BF16>(vec);
+        return resident_fused_dt<AR_BF16>();
     }
     return 0;
 }
