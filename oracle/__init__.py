@@ -8,6 +8,7 @@ imports it, and it imports nothing from the GPU library.
 Arrays are numpy, rank-major ``[R, N]``.  bfloat16 arrays are carried as
 ``uint16`` bit patterns and named by ``dtype="bf16"``.
 """
+import contextlib
 import ctypes
 import os
 
@@ -18,16 +19,33 @@ from . import build as _build
 _DT = {"int32": 0, "float32": 1, "bf16": 2}
 OPS = {"sum": 0, "max": 1, "min": 2, "avg": 3}
 _NP = {"int32": np.int32, "float32": np.float32, "bf16": np.uint16}
-_lib = None
+_libs = {}
+_use_omp = False
+
+
+@contextlib.contextmanager
+def parallel(threads):
+    """Inside the block, oracle calls run on the OpenMP build of the same
+    code with `threads` threads (parallel over elements within each step;
+    every element keeps its summation order, so the results are the same
+    bits).  Yields the number of threads OpenMP reports it will use."""
+    global _use_omp
+    prev = _use_omp
+    _use_omp = True
+    try:
+        yield int(lib().orc_set_threads(int(threads)))
+    finally:
+        _use_omp = prev
 
 
 def lib():
-    """Load liboracle.so, compiling it first only if it is not there."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_build.LIB):
+    """Load the oracle library (the OpenMP build inside `parallel()`, else the
+    single-threaded one), compiling both first only if either is missing."""
+    path = _build.LIB_OMP if _use_omp else _build.LIB
+    if path not in _libs:
+        if not (os.path.exists(_build.LIB) and os.path.exists(_build.LIB_OMP)):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         for name in ("orc_ring_allreduce", "orc_ring_reduce_scatter",
                      "orc_ring_all_gather", "orc_tree_allreduce"):
@@ -55,14 +73,10 @@ def lib():
         L.orc_f32_from_bf16.restype = ctypes.c_float
         L.orc_bf16_from_f32_array.argtypes = [vp, vp, sz]
         L.orc_bf16_from_f32_array.restype = None
-        L.orc_ll_pack.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
-        L.orc_ll_pack.restype = ctypes.c_uint64
-        L.orc_ll_data.argtypes = [ctypes.c_uint64]
-        L.orc_ll_data.restype = ctypes.c_uint32
-        L.orc_ll_flag.argtypes = [ctypes.c_uint64]
-        L.orc_ll_flag.restype = ctypes.c_uint32
-        _lib = L
-    return _lib
+        L.orc_set_threads.argtypes = [i]
+        L.orc_set_threads.restype = i
+        _libs[path] = L
+    return _libs[path]
 
 
 def _dtype_of(x, dtype):
@@ -173,10 +187,3 @@ def f32_from_bf16(h):
     h = np.ascontiguousarray(h, dtype=np.uint16)
     return (h.astype(np.uint32) << 16).view(np.float32)
 
-
-def ll_pack(data_bits, flag):
-    return int(lib().orc_ll_pack(data_bits, flag))
-
-
-def ll_unpack(line):
-    return int(lib().orc_ll_data(line)), int(lib().orc_ll_flag(line))

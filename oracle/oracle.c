@@ -11,6 +11,14 @@
  * Reduction operators: sum (the pages' worked examples), max, min, and
  * average (sum / R).
  *
+ * The LL protocol changes no value (data and flag share one store; the flag
+ * only tells the reader the data arrived), so the oracle has no LL format.
+ *
+ * Threads: built plain (one thread) and again with OpenMP, where loops over
+ * the elements (or ranks) of one step run in parallel; every element is
+ * still folded by one thread in the schedule's order, so both builds give
+ * the same bits.
+ *
  * Parity status: every function here is pinned by CPU tests (closed forms,
  * brute force, hand-computed rounding-order cases, a library conversion
  * routine, and the pages' worked examples); none is "parity unpinned".
@@ -45,6 +53,25 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads.  The oracle is built twice: plain (one thread) and with OpenMP,
+ * where the loops marked below run in parallel over elements (or ranks)
+ * *within* one step.  Every element is still folded by one thread in the
+ * schedule's order, so both builds give the same bits. */
+int orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 enum { ORC_INT32 = 0, ORC_FLOAT32 = 1, ORC_BF16 = 2 };
 /* Reduction operators: sum, max, min, and average = sum / R ("NCCL, NIXL,
@@ -97,19 +124,6 @@ void orc_bf16_from_f32_array(const float* in, uint16_t* out, size_t n)
     for (size_t i = 0; i < n; ++i)
         out[i] = orc_bf16_from_f32(in[i]);
 }
-
-/* ---- LL line --------------------------------------------------------- */
-
-/* The LL protocol puts data and its arrival flag into one 8-byte write
- * ("Demystifying NVSHMEM ..." summary, paragraph on collectives: LL/LL128
- * pack data and an arrival flag into one atomic write).  Reading: data bits
- * in the low 32 bits, flag in the high 32 bits. */
-uint64_t orc_ll_pack(uint32_t data_bits, uint32_t flag)
-{
-    return ((uint64_t)flag << 32) | (uint64_t)data_bits;
-}
-uint32_t orc_ll_data(uint64_t line) { return (uint32_t)(line & 0xffffffffu); }
-uint32_t orc_ll_flag(uint64_t line) { return (uint32_t)(line >> 32); }
 
 /* ---- element access -------------------------------------------------- */
 
@@ -236,6 +250,7 @@ static int ring_reduce_phase(int R, size_t N, int dtype, int op, int m, size_t S
             int p = mod(q - m, R);
             size_t lo, hi;
             sub_range(N, R, c, Sk, k, &lo, &hi);
+#pragma omp parallel for schedule(static)
             for (size_t e = lo; e < hi; ++e) {
                 acc_t in = (s == 0) ? widen(dtype, send, (size_t)p * N + e)
                                     : part[(size_t)p * N + e];
@@ -260,6 +275,8 @@ static void ring_gather_phase(int R, size_t N, int dtype, int m, size_t Sk, int 
 {
     int es = elem_size(dtype);
     for (int s = 0; s <= R - 2; ++s) {
+        /* within a step rank q writes only its own row, segment c */
+#pragma omp parallel for schedule(static)
         for (int q = 0; q < R; ++q) {
             int c = mod(q - (1 + s) * m, R);
             int p = mod(q - m, R);
@@ -485,6 +502,7 @@ int orc_tree_allreduce_op(int R, size_t N, int dtype, int op, const void* send, 
                 root[t] = r;
         }
     size_t H = (N + 1) / 2;
+#pragma omp parallel for schedule(static)
     for (size_t e = 0; e < N; ++e) {
         int t = e < H ? 0 : 1;
         acc_t v = acc_final(op, R, tree_fold(R, parent + t * R, dtype, op, send, N, root[t], e));
@@ -510,6 +528,7 @@ int orc_exact_sum(int R, size_t N, int dtype, const void* send, double* out)
     int rc = check_args(R, dtype, send, out);
     if (rc)
         return rc;
+#pragma omp parallel for schedule(static)
     for (size_t e = 0; e < N; ++e) {
         double s = 0.0;
         for (int r = 0; r < R; ++r) {

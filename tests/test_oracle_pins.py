@@ -405,18 +405,6 @@ def test_bf16_matches_torch(orc):
     assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
 
 
-def test_ll_line_round_trip(orc):
-    rng = np.random.default_rng(1)
-    for _ in range(200):
-        d, f = (int(v) for v in rng.integers(0, 2 ** 32, size=2, dtype=np.uint64))
-        line = orc.ll_pack(d, f)
-        assert orc.ll_unpack(line) == (d, f)
-        assert line == (f << 32) | d
-    # float data travel as their bit pattern
-    bits = int(np.array([1.5], np.float32).view(np.uint32)[0])
-    assert orc.ll_unpack(orc.ll_pack(bits, 7)) == (0x3FC00000, 7)
-
-
 # ---------------------------------------------------------------- max / min / avg
 
 @pytest.mark.parametrize("R", [2, 3, 5, 8, 16])
@@ -563,3 +551,31 @@ def test_channel_strides_must_visit_every_rank(orc):
         orc.ring_allreduce(x, strides=[2])     # gcd(2, 4) = 2
     with pytest.raises(RuntimeError):
         orc.ring_allreduce(x, strides=[4])
+
+
+# ---------------------------------------------------------------- all-cores build
+
+@pytest.mark.parametrize("R,N", [(2, 1), (3, 1000), (8, 4097), (16, 16 * 333)])
+def test_openmp_build_gives_the_same_bits(orc, R, N):
+    """The OpenMP build parallelises only over elements (or ranks) within a
+    step, so every element keeps its fold order: the same bits as one
+    thread, for every collective and operator."""
+    rng = np.random.default_rng(R * 1000 + N)
+    x = rng.standard_normal((R, N)).astype(np.float32)
+    xi = rng.integers(-1000, 1000, size=(R, N), endpoint=True).astype(np.int32)
+    xb = orc.bf16_from_f32(x * 0.02)
+    n = N - N % R
+    want = [orc.ring_allreduce(x), orc.ring_allreduce(xi), orc.ring_allreduce(xb, "bf16"),
+            orc.ring_allreduce(x, op="max"), orc.ring_allreduce(x, op="avg"),
+            orc.tree_allreduce(x), orc.tree_allreduce(xb, "bf16"), orc.exact_sum(x),
+            orc.ring_reduce_scatter(x[:, :n]), orc.ring_all_gather(xb, "bf16"),
+            orc.ring_allreduce(x, strides=[1, R - 1] if R > 2 else [1])]
+    with orc.parallel(4) as threads:
+        assert threads == 4
+        got = [orc.ring_allreduce(x), orc.ring_allreduce(xi), orc.ring_allreduce(xb, "bf16"),
+               orc.ring_allreduce(x, op="max"), orc.ring_allreduce(x, op="avg"),
+               orc.tree_allreduce(x), orc.tree_allreduce(xb, "bf16"), orc.exact_sum(x),
+               orc.ring_reduce_scatter(x[:, :n]), orc.ring_all_gather(xb, "bf16"),
+               orc.ring_allreduce(x, strides=[1, R - 1] if R > 2 else [1])]
+    for w, g in zip(want, got):
+        assert w.tobytes() == g.tobytes()
