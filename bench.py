@@ -3,11 +3,27 @@
 
 Default run (one JSON line on stdout): ring all-reduce (sum), R = 8 logical
 ranks, float32, 16,777,216 elements (64 MiB) per rank, N(0,1) inputs from
-seed 2, simple protocol, 512 KiB chunks.  One step = one all-reduce of the
-whole [8, 16M] buffer, inputs resident in HBM before the timed region.
+seed 2, in the library's default launch form (fused: one persistent kernel;
+each wave carries a tile of every rank row through all 2(R-1) steps, the
+hand-offs stay in the XCD's L2).  One step = one all-reduce of the whole
+[8, 16M] buffer, inputs resident in HBM before the timed region.
 
   value  = busBW = algBW * 2(R-1)/R,  algBW = per-rank bytes / time
-  roofline.achieved = algorithmic HBM bytes 5(R-1) N s / kernel time
+  roofline.achieved = HBM bytes per launch / kernel time, where the HBM bytes
+           are 2 R N s for the fused form (every input row read once, every
+           output row written once: its hops are L2-served) and the hop bytes
+           5 (R-1) N s for the forms whose every hop goes through memory;
+           roofline.traffic = the bytes rocprofv3's counters saw per launch.
+  hop_rate_GBps = 5 (R-1) N s / time: every hop's load and store counted,
+           most of them served by L2 in the fused form (not an HBM rate).
+
+The same line carries, unless --no-extras: the config 3 sweep (8 B .. 1 GiB
+per rank) with its alpha-beta fit; config 4 (tree + LL against the ring
+forms, 8 B .. 256 KiB) with the crossovers and AR_AUTO's choices; a few
+config 5 gradient buckets (R = 16 bf16 reduce-scatter, all-gather, checked
+against the oracle); the pipelined ring (simple protocol, 512 KiB chunks)
+on the headline workload; and a 512 MiB copy as the streaming ceiling.
+cpu_baseline times the oracle on one thread and on all host cores.
 
 Other modes (--mode): config1 (R = 4 int32, 4096 per rank, every form), matrix
 (fused, 64 MiB per rank, R = 2..16, every dtype),
@@ -19,9 +35,11 @@ another stream).  They write a summary line to stdout (and JSON lines to
 --out where a mode has several points).
 """
 import argparse
+import contextlib
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -35,7 +53,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the traffic file stays valid while these hash the same.
 _CSRC = "collective_communication_ring_amd/csrc/"
 KERNEL_SOURCES = {
-    "fused": [_CSRC + f for f in ("ar_ring.hip", "ar_slots.h", "ar_elem.h", "ar_internal.h")],
+    "fused": [_CSRC + f for f in ("ar_fused.hip", "ar_ring.hip", "ar_slots.h", "ar_elem.h",
+                                  "ar_internal.h")],
     "step": [_CSRC + f for f in ("ar_ring.hip", "ar_slots.h", "ar_elem.h", "ar_internal.h")],
     "pipelined": [_CSRC + f for f in ("ar_pipe.hip", "ar_elem.h", "ar_internal.h")],
 }
@@ -81,7 +100,8 @@ def measured_traffic(key):
 
 def time_calls(fn, steps, warmup, torch):
     """Run fn warmup times, then time `steps` back-to-back calls with events
-    on the current stream.  Returns (per-call ms list, total ms, wall s)."""
+    on the current stream (the stream the library launches on).  Returns
+    (per-call ms list, total ms, wall s)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -97,14 +117,16 @@ def time_calls(fn, steps, warmup, torch):
     return per, ev[0].elapsed_time(ev[steps]), wall
 
 
-def time_graph(fn, calls, torch, reps=3):
-    """Capture `calls` back-to-back calls of fn in one HIP graph, replay it
-    once untimed, then time `reps` replays with events.  Returns ms per call.
-    Removes the host's enqueue pacing from small-message timings."""
+def time_graph(fn, calls, torch, reps=1, warmup=5):
+    """`warmup` eager calls, then `calls` back-to-back calls captured in one
+    HIP graph; one untimed replay, then `reps` timed replays.  Returns ms per
+    call.  Removes the host's enqueue pacing from small-message timings
+    (config 3: 5 warm-up, then 20 timed calls)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        fn()
+        for _ in range(max(1, warmup)):
+            fn()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -124,33 +146,97 @@ def time_graph(fn, calls, torch, reps=3):
     return ms
 
 
-def cpu_baseline_leg(call, target_s=3.0, max_calls=50):
+def cpu_info():
+    """Host facts for the CPU baseline: logical CPUs (nproc), the CPUs this
+    process may run on, the threads the all-cores leg uses (OMP_NUM_THREADS
+    when set, else those CPUs) and the CPU model (lscpu)."""
+    nproc = os.cpu_count()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = nproc
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                             text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    threads = int(env) if env.isdigit() and int(env) > 0 else usable
+    return dict(nproc=nproc, usable_cpus=usable, threads=threads, cpu_model=model)
+
+
+def cpu_baseline_leg(call, target_s=3.0, max_calls=50, threads=None, warmup=0):
     """The CPU-baseline leg of a mode: runs the oracle on the host, as it is,
-    for a bounded sample (at least one call, then until target_s seconds or
-    max_calls calls).  `call(oracle)` makes one oracle call.  Returns its last
-    result (which the mode also uses to check the GPU's), the average seconds
-    per call and the number of calls.  This is the only place bench.py runs
-    the oracle."""
+    for a bounded sample (`warmup` untimed calls, then at least one timed
+    call, then until target_s seconds or max_calls calls).  `call(oracle)`
+    makes one oracle call.  With `threads`, the calls run on the oracle's
+    OpenMP build with that many threads.  Returns its last result (which the
+    mode also uses to check the GPU's), the average seconds per call, the
+    number of calls and the threads used.  This and the oracle checks of the
+    extras are the only places bench.py runs the oracle."""
     import oracle
-    ts = []
-    y = None
-    t_start = time.perf_counter()
-    while not ts or (time.perf_counter() - t_start < target_s and len(ts) < max_calls):
-        t0 = time.perf_counter()
-        y = call(oracle)
-        ts.append(time.perf_counter() - t0)
-    return y, sum(ts) / len(ts), len(ts)
+    ctx = oracle.parallel(threads) if threads else contextlib.nullcontext(1)
+    with ctx as used:
+        for _ in range(warmup):
+            call(oracle)
+        ts = []
+        y = None
+        t_start = time.perf_counter()
+        while not ts or (time.perf_counter() - t_start < target_s and len(ts) < max_calls):
+            t0 = time.perf_counter()
+            y = call(oracle)
+            ts.append(time.perf_counter() - t0)
+    return y, sum(ts) / len(ts), len(ts), used
 
 
-def cpu_baseline(x, R, N, s, target_s=12.0, strides=None):
-    """The headline's CPU baseline: the full all-reduce on the host until about
-    target_s seconds of CPU work; report its busBW.  `strides` are the ring
-    channels' strides (one ring of stride 1 by default)."""
-    y, t, n = cpu_baseline_leg(lambda o: o.ring_allreduce(x, strides=strides), target_s, 100)
-    algbw = N * s / t / 1e9
-    return y, dict(value=round(algbw * 2 * (R - 1) / R, 3), unit="GB/s", cores=1, kind="oracle",
-                   sample="the full workload (8 ranks x 64 MiB), %d call(s), %.2f s each; "
-                          "single-threaded C replay of the same ring order" % (n, t))
+def cpu_baseline(x, R, N, s, strides=None):
+    """The headline's CPU baseline: the full all-reduce by the oracle, 5
+    warm-up then up to 20 timed calls (at most ~8 s) on one thread, then the
+    same on all host cores; both legs must give the same bits.  Reports the
+    all-cores busBW as `value` and the one-thread leg beside it."""
+    info = cpu_info()
+    call = lambda o: o.ring_allreduce(x, strides=strides)
+    y1, t1, n1, _ = cpu_baseline_leg(call, 8.0, 20, warmup=1)
+    yn, tn, nn, used = cpu_baseline_leg(call, 8.0, 20, threads=info["threads"], warmup=5)
+    same = y1.tobytes() == yn.tobytes()
+    busbw = lambda t: round(N * s / t / 1e9 * 2 * (R - 1) / R, 3)
+    return y1, dict(
+        value=busbw(tn), unit="GB/s", cores=used, kind="oracle",
+        sample="the full workload (8 ranks x 64 MiB per rank); all cores: %d timed call(s) after 5 "
+               "warm-up, %.3f s each, %d OpenMP threads (parallel over the elements of each "
+               "step, each element folded in the ring's order); one thread: %d call(s), %.3f s "
+               "each" % (nn, tn, used, n1, t1),
+        single_thread=dict(value=busbw(t1), unit="GB/s", cores=1, s_per_call=round(t1, 4),
+                           calls=n1),
+        all_cores=dict(value=busbw(tn), unit="GB/s", cores=used, s_per_call=round(tn, 4),
+                       calls=nn),
+        legs_bit_identical=same, **info)
+
+
+def run_extra(extras, name, fn):
+    """Run one extra measurement; a failure is reported in its key instead of
+    ending the run (its error is also logged)."""
+    t0 = time.perf_counter()
+    try:
+        extras[name] = fn()
+    except Exception as e:  # noqa: BLE001 -- reported in the output line
+        log("extra %s failed: %r" % (name, e))
+        extras[name] = dict(error=repr(e))
+    log("extra %s: %.1f s" % (name, time.perf_counter() - t0))
 
 
 def headline(args):
@@ -174,17 +260,29 @@ def headline(args):
     t = ms / 1e3
     algbw = N * s / t / 1e9
     busbw = algbw * measure.busbw_factor("allreduce", R)
-    b_alg = measure.allreduce_alg_bytes(R, N, s)
+    hop_bytes = measure.allreduce_alg_bytes(R, N, s)
+    hbm_bytes = measure.allreduce_hbm_bytes(R, N, s)
+    # the form's HBM bytes: the fused form's hops are L2-served by design;
+    # every other form moves each hop through memory
+    alg_bytes = hbm_bytes if launch_name == "fused" else hop_bytes
     kernel_ms = sum(per) / len(per)
-    achieved = b_alg / (kernel_ms / 1e3) / 1e9
-    kernel = {"fused": "k_ring_fused<float32, 16-byte slots, all-reduce>",
-              "pipelined": "k_ring_pipelined<float32, 16-byte slots, all-reduce>",
+    achieved = alg_bytes / (kernel_ms / 1e3) / 1e9
+    kernel = {"fused": "k_ring_fused_vec<float32, all-reduce, sum> (one launch)",
+              "pipelined": "k_ring_pipelined<float32, 16-byte slots, all-reduce> (one launch)",
               "ll": "k_ring_ll<float32, all-reduce> (one launch per piece)",
               "step": "k_ring_reduce_step + k_ring_copy_step (2(R-1) launches)"}[launch_name]
     if args.channels > 1:
         kernel += ", one launch per channel x %d channels" % args.channels
     traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_" + launch_name) \
         if args.channels == 1 else None
+    form = {"fused": "fused launch form: one persistent kernel, each wave64 carries a tile of "
+                     "2 KiB of every rank row through all 14 steps; every hop is a store and a "
+                     "load of the hand-off slot in the XCD's L2; no flags (tiles are "
+                     "independent), so the 512 KiB chunk does not apply",
+            "pipelined": "pipelined launch form: simple protocol, 512 KiB chunks handed from rank "
+                         "to rank through ready flags",
+            "step": "step launch form: one kernel per ring step",
+            "ll": "ring with the LL protocol (8-byte lines: 4 B data + 4 B flag)"}[launch_name]
     line = {
         "metric": METRIC,
         "value": round(busbw, 3),
@@ -199,24 +297,28 @@ def headline(args):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "ring all-reduce (sum), R=8 logical ranks, fp32, 16,777,216 "
-                               "elements (64 MiB) per rank, N(0,1) seed 2, simple protocol, "
-                               "512 KiB chunks",
+                               "elements (64 MiB) per rank, N(0,1) seed 2; " + form,
                    "R": R, "count_per_rank": N, "launch": launch_name,
                    "channels": args.channels},
         "algbw_GBps": round(algbw, 3),
         "busbw_GBps": round(busbw, 3),
-        "hbm_alg_GBps": round(b_alg / t / 1e9, 3),
-        "hbm_alg_frac_of_peak": round(b_alg / t / 1e9 / PEAK_HBM_GBPS, 4),
-        # the bytes the counters saw move (roofline.traffic) over the same time:
-        # the HBM rate proper, which the algorithmic rate overstates when the
-        # L2 serves the hand-off re-reads
-        "hbm_measured_GBps": round(traffic / (kernel_ms / 1e3) / 1e9, 3) if traffic else None,
-        "hbm_measured_frac_of_peak": round(traffic / (kernel_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+        # HBM: the bytes the form must move over the time of one call
+        "hbm_GBps": round(alg_bytes / t / 1e9, 3),
+        "hbm_frac_of_peak": round(alg_bytes / t / 1e9 / PEAK_HBM_GBPS, 4),
+        # the bytes the counters saw move, over the same time
+        "hbm_measured_GBps": round(traffic / t / 1e9, 3) if traffic else None,
+        "hbm_measured_frac_of_peak": round(traffic / t / 1e9 / PEAK_HBM_GBPS, 4)
         if traffic else None,
+        # every hop's load and store counted (L2-served in the fused form):
+        # not an HBM rate
+        "hop_rate_GBps": round(hop_bytes / t / 1e9, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": b_alg
-                     if launch_name != "step" else None},
+                     "traffic": traffic, "kernel": kernel, "alg_bytes_per_launch": alg_bytes,
+                     "alg_bytes_formula": "2 R N s (R input rows read, R output rows written)"
+                     if launch_name == "fused" else "5 (R-1) N s (every hop through memory)",
+                     "hop_bytes_per_launch": hop_bytes,
+                     "kernel_ms": round(kernel_ms, 6)},
         "wall_s_timed": round(wall, 4),
     }
     y = None
@@ -224,78 +326,277 @@ def headline(args):
         y, line["cpu_baseline"] = cpu_baseline(x, R, N, s, strides=comm.channel_strides())
     else:
         line["cpu_baseline"] = None
+    ok = True
     if y is not None:
         got = recv.cpu().numpy()
         line["verified_vs_oracle"] = bool(got.tobytes() == y.tobytes())
+        ok = line["verified_vs_oracle"] and line["cpu_baseline"]["legs_bit_identical"]
         if not line["verified_vs_oracle"]:
             log("ERROR: GPU result differs from the oracle")
+    if not args.no_extras:
+        extras = {}
+        run_extra(extras, "stream_ceiling", lambda: copy_ceiling(torch, api))
+        run_extra(extras, "pipelined_ring",
+                  lambda: pipelined_headline(torch, api, measure, send, recv, y, R, N, s))
+        del send, recv
+        torch.cuda.empty_cache()
+        run_extra(extras, "sweep", lambda: sweep_fit(torch, api, measure, inputs, np))
+        run_extra(extras, "tree_vs_ring", lambda: tree_vs_ring_fit(torch, api, measure, inputs, np))
+        run_extra(extras, "buckets", lambda: buckets_few(torch, api, measure, inputs, np,
+                                                         args.extra_buckets))
+        for k, v in extras.items():
+            line[k] = v
+            if isinstance(v, dict) and (v.get("error") or v.get("exact") is False):
+                ok = False
     print(json.dumps(line), flush=True)
-    return 0 if line.get("verified_vs_oracle", True) else 1
+    return 0 if ok else 1
 
 
-def mode_sweep(args):
-    """Config 3: ring all-reduce, R = 8, fp32, 8 B .. 1 GiB per rank in powers
-    of two, 5 warm-up + 20 timed calls each; alpha-beta fit."""
-    import torch
-    from collective_communication_ring_amd import api, inputs, measure
+def copy_ceiling(torch, api):
+    """A plain 512 MiB device copy (non-temporal loads and stores): the
+    streaming ceiling the kernels are compared with."""
+    dev = torch.device("cuda:0")
+    n = (512 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    c = torch.empty_like(a)
+    a.fill_(1)
+    st = torch.cuda.current_stream().cuda_stream
+    _, ms, _ = time_calls(lambda: api.ar_stream_copy(a.data_ptr(), c.data_ptr(), n, st), 20, 5,
+                          torch)
+    gbps = 2 * n / (ms / 20 / 1e3) / 1e9
+    del a, c
+    return dict(bytes=n, copy_GBps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4))
+
+
+def pipelined_headline(torch, api, measure, send, recv, y, R, N, s):
+    """The headline workload through the pipelined ring: the simple protocol
+    (512 KiB chunks handed on through ready flags, device-scope write-through
+    stores), one rank per XCD -- the form that maps onto one rank per GPU."""
+    comm = api.Comm(R, N, "float32", device=torch.device("cuda:0"), chunk_bytes=512 * 1024,
+                    **ring_kw("pipelined"))
+    per, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), 20, 5, torch)
+    ok = comm.check() == api.AR_SUCCESS
+    t = total_ms / 20 / 1e3
+    exact = bool(ok and (y is None or recv.cpu().numpy().tobytes() == y.tobytes()))
+    hop = measure.allreduce_alg_bytes(R, N, s)
+    traffic = measured_traffic("ring_allreduce_f32_r8_64MiB_pipelined")
+    comm.close()
+    return dict(ms=round(t * 1e3, 4), busbw_GBps=round(N * s / t / 1e9 * 1.75, 1),
+                hbm_GBps=round(hop / t / 1e9, 1), hbm_frac_of_peak=round(hop / t / 1e9 / 8000, 4),
+                traffic=traffic, exact=exact, chunk_bytes=512 * 1024)
+
+
+def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused"):
+    """Config 3: R = 8 fp32 N(0,1), 8 B .. 1 GiB per rank (28 sizes), 5
+    warm-up then 20 timed calls each (one graph replay), fit T = a + b n."""
     R, s = 8, 4
     dev = torch.device("cuda:0")
-    max_bytes = args.max_bytes
     counts = inputs.sweep_counts(8, max_bytes, s)
     Nmax = counts[-1]
     g = torch.Generator(device=dev)
     g.manual_seed(3)
-    # flat buffers: the first R*N elements viewed as [R, N] are rank-major
     send_flat = torch.randn(R * Nmax, generator=g, device=dev, dtype=torch.float32)
     recv_flat = torch.empty_like(send_flat)
-    comm = api.Comm(R, Nmax, "float32", device=dev, chunk_bytes=512 * 1024, grid=args.grid,
-                    **ring_kw(args.launch, args.channels))
-    rows = []
-    out = open(args.out, "w") if args.out else None
+    comm = api.Comm(R, Nmax, "float32", device=dev, chunk_bytes=512 * 1024, **ring_kw(launch))
+    pts = []
+    exact = True
     for N in counts:
         sv = send_flat[:R * N].view(R, N)
         rv = recv_flat[:R * N].view(R, N)
-        if args.eager:
-            per, total_ms, _ = time_calls(lambda: comm.allreduce(sv, rv), 20, 5, torch)
-            t = total_ms / 20 / 1e3
-        else:
-            t = time_graph(lambda: comm.allreduce(sv, rv), 20, torch) / 1e3
-        row = dict(mode="sweep", bytes_per_rank=N * s, count=N, t_us=t * 1e6,
-                   algbw_GBps=N * s / t / 1e9,
-                   busbw_GBps=N * s / t / 1e9 * measure.busbw_factor("allreduce", R),
-                   hbm_alg_GBps=measure.allreduce_alg_bytes(R, N, s) / t / 1e9,
-                   launch=args.launch)
-        rows.append(row)
-        log("sweep %10d B/rank  %10.2f us  busBW %8.2f GB/s" % (N * s, t * 1e6, row["busbw_GBps"]))
-        if out:
-            out.write(json.dumps(row) + "\n")
-            out.flush()
-        del sv, rv
-    assert comm.check() == api.AR_SUCCESS
-    cpu = []
-    for N in [n for n in (256, 65536, 1 << 22) if n <= Nmax]:  # 1 KiB, 256 KiB, 16 MiB per rank
-        xs = send_flat[:R * N].view(R, N).cpu().numpy()
-        _, t_or, n_or = cpu_baseline_leg(lambda o: o.ring_allreduce(xs), 3.0)
-        cpu.append(dict(bytes_per_rank=N * s, t_us=t_or * 1e6, calls=n_or))
-        log("oracle %10d B/rank  %10.1f us" % (N * s, t_or * 1e6))
-    fit = measure.fit_alpha_beta([r["bytes_per_rank"] for r in rows], [r["t_us"] / 1e6 for r in rows])
-    small = [r["t_us"] for r in rows if r["bytes_per_rank"] <= 4096]
-    large = [r for r in rows if r["bytes_per_rank"] >= 64 << 20]
-    cross = {}
+        t = time_graph(lambda: comm.allreduce(sv, rv), 20, torch) / 1e3
+        pts.append([N * s, round(t * 1e6, 3)])
+        if N * s <= (1 << 20):  # check the small and mid sizes against the oracle
+            xs = sv.cpu().numpy()
+            ref, _, _, _ = cpu_baseline_leg(lambda o: o.ring_allreduce(xs), 0.0, 1,
+                                            threads=cpu_info()["threads"])
+            exact &= rv.cpu().numpy().tobytes() == ref.tobytes()
+    exact &= comm.check() == api.AR_SUCCESS
+    comm.close()
+    del send_flat, recv_flat
+    torch.cuda.empty_cache()
+    n = [p[0] for p in pts]
+    ts = [p[1] / 1e6 for p in pts]
+    fit = measure.fit_alpha_beta(n, ts)
+    small = sorted(p[1] for p in pts if p[0] <= 4096)
+    large = [p for p in pts if p[0] >= 64 << 20]
+    out = dict(launch=launch, R=R, dtype="f32", sizes=len(pts), timing="5 warm-up + 20 timed "
+               "calls per size, one graph replay", exact_up_to_1MiB=bool(exact), exact=bool(exact),
+               alpha_us=round(fit["alpha_us"], 3), inv_beta_GBps=round(fit["inv_beta_GBps"], 1),
+               bus_rate_GBps=round(fit["inv_beta_GBps"] * measure.busbw_factor("allreduce", R), 1),
+               r2=round(fit["r2"], 5), max_rel_residual=round(fit["max_rel_residual"], 4),
+               points_bytes_us=pts)
     if small:
-        cross["alpha_median_small_us"] = sorted(small)[len(small) // 2]
+        out["alpha_median_le_4KiB_us"] = small[len(small) // 2]
     if len(large) >= 2:
         a, b = large[0], large[-1]
-        cross["inv_beta_large_GBps"] = (b["bytes_per_rank"] - a["bytes_per_rank"]) / (
-            (b["t_us"] - a["t_us"]) / 1e6) / 1e9
-    summary = dict(mode="sweep_fit", R=R, dtype="f32", launch=args.launch, **fit,
-                   bus_rate_GBps=fit["inv_beta_GBps"] * measure.busbw_factor("allreduce", R),
-                   **cross, cpu_baseline=dict(kind="oracle", cores=1, points=cpu))
-    if out:
-        out.write(json.dumps(summary) + "\n")
-        out.close()
-    print(json.dumps(summary), flush=True)
-    return 0
+        out["inv_beta_ge_64MiB_GBps"] = round((b[0] - a[0]) / ((b[1] - a[1]) / 1e6) / 1e9, 1)
+    return out
+
+
+TVR_VARIANTS = [("tree-ll", dict(algo="tree", proto="ll")),
+                ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
+                ("ring-pipelined", dict(algo="ring", proto="simple", launch="pipelined")),
+                ("ring-ll", dict(algo="ring", proto="ll")),
+                ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
+
+
+def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024):
+    """Config 4: R = 8 fp32 U[-1,1), 8 B .. 256 KiB per rank (16 sizes): the
+    double binary tree with LL against every ring form (5 warm-up + 20 timed
+    calls per size, one graph replay); an alpha-beta fit per variant, the
+    crossover of the tree with each ring form (measured and from the fits),
+    and AR_AUTO's choice before and after loading the fitted lines."""
+    R, s = 8, 4
+    dev = torch.device("cuda:0")
+    counts = inputs.sweep_counts(8, max_bytes, s)
+    Nmax = counts[-1]
+    x = inputs.draw("uniform_pm1", R, Nmax, seed=4)
+    send_flat = torch.from_numpy(x).to(dev).reshape(-1)
+    recv_flat = torch.empty_like(send_flat)
+    comms = {name: api.Comm(R, Nmax, "float32", device=dev, **kw) for name, kw in TVR_VARIANTS}
+    res = {name: [] for name, _ in TVR_VARIANTS}
+    exact = True
+    threads = cpu_info()["threads"]
+    for N in counts:
+        sv = send_flat[:R * N].view(R, N)
+        rv = recv_flat[:R * N].view(R, N)
+        xs = sv.cpu().numpy()
+        for name, _ in TVR_VARIANTS:
+            c = comms[name]
+            res[name].append(round(time_graph(lambda: c.allreduce(sv, rv), 20, torch) * 1e3, 3))
+            if N in (counts[0], counts[len(counts) // 2], counts[-1]):
+                ref, _, _, _ = cpu_baseline_leg(
+                    (lambda o: o.tree_allreduce(xs)) if name == "tree-ll"
+                    else (lambda o: o.ring_allreduce(xs)), 0.0, 1, threads=threads)
+                exact &= rv.cpu().numpy().tobytes() == ref.tobytes()
+    for c in comms.values():
+        exact &= c.check() == api.AR_SUCCESS
+        c.close()
+    sizes = [n * s for n in counts]
+    fits = {name: measure.fit_alpha_beta(sizes, [t / 1e6 for t in ts]) for name, ts in res.items()}
+    crossover = {}
+    for name, _ in TVR_VARIANTS[1:]:
+        # the smallest size from which this ring form is faster than the tree
+        # at every larger size of the range
+        meas = None
+        for i in range(len(sizes)):
+            if all(res[name][j] < res["tree-ll"][j] for j in range(i, len(sizes))):
+                meas = sizes[i]
+                break
+        fitted = measure.crossover_bytes(fits["tree-ll"], fits[name])
+        crossover[name] = dict(measured_bytes=meas,
+                               fit_bytes=round(fitted) if fitted is not None else None)
+    # AR_AUTO's choice for each ring form: with the library's default lines,
+    # then with the lines fitted here; and how often the choice matches the
+    # faster of the two measured times
+    probe = api.Comm(R, Nmax, "float32", "auto", device=dev)
+    auto = {}
+    forms = {"ring-fused": dict(launch=api.AR_LAUNCH_FUSED, proto=api.AR_SIMPLE),
+             "ring-pipelined": dict(launch=api.AR_LAUNCH_PIPELINED, proto=api.AR_SIMPLE),
+             "ring-step": dict(launch=api.AR_LAUNCH_STEP, proto=api.AR_SIMPLE),
+             "ring-ll": dict(launch=api.AR_LAUNCH_FUSED, proto=api.AR_LL)}
+
+    def choices():
+        out = {}
+        for name, f in forms.items():
+            probe.set_option(api.AR_OPT_LAUNCH, f["launch"])
+            probe.set_option(api.AR_OPT_PROTO, f["proto"])
+            plan = [probe.plan(n)[0] for n in counts]
+            faster = [api.AR_TREE if res["tree-ll"][i] < res[name][i] else api.AR_RING
+                      for i in range(len(counts))]
+            out[name] = dict(tree_max_bytes=api.ar_auto_tree_max_bytes(probe.handle),
+                             matches_measured=sum(p == q for p, q in zip(plan, faster)),
+                             of=len(counts))
+        return out
+
+    auto["default_lines"] = choices()
+    for name, f in fits.items():
+        # a line that barely rises over this range fits a huge (or negative)
+        # bandwidth: cap it at 1e6 GB/s, which adds < 1 ns at 256 KiB
+        bw = f["inv_beta_GBps"]
+        bw = 1e6 if not (0 < bw < 1e6) else bw
+        api.ar_set_cost(probe.handle, api.COST_FORMS[name], max(0.0, f["alpha_us"]), bw)
+    auto["fitted_lines"] = choices()
+    probe.close()
+    hop = ll_hop_latency_us(torch)
+    st = torch.cuda.current_stream().cuda_stream
+    floor = time_graph(lambda: api.ar_stream_copy(send_flat.data_ptr(), recv_flat.data_ptr(), 16,
+                                                  st), 20, torch) * 1e3
+    del send_flat, recv_flat
+    _, t_or, n_or, used = cpu_baseline_leg(lambda o: o.tree_allreduce(x), 1.0, 5)
+    return dict(R=R, dtype="f32", sizes_bytes=sizes, t_us=res, exact=bool(exact),
+                fits={k: dict(alpha_us=round(v["alpha_us"], 3),
+                              inv_beta_GBps=round(v["inv_beta_GBps"], 2), r2=round(v["r2"], 4))
+                      for k, v in fits.items()},
+                crossover=crossover, auto=auto, ll_hop_us=hop, tree_hops=2 * 3,
+                ring_hops=2 * (R - 1), launch_floor_us=round(floor, 3),
+                cpu_baseline=dict(kind="oracle", cores=used, us_per_call=round(t_or * 1e6, 1),
+                                  sample="tree all-reduce at 256 KiB per rank, %d call(s)" % n_or))
+
+
+def buckets_few(torch, api, measure, inputs, np, nb=4):
+    """Config 5 on its first `nb` buckets: R = 16 bf16 N(0,0.02), 13,107,200
+    elements (25 MiB) per rank each; reduce-scatter, then all-gather, then
+    all-reduce of every bucket in turn, timed per bucket (5 warm-up passes
+    over the buckets, then 20 timed).  Every bucket is checked: the
+    reduce-scatter against the oracle's, the all-gather against the oracle's
+    all-gather of those shards, and RS then AG equal to the all-reduce bit for
+    bit."""
+    w = inputs.WORKLOADS["buckets_bf16_r16"]
+    R, N, s = w["R"], w["count"], 2
+    n = N // R
+    dev = torch.device("cuda:0")
+    xs = [inputs.device_bucket_bf16(R, N, w["seed"], b, dev) for b in range(nb)]
+    shards = [torch.empty((R, n), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    fulls = [torch.empty((R, N), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    ars = [torch.empty((R, N), dtype=torch.bfloat16, device=dev) for _ in range(nb)]
+    comm = api.Comm(R, N, "bf16", device=dev)
+
+    def each(fn):
+        return lambda: [fn(b) for b in range(nb)]
+
+    out = {}
+    for name, fn, hbm in (
+            ("reduce_scatter", each(lambda b: comm.reduce_scatter(xs[b], shards[b])),
+             measure.reduce_scatter_hbm_bytes(R, N, s)),
+            ("all_gather", each(lambda b: comm.all_gather(shards[b], fulls[b])),
+             measure.all_gather_hbm_bytes(R, N, s)),
+            ("allreduce", each(lambda b: comm.allreduce(xs[b], ars[b])),
+             measure.allreduce_hbm_bytes(R, N, s))):
+        _, total_ms, _ = time_calls(fn, 20, 5, torch)
+        t = total_ms / 20 / nb / 1e3
+        f = measure.busbw_factor("allreduce" if name == "allreduce" else "rs", R)
+        out[name] = dict(us_per_bucket=round(t * 1e6, 2), busbw_GBps=round(N * s / t / 1e9 * f, 1),
+                         hbm_GBps=round(hbm / t / 1e9, 1),
+                         hbm_frac_of_peak=round(hbm / t / 1e9 / PEAK_HBM_GBPS, 4))
+    ok = comm.check() == api.AR_SUCCESS
+    threads = cpu_info()["threads"]
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(nb):
+        xb = bits(xs[b])
+        ref_rs, _, _, _ = cpu_baseline_leg(lambda o: o.ring_reduce_scatter(xb, "bf16"), 0.0, 1,
+                                           threads=threads)
+        ref_ag, _, _, _ = cpu_baseline_leg(lambda o: o.ring_all_gather(ref_rs, "bf16"), 0.0, 1,
+                                           threads=threads)
+        ok &= np.array_equal(bits(shards[b]), ref_rs)
+        ok &= np.array_equal(bits(fulls[b]), ref_ag)
+        ok &= torch.equal(fulls[b].view(torch.int16), ars[b].view(torch.int16))
+    comm.close()
+    del xs, shards, fulls, ars
+    torch.cuda.empty_cache()
+    return dict(R=R, dtype="bf16", buckets=nb, count_per_rank=N, exact=bool(ok), **out)
+
+
+def mode_sweep(args):
+    """Config 3 alone: ring all-reduce, R = 8, fp32, 8 B .. --max-bytes per
+    rank in powers of two, 5 warm-up + 20 timed calls each; alpha-beta fit."""
+    import numpy as np
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+    out = sweep_fit(torch, api, measure, inputs, np, args.max_bytes, args.launch
+                    if args.launch != "auto" else "fused")
+    print(json.dumps(dict(mode="sweep_fit", **out)), flush=True)
+    return 0 if out["exact"] else 1
 
 
 def ll_hop_latency_us(torch, iters=20000):
@@ -322,63 +623,14 @@ def ll_hop_latency_us(torch, iters=20000):
 
 
 def mode_tree_vs_ring(args):
-    """Config 4: R = 8, fp32 U[-1,1), 8 B .. 256 KiB per rank; tree + LL
-    against ring (fused and step) at the same sizes."""
+    """Config 4 alone (up to --tvr-max-bytes per rank): tree + LL against every
+    ring form, fits, crossovers and AR_AUTO's choices."""
+    import numpy as np
     import torch
-    from collective_communication_ring_amd import api, inputs
-    R, s = 8, 4
-    dev = torch.device("cuda:0")
-    counts = inputs.sweep_counts(8, args.tvr_max_bytes, s)
-    Nmax = counts[-1]
-    x = inputs.draw("uniform_pm1", R, Nmax, seed=4)
-    send_flat = torch.from_numpy(x).to(dev).reshape(-1)
-    recv_flat = torch.empty_like(send_flat)
-    variants = [("tree-ll", dict(algo="tree", proto="ll")),
-                ("ring-ll", dict(algo="ring", proto="ll")),
-                ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
-                ("ring-pipelined", dict(algo="ring", proto="simple", launch="pipelined")),
-                ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
-    comms = {name: api.Comm(R, Nmax, "float32", device=dev, **kw) for name, kw in variants}
-    out = open(args.out, "w") if args.out else None
-    res = {}
-    for N in counts:
-        sv = send_flat[:R * N].view(R, N)
-        rv = recv_flat[:R * N].view(R, N)
-        for name, _ in variants:
-            c = comms[name]
-            if args.eager:
-                _, total_ms, _ = time_calls(lambda: c.allreduce(sv, rv), 20, 5, torch)
-                t_us = total_ms / 20 * 1e3
-            else:
-                t_us = time_graph(lambda: c.allreduce(sv, rv), 20, torch) * 1e3
-            res.setdefault(name, []).append(t_us)
-            row = dict(mode="tree_vs_ring", variant=name, bytes_per_rank=N * s, t_us=t_us)
-            log("%-10s %8d B/rank %9.2f us" % (name, N * s, t_us))
-            if out:
-                out.write(json.dumps(row) + "\n")
-    for c in comms.values():
-        assert c.check() == api.AR_SUCCESS
-    hop = ll_hop_latency_us(torch)
-    log("LL one-way hop latency: %s" % hop)
-    # the launch floor: one single-workgroup kernel (a 16-byte copy) per call
-    st = lambda: torch.cuda.current_stream().cuda_stream
-    launch_floor = time_graph(lambda: api.ar_stream_copy(send_flat.data_ptr(), recv_flat.data_ptr(),
-                                                         16, st()), 20, torch) * 1e3
-    log("launch floor (16-byte copy kernel, graph-replayed): %.2f us" % launch_floor)
-    # latency roofline of the tree: 2 * depth hops (up, then down) per call
-    depth = 3 if R == 8 else None
-    _, t_or, n_or = cpu_baseline_leg(lambda o: o.tree_allreduce(x), 3.0)
-    summary = dict(mode="tree_vs_ring_summary", sizes=[n * s for n in counts], t_us=res,
-                   ll_hop_us=hop, tree_depth=depth, launch_floor_us=launch_floor,
-                   tree_hop_bound_us=2 * depth * hop["xcd_apart"] if depth else None,
-                   cpu_baseline=dict(kind="oracle", cores=1, value_us=t_or * 1e6,
-                                     sample="tree all-reduce, %d B/rank, %d calls"
-                                            % (Nmax * s, n_or)))
-    if out:
-        out.write(json.dumps(summary) + "\n")
-        out.close()
-    print(json.dumps(summary), flush=True)
-    return 0
+    from collective_communication_ring_amd import api, inputs, measure
+    out = tree_vs_ring_fit(torch, api, measure, inputs, np, args.tvr_max_bytes)
+    print(json.dumps(dict(mode="tree_vs_ring", **out)), flush=True)
+    return 0 if out["exact"] else 1
 
 
 def mode_buckets(args):
@@ -421,8 +673,8 @@ def mode_buckets(args):
     assert comm.check() == api.AR_SUCCESS
     import numpy as np
     xh = xs[0].view(torch.int16).cpu().numpy().view(np.uint16)
-    sh, t_rs, _ = cpu_baseline_leg(lambda o: o.ring_reduce_scatter(xh, "bf16"), 0.0, 1)
-    _, t_ag, _ = cpu_baseline_leg(lambda o: o.ring_all_gather(sh, "bf16"), 0.0, 1)
+    sh, t_rs, _, _ = cpu_baseline_leg(lambda o: o.ring_reduce_scatter(xh, "bf16"), 0.0, 1)
+    _, t_ag, _, _ = cpu_baseline_leg(lambda o: o.ring_all_gather(sh, "bf16"), 0.0, 1)
     rep["cpu_baseline"] = dict(kind="oracle", cores=1, sample="bucket 0, one call each",
                                reduce_scatter_us=t_rs * 1e6, all_gather_us=t_ag * 1e6)
     summary = dict(mode="buckets", R=R, dtype="bf16", buckets=B, count_per_rank=N, **rep)
@@ -555,7 +807,8 @@ def mode_overlap(args):
 def mode_counters(args):
     """A short program for byte-counter runs (rocprofv3 --pmc): a copy of a
     known size (the calibration), then 3 all-reduces of the headline workload
-    in each launch form, then a small tree-LL all-reduce."""
+    in each launch form, then 3 small tree-LL all-reduces, then 3 reduce-
+    scatters, all-gathers and all-reduces of one config 5 bucket."""
     import torch
     from collective_communication_ring_amd import api, inputs
     dev = torch.device("cuda:0")
@@ -582,7 +835,23 @@ def mode_counters(args):
     for _ in range(3):
         comm.allreduce(small, out)
     torch.cuda.synchronize()
-    print(json.dumps(dict(mode="counters", copy_bytes=n * 4, allreduce_count=N)), flush=True)
+    del send, recv, small, out
+    # one gradient bucket of config 5: reduce-scatter, all-gather, all-reduce
+    w = inputs.WORKLOADS["buckets_bf16_r16"]
+    Rb, Nb = w["R"], w["count"]
+    xb = inputs.device_bucket_bf16(Rb, Nb, w["seed"], 0, dev)
+    shard = torch.empty((Rb, Nb // Rb), dtype=torch.bfloat16, device=dev)
+    full = torch.empty((Rb, Nb), dtype=torch.bfloat16, device=dev)
+    comm = api.Comm(Rb, Nb, "bf16", device=dev)
+    for _ in range(3):
+        comm.reduce_scatter(xb, shard)
+    for _ in range(3):
+        comm.all_gather(shard, full)
+    for _ in range(3):
+        comm.allreduce(xb, full)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(mode="counters", copy_bytes=n * 4, allreduce_count=N,
+                          bucket_count=Nb)), flush=True)
     return 0
 
 
@@ -596,7 +865,7 @@ def mode_config1(args):
     R, N = 4, 4096
     dev = torch.device("cuda:0")
     x = inputs.host_inputs("ring_int32_r4")
-    ref, t_or, n_or = cpu_baseline_leg(lambda o: o.ring_allreduce(x), 2.0)
+    ref, t_or, n_or, _ = cpu_baseline_leg(lambda o: o.ring_allreduce(x), 2.0)
     exact = x.astype(np.int64).sum(axis=0).astype(np.int32)
     send = torch.from_numpy(x).to(dev)
     recv = torch.empty_like(send)
@@ -647,7 +916,7 @@ def mode_matrix(args):
             t = total_ms / args.steps / 1e3
             got = recv.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" \
                 else recv.cpu().numpy()
-            ref, t_or, _ = cpu_baseline_leg(lambda o: o.ring_allreduce(x, dtype), 0.0, 1)
+            ref, t_or, _, _ = cpu_baseline_leg(lambda o: o.ring_allreduce(x, dtype), 0.0, 1)
             exact = got.tobytes() == ref.tobytes()
             row = dict(dtype=dtype, R=R, bytes_per_rank=N * s, ms=round(t * 1e3, 4),
                        busbw_GBps=round(N * s / t / 1e9 * measure.busbw_factor("allreduce", R), 1),
@@ -686,7 +955,7 @@ def mode_tune(args):
         comm = api.Comm(R, N, "float32", device=dev, chunk_bytes=args.chunk_bytes, grid=grid,
                         **ring_kw(args.launch, args.channels))
         if ref is None:
-            ref, t_or, _ = cpu_baseline_leg(
+            ref, t_or, _, _ = cpu_baseline_leg(
                 lambda o: o.ring_allreduce(x, strides=comm.channel_strides()), 0.0, 1)
         _, total_ms, _ = time_calls(lambda: comm.allreduce(send, recv), args.steps, args.warmup,
                                     torch)
@@ -723,6 +992,11 @@ def main():
                     help="overlap mode: CUs reserved for the collective (0: no CU masks)")
     ap.add_argument("--chunk-bytes", type=int, default=512 * 1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline: only the headline workload (no sweep, tree-vs-ring, buckets, "
+                         "pipelined ring or copy ceiling)")
+    ap.add_argument("--extra-buckets", type=int, default=4,
+                    help="headline: config 5 buckets timed and checked in the extras")
     ap.add_argument("--channels", type=int, default=1,
                     help="ring channels (each its own ring stride over a sub-range of "
                          "every segment)")

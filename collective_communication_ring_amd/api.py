@@ -25,6 +25,11 @@ AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 
  AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK, AR_OPT_REDOP,
  AR_OPT_CHANNELS) = range(11)
 AR_SUM, AR_MAX, AR_MIN, AR_AVG = 0, 1, 2, 3
+(AR_COST_TREE_LL, AR_COST_RING_FUSED, AR_COST_RING_PIPELINED, AR_COST_RING_STEP,
+ AR_COST_RING_LL) = range(5)
+COST_FORMS = {"tree-ll": AR_COST_TREE_LL, "ring-fused": AR_COST_RING_FUSED,
+              "ring-pipelined": AR_COST_RING_PIPELINED, "ring-step": AR_COST_RING_STEP,
+              "ring-ll": AR_COST_RING_LL}
 REDOPS = {"sum": AR_SUM, "max": AR_MAX, "min": AR_MIN, "avg": AR_AVG}
 
 DTYPES = {"int32": AR_INT32, "float32": AR_FLOAT32, "bf16": AR_BF16}
@@ -64,6 +69,9 @@ def lib():
         "ar_set_option": ([vp, i, i64], i),
         "ar_get_option": ([vp, i, ctypes.POINTER(i64)], i),
         "ar_plan": ([vp, sz, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
+        "ar_set_cost": ([vp, i, ctypes.c_double, ctypes.c_double], i),
+        "ar_get_cost": ([vp, i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], i),
+        "ar_auto_tree_max_bytes": ([vp], i64),
         "ar_ring_segment": ([vp, sz, i, ctypes.POINTER(sz), ctypes.POINTER(sz)], i),
         "ar_tree_parent": ([vp, i, i], i),
         "ar_ring_channel_stride": ([vp, i], i),
@@ -140,6 +148,20 @@ def ar_plan(comm, count):
     a, p, l = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _ok(lib().ar_plan(comm, count, ctypes.byref(a), ctypes.byref(p), ctypes.byref(l)), "ar_plan")
     return a.value, p.value, l.value
+
+
+def ar_set_cost(comm, form, alpha_us, bw_gbps):
+    _ok(lib().ar_set_cost(comm, form, alpha_us, bw_gbps), "ar_set_cost")
+
+
+def ar_get_cost(comm, form):
+    a, b = ctypes.c_double(), ctypes.c_double()
+    _ok(lib().ar_get_cost(comm, form, ctypes.byref(a), ctypes.byref(b)), "ar_get_cost")
+    return a.value, b.value
+
+
+def ar_auto_tree_max_bytes(comm):
+    return int(lib().ar_auto_tree_max_bytes(comm))
 
 
 def ar_ring_segment(comm, count, c):

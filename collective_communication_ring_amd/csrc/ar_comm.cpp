@@ -24,9 +24,21 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kDefaultChunkBytes = 512 * 1024;
 constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
-// AR_AUTO: tree up to this many bytes per rank (the measured crossover with
-// the pipelined ring at R = 8: the tree wins at 256 KiB, the ring at 512 KiB)
-constexpr int64_t kDefaultTreeMaxBytes = 256 * 1024;
+// AR_AUTO's cost model: one line T(n) = alpha + n / bw per algorithm and ring
+// launch form (n = bytes per rank), indexed by ar_cost_form_t.  Defaults are
+// least-squares fits (weighted by 1/T^2) of graph-replayed all-reduces on
+// MI355X, R = 8 float32, 8 B - 256 KiB per rank.
+struct CostLine {
+    double alpha_us;
+    double bw_gbps;
+};
+constexpr CostLine kDefaultCost[AR_COST_FORMS] = {
+    {8.3, 27.0},    // tree + LL
+    {5.4, 350.0},   // ring, fused
+    {20.5, 180.0},  // ring, pipelined (simple protocol: ready flags)
+    {27.5, 190.0},  // ring, one launch per step
+    {19.5, 120.0},  // ring + LL
+};
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
 constexpr uint64_t kMaxChunkBytes = 1ull << 30;      // pipelined ring: largest chunk
 
@@ -117,7 +129,9 @@ struct ar_comm {
     int64_t grid = 0;
     int64_t timeout_us = kDefaultTimeoutUs;
     int64_t debug = 0;
-    int64_t tree_max_bytes = kDefaultTreeMaxBytes;
+    int64_t tree_max_bytes = -1;  // AR_AUTO: -1 = by the cost model, else a fixed threshold
+    CostLine cost[AR_COST_FORMS] = {kDefaultCost[0], kDefaultCost[1], kDefaultCost[2],
+                                    kDefaultCost[3], kDefaultCost[4]};
     int64_t mute_rank = -1;  // testing the watchdog only
     int64_t redop = AR_SUM;
     int64_t channels = 1;
@@ -205,19 +219,39 @@ int resolve_launch(const ar_comm* c)
     return AR_LAUNCH_FUSED;
 }
 
-// AR_AUTO: tree for small messages, ring for large ones ("NCCL and NVSHMEM
-// -- two GPU communication models, side by side": NCCL picks by size).  The
-// threshold is the measured crossover between the tree and the ring forms in
-// which every hop is a hand-off between ranks (step, pipelined).  The fused
-// ring has no hand-offs and is faster than the tree at every size on one
-// GPU, so with it the ring is kept.
+// The cost-model line of the ring as this comm would run it.
+int ring_cost_form(const ar_comm* c)
+{
+    if (c->proto == AR_LL)
+        return AR_COST_RING_LL;
+    switch (resolve_launch(c)) {
+    case AR_LAUNCH_STEP:
+        return AR_COST_RING_STEP;
+    case AR_LAUNCH_PIPELINED:
+        return AR_COST_RING_PIPELINED;
+    default:
+        return AR_COST_RING_FUSED;
+    }
+}
+
+double cost_us(const CostLine& l, double bytes) { return l.alpha_us + bytes / (l.bw_gbps * 1e3); }
+
+// AR_AUTO: tree for small messages, ring for large ones, chosen by size
+// ("NCCL and NVSHMEM -- two GPU communication models, side by side": the
+// tree for latency at small sizes, the ring for bandwidth at large ones, and
+// NCCL picks automatically).  The choice is whichever line of the cost model
+// is lower at this size: the tree's, or that of the ring form the call would
+// use.  A fixed threshold (AR_OPT_TREE_MAX_BYTES >= 0) overrides the model.
 int resolve_algo(const ar_comm* c, size_t count)
 {
     if (c->algo != AR_AUTO)
         return c->algo;
-    if (resolve_launch(c) == AR_LAUNCH_FUSED)
-        return AR_RING;
-    return (int64_t)(count * (size_t)elem_size(c->dtype)) <= c->tree_max_bytes ? AR_TREE : AR_RING;
+    const double bytes = (double)count * elem_size(c->dtype);
+    if (c->tree_max_bytes >= 0)
+        return bytes <= (double)c->tree_max_bytes ? AR_TREE : AR_RING;
+    return cost_us(c->cost[AR_COST_TREE_LL], bytes) < cost_us(c->cost[ring_cost_form(c)], bytes)
+               ? AR_TREE
+               : AR_RING;
 }
 
 // Do the 16-byte vector kernels apply?  Every row start and every segment
@@ -385,6 +419,16 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         const uint64_t waves = (uint64_t)(kBlock / 64);
         const int64_t want = c->grid > 0 ? c->grid : 2 * (int64_t)c->ncu;
         uint64_t g = std::min<uint64_t>((units + waves - 1) / waves, (uint64_t)want);
+        // does any segment of this channel end inside a tile? (then the kernel
+        // with the checked path for a segment's last tile is launched)
+        a.ragged = 0;
+        for (int sc = 0; sc < a.R && !a.ragged; ++sc) {
+            const uint64_t slo = std::min<uint64_t>((uint64_t)sc * a.S, a.N);
+            const uint64_t send_ = std::min<uint64_t>((uint64_t)(sc + 1) * a.S, a.N);
+            const uint64_t x0 = std::min<uint64_t>(slo + a.sub_lo, send_);
+            const uint64_t x1 = std::min<uint64_t>(slo + a.sub_lo + a.sub_len, send_);
+            a.ragged = ((x1 - x0) % (kWaveTileSlots * V)) != 0;
+        }
         a.stage_wave = 0;
         a.max_units = 0xffffffffu;
         if (a.op != kOpAllGather && a.part == (void*)(c->ws + c->off_part)) {
@@ -853,7 +897,7 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
         c->proto = (int)v;
         return AR_SUCCESS;
     case AR_OPT_TREE_MAX_BYTES:
-        if (v < 0)
+        if (v < -1)
             return AR_ERR_INVALID_ARG;
         c->tree_max_bytes = v;
         return AR_SUCCESS;
@@ -904,6 +948,50 @@ int ar_plan(ar_comm_t c, size_t count, int* algo, int* proto, int* launch)
     *proto = (*algo == AR_TREE) ? AR_LL : c->proto;
     *launch = (*algo == AR_TREE || *proto == AR_LL) ? AR_LAUNCH_AUTO : resolve_launch(c);
     return AR_SUCCESS;
+}
+
+int ar_set_cost(ar_comm_t c, int form, double alpha_us, double bw_gbps)
+{
+    // written as negations so that a NaN is refused too
+    if (!c || form < 0 || form >= AR_COST_FORMS || !(alpha_us >= 0.0) || !(bw_gbps > 0.0) ||
+        !(alpha_us < 1e9) || !(bw_gbps < 1e9))
+        return AR_ERR_INVALID_ARG;
+    c->cost[form] = CostLine{alpha_us, bw_gbps};
+    return AR_SUCCESS;
+}
+
+int ar_get_cost(ar_comm_t c, int form, double* alpha_us, double* bw_gbps)
+{
+    if (!c || form < 0 || form >= AR_COST_FORMS || !alpha_us || !bw_gbps)
+        return AR_ERR_INVALID_ARG;
+    *alpha_us = c->cost[form].alpha_us;
+    *bw_gbps = c->cost[form].bw_gbps;
+    return AR_SUCCESS;
+}
+
+int64_t ar_auto_tree_max_bytes(ar_comm_t c)
+{
+    if (!c)
+        return -1;
+    if (c->tree_max_bytes >= 0)
+        return c->tree_max_bytes;
+    // the lines cross once at most: the tree is cheaper below the crossing
+    const CostLine t = c->cost[AR_COST_TREE_LL], r = c->cost[ring_cost_form(c)];
+    const double bt = 1.0 / (t.bw_gbps * 1e3), br = 1.0 / (r.bw_gbps * 1e3);  // us per byte
+    if (t.alpha_us >= r.alpha_us && bt >= br)
+        return 0;  // the ring is never slower
+    if (t.alpha_us < r.alpha_us && bt <= br)
+        return INT64_MAX;  // the tree is never slower
+    const double n = (r.alpha_us - t.alpha_us) / (bt - br);
+    if (n <= 0.0)
+        return 0;
+    if (n >= 9e18)
+        return INT64_MAX;
+    // the largest size the tree still takes (resolve_algo's strict <)
+    int64_t b = (int64_t)n;
+    while (b > 0 && !(cost_us(t, (double)b) < cost_us(r, (double)b)))
+        --b;
+    return b;
 }
 
 int ar_ring_segment(ar_comm_t c, size_t count, int seg, size_t* lo, size_t* hi)

@@ -54,10 +54,12 @@ typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
  * NVSHMEM -- two GPU communication models, side by side", section "double
  * binary tree").  AR_AUTO picks by message size: tree for small messages,
  * ring for large ones (same page: tree for small messages, ring for large,
- * chosen automatically) -- when the ring would run in a form whose every
- * step is a hand-off between ranks (AR_LAUNCH_STEP / AR_LAUNCH_PIPELINED);
- * the default fused ring is faster than the tree at every size on one GPU
- * and is kept. */
+ * chosen automatically).  The choice compares two lines of a cost model
+ * (ar_set_cost): the tree's and the one of the ring launch form the call
+ * would use.  With the default fused ring, whose latency floor is below the
+ * tree's on one GPU, the model keeps the ring at every size; with a form in
+ * which every step is a hand-off between ranks (AR_LAUNCH_STEP,
+ * AR_LAUNCH_PIPELINED, AR_LL) it sends small messages by tree. */
 typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
 
 /* AR_SIMPLE: bulk data, then a release, then a ready flag (or a kernel
@@ -122,8 +124,8 @@ typedef enum {
     AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
     AR_OPT_PROTO = 6,         /* an ar_proto_t, overriding the one given to ar_init */
-    AR_OPT_TREE_MAX_BYTES = 7, /* AR_AUTO: largest per-rank message sent by tree
-                                  (default 256 KiB) */
+    AR_OPT_TREE_MAX_BYTES = 7, /* AR_AUTO: largest per-rank message (bytes) sent by tree;
+                                  -1 (default) = chosen by the cost model (ar_set_cost) */
     AR_OPT_DEBUG_MUTE_RANK = 8, /* testing the watchdog only: this logical rank's workgroups
                                    skip publishing (LL lines, ready flags), so its consumers'
                                    bounded waits expire; -1 (default) = none */
@@ -205,6 +207,31 @@ int ar_get_option(ar_comm_t comm, int option, int64_t* value);
 /* Resolved algorithm, protocol and launch that a call with `count` elements
  * per rank would use (values of ar_algo_t, ar_proto_t, ar_launch_t). */
 int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
+
+/* The cost model behind AR_AUTO: for each algorithm and ring launch form a
+ * line T(n) = alpha_us + n / (bw_gbps * 1e3) microseconds, n = bytes per
+ * rank -- the alpha-beta model ("NCCL and NVSHMEM -- two GPU communication
+ * models, side by side", cost-model paragraph: alpha is the latency floor,
+ * beta the reciprocal bandwidth).  AR_AUTO takes the tree where the tree's
+ * line is strictly below the line of the ring form the call would use.  The
+ * defaults are fits measured on MI355X at R = 8, float32; a caller with its
+ * own measurements (other R, dtype or machine) sets them here.
+ * ar_set_cost: AR_ERR_INVALID_ARG for an unknown form, alpha_us < 0,
+ *   bw_gbps <= 0 or a NaN.
+ * ar_auto_tree_max_bytes: the largest per-rank message AR_AUTO sends by tree
+ *   under the comm's current options (0: none; INT64_MAX: every size); -1
+ *   for a NULL comm. */
+typedef enum {
+    AR_COST_TREE_LL = 0,
+    AR_COST_RING_FUSED = 1,
+    AR_COST_RING_PIPELINED = 2,
+    AR_COST_RING_STEP = 3,
+    AR_COST_RING_LL = 4,
+    AR_COST_FORMS = 5
+} ar_cost_form_t;
+int ar_set_cost(ar_comm_t comm, int form, double alpha_us, double bw_gbps);
+int ar_get_cost(ar_comm_t comm, int form, double* alpha_us, double* bw_gbps);
+int64_t ar_auto_tree_max_bytes(ar_comm_t comm);
 
 /* Host-side views of the schedule, for checking and tooling.
  * ar_ring_segment: [*lo, *hi) element range of segment c for a count of

@@ -85,18 +85,48 @@ def test_options_round_trip(api):
 
 
 def test_plan_picks_tree_for_small_and_ring_for_large(api):
-    c = api.ar_init(8, 1 << 20, api.AR_FLOAT32, api.AR_AUTO)
+    c = api.ar_init(8, 1 << 22, api.AR_FLOAT32, api.AR_AUTO)
     try:
-        assert api.ar_plan(c, 16)[0] == api.AR_RING  # default fused ring: no tree
+        assert api.ar_get_option(c, api.AR_OPT_TREE_MAX_BYTES) == -1  # by the cost model
+        # the default fused ring's line is below the tree's at every size
+        ta, tb = api.ar_get_cost(c, api.AR_COST_TREE_LL)
+        fa, fb = api.ar_get_cost(c, api.AR_COST_RING_FUSED)
+        assert fa < ta and fb > tb
+        assert api.ar_auto_tree_max_bytes(c) == 0
+        assert api.ar_plan(c, 1)[0] == api.AR_RING and api.ar_plan(c, 1 << 22)[0] == api.AR_RING
+        # with the pipelined ring the lines cross: tree below, ring above
         api.ar_set_option(c, api.AR_OPT_LAUNCH, api.AR_LAUNCH_PIPELINED)
-        assert api.ar_plan(c, 16)[0] == api.AR_TREE
-        assert api.ar_plan(c, 64 * 1024)[0] == api.AR_TREE   # 256 KiB default
-        assert api.ar_plan(c, 64 * 1024 + 1)[0] == api.AR_RING
+        n = api.ar_auto_tree_max_bytes(c)
+        pa, pb = api.ar_get_cost(c, api.AR_COST_RING_PIPELINED)
+        cross = (pa - ta) / (1e-3 / tb - 1e-3 / pb)  # bytes where the lines meet
+        assert 0 < n <= cross < n + 2
+        assert api.ar_plan(c, 1)[0] == api.AR_TREE
+        assert api.ar_plan(c, n // 4)[0] == api.AR_TREE
+        assert api.ar_plan(c, n // 4 + 1)[0] == api.AR_RING
+        # a caller's own fits move the crossing
+        api.ar_set_cost(c, api.AR_COST_RING_PIPELINED, pa, pb * 4)
+        assert api.ar_auto_tree_max_bytes(c) < n
+        # ring + LL uses its own line
+        api.ar_set_option(c, api.AR_OPT_PROTO, api.AR_LL)
+        la, lb = api.ar_get_cost(c, api.AR_COST_RING_LL)
+        assert abs(api.ar_auto_tree_max_bytes(c) - (la - ta) / (1e-3 / tb - 1e-3 / lb)) < 2
+        api.ar_set_option(c, api.AR_OPT_PROTO, api.AR_SIMPLE)
+        # a fixed threshold overrides the model
         api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, 64 * 1024)
+        assert api.ar_auto_tree_max_bytes(c) == 64 * 1024
         assert api.ar_plan(c, 16)[0] == api.AR_TREE
         assert api.ar_plan(c, 16 * 1024)[0] == api.AR_TREE
         assert api.ar_plan(c, 16 * 1024 + 1)[0] == api.AR_RING
         assert api.ar_plan(c, 1 << 20)[0] == api.AR_RING
+        api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, -1)
+        assert api.ar_auto_tree_max_bytes(c) < n
+        # bad models are refused
+        for form, a, b in ((5, 1.0, 1.0), (-1, 1.0, 1.0), (0, -1.0, 1.0), (0, 1.0, 0.0),
+                           (0, float("nan"), 1.0), (0, 1.0, float("nan"))):
+            with pytest.raises(api.ArError):
+                api.ar_set_cost(c, form, a, b)
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, -2)
     finally:
         api.ar_destroy(c)
 

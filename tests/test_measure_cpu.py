@@ -36,3 +36,24 @@ def test_byte_counts():
     assert measure.reduce_scatter_alg_bytes(2, 1024, 4) == 12 * 1024
     assert abs(measure.busbw_factor("allreduce", 8) - 1.75) < 1e-12
     assert abs(measure.busbw_factor("rs", 16) - 15 / 16) < 1e-12
+
+
+def test_hbm_byte_counts():
+    # R = 8 fp32 64 MiB per rank: 8 rows read + 8 rows written = 1 GiB
+    assert measure.allreduce_hbm_bytes(8, 16_777_216, 4) == 1 << 30
+    # R = 16 bf16 25 MiB buckets: 400 MiB read + 25 MiB written, and back
+    N = 13_107_200
+    assert measure.reduce_scatter_hbm_bytes(16, N, 2) == 425 << 20
+    assert measure.all_gather_hbm_bytes(16, N, 2) == 425 << 20
+
+
+def test_crossover_of_two_lines():
+    # tree: 8 us + n / 20 GB/s; ring: 20 us + n / 200 GB/s -> equal at
+    # n = 12 us / (1/20 - 1/200) us per kB = 266,666.7 bytes
+    tree = dict(alpha_us=8.0, inv_beta_GBps=20.0)
+    ring = dict(alpha_us=20.0, inv_beta_GBps=200.0)
+    n = measure.crossover_bytes(tree, ring)
+    assert abs(n - 12.0 / (1e-3 / 20 - 1e-3 / 200)) < 1e-6
+    assert abs((8.0 + n * 1e-3 / 20) - (20.0 + n * 1e-3 / 200)) < 1e-9
+    # a ring that is cheaper at every size never crosses
+    assert measure.crossover_bytes(tree, dict(alpha_us=5.0, inv_beta_GBps=300.0)) is None
