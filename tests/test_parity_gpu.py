@@ -289,12 +289,73 @@ def test_auto_selects_tree_then_ring(env):
         assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
 
 
+# ---------------------------------------------------------------- wave tiles
+
+# 16-byte slots per lane of the fused form's wave tile (kWaveSlots): a tile is
+# 64 * 2 slots, i.e. 512 elements of 32-bit T or 1024 of bf16, per rank row
+TILE_SLOTS = 128
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [2, 3, 8, 16])
+@pytest.mark.parametrize("channels", [1, 2])
+def test_fused_wave_tile_seams(env, dtype, R, channels):
+    """The fused vector path around tile boundaries: every segment a whole
+    number of tiles (the lean kernel), one element more or less (the kernel
+    with the checked path for a segment's last tile), and only the last
+    segment short.  All-reduce (out of place and in place), reduce-scatter and
+    all-gather against the oracle, with one and two ring channels."""
+    api, orc, torch = env["api"], env["orc"], env["torch"]
+    V = 8 if dtype == "bf16" else 4
+    te = TILE_SLOTS * V  # elements per rank row in one tile
+    K = min(channels, len([m for m in range(1, R) if np.gcd(m, R) == 1]))
+    strides = [1, R - 1][:K]
+    for segs in (te, 3 * te, te + V, 3 * te - V, 2 * te + 8):
+        for N in (R * segs, R * segs - V if R * segs - V > (R - 1) * segs else R * segs - 1):
+            x = rand_input(env, dtype, R, N, seed=N * 7 + R)
+            comm = api.Comm(R, N, dtype, device=env["dev"], launch="fused", channels=K)
+            send = to_dev(env, x, dtype)
+            recv = poisoned(env, (R, N), dtype)
+            comm.allreduce(send, recv)
+            want = orc.ring_allreduce(x, dtype, strides=strides)
+            assert from_dev(env, recv, dtype).tobytes() == want.tobytes(), (N, "ar")
+            inplace = to_dev(env, x, dtype)
+            comm.allreduce(inplace, inplace)
+            assert from_dev(env, inplace, dtype).tobytes() == want.tobytes(), (N, "in place")
+            if N % R == 0:
+                shard = poisoned(env, (R, N // R), dtype)
+                comm.reduce_scatter(send, shard)
+                rs = orc.ring_reduce_scatter(x, dtype, strides=strides)
+                assert from_dev(env, shard, dtype).tobytes() == rs.tobytes(), (N, "rs")
+                full = poisoned(env, (R, N), dtype)
+                comm.all_gather(to_dev(env, rs, dtype), full)
+                ag = orc.ring_all_gather(rs, dtype, strides=strides)
+                assert from_dev(env, full, dtype).tobytes() == ag.tobytes(), (N, "ag")
+            assert comm.check() == api.AR_SUCCESS
+            comm.close()
+
+
+@pytest.mark.parametrize("grid", [1, 3, 64, 4096])
+def test_fused_staging_with_any_grid(env, grid):
+    """bf16 hands its float32 running value on through one staging slot per
+    wave; the launch is capped at the waves the staging holds, whatever grid
+    is asked for, and a grid smaller than the tiles loops over them."""
+    api, orc = env["api"], env["orc"]
+    R, N = 16, 16 * 1024 * 40 + 16 * 8
+    x = rand_input(env, "bf16", R, N, seed=grid)
+    (y,) = run_allreduce(env, x, "bf16", launch="fused", grid=grid)
+    assert y.tobytes() == orc.ring_allreduce(x, "bf16").tobytes()
+
+
 # ---------------------------------------------------------------- config 5
 
 def test_cfg5_gradient_buckets_bf16_r16(env):
     """40 buckets x 13,107,200 bf16 per rank, R = 16: reduce-scatter then
-    all-gather equals all-reduce bit for bit on every bucket; buckets 0 and 39
-    are also replayed by the oracle."""
+    all-gather equals all-reduce bit for bit on every bucket.  Every bucket is
+    also compared with the oracle: 64 sampled elements of each segment (the
+    fold of an element depends only on its segment, so the samples laid out
+    as [R, R*64] fold in the same order), the all-reduce output and the
+    reduce-scatter shards at those elements; buckets 0 and 39 in full."""
     api, orc, inputs, torch = env["api"], env["orc"], env["inputs"], env["torch"]
     w = inputs.WORKLOADS["buckets_bf16_r16"]
     R, N, B = w["R"], w["count"], w["buckets"]
@@ -303,6 +364,7 @@ def test_cfg5_gradient_buckets_bf16_r16(env):
     shard = torch.empty((R, n), dtype=torch.bfloat16, device=env["dev"])
     full = torch.empty((R, N), dtype=torch.bfloat16, device=env["dev"])
     ar = torch.empty((R, N), dtype=torch.bfloat16, device=env["dev"])
+    rng, m = np.random.default_rng(5), 64
     for b in range(B):
         x = inputs.device_bucket_bf16(R, N, w["seed"], b, env["dev"])
         full.fill_(float("nan"))
@@ -311,6 +373,14 @@ def test_cfg5_gradient_buckets_bf16_r16(env):
         comm.allreduce(x, ar)
         assert torch.equal(full.view(torch.int16), ar.view(torch.int16)), b
         assert torch.equal(ar.view(torch.int16), ar[0:1].expand(R, N).view(torch.int16)), b
+        idx = _segment_samples(rng, N, R, m)
+        ti = torch.from_numpy(idx).to(env["dev"])
+        ref = orc.ring_allreduce(from_dev(env, x[:, ti].contiguous(), "bf16"), "bf16")
+        assert from_dev(env, ar[:, ti].contiguous(), "bf16").tobytes() == ref.tobytes(), b
+        sh = from_dev(env, shard, "bf16")
+        for c in range(R):
+            cols = idx[c * m:(c + 1) * m]
+            assert np.array_equal(sh[c, cols - c * n], ref[c, c * m:(c + 1) * m]), (b, c)
         if b in (0, B - 1):
             xh = from_dev(env, x, "bf16")
             y = from_dev(env, ar, "bf16")
