@@ -197,77 +197,6 @@ __device__ inline void store_a(typename E::A* p, const typename E::A (&v)[V])
     }
 }
 
-// s_waitcnt vmcnt(0), leaving the other counters alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// ---- LL lines ---------------------------------------------------------------
-// An LL line is 8 bytes: the data bits in the low half, the arrival flag in
-// the high half, written and read as one 64-bit agent-scope atomic.
-
-__device__ inline void ll_store(uint64_t* line, uint32_t data, uint32_t flag)
-{
-    __hip_atomic_store(line, ((uint64_t)flag << 32) | (uint64_t)data, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait for K lines at once: every pass issues the loads of all lines still
-// pending, so the K waits overlap instead of adding up.  Line k is complete
-// when its flag half equals flag[k].  Lines with pending[k] == false on entry
-// are skipped.  Gives up (returns false) when `deadline` passes or the error
-// word is set; data[k] of a line that never arrived is left 0.
-template <int K>
-__device__ inline bool ll_wait_lines(const uint64_t* const (&line)[K], bool (&pending)[K],
-                                     const uint32_t (&flag)[K], uint64_t deadline,
-                                     const uint32_t* err, uint32_t (&data)[K])
-{
-    for (uint32_t spin = 0;; ++spin) {
-        uint64_t v[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (pending[k])
-                v[k] = __hip_atomic_load(line[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every value is checked at once; saying so explicitly lets the
-        // compiler see that none of these conditional loads is still
-        // outstanding afterwards, so later stores need no wait of their own
-        wait_vmem_all();
-        bool any = false;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (pending[k]) {
-                if ((uint32_t)(v[k] >> 32) == flag[k]) {
-                    data[k] = (uint32_t)v[k];
-                    pending[k] = false;
-                } else {
-                    any = true;
-                }
-            }
-        }
-        if (!any)
-            return true;
-        if ((spin & 63u) == 63u) {
-            if ((uint64_t)wall_clock64() > deadline)
-                return false;
-            if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-                return false;
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-}
-
-// The same with one flag for every line.
-template <int K>
-__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pending)[K],
-                                     uint32_t flag, uint64_t deadline, const uint32_t* err,
-                                     uint32_t (&data)[K])
-{
-    uint32_t f[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-        f[k] = flag;
-    return ll_wait_lines<K>(line, pending, f, deadline, err, data);
-}
-
 // Keeps the compiler from carrying a value stored by one ring step into the
 // next step's load of the same address: every step must read the buffer of
 // the rank it receives from.  Emits no instruction.

@@ -21,6 +21,7 @@
 // is bounded by the kernel-wide deadline.
 #include "ar_elem.h"
 #include "ar_internal.h"
+#include "ar_ll.h"
 
 namespace ar {
 namespace {

@@ -40,6 +40,7 @@
 // its lines only carry flags up to it.
 #include "ar_elem.h"
 #include "ar_internal.h"
+#include "ar_ll.h"
 
 namespace ar {
 namespace {
