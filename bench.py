@@ -364,8 +364,20 @@ def copy_ceiling(torch, api):
     _, ms, _ = time_calls(lambda: api.ar_stream_copy(a.data_ptr(), c.data_ptr(), n, st), 20, 5,
                           torch)
     gbps = 2 * n / (ms / 20 / 1e3) / 1e9
+    # the headline's row pattern without its hops: 8 rows of 64 MiB read and
+    # 8 written back from L2, tile by tile (1 GiB moved, like one all-reduce)
+    R, rb = 8, 64 << 20
+    c.zero_()
+    _, ms2, _ = time_calls(lambda: api.ar_stream_rows(a.data_ptr(), c.data_ptr(), R, rb, st),
+                           20, 5, torch)
+    rows_gbps = 2 * n / (ms2 / 20 / 1e3) / 1e9
+    ok = torch.equal(a, c)
     del a, c
-    return dict(bytes=n, copy_GBps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4))
+    return dict(bytes=n, copy_GBps=round(gbps, 1), frac_of_peak=round(gbps / PEAK_HBM_GBPS, 4),
+                rows_pattern_GBps=round(rows_gbps, 1),
+                rows_pattern_frac_of_peak=round(rows_gbps / PEAK_HBM_GBPS, 4),
+                rows_pattern="8 rows of 64 MiB, 2 KiB tiles per wave, non-temporal loads, "
+                             "plain stores", rows_copy_ok=bool(ok))
 
 
 def pipelined_headline(torch, api, measure, send, recv, y, R, N, s):
@@ -386,7 +398,17 @@ def pipelined_headline(torch, api, measure, send, recv, y, R, N, s):
                 traffic=traffic, exact=exact, chunk_bytes=512 * 1024)
 
 
-def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused"):
+def timed_point(fn, torch, eager):
+    """ms per call of one sweep point: 5 warm-up then 20 timed calls, as one
+    graph replay, or enqueued one by one (eager: one traced dispatch per call,
+    for profiler runs)."""
+    if eager:
+        _, total_ms, _ = time_calls(fn, 20, 5, torch)
+        return total_ms / 20
+    return time_graph(fn, 20, torch)
+
+
+def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused", eager=False):
     """Config 3: R = 8 fp32 N(0,1), 8 B .. 1 GiB per rank (28 sizes), 5
     warm-up then 20 timed calls each (one graph replay), fit T = a + b n."""
     R, s = 8, 4
@@ -403,7 +425,7 @@ def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused"
     for N in counts:
         sv = send_flat[:R * N].view(R, N)
         rv = recv_flat[:R * N].view(R, N)
-        t = time_graph(lambda: comm.allreduce(sv, rv), 20, torch) / 1e3
+        t = timed_point(lambda: comm.allreduce(sv, rv), torch, eager) / 1e3
         pts.append([N * s, round(t * 1e6, 3)])
         if N * s <= (1 << 20):  # check the small and mid sizes against the oracle
             xs = sv.cpu().numpy()
@@ -420,7 +442,8 @@ def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused"
     small = sorted(p[1] for p in pts if p[0] <= 4096)
     large = [p for p in pts if p[0] >= 64 << 20]
     out = dict(launch=launch, R=R, dtype="f32", sizes=len(pts), timing="5 warm-up + 20 timed "
-               "calls per size, one graph replay", exact_up_to_1MiB=bool(exact), exact=bool(exact),
+               "calls per size, " + ("enqueued one by one" if eager else "one graph replay"),
+               exact_up_to_1MiB=bool(exact), exact=bool(exact),
                alpha_us=round(fit["alpha_us"], 3), inv_beta_GBps=round(fit["inv_beta_GBps"], 1),
                bus_rate_GBps=round(fit["inv_beta_GBps"] * measure.busbw_factor("allreduce", R), 1),
                r2=round(fit["r2"], 5), max_rel_residual=round(fit["max_rel_residual"], 4),
@@ -440,7 +463,7 @@ TVR_VARIANTS = [("tree-ll", dict(algo="tree", proto="ll")),
                 ("ring-step", dict(algo="ring", proto="simple", launch="step"))]
 
 
-def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024):
+def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eager=False):
     """Config 4: R = 8 fp32 U[-1,1), 8 B .. 256 KiB per rank (16 sizes): the
     double binary tree with LL against every ring form (5 warm-up + 20 timed
     calls per size, one graph replay); an alpha-beta fit per variant, the
@@ -463,7 +486,7 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024):
         xs = sv.cpu().numpy()
         for name, _ in TVR_VARIANTS:
             c = comms[name]
-            res[name].append(round(time_graph(lambda: c.allreduce(sv, rv), 20, torch) * 1e3, 3))
+            res[name].append(round(timed_point(lambda: c.allreduce(sv, rv), torch, eager) * 1e3, 3))
             if N in (counts[0], counts[len(counts) // 2], counts[-1]):
                 ref, _, _, _ = cpu_baseline_leg(
                     (lambda o: o.tree_allreduce(xs)) if name == "tree-ll"
@@ -594,7 +617,7 @@ def mode_sweep(args):
     import torch
     from collective_communication_ring_amd import api, inputs, measure
     out = sweep_fit(torch, api, measure, inputs, np, args.max_bytes, args.launch
-                    if args.launch != "auto" else "fused")
+                    if args.launch != "auto" else "fused", eager=args.eager)
     print(json.dumps(dict(mode="sweep_fit", **out)), flush=True)
     return 0 if out["exact"] else 1
 
@@ -628,7 +651,7 @@ def mode_tree_vs_ring(args):
     import numpy as np
     import torch
     from collective_communication_ring_amd import api, inputs, measure
-    out = tree_vs_ring_fit(torch, api, measure, inputs, np, args.tvr_max_bytes)
+    out = tree_vs_ring_fit(torch, api, measure, inputs, np, args.tvr_max_bytes, eager=args.eager)
     print(json.dumps(dict(mode="tree_vs_ring", **out)), flush=True)
     return 0 if out["exact"] else 1
 
@@ -660,15 +683,19 @@ def mode_buckets(args):
             comm.allreduce(xs[b], full)
 
     rep = {}
-    for name, fn, op, alg in (("reduce_scatter", rs_all, "rs", measure.reduce_scatter_alg_bytes(R, N, s)),
-                              ("all_gather", ag_all, "ag", measure.all_gather_alg_bytes(R, N, s)),
-                              ("allreduce", ar_all, "ar", None)):
+    for name, fn, op, hbm, hop in (
+            ("reduce_scatter", rs_all, "rs", measure.reduce_scatter_hbm_bytes(R, N, s),
+             measure.reduce_scatter_alg_bytes(R, N, s)),
+            ("all_gather", ag_all, "ag", measure.all_gather_hbm_bytes(R, N, s),
+             measure.all_gather_alg_bytes(R, N, s)),
+            ("allreduce", ar_all, "ar", measure.allreduce_hbm_bytes(R, N, s), None)):
         _, total_ms, _ = time_calls(fn, args.steps, 1, torch)
         t = total_ms / args.steps / B / 1e3  # per bucket
         algbw = N * s / t / 1e9
         f = measure.busbw_factor("allreduce" if op == "ar" else op, R)
         rep[name] = dict(t_us_per_bucket=t * 1e6, algbw_GBps=algbw, busbw_GBps=algbw * f,
-                         hbm_alg_GBps=(alg / t / 1e9) if alg else None)
+                         hbm_GBps=hbm / t / 1e9, hbm_frac_of_peak=hbm / t / 1e9 / PEAK_HBM_GBPS,
+                         hop_rate_GBps=(hop / t / 1e9) if hop else None)
         log(name, rep[name])
     assert comm.check() == api.AR_SUCCESS
     import numpy as np
@@ -684,8 +711,9 @@ def mode_buckets(args):
 
 def mode_stream(args):
     """Reference kernels: c = a + b over float32 (the access mix of one reduce
-    step) and a plain copy, each on 512 MiB arrays (larger than the 256 MB
-    infinity cache)."""
+    step), a plain copy, and the all-reduce's row pattern without hops (R rows
+    read and written back tile by tile, ar_stream_rows), each on 512 MiB
+    arrays (larger than the 256 MB infinity cache)."""
     import torch
     from collective_communication_ring_amd import api
     dev = torch.device("cuda:0")
@@ -702,9 +730,18 @@ def mode_stream(args):
     copy_gbps = 2 * n * 4 / (ms2 / args.steps / 1e3) / 1e9
     torch.cuda.synchronize()
     ok = torch.equal(c, a)
+    rows = {}
+    for R in (2, 4, 8, 16):  # the all-reduce's row pattern without hops, R rows
+        c.zero_()
+        _, ms3, _ = time_calls(lambda: api.ar_stream_rows(a.data_ptr(), c.data_ptr(), R,
+                                                          n * 4 // R, st),
+                               args.steps, args.warmup, torch)
+        torch.cuda.synchronize()
+        rows[R] = dict(GBps=round(2 * n * 4 / (ms3 / args.steps / 1e3) / 1e9, 1),
+                       ok=bool(torch.equal(c, a)))
     summary = dict(mode="stream", bytes_per_array=n * 4, add_GBps=add_gbps,
                    add_frac=add_gbps / PEAK_HBM_GBPS, copy_GBps=copy_gbps,
-                   copy_frac=copy_gbps / PEAK_HBM_GBPS, copy_ok=ok)
+                   copy_frac=copy_gbps / PEAK_HBM_GBPS, copy_ok=ok, rows_pattern=rows)
     print(json.dumps(summary), flush=True)
     return 0
 
@@ -806,7 +843,8 @@ def mode_overlap(args):
 
 def mode_counters(args):
     """A short program for byte-counter runs (rocprofv3 --pmc): a copy of a
-    known size (the calibration), then 3 all-reduces of the headline workload
+    known size (the calibration) and the headline's row pattern without hops
+    (ar_stream_rows), then 3 all-reduces of the headline workload
     in each launch form, then 3 small tree-LL all-reduces, then 3 reduce-
     scatters, all-gathers and all-reduces of one config 5 bucket."""
     import torch
@@ -818,6 +856,9 @@ def mode_counters(args):
     c = torch.empty_like(a)
     for _ in range(3):
         api.ar_stream_copy(a.data_ptr(), c.data_ptr(), n * 4, st)
+    # the headline's row pattern without hops: 8 rows of 64 MiB
+    for _ in range(3):
+        api.ar_stream_rows(a.data_ptr(), c.data_ptr(), 8, n * 4 // 8, st)
     torch.cuda.synchronize()
     del a, c
     R, N = 8, 16_777_216

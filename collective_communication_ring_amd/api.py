@@ -79,6 +79,7 @@ def lib():
         "ar_last_hip_error": ([vp], i),
         "ar_stream_add": ([vp, vp, vp, sz, vp], i),
         "ar_stream_copy": ([vp, vp, sz, vp], i),
+        "ar_stream_rows": ([vp, vp, i, sz, vp], i),
         "ar_ll_pingpong": ([vp, vp, i, i, i64, vp], i),
         "ar_stream_create_cu_masked": ([ctypes.POINTER(vp), ctypes.c_uint32,
                                         ctypes.POINTER(ctypes.c_uint32)], i),
@@ -193,6 +194,10 @@ def ar_stream_add(a_ptr, b_ptr, c_ptr, n, stream=0):
 
 def ar_stream_copy(src_ptr, dst_ptr, nbytes, stream=0):
     _ok(lib().ar_stream_copy(src_ptr, dst_ptr, nbytes, stream), "ar_stream_copy")
+
+
+def ar_stream_rows(src_ptr, dst_ptr, rows, row_bytes, stream=0):
+    _ok(lib().ar_stream_rows(src_ptr, dst_ptr, rows, row_bytes, stream), "ar_stream_rows")
 
 
 def ar_ll_pingpong(lines_ptr, result_ptr, iters, xcd_apart, timeout_us=2_000_000, stream=0):

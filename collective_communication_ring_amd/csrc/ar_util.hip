@@ -120,6 +120,76 @@ extern "C" int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* s
     return hipGetLastError() == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
 }
 
+// ---- the fused ring's row pattern without its hops -----------------------------
+
+namespace ar {
+namespace {
+
+// `rows` rows of row_vec 16-byte vectors, copied src -> dst tile by tile in
+// the fused ring's access shape: a wave takes a tile of kWaveSlots slots per
+// lane at one offset, loads it from every row (non-temporal, as the ring
+// loads its inputs), then stores it at the same offset of every dst row with
+// plain stores (written back from L2, as the ring's outputs are).  Rows go
+// in groups of 8 (loads of a group in flight together).  The host checks
+// that row_vec is a whole number of tiles.
+__global__ __launch_bounds__(kBlock) void k_stream_rows(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int rows,
+                                                        uint64_t row_vec)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t unit = (uint64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const uint64_t nunits = (uint64_t)gridDim.x * (kBlock / 64);
+    const uint64_t ntiles = row_vec / kWaveTileSlots;
+    for (uint64_t t = unit; t < ntiles; t += nunits) {
+        const uint64_t base = t * kWaveTileSlots + lane;
+        for (int r0 = 0; r0 < rows; r0 += 8) {
+            const int nr = rows - r0 < 8 ? rows - r0 : 8;
+            u32x4 v[8][kWaveSlots];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < nr)
+#pragma unroll
+                    for (int u = 0; u < kWaveSlots; ++u)
+                        v[i][u] = __builtin_nontemporal_load(src + (uint64_t)(r0 + i) * row_vec +
+                                                             base + u * 64);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (i < nr)
+#pragma unroll
+                    for (int u = 0; u < kWaveSlots; ++u)
+                        dst[(uint64_t)(r0 + i) * row_vec + base + u * 64] = v[i][u];
+        }
+    }
+}
+
+}  // namespace
+}  // namespace ar
+
+extern "C" int ar_stream_rows(const void* src, void* dst, int rows, size_t row_bytes, void* stream)
+{
+    using namespace ar;
+    const size_t tile = (size_t)kWaveTileSlots * 16;
+    if (rows <= 0 || row_bytes == 0)
+        return rows < 0 ? AR_ERR_INVALID_ARG : AR_SUCCESS;
+    if (!src || !dst || (((uintptr_t)src | (uintptr_t)dst) & 15u) || row_bytes % tile)
+        return AR_ERR_INVALID_ARG;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 256;
+    const uint64_t tiles = row_bytes / tile;
+    const uint64_t waves = kBlock / 64;
+    const uint64_t grid = std::max<uint64_t>(1, std::min<uint64_t>((tiles + waves - 1) / waves,
+                                                                    2 * (uint64_t)ncu));
+    hipLaunchKernelGGL(k_stream_rows, dim3((unsigned)grid), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const u32x4*>(src),
+                       reinterpret_cast<u32x4*>(dst), rows, (uint64_t)(row_bytes / 16));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        g_util_hip_error = (int)e;
+    return e == hipSuccess ? AR_SUCCESS : AR_ERR_HIP;
+}
+
 // ---- LL hop-latency probe ---------------------------------------------------
 
 namespace ar {

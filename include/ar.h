@@ -257,6 +257,16 @@ int ar_ring_channel_stride(ar_comm_t comm, int k);
 int ar_stream_add(const float* a, const float* b, float* c, size_t n, void* stream);
 int ar_stream_copy(const void* src, void* dst, size_t nbytes, void* stream);
 
+/* Measurement utility: the fused ring's HBM access pattern without its hops.
+ * Copies `rows` rows of `row_bytes` bytes (src and dst rank-major, rows
+ * contiguous) tile by tile: a wave loads a 2 KiB tile at one offset from
+ * every row, then stores it at that offset of every dst row with plain
+ * stores, i.e. the R input rows read and the R output rows written back from
+ * L2 that one all-reduce moves.  Its rate is the ceiling of that pattern.
+ * row_bytes must be a multiple of 2048 and the pointers 16-byte aligned
+ * (AR_ERR_INVALID_ARG otherwise); rows == 0 or row_bytes == 0 is a no-op. */
+int ar_stream_rows(const void* src, void* dst, int rows, size_t row_bytes, void* stream);
+
 /* Stream with a CU mask (runtime utility for overlapping a collective with
  * compute, "NCCL, NIXL, and Distributed GPU Communication", performance
  * checklist: overlap communication with computation).  On one GPU the

@@ -164,6 +164,11 @@ def test_utilities_reject_bad_arguments(api):
     assert L.ar_stream_add(None, None, None, 16, None) == api.AR_ERR_INVALID_ARG
     assert L.ar_stream_add(None, None, None, 0, None) == api.AR_SUCCESS
     assert L.ar_stream_copy(16, 32, 15, None) == api.AR_ERR_INVALID_ARG  # not a multiple of 16
+    assert L.ar_stream_rows(16, 32, 8, 1024, None) == api.AR_ERR_INVALID_ARG  # not whole tiles
+    assert L.ar_stream_rows(None, None, 8, 2048, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_stream_rows(8, 32, 8, 2048, None) == api.AR_ERR_INVALID_ARG  # misaligned
+    assert L.ar_stream_rows(16, 32, -1, 2048, None) == api.AR_ERR_INVALID_ARG
+    assert L.ar_stream_rows(None, None, 0, 2048, None) == api.AR_SUCCESS    # nothing to do
     assert L.ar_ll_pingpong(None, None, 10, 1, 1000, None) == api.AR_ERR_INVALID_ARG
     assert L.ar_ll_pingpong(256, 512, 0, 1, 1000, None) == api.AR_ERR_INVALID_ARG
 

@@ -581,6 +581,12 @@ def test_measurement_utilities(env):
     api.ar_stream_copy(a.data_ptr(), d.data_ptr(), 4096 * 4, st)
     torch.cuda.synchronize()
     assert torch.equal(d[:4096], a[:4096])
+    for rows in (1, 3, 8, 11):  # whole groups of 8 rows and a remainder
+        src = torch.randn((rows, 12 * 512), device=env["dev"])  # 12 tiles of 2 KiB per row
+        dst = torch.zeros_like(src)
+        api.ar_stream_rows(src.data_ptr(), dst.data_ptr(), rows, src.shape[1] * 4, st)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst), rows
     lines = torch.zeros(64, dtype=torch.int64, device=env["dev"])
     res = torch.ones(1, dtype=torch.int32, device=env["dev"])
     for apart in (1, 0):
