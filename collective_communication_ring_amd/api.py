@@ -63,6 +63,7 @@ def lib():
         "ar_workspace_bytes": ([vp], sz),
         "ar_set_workspace": ([vp, vp, sz, vp], i),
         "ar_allreduce": ([vp, vp, vp, sz, vp], i),
+        "ar_allreduce_noalloc": ([vp, vp, vp, sz, vp], i),
         "ar_reduce_scatter": ([vp, vp, vp, sz, vp], i),
         "ar_all_gather": ([vp, vp, vp, sz, vp], i),
         "ar_check": ([vp], i),
@@ -120,6 +121,11 @@ def ar_set_workspace(comm, dev_ptr, nbytes, stream=0):
 
 def ar_allreduce(comm, send_ptr, recv_ptr, count, stream=0):
     _ok(lib().ar_allreduce(comm, send_ptr, recv_ptr, count, stream), "ar_allreduce")
+
+
+def ar_allreduce_noalloc(comm, send_ptr, recv_ptr, count, stream=0):
+    _ok(lib().ar_allreduce_noalloc(comm, send_ptr, recv_ptr, count, stream),
+        "ar_allreduce_noalloc")
 
 
 def ar_reduce_scatter(comm, send_ptr, recv_ptr, recvcount, stream=0):

@@ -362,11 +362,21 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
     return AR_SUCCESS;
 }
 
-int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st);
+// How one ring call runs beyond its arguments: where the fused form may stage
+// hand-offs (a.part, when it is this region), and whether the call must take
+// the fused form whatever the comm's options say (the allocation-free entry
+// point, which has no flags or lines to offer the other forms).
+struct RunOpts {
+    const void* stage = nullptr;  // the region a.part points at when staging is allowed
+    size_t stage_bytes = 0;
+    bool fused_only = false;
+};
+
+int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o);
 
 // One ring collective: every channel covers its own sub-range of every
 // segment with its own ring stride, launched one after the other.
-int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
+int run_ring(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
 {
     const uint64_t K = (uint64_t)c->channels;
     const uint64_t Sk = ((a.S + K - 1) / K + 7) / 8 * 8;
@@ -379,21 +389,21 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st)
         // length to what a full segment holds changes no range, and keeps grids
         // and LL pieces from covering a rounded-up tail
         a.sub_len = std::min<uint64_t>(Sk, a.S - a.sub_lo);
-        const int rc = run_ring_channel(c, a, st);
+        const int rc = run_ring_channel(c, a, st, o);
         if (rc)
             return rc;
     }
     return AR_SUCCESS;
 }
 
-int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
+int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
 {
-    if (c->proto == AR_LL)
+    if (c->proto == AR_LL && !o.fused_only)
         return run_ring_ll(c, a, st);
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
     const bool vec = vector_ok(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row);
-    const int launch = resolve_launch(c);
+    const int launch = o.fused_only ? AR_LAUNCH_FUSED : resolve_launch(c);
     hipError_t e = hipSuccess;
     int grid = 0;
     if (launch == AR_LAUNCH_STEP) {
@@ -431,11 +441,11 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st)
         }
         a.stage_wave = 0;
         a.max_units = 0xffffffffu;
-        if (a.op != kOpAllGather && a.part == (void*)(c->ws + c->off_part)) {
-            // the hand-off goes through each wave's staging slot in the workspace's
-            // hand-off region: at most as many waves as it holds slots take tiles
+        if (a.op != kOpAllGather && o.stage && a.part == o.stage) {
+            // the hand-off goes through each wave's staging slot in the hand-off
+            // region: at most as many waves as it holds slots take tiles
             a.stage_wave = (uint64_t)kWaveTileSlots * V;
-            const uint64_t slots = c->part_bytes / (a.stage_wave * 4);
+            const uint64_t slots = o.stage_bytes / (a.stage_wave * 4);
             if (slots < 1)
                 return AR_ERR_INTERNAL;
             a.max_units = (uint32_t)std::min<uint64_t>(slots, 0xffffffffu);
@@ -576,6 +586,15 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
                      (unsigned long long)N, dtype_name(c->dtype), (unsigned long long)piece,
                      launches);
     return AR_SUCCESS;
+}
+
+// The workspace's hand-off region, where the collectives stage hand-offs.
+RunOpts ws_opts(const ar_comm* c)
+{
+    RunOpts o;
+    o.stage = c->ws + c->off_part;
+    o.stage_bytes = c->part_bytes;
+    return o;
 }
 
 // Checks shared by the collectives.  A zero-element call is a successful
@@ -761,7 +780,55 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
     a.R = c->R;
     a.op = kOpAllReduce;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st);
+    return run_ring(c, a, st, ws_opts(c));
+}
+
+int ar_allreduce_noalloc(ar_comm_t c, const void* send, void* recv, size_t count, void* stream)
+{
+    if (!c || count > c->cap)
+        return AR_ERR_INVALID_ARG;
+    if (count == 0)
+        return AR_SUCCESS;
+    if (!send || !recv)
+        return AR_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)c->R * count * elem_size(c->dtype);
+    if (send != recv && overlaps(send, bytes, recv, bytes))
+        return AR_ERR_INVALID_USAGE;
+    int rc = device_ready(c);
+    if (rc)
+        return rc;
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    hipError_t e = noalloc_scratch(&scratch, &scratch_bytes);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    c->last_stream = st;
+    RingArgs a{};
+    a.send = send;
+    // as ar_allreduce, with the device array in place of the workspace row
+    const bool staged = c->dtype == AR_BF16 || send == recv;
+    a.part = staged ? scratch : recv;
+    a.part_seg = staged ? 0 : count;
+    a.out = recv;
+    a.ctrl = nullptr;  // the fused form has no flags, lines or error word
+    a.N = count;
+    a.S = (count + c->R - 1) / c->R;
+    a.send_row = count;
+    a.out_row = count;
+    a.R = c->R;
+    a.op = kOpAllReduce;
+    // the vector path stages per wave (the launch takes as many waves as the
+    // array holds slots); the scalar path keeps one accumulator per element,
+    // which must fit
+    if (staged && !vector_ok(c, send, a.part, recv, a.N, a.S, a.send_row, a.out_row) &&
+        count * 4 > scratch_bytes)
+        return AR_ERR_INVALID_ARG;
+    RunOpts o;
+    o.stage = scratch;
+    o.stage_bytes = scratch_bytes;
+    o.fused_only = true;
+    return run_ring(c, a, st, o);
 }
 
 int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcount, void* stream)
@@ -799,7 +866,7 @@ int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcoun
     a.R = c->R;
     a.op = kOpReduceScatter;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st);
+    return run_ring(c, a, st, ws_opts(c));
 }
 
 int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, void* stream)
@@ -832,7 +899,7 @@ int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, v
     a.R = c->R;
     a.op = kOpAllGather;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st);
+    return run_ring(c, a, st, ws_opts(c));
 }
 
 int ar_check(ar_comm_t c)

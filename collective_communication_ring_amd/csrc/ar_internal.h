@@ -83,6 +83,7 @@ struct RingArgs {
                          //   part[c * part_seg + e]
     uint32_t max_units;  // fused form, vector path: waves that take tiles (the staging holds
                          //   this many); waves of the grid past it exit
+    int ragged;          // fused form, vector path: some segment ends inside a wave tile
     uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
     uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
     int m;            // this channel's ring stride: rank q receives from q - m
@@ -158,6 +159,12 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 
 // Last HIP error of the utility calls (ar_stream_*, ar_ll_pingpong).
 extern int g_util_hip_error;
+
+// The allocation-free all-reduce's device array (ar_noalloc.hip): 8 MiB per
+// GPU, the hand-off staging of 2,048 waves for bfloat16 (4,096 for 32-bit
+// types).  noalloc_scratch gives the current device's copy and its size.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
 // Largest number of workgroups of each persistent kernel that can be
 // resident at once on the current device (0 on error).

@@ -179,6 +179,30 @@ int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
  * ascending rank order. */
 int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, void* stream);
 
+/* All-reduce that allocates nothing, for callers that cannot allocate device
+ * memory when they call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, result and summation
+ * order as ar_allreduce with the ring in its fused form.  It always runs the
+ * fused ring (the comm's algorithm, protocol and launch options are not
+ * consulted) and needs no workspace: ar_set_workspace is not required.
+ * Where ar_allreduce stages the float32 running value in the workspace
+ * (bfloat16, or send == recv), this call uses a device array of 8 MiB that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * launch then takes at most as many waves as the array holds staging slots
+ * (2,048 for bfloat16, 4,096 for 32-bit types), so every count up to the
+ * comm's capacity runs.  Limit: when the buffers are not 16-byte aligned
+ * row by row (or segments are shorter than 2 KiB) the call takes the scalar
+ * path, which keeps one float32 per element in the array; there, with the
+ * running value staged, count * 4 must not exceed 8 MiB, and a larger count
+ * returns AR_ERR_INVALID_ARG without launching anything.  Nothing in the
+ * array needs clearing (a call writes every slot before reading it).  All
+ * calls on one GPU share its array: two of them in flight at once on one GPU
+ * (on different streams, or from different comms) race and give wrong
+ * results; order them on one stream.  Errors: as ar_allreduce, plus
+ * AR_ERR_HIP when the array's address cannot be looked up. */
+int ar_allreduce_noalloc(ar_comm_t comm, const void* send, void* recv, size_t count,
+                         void* stream);
+
 /* Reduce-scatter (sum, or the comm's AR_OPT_REDOP), ring only.  send is
  * [R][R*recvcount], recv is [R][recvcount], not overlapping: row q of recv
  * receives segment q of the reduction ("NCCL, NIXL, and Distributed GPU
