@@ -127,32 +127,49 @@ struct Tile {
     uint32_t lane;
 };
 
-// Rows of the tile: rank r's input and output, 2 KiB (32-bit T) each.
+// The tile's place in the rows of one rank-major array, walked around the
+// ring: rank r's row is at base + r * row bytes; next() moves to rank r + m
+// with an add and a wrap instead of a multiply, so that no chain of scalar
+// multiplies sits between one step's store and the next step's load.
+struct RowWalk {
+    const char* p;    // the current rank's tile
+    const char* end;  // base + R * row: one past the last rank
+    uint64_t step;    // m * row bytes
+    uint64_t wrap;    // R * row bytes
+    __device__ void next()
+    {
+        p += step;
+        if (p >= end)
+            p -= wrap;
+    }
+    __device__ rsrc_t rsrc() const { return tile_rsrc(p, kTileSlots * 16u); }
+};
+
+// Walk over the tile in `arr` ([R][row] elements of T) starting at rank r.
 template <class E, int V>
-__device__ inline rsrc_t in_tile(const RingArgs& a, const Tile& t, int r)
+__device__ inline RowWalk row_walk(const void* arr, uint64_t row, const RingArgs& a, const Tile& t,
+                                   int r)
 {
-    const typename E::T* p = static_cast<const typename E::T*>(a.send) + (uint64_t)r * a.send_row +
-                             t.lo + t.first * V;
-    return tile_rsrc(p, kTileSlots * 16u);
-}
-template <class E, int V>
-__device__ inline rsrc_t out_tile(const RingArgs& a, const Tile& t, int r)
-{
-    typename E::T* p = static_cast<typename E::T*>(a.out) + (uint64_t)r * a.out_row + t.lo +
-                       t.first * V;
-    return tile_rsrc(p, kTileSlots * 16u);
+    const uint64_t rb = row * sizeof(typename E::T);
+    const char* base = static_cast<const char*>(arr) + (t.lo + t.first * V) * sizeof(typename E::T);
+    RowWalk w;
+    w.p = base + (uint64_t)r * rb;
+    w.end = base + (uint64_t)a.R * rb;
+    w.step = (uint64_t)a.m * rb;
+    w.wrap = (uint64_t)a.R * rb;
+    return w;
 }
 
 // One reduce step of a whole wave tile.  x holds the received value: on entry
 // at step 0 (the predecessor's input), else loaded here from the hand-off slot
 // the previous step stored (LOADX).  With PREFETCH the input of the next
-// step's rank (*rn, advanced by m) is loaded into `nxt` after the hand-off
+// step's rank (the walker `in`, then advanced by m) is loaded into `nxt` after the hand-off
 // load, so a wait for the hand-off leaves it in flight; `own` was loaded the
 // same way one step earlier.  LAST: the owner's step, written as T.
 template <class E, int V, int RED, bool LOADX, bool PREFETCH, bool LAST>
 __device__ inline void wt_step(const RingArgs& a, const Tile& t, typename E::A (&x)[kWaveSlots][V],
                                const u32x4 (&own)[kWaveSlots], u32x4 (&nxt)[kWaveSlots],
-                               rsrc_t hand, rsrc_t fin, int* rn)
+                               rsrc_t hand, rsrc_t fin, RowWalk* in)
 {
     if constexpr (LOADX) {
 #pragma unroll
@@ -160,13 +177,11 @@ __device__ inline void wt_step(const RingArgs& a, const Tile& t, typename E::A (
             a_load<E, V>(hand, t.lane, u, x[u]);
     }
     if constexpr (PREFETCH) {
-        const rsrc_t q = in_tile<E, V>(a, t, *rn);
+        const rsrc_t q = in->rsrc();
 #pragma unroll
         for (int u = 0; u < kWaveSlots; ++u)
             nxt[u] = bload<kPolStream>(q, t_off(u, t.lane));
-        *rn += a.m;
-        if (*rn >= a.R)
-            *rn -= a.R;
+        in->next();
     }
 #pragma unroll
     for (int u = 0; u < kWaveSlots; ++u) {
@@ -193,26 +208,24 @@ template <class E, int V, int RED>
 __device__ inline void wt_reduce(const RingArgs& a, const Tile& t, rsrc_t hand, rsrc_t fin)
 {
     using A = typename E::A;
-    const int R = a.R, m = a.m;
-    int r1 = t.c + m;
+    const int R = a.R;
+    int r1 = t.c + a.m;
     if (r1 >= R)
         r1 -= R;
-    int r2 = r1 + m;
-    if (r2 >= R)
-        r2 -= R;
+    RowWalk rn = row_walk<E, V>(a.send, a.send_row, a, t, r1);
     A x[kWaveSlots][V];
     u32x4 b0[kWaveSlots], b1[kWaveSlots];
     {
-        const rsrc_t q1 = in_tile<E, V>(a, t, r1), q2 = in_tile<E, V>(a, t, r2);
+        const rsrc_t q1 = rn.rsrc();
+        rn.next();
+        const rsrc_t q2 = rn.rsrc();
+        rn.next();  // now the rank whose input step 1 adds
 #pragma unroll
         for (int u = 0; u < kWaveSlots; ++u) {
             widen_slot<E, V>(bload<kPolStream>(q1, t_off(u, t.lane)), x[u]);
             b0[u] = bload<kPolStream>(q2, t_off(u, t.lane));
         }
     }
-    int rn = r2 + m;  // the rank whose input step 1 adds
-    if (rn >= R)
-        rn -= R;
     if (R == 2) {
         wt_step<E, V, RED, false, false, true>(a, t, x, b0, b1, hand, fin, &rn);
         return;
@@ -238,27 +251,26 @@ __device__ inline void wt_reduce(const RingArgs& a, const Tile& t, rsrc_t hand, 
 template <class E, int V, int OP>
 __device__ inline void wt_copy(const RingArgs& a, const Tile& t)
 {
+    RowWalk w = row_walk<E, V>(a.out, a.out_row, a, t, t.c);
+    rsrc_t src = w.rsrc();
     if constexpr (OP == kOpAllGather) {
         // send is [R][S]: the owner's shard, at the same offset within it
-        const typename E::T* src = static_cast<const typename E::T*>(a.send) +
+        const typename E::T* own = static_cast<const typename E::T*>(a.send) +
                                    (uint64_t)t.c * a.send_row + (t.lo - (uint64_t)t.c * a.S) +
                                    t.first * V;
-        const rsrc_t s = tile_rsrc(src, kTileSlots * 16u), d = out_tile<E, V>(a, t, t.c);
+        const rsrc_t s = tile_rsrc(own, kTileSlots * 16u);
         u32x4 v[kWaveSlots];
 #pragma unroll
         for (int u = 0; u < kWaveSlots; ++u)
             v[u] = bload<kPolStream>(s, t_off(u, t.lane));
 #pragma unroll
         for (int u = 0; u < kWaveSlots; ++u)
-            bstore<kPolPlain>(d, t_off(u, t.lane), v[u]);
+            bstore<kPolPlain>(src, t_off(u, t.lane), v[u]);
         step_boundary();
     }
-    int p = t.c;
     for (int s = 0; s <= a.R - 2; ++s) {
-        int q = p + a.m;
-        if (q >= a.R)
-            q -= a.R;
-        const rsrc_t src = out_tile<E, V>(a, t, p), dst = out_tile<E, V>(a, t, q);
+        w.next();
+        const rsrc_t dst = w.rsrc();
         u32x4 v[kWaveSlots];
 #pragma unroll
         for (int u = 0; u < kWaveSlots; ++u)
@@ -267,7 +279,7 @@ __device__ inline void wt_copy(const RingArgs& a, const Tile& t)
         for (int u = 0; u < kWaveSlots; ++u)
             bstore<kPolPlain>(dst, t_off(u, t.lane), v[u]);
         step_boundary();
-        p = q;
+        src = dst;
     }
 }
 
@@ -323,7 +335,10 @@ __device__ inline void wt_ragged(const RingArgs& a, const Tile& t, typename E::A
     }
 }
 
-template <int DT, int OP, int RED>
+// RAGGED: some segment ends inside a tile (the host knows from the sizes);
+// without it every tile is whole and the checked path is not compiled in,
+// which keeps the kernel's registers (and so its occupancy) to the chain's.
+template <int DT, int OP, int RED, bool RAGGED>
 __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits, uint32_t lane)
 {
     using E = Elem<DT>;
@@ -357,7 +372,7 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
                 }
                 if constexpr (OP != kOpReduceScatter)
                     wt_copy<E, V, OP>(a, tl);
-            } else {
+            } else if constexpr (RAGGED) {
                 wt_ragged<E, V, OP>(a, tl, acc);
             }
         }
@@ -369,7 +384,9 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
     }
 }
 
-template <int DT, int OP>
+// The reduction operator is a template argument (the host picks the
+// instantiation), so each kernel holds one operator's code.
+template <int DT, int OP, int RED, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void k_ring_fused_vec(RingArgs a)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -377,22 +394,37 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused_vec(RingArgs a)
     const uint32_t nunits = min(gridDim.x * (uint32_t)kWaves, a.max_units);
     if (unit >= nunits)
         return;
+    wt_run<DT, OP, RED, RAGGED>(a, unit, nunits, lane);
+}
+
+template <int DT, int OP, int RED>
+void fused_vec_go(const RingArgs& a, int grid, hipStream_t st)
+{
+    if (a.ragged)
+        hipLaunchKernelGGL((k_ring_fused_vec<DT, OP, RED, true>), dim3(grid), dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_ring_fused_vec<DT, OP, RED, false>), dim3(grid), dim3(kBlock), 0, st, a);
+}
+
+template <int DT, int OP>
+void fused_vec_op(const RingArgs& a, int grid, hipStream_t st)
+{
     if constexpr (OP == kOpAllGather) {
-        wt_run<DT, OP, AR_SUM>(a, unit, nunits, lane);
+        fused_vec_go<DT, OP, AR_SUM>(a, grid, st);  // a copy: no operator
     } else {
         switch (a.redop) {
         case AR_MAX:
-            wt_run<DT, OP, AR_MAX>(a, unit, nunits, lane);
+            fused_vec_go<DT, OP, AR_MAX>(a, grid, st);
             break;
         case AR_MIN:
-            wt_run<DT, OP, AR_MIN>(a, unit, nunits, lane);
+            fused_vec_go<DT, OP, AR_MIN>(a, grid, st);
             break;
         case AR_AVG:
-            if constexpr (DT != AR_INT32)
-                wt_run<DT, OP, AR_AVG>(a, unit, nunits, lane);
+            if constexpr (DT != AR_INT32)  // no integer average (refused by the host)
+                fused_vec_go<DT, OP, AR_AVG>(a, grid, st);
             break;
         default:
-            wt_run<DT, OP, AR_SUM>(a, unit, nunits, lane);
+            fused_vec_go<DT, OP, AR_SUM>(a, grid, st);
             break;
         }
     }
@@ -402,12 +434,11 @@ template <int DT>
 hipError_t fused_vec_launch(const RingArgs& a, int grid, hipStream_t st)
 {
     if (a.op == kOpAllReduce)
-        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+        fused_vec_op<DT, kOpAllReduce>(a, grid, st);
     else if (a.op == kOpReduceScatter)
-        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st,
-                           a);
+        fused_vec_op<DT, kOpReduceScatter>(a, grid, st);
     else
-        hipLaunchKernelGGL((k_ring_fused_vec<DT, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+        fused_vec_op<DT, kOpAllGather>(a, grid, st);
     return hipGetLastError();
 }
 
@@ -418,7 +449,7 @@ int resident_vec_dt()
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring_fused_vec<DT, kOpAllReduce>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring_fused_vec<DT, kOpAllReduce, AR_SUM, true>,
                                                      kBlock, 0) != hipSuccess)
         return 0;
     return per_cu * ncu;
