@@ -21,39 +21,36 @@ __device__ inline void ll_store(uint64_t* line, uint32_t data, uint32_t flag)
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait for K lines at once: every pass issues the loads of all lines still
-// pending, so the K waits overlap instead of adding up.  Line k is complete
-// when its flag half equals flag[k].  Lines with pending[k] == false on entry
-// are skipped.  Gives up (returns false) when `deadline` passes or the error
-// word is set; data[k] of a line that never arrived is left 0.
+// Wait for K lines at once, without per-lane branches in the poll: every
+// pass loads line k in every lane of a wave in which any lane waits for it
+// (a lane that does not, want[k] == false, must still hold a valid address;
+// its value is ignored), then checks all flags.  Line k is skipped as a whole
+// (a scalar branch) when no lane of the wave waits for it, so a short message
+// polls one line, not K.  A line that has arrived keeps its value for the
+// rest of the call (one writer per call), so loading it again is harmless; a
+// pass is a handful of instructions, so a line is seen soon after it lands.
+// Gives up (returns false) when `deadline` passes or the error word is set.
 template <int K>
-__device__ inline bool ll_wait_lines(const uint64_t* const (&line)[K], bool (&pending)[K],
-                                     const uint32_t (&flag)[K], uint64_t deadline,
-                                     const uint32_t* err, uint32_t (&data)[K])
+__device__ inline bool ll_wait_all(const uint64_t* const (&line)[K], const bool (&want)[K],
+                                   const uint32_t (&flag)[K], uint64_t deadline,
+                                   const uint32_t* err, uint32_t (&data)[K])
 {
+    bool live[K];  // wave-uniform
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        live[k] = __builtin_amdgcn_ballot_w64(want[k]) != 0;
     for (uint32_t spin = 0;; ++spin) {
         uint64_t v[K];
 #pragma unroll
         for (int k = 0; k < K; ++k)
-            if (pending[k])
-                v[k] = __hip_atomic_load(line[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // every value is checked at once; saying so explicitly lets the
-        // compiler see that none of these conditional loads is still
-        // outstanding afterwards, so later stores need no wait of their own
-        wait_vmem_all();
-        bool any = false;
+            v[k] = live[k] ? __hip_atomic_load(line[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        bool done = true;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            if (pending[k]) {
-                if ((uint32_t)(v[k] >> 32) == flag[k]) {
-                    data[k] = (uint32_t)v[k];
-                    pending[k] = false;
-                } else {
-                    any = true;
-                }
-            }
+            done &= !want[k] || (uint32_t)(v[k] >> 32) == flag[k];
+            data[k] = (uint32_t)v[k];
         }
-        if (!any)
+        if (done)
             return true;
         if ((spin & 63u) == 63u) {
             if ((uint64_t)wall_clock64() > deadline)
@@ -67,7 +64,7 @@ __device__ inline bool ll_wait_lines(const uint64_t* const (&line)[K], bool (&pe
 
 // The same with one flag for every line.
 template <int K>
-__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pending)[K],
+__device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], const bool (&want)[K],
                                      uint32_t flag, uint64_t deadline, const uint32_t* err,
                                      uint32_t (&data)[K])
 {
@@ -75,7 +72,7 @@ __device__ inline bool ll_wait_batch(const uint64_t* const (&line)[K], bool (&pe
 #pragma unroll
     for (int k = 0; k < K; ++k)
         f[k] = flag;
-    return ll_wait_lines<K>(line, pending, f, deadline, err, data);
+    return ll_wait_all<K>(line, want, f, deadline, err, data);
 }
 
 }  // namespace ar

@@ -26,20 +26,9 @@
 namespace ar {
 namespace {
 
-template <class E>
-__device__ inline typename E::A combine_rt(int redop, typename E::A a, typename E::A b)
-{
-    switch (redop) {
-    case AR_MAX:
-        return combine<E, AR_MAX>(a, b);
-    case AR_MIN:
-        return combine<E, AR_MIN>(a, b);
-    default:
-        return combine<E, AR_SUM>(a, b);
-    }
-}
-
-template <int DT, int OP>
+// The reduction operator is a template argument (the host picks the
+// instantiation; the all-gather has none and takes AR_SUM).
+template <int DT, int OP, int RED>
 __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
 {
     using E = Elem<DT>;
@@ -112,15 +101,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                         in[k] = E::widen(send[(uint64_t)p * a.send_row + e0 + (ok[k] ? i[k] : 0)]);
                 } else {
                     const uint64_t* ln[K];
-                    bool pend[K];
                     uint32_t d[K];
 #pragma unroll
-                    for (int k = 0; k < K; ++k) {
+                    for (int k = 0; k < K; ++k)
                         ln[k] = theirs + (ok[k] ? i[k] : 0);
-                        pend[k] = ok[k];
-                        d[k] = 0;
-                    }
-                    if (!ll_wait_batch<K>(ln, pend, f_red, deadline, err, d))
+                    if (!ll_wait_batch<K>(ln, ok, f_red, deadline, err, d))
                         timed_out = true;
 #pragma unroll
                     for (int k = 0; k < K; ++k)
@@ -131,12 +116,12 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                 for (int k = 0; k < K; ++k) {
                     if (!ok[k])
                         continue;
-                    A v = combine_rt<E>(a.redop, in[k], E::widen(own[k]));
+                    A v = combine<E, RED>(in[k], E::widen(own[k]));
                     if (!last_reduce) {
                         if (publish)
                             ll_store(mine + i[k], E::to_bits(v), f_red);
                     } else {
-                        if (a.redop == AR_AVG)
+                        if constexpr (RED == AR_AVG)
                             v = finalize<E, AR_AVG>(v, fr);
                         if (OP == kOpAllReduce && publish)  // the owner starts the copy phase
                             ll_store(mine + i[k], E::to_bits(v), f_copy);
@@ -161,15 +146,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
                 }
             } else {
                 const uint64_t* ln[K];
-                bool pend[K];
                 uint32_t d[K];
 #pragma unroll
-                for (int k = 0; k < K; ++k) {
+                for (int k = 0; k < K; ++k)
                     ln[k] = theirs + (ok[k] ? i[k] : 0);
-                    pend[k] = ok[k];
-                    d[k] = 0;
-                }
-                if (!ll_wait_batch<K>(ln, pend, f_copy, deadline, err, d))
+                if (!ll_wait_batch<K>(ln, ok, f_copy, deadline, err, d))
                     timed_out = true;
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
@@ -205,15 +186,35 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     }
 }
 
+template <int DT, int OP>
+void ring_ll_launch_op(const RingLLArgs& a, int grid, hipStream_t st)
+{
+    switch (a.redop) {
+    case AR_MAX:
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MAX>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_MIN:
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MIN>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_AVG:
+        if constexpr (DT != AR_INT32)  // no integer average (refused by the host)
+            hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_AVG>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    default:
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    }
+}
+
 template <int DT>
 hipError_t ring_ll_launch(const RingLLArgs& a, int grid, hipStream_t st)
 {
     if (a.op == kOpAllReduce)
-        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllReduce>), dim3(grid), dim3(kBlock), 0, st, a);
+        ring_ll_launch_op<DT, kOpAllReduce>(a, grid, st);
     else if (a.op == kOpReduceScatter)
-        hipLaunchKernelGGL((k_ring_ll<DT, kOpReduceScatter>), dim3(grid), dim3(kBlock), 0, st, a);
+        ring_ll_launch_op<DT, kOpReduceScatter>(a, grid, st);
     else
-        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllGather>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllGather, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 
@@ -224,9 +225,9 @@ int resident_ring_ll_dt()
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, k_ring_ll<DT, kOpAllReduce>, kBlock, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, k_ring_ll<DT, kOpReduceScatter>, kBlock, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a3, k_ring_ll<DT, kOpAllGather>, kBlock, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, k_ring_ll<DT, kOpAllReduce, AR_SUM>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, k_ring_ll<DT, kOpReduceScatter, AR_SUM>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a3, k_ring_ll<DT, kOpAllGather, AR_SUM>, kBlock, 0) != hipSuccess)
         return 0;
     return min(a1, min(a2, a3)) * ncu;
 }

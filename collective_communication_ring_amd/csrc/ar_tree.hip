@@ -45,22 +45,9 @@
 namespace ar {
 namespace {
 
-// The reduction operator is uniform per launch (a runtime switch is enough
-// on this latency-bound path).
-template <class E>
-__device__ inline typename E::A combine_rt(int redop, typename E::A a, typename E::A b)
-{
-    switch (redop) {
-    case AR_MAX:
-        return combine<E, AR_MAX>(a, b);
-    case AR_MIN:
-        return combine<E, AR_MIN>(a, b);
-    default:
-        return combine<E, AR_SUM>(a, b);
-    }
-}
-
-template <int DT>
+// The reduction operator is a template argument (the host picks the
+// instantiation): on this latency-bound path every branch counts.
+template <int DT, int RED>
 __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 {
     using E = Elem<DT>;
@@ -139,38 +126,38 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
             const uint64_t* up_c0 = a.up + ((uint64_t)t * R + child0) * a.line_stride;
             const uint64_t* up_c1 = a.up + ((uint64_t)t * R + child1) * a.line_stride;
             const uint64_t* ln[2 * K];
-            bool pend[2 * K];
+            bool want[2 * K];
             uint32_t fl[2 * K];
             uint32_t d[2 * K];
 #pragma unroll
             for (int k = 0; k < K; ++k) {
+                // a line this lane does not wait for is read at offset 0 (valid)
                 ln[k] = up_c0 + (ok[k] ? idx[k] : 0);
-                ln[K + k] = up_c1 + (ok[k] ? idx[k] : 0);
-                pend[k] = ok[k];
-                pend[K + k] = ok[k] && nchild > 1;
+                ln[K + k] = (nchild > 1 ? up_c1 : up_c0) + (ok[k] ? idx[k] : 0);
+                want[k] = ok[k];
+                want[K + k] = ok[k] && nchild > 1;
                 fl[k] = flag[k];
                 fl[K + k] = flag[k];
-                d[k] = 0;
-                d[K + k] = 0;
             }
-            if (!ll_wait_lines<2 * K>(ln, pend, fl, deadline, err, d))
+            if (!ll_wait_all<2 * K>(ln, want, fl, deadline, err, d))
                 timed_out = true;
+            // own value first, then the children in ascending rank order; a
+            // lane past the end combines junk it never stores
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (ok[k])
-                    acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d[k]));
+                acc[k] = combine<E, RED>(acc[k], E::from_bits(d[k]));
             if (nchild > 1) {
 #pragma unroll
                 for (int k = 0; k < K; ++k)
-                    if (ok[k])
-                        acc[k] = combine_rt<E>(a.redop, acc[k], E::from_bits(d[K + k]));
+                    acc[k] = combine<E, RED>(acc[k], E::from_bits(d[K + k]));
             }
         }
-        if (parent < 0 && a.redop == AR_AVG) {  // the root's sum is final: average it once
+        if constexpr (RED == AR_AVG) {
+            if (parent < 0) {  // the root's sum is final: average it once
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                if (ok[k])
+                for (int k = 0; k < K; ++k)
                     acc[k] = finalize<E, AR_AVG>(acc[k], (float)R);
+            }
         }
         if (parent >= 0) {
 #pragma unroll
@@ -179,20 +166,15 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
                     ll_store(up_mine + idx[k], E::to_bits(acc[k]), flag[k]);
             // broadcast down: the root's value arrives from the parent
             const uint64_t* ln[K];
-            bool pend[K];
             uint32_t d[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
+            for (int k = 0; k < K; ++k)
                 ln[k] = down_mine + (ok[k] ? idx[k] : 0);
-                pend[k] = ok[k];
-                d[k] = 0;
-            }
-            if (!ll_wait_lines<K>(ln, pend, flag, deadline, err, d))
+            if (!ll_wait_all<K>(ln, ok, flag, deadline, err, d))
                 timed_out = true;
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (ok[k])
-                    acc[k] = E::from_bits(d[k]);
+                acc[k] = E::from_bits(d[k]);
         }
         // broadcast down to the children first (they are waiting), then
         // write this rank's output
@@ -231,10 +213,34 @@ int resident_tree_dt()
         return 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_ll<DT>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_ll<DT, AR_SUM>, kBlock, 0) !=
         hipSuccess)
         return 0;
     return per_cu * ncu;
+}
+
+}  // namespace
+
+namespace {
+
+template <int DT>
+void tree_launch_dt(const TreeArgs& a, int grid, hipStream_t st)
+{
+    switch (a.redop) {
+    case AR_MAX:
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_MAX>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_MIN:
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_MIN>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    case AR_AVG:
+        if constexpr (DT != AR_INT32)  // no integer average (refused by the host)
+            hipLaunchKernelGGL((k_tree_ll<DT, AR_AVG>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    default:
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
+        break;
+    }
 }
 
 }  // namespace
@@ -243,13 +249,13 @@ hipError_t launch_tree_ll(int dtype, const TreeArgs& a, int grid, hipStream_t st
 {
     switch (dtype) {
     case AR_INT32:
-        hipLaunchKernelGGL(k_tree_ll<AR_INT32>, dim3(grid), dim3(kBlock), 0, st, a);
+        tree_launch_dt<AR_INT32>(a, grid, st);
         break;
     case AR_FLOAT32:
-        hipLaunchKernelGGL(k_tree_ll<AR_FLOAT32>, dim3(grid), dim3(kBlock), 0, st, a);
+        tree_launch_dt<AR_FLOAT32>(a, grid, st);
         break;
     case AR_BF16:
-        hipLaunchKernelGGL(k_tree_ll<AR_BF16>, dim3(grid), dim3(kBlock), 0, st, a);
+        tree_launch_dt<AR_BF16>(a, grid, st);
         break;
     default:
         return hipErrorInvalidValue;
