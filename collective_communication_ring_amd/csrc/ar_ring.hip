@@ -30,15 +30,19 @@
 // Two launch forms live in this file:
 //   step  -- one launch per step over all R ranks; the kernel boundary
 //            orders the steps.
-//   fused -- one persistent launch; a workgroup takes a tile of a segment
-//            through all 2(R-1) steps in order.  Each thread touches the same
-//            element positions at every step, so the value it stored for rank
-//            q is the one it loads back as rank q+1's input (same-thread
-//            program order; the compiler is kept from forwarding it in
-//            registers, so every step really reads the hand-off slot).  Tiles
-//            of a step are independent, so there are no flags and no fences;
-//            the slot a step writes is still hot in this XCD's L2 when the
-//            next step reads and overwrites it.
+//   fused, scalar path -- one persistent launch; a workgroup takes a tile of
+//            a segment through all 2(R-1) steps in order, one element per
+//            thread and step.  Each thread touches the same element positions
+//            at every step, so the value it stored for rank q is the one it
+//            loads back as rank q+1's input (same-thread program order; the
+//            compiler is kept from forwarding it in registers, so every step
+//            really reads the hand-off slot).  It serves views whose rows are
+//            not 16-byte aligned and counts too small for a vector tile.
+// The fused form's vector path (wave tiles, 16-byte buffer loads and stores)
+// lives in ar_fused.hip; ar_comm.cpp chooses between the two paths per call.
+// Tiles of a step are independent, so neither fused path has flags or
+// fences; the slot a step writes is still hot in this XCD's L2 when the next
+// step reads and overwrites it.
 #include "ar_elem.h"
 #include "ar_internal.h"
 #include "ar_slots.h"

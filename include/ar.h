@@ -147,10 +147,13 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
             ar_proto_t proto);
 
 /* Release the host state of a communicator.  Does not free caller memory.
- * NULL is a no-op. */
+ * NULL is a no-op.  No page defines this call: it is this library's own
+ * boundary design (the handle's lifetime). */
 int ar_destroy(ar_comm_t comm);
 
-/* Bytes of device workspace this communicator needs: one row of `count`
+/* Bytes of device workspace this communicator needs (no page defines this
+ * call: it is this library's own boundary design, so that the caller owns
+ * every device allocation): one row of `count`
  * 4-byte accumulators for the ring's hand-off (used by bfloat16 and by an
  * in-place all-reduce; otherwise a segment's running value is handed on
  * through its owner's row of recv), LL lines for the tree and the ring-LL
@@ -161,7 +164,9 @@ size_t ar_workspace_bytes(ar_comm_t comm);
 
 /* Hand the workspace to the communicator and clear its control block and
  * LL lines (enqueued on `stream`; ordered before any later call on the same
- * stream).  The memory stays owned by the caller and must outlive every
+ * stream).  No page defines this call: it is this library's own boundary
+ * design; the stream argument lets the clearing be ordered with the caller's
+ * own work instead of synchronizing the device.  The memory stays owned by the caller and must outlive every
  * collective issued on this comm.  Returns AR_ERR_INVALID_ARG when `bytes`
  * is smaller than ar_workspace_bytes or `dev` is NULL or misaligned. */
 int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
@@ -220,7 +225,8 @@ int ar_all_gather(ar_comm_t comm, const void* send, void* recv, size_t sendcount
 
 /* Synchronize the comm's last stream and report its device error word:
  * AR_ERR_TIMEOUT when a bounded wait expired in an earlier call, else
- * AR_SUCCESS.  Clears the word. */
+ * AR_SUCCESS.  Clears the word.  No page defines this call: it is this
+ * library's own boundary design (the kernels' bounded waits report here). */
 int ar_check(ar_comm_t comm);
 
 /* Set / read one tunable (ar_option_t).  Unknown options or out-of-range
@@ -313,7 +319,8 @@ int ar_stream_destroy(void* stream);
 int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int xcd_apart,
                    int64_t timeout_us, void* stream);
 
-/* Message for a status code (static storage). */
+/* Message for a status code (static storage).  No page defines this call:
+ * it is this library's own boundary design. */
 const char* ar_status_string(int status);
 
 /* Last hipError_t seen by this comm (0 if none); with comm == NULL, the last
