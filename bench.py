@@ -542,9 +542,10 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
     auto["fitted_lines"] = choices()
     probe.close()
     hop = ll_hop_latency_us(torch)
-    st = torch.cuda.current_stream().cuda_stream
+    # the stream is looked up at each call: under capture it is the graph's
     floor = time_graph(lambda: api.ar_stream_copy(send_flat.data_ptr(), recv_flat.data_ptr(), 16,
-                                                  st), 20, torch) * 1e3
+                                                  torch.cuda.current_stream().cuda_stream),
+                       20, torch) * 1e3
     del send_flat, recv_flat
     _, t_or, n_or, used = cpu_baseline_leg(lambda o: o.tree_allreduce(x), 1.0, 5)
     return dict(R=R, dtype="f32", sizes_bytes=sizes, t_us=res, exact=bool(exact),
