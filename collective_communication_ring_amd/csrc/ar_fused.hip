@@ -26,10 +26,14 @@
 //
 // Where the running value is handed on: in the owner's output row when the
 // accumulator type is the element type (the final value lands on the same
-// lines), else in a per-wave staging slot of the workspace that the wave
-// reuses for every tile it takes, so those lines stay in L2 and never become
-// a row of write-backs.  The staging slot keeps each 16-byte half of a lane's
-// accumulator slot in its own 1 KiB run, so one store instruction writes
+// lines).  A bfloat16 all-reduce (not in place, R >= 3) hands its float32
+// value on through the tile's lines of output rows c+m and c+2m, one 16-byte
+// half of each lane's accumulator slot in each: copy steps 0 and 1 later
+// overwrite those lines with the result, so the hand-off adds no lines of its
+// own.  Otherwise (reduce-scatter, in place, R = 2) it goes through a per-wave
+// staging slot of the workspace that the wave reuses for every tile it takes,
+// so those lines stay in L2 rather than becoming a row of write-backs.  Each
+// half is a run of the row tile's shape, so one store instruction writes
 // whole lines.
 //
 // Every access goes through a buffer resource that spans exactly the tile it
@@ -73,21 +77,24 @@ __device__ inline void bstore(rsrc_t r, uint32_t off, u32x4 v)
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, POL);
 }
 
-// Byte offset of slot u of `lane` in a row tile (16-byte slots of T) ...
+// Byte offset of slot u of `lane` in a row tile (16-byte slots of T).  A
+// lane's accumulator slot (V/4 16-byte halves) keeps half h in its own run
+// of the same shape, so each half is a row tile of its own.
 __device__ inline uint32_t t_off(int u, uint32_t lane) { return ((uint32_t)u * 64u + lane) * 16u; }
-// ... and of 16-byte half h of its accumulator slot (V/4 halves).
-template <int V>
-__device__ inline uint32_t a_off(int u, int h, uint32_t lane)
-{
-    return (((uint32_t)u * (V / 4) + (uint32_t)h) * 64u + lane) * 16u;
-}
+
+// Where a whole tile's running value is handed on: half h of every
+// accumulator slot in the run behind h[h] (one run for 32-bit T, two for
+// bfloat16), each kTileSlots * 16 bytes.
+struct Hand {
+    rsrc_t h[2];
+};
 
 template <class E, int V>
-__device__ inline void a_load(rsrc_t r, uint32_t lane, int u, typename E::A (&o)[V])
+__device__ inline void a_load(const Hand& r, uint32_t lane, int u, typename E::A (&o)[V])
 {
 #pragma unroll
     for (int h = 0; h < V / 4; ++h) {
-        const u32x4 q = bload<kPolPlain>(r, a_off<V>(u, h, lane));
+        const u32x4 q = bload<kPolPlain>(r.h[h], t_off(u, lane));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             o[4 * h + i] = E::from_bits(q[i]);
@@ -95,7 +102,7 @@ __device__ inline void a_load(rsrc_t r, uint32_t lane, int u, typename E::A (&o)
 }
 
 template <class E, int V>
-__device__ inline void a_store(rsrc_t r, uint32_t lane, int u, const typename E::A (&v)[V])
+__device__ inline void a_store(const Hand& r, uint32_t lane, int u, const typename E::A (&v)[V])
 {
 #pragma unroll
     for (int h = 0; h < V / 4; ++h) {
@@ -103,7 +110,7 @@ __device__ inline void a_store(rsrc_t r, uint32_t lane, int u, const typename E:
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             q[i] = E::to_bits(v[4 * h + i]);
-        bstore<kPolPlain>(r, a_off<V>(u, h, lane), q);
+        bstore<kPolPlain>(r.h[h], t_off(u, lane), q);
     }
 }
 
@@ -177,7 +184,7 @@ __device__ inline RowWalk row_walk(const void* arr, uint64_t row, const RingArgs
 template <class E, int V, int RED, int FP, bool LOADX, bool PREFETCH, bool LAST>
 __device__ inline void wt_step(const RingArgs& a, const Tile& t, typename E::A (&x)[kWaveSlots][V],
                                const u32x4 (&own)[kWaveSlots], u32x4 (&nxt)[kWaveSlots],
-                               rsrc_t hand, rsrc_t fin, RowWalk* in)
+                               const Hand& hand, rsrc_t fin, RowWalk* in)
 {
     if constexpr (LOADX) {
 #pragma unroll
@@ -213,7 +220,7 @@ __device__ inline void wt_step(const RingArgs& a, const Tile& t, typename E::A (
 // c + (s+2)m; its input was loaded during step s-1 into the other of two
 // register sets.
 template <class E, int V, int RED, int FP>
-__device__ inline void wt_reduce(const RingArgs& a, const Tile& t, rsrc_t hand, rsrc_t fin)
+__device__ inline void wt_reduce(const RingArgs& a, const Tile& t, const Hand& hand, rsrc_t fin)
 {
     using A = typename E::A;
     const int R = a.R;
@@ -357,6 +364,8 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
     const uint64_t ntiles = tps * (uint64_t)a.R;
     // this wave's staging slot, or the running value in part at c*part_seg + e
     A* stage = a.stage_wave ? static_cast<A*>(a.part) + (uint64_t)unit * a.stage_wave : nullptr;
+    // whole bfloat16 all-reduce tiles stage in the output rows when they can
+    const bool OUTSTAGE = DT == AR_BF16 && OP == kOpAllReduce && a.R >= 3 && a.send != a.out;
     int c = (int)(unit / tps);
     uint64_t k = unit % tps;
     for (uint64_t t = unit; t < ntiles; t += nunits) {
@@ -372,7 +381,27 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
                            : static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + tl.lo;
             if ((tl.first + kTileSlots) * V <= tl.len) {
                 if constexpr (OP != kOpAllGather) {
-                    const rsrc_t hand = tile_rsrc(acc + tl.first * V, kTileSlots * V * 4u);
+                    Hand hand;
+                    constexpr uint32_t half = kTileSlots * 16u;  // bytes of one half-run
+                    if (OUTSTAGE) {
+                        // bfloat16 all-reduce, not in place, R >= 3: the two halves
+                        // live in this tile's lines of output rows c+m and c+2m,
+                        // which copy steps 0 and 1 overwrite with the result, so
+                        // the hand-off adds no lines of its own to write back
+                        int r1 = c + a.m;
+                        if (r1 >= a.R)
+                            r1 -= a.R;
+                        int r2 = r1 + a.m;
+                        if (r2 >= a.R)
+                            r2 -= a.R;
+                        const T* o = static_cast<const T*>(a.out) + tl.lo + tl.first * V;
+                        hand.h[0] = tile_rsrc(o + (uint64_t)r1 * a.out_row, half);
+                        hand.h[1] = tile_rsrc(o + (uint64_t)r2 * a.out_row, half);
+                    } else {
+                        const char* b = reinterpret_cast<const char*>(acc + tl.first * V);
+                        hand.h[0] = tile_rsrc(b, half);
+                        hand.h[1] = tile_rsrc(b + half, half);
+                    }
                     T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
                              (OP == kOpReduceScatter ? tl.lo - (uint64_t)c * a.S : tl.lo) +
                              tl.first * V;
