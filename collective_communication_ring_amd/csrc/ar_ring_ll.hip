@@ -27,8 +27,13 @@ namespace ar {
 namespace {
 
 // The reduction operator is a template argument (the host picks the
-// instantiation; the all-gather has none and takes AR_SUM).
-template <int DT, int OP, int RED>
+// instantiation; the all-gather has none and takes AR_SUM).  K is the number
+// of sub-blocks a thread takes per pass: 1 when every workgroup has at most
+// one sub-block per step (small messages), else kRingLLEPT.  A step is
+// latency-bound, and a lone wave issues about one instruction every few
+// cycles, so the step's own instruction count is part of every hop: with
+// K = 1 there is one line per lane and no per-line branches.
+template <int DT, int OP, int RED, int K>
 __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
 {
     using E = Elem<DT>;
@@ -57,10 +62,10 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     T* out = static_cast<T*>(a.out);
     const float fr = (float)R;
     bool timed_out = false;
-    constexpr int K = kRingLLEPT;
 
-    for (int s = 0; s < (idle ? 0 : nsteps); ++s) {
-        const int c = (OP == kOpAllGather) ? mod_r(q - s * m, R) : mod_r(q - (s + 2) * m, R);
+    // segment of step 0; every later step takes the one m below (no division)
+    int c = (OP == kOpAllGather) ? q : mod_r(q - 2 * m, R);
+    for (int s = 0; s < (idle ? 0 : nsteps); ++s, c = (c >= m) ? c - m : c - m + R) {
         uint64_t lo, hi;
         seg_range(a.N, a.S, c, a.sub_lo, a.sub_len, &lo, &hi);
         const uint64_t len = hi - lo;
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
         const bool reduce = (OP != kOpAllGather) && s <= R - 2;
         const bool last_reduce = reduce && s == R - 2;
         // the last receiver of a segment's final does not pass it on
-        const bool forward = !reduce && (mod_r(c - m, R) != q);
+        const bool forward = !reduce && (((c >= m) ? c - m : c - m + R) != q);
         // sub-blocks of kBlock offsets: sub-block j belongs to workgroup j mod G
         // of every rank; a thread takes K of its workgroup's sub-blocks at once
         const uint64_t nsub = (plen + kBlock - 1) / kBlock;
@@ -186,35 +191,47 @@ __global__ __launch_bounds__(kBlock) void k_ring_ll(RingLLArgs a)
     }
 }
 
-template <int DT, int OP>
+template <int DT, int OP, int K>
 void ring_ll_launch_op(const RingLLArgs& a, int grid, hipStream_t st)
 {
     switch (a.redop) {
     case AR_MAX:
-        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MAX>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MAX, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     case AR_MIN:
-        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MIN>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_MIN, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     case AR_AVG:
         if constexpr (DT != AR_INT32)  // no integer average (refused by the host)
-            hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_AVG>), dim3(grid), dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_AVG, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     default:
-        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_ring_ll<DT, OP, AR_SUM, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     }
+}
+
+template <int DT, int K>
+void ring_ll_launch_k(const RingLLArgs& a, int grid, hipStream_t st)
+{
+    if (a.op == kOpAllReduce)
+        ring_ll_launch_op<DT, kOpAllReduce, K>(a, grid, st);
+    else if (a.op == kOpReduceScatter)
+        ring_ll_launch_op<DT, kOpReduceScatter, K>(a, grid, st);
+    else
+        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllGather, AR_SUM, K>), dim3(grid), dim3(kBlock), 0, st,
+                           a);
 }
 
 template <int DT>
 hipError_t ring_ll_launch(const RingLLArgs& a, int grid, hipStream_t st)
 {
-    if (a.op == kOpAllReduce)
-        ring_ll_launch_op<DT, kOpAllReduce>(a, grid, st);
-    else if (a.op == kOpReduceScatter)
-        ring_ll_launch_op<DT, kOpReduceScatter>(a, grid, st);
+    // one sub-block per workgroup and step at most: one line per thread
+    const uint64_t nsub = (a.piece_len + kBlock - 1) / kBlock;
+    if (nsub <= (uint64_t)a.per_rank_wg)
+        ring_ll_launch_k<DT, 1>(a, grid, st);
     else
-        hipLaunchKernelGGL((k_ring_ll<DT, kOpAllGather, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
+        ring_ll_launch_k<DT, kRingLLEPT>(a, grid, st);
     return hipGetLastError();
 }
 
@@ -225,9 +242,9 @@ int resident_ring_ll_dt()
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, k_ring_ll<DT, kOpAllReduce, AR_SUM>, kBlock, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, k_ring_ll<DT, kOpReduceScatter, AR_SUM>, kBlock, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a3, k_ring_ll<DT, kOpAllGather, AR_SUM>, kBlock, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&a1, k_ring_ll<DT, kOpAllReduce, AR_SUM, kRingLLEPT>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a2, k_ring_ll<DT, kOpReduceScatter, AR_SUM, kRingLLEPT>, kBlock, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&a3, k_ring_ll<DT, kOpAllGather, AR_SUM, kRingLLEPT>, kBlock, 0) != hipSuccess)
         return 0;
     return min(a1, min(a2, a3)) * ncu;
 }

@@ -46,8 +46,11 @@ namespace ar {
 namespace {
 
 // The reduction operator is a template argument (the host picks the
-// instantiation): on this latency-bound path every branch counts.
-template <int DT, int RED>
+// instantiation): on this latency-bound path every branch counts.  K is the
+// number of sub-blocks a thread takes per pass: 1 when every workgroup has at
+// most one sub-block (small messages: one line per lane, no per-line
+// branches), else kTreeEPT.
+template <int DT, int RED, int K>
 __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
 {
     using E = Elem<DT>;
@@ -84,7 +87,6 @@ __global__ __launch_bounds__(kBlock) void k_tree_ll(TreeArgs a)
     uint64_t* down_mine = a.down + ((uint64_t)t * R + v) * a.line_stride;
     uint32_t* epochs = a.epochs + (uint64_t)t * a.line_groups;
 
-    constexpr int K = kTreeEPT;
     const bool publish = (v != a.mute_rank);
     const uint64_t wave_first = threadIdx.x & ~(uint64_t)(kTreeGroup - 1);
     bool timed_out = false;
@@ -213,7 +215,7 @@ int resident_tree_dt()
         return 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_ll<DT, AR_SUM>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_tree_ll<DT, AR_SUM, kTreeEPT>, kBlock, 0) !=
         hipSuccess)
         return 0;
     return per_cu * ncu;
@@ -223,24 +225,38 @@ int resident_tree_dt()
 
 namespace {
 
-template <int DT>
-void tree_launch_dt(const TreeArgs& a, int grid, hipStream_t st)
+template <int DT, int K>
+void tree_launch_k(const TreeArgs& a, int grid, hipStream_t st)
 {
     switch (a.redop) {
     case AR_MAX:
-        hipLaunchKernelGGL((k_tree_ll<DT, AR_MAX>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_MAX, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     case AR_MIN:
-        hipLaunchKernelGGL((k_tree_ll<DT, AR_MIN>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_MIN, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     case AR_AVG:
         if constexpr (DT != AR_INT32)  // no integer average (refused by the host)
-            hipLaunchKernelGGL((k_tree_ll<DT, AR_AVG>), dim3(grid), dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL((k_tree_ll<DT, AR_AVG, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     default:
-        hipLaunchKernelGGL((k_tree_ll<DT, AR_SUM>), dim3(grid), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL((k_tree_ll<DT, AR_SUM, K>), dim3(grid), dim3(kBlock), 0, st, a);
         break;
     }
+}
+
+template <int DT>
+void tree_launch_dt(const TreeArgs& a, int grid, hipStream_t st)
+{
+    // the larger tree half's sub-blocks: at most one per workgroup means one
+    // line per thread
+    const uint64_t half = a.H > a.N - a.H ? a.H : a.N - a.H;
+    const uint64_t plen = a.piece_lo < half ? (a.piece_len < half - a.piece_lo ? a.piece_len : half - a.piece_lo) : 0;
+    const uint64_t nsub = (plen + kBlock - 1) / kBlock;
+    if (nsub <= (uint64_t)a.blocks_per_rank)
+        tree_launch_k<DT, 1>(a, grid, st);
+    else
+        tree_launch_k<DT, kTreeEPT>(a, grid, st);
 }
 
 }  // namespace
