@@ -29,19 +29,19 @@ constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
 // least-squares fits (weighted by 1/T^2) of graph-replayed all-reduces on
 // MI355X, R = 8 float32, 8 B - 4 MiB per rank; the fused ring's line is the
 // fit of its full 8 B - 1 GiB sweep.  With them the tree takes messages up to
-// ~670 KB/rank against the pipelined ring, ~735 KB against ring + LL and
-// ~1 MB against the step ring (measured: the tree is faster up to 512 KiB and
-// slower from 1 MiB), and none against the fused ring.
+// ~640 KB/rank against the pipelined ring, ~460 KB against ring + LL and
+// ~1 MB against the step ring (measured: the tree is faster than each of them
+// up to 512 KiB and slower from 1 MiB), and none against the fused ring.
 struct CostLine {
     double alpha_us;
     double bw_gbps;
 };
 constexpr CostLine kDefaultCost[AR_COST_FORMS] = {
-    {6.5, 37.2},    // tree + LL
-    {5.0, 370.0},   // ring, fused
-    {22.2, 281.0},  // ring, pipelined (simple protocol: ready flags)
-    {29.1, 189.0},  // ring, one launch per step
-    {16.3, 73.4},   // ring + LL
+    {5.9, 35.5},    // tree + LL
+    {3.9, 356.0},   // ring, fused
+    {21.7, 278.0},  // ring, pipelined (simple protocol: ready flags)
+    {28.9, 179.0},  // ring, one launch per step
+    {11.6, 63.2},   // ring + LL
 };
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
 constexpr uint64_t kMaxChunkBytes = 1ull << 30;      // pipelined ring: largest chunk

@@ -122,33 +122,32 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 // so the compiler waits for them right there (leaving the prefetch in
 // flight) instead of moving each load into its store's branch and waiting
 // for everything outstanding.
-template <class E, int RED, bool LOADX, bool PREFETCH, bool LAST>
-__device__ inline void scalar_step(typename E::A (&x)[kUnroll], const typename E::T (&own)[kUnroll],
-                                   typename E::T (&nxt)[kUnroll], typename E::A* acc,
+template <class E, int RED, int U, bool LOADX, bool PREFETCH, bool LAST>
+__device__ inline void scalar_step(typename E::A (&x)[U], const typename E::T (&own)[U],
+                                   typename E::T (&nxt)[U], typename E::A* acc,
                                    typename E::T* fin, const typename E::T* next_row,
-                                   const uint64_t (&e)[kUnroll], const bool (&ok)[kUnroll],
-                                   float R)
+                                   const uint64_t (&e)[U], const bool (&ok)[U], float R)
 {
     using A = typename E::A;
     if constexpr (LOADX) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             x[u] = acc[e[u]];
     }
     if constexpr (PREFETCH) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             nxt[u] = next_row[e[u]];
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
         __asm__ __volatile__("" ::"v"(x[u]));
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         A v = combine<E, RED>(x[u], E::widen(own[u]));
         if constexpr (LAST)
             v = finalize<E, RED>(v, R);
-        if (ok[u]) {
+        if (U == 1 || ok[u]) {  // with one slot per thread, every active thread's slot is in range
             if constexpr (LAST)
                 fin[e[u]] = E::narrow(v);
             else
@@ -160,13 +159,15 @@ __device__ inline void scalar_step(typename E::A (&x)[kUnroll], const typename E
 }
 
 // The R-1 reduce steps of a tile on the scalar path (segments shorter than
-// one 128-byte line).  Each active thread has the kUnroll elements j0 + u*js
-// of segment c; one past the end reads the thread's first element instead
-// and stores nothing, so every load is unconditional.  As on the vector path,
-// the input of the next step's rank is loaded before this step's store, into
-// the other of two register sets, so its HBM latency overlaps the hand-off
-// instead of adding to each step.
-template <class E, int RED>
+// one 128-byte line).  Each active thread has the U elements j0 + u*js of
+// segment c (U = 1 when the tile has at most one element per thread); one
+// past the end reads the thread's first element instead and stores nothing,
+// so every load is unconditional.  As on the vector path, the input of the
+// next step's rank is loaded before this step's store, into the other of two
+// register sets, so its HBM latency overlaps the hand-off instead of adding
+// to each step.  The rank whose row a step reads advances by m (no division:
+// each step is latency-bound, and its instruction count is part of it).
+template <class E, int RED, int U>
 __device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t len,
                                            uint64_t j0, uint64_t js)
 {
@@ -179,61 +180,119 @@ __device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo
     A* acc = static_cast<A*>(a.part) + (uint64_t)c * a.part_seg + lo;
     T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
              (a.op == kOpReduceScatter ? lo - (uint64_t)c * a.S : lo);
-    // x_{c+km}: the input of the rank that adds at step k-2
-    auto row = [&](int k) { return send + (uint64_t)mod_r(c + k * m, R) * a.send_row; };
-    uint64_t e[kUnroll];
-    bool ok[kUnroll];
+    // x_{c+km}: the input of the rank that adds at step k-2; rk walks c+m, c+2m, ...
+    int rk = c;
+    auto next_row = [&]() {
+        rk += m;
+        if (rk >= R)
+            rk -= R;
+        return send + (uint64_t)rk * a.send_row;
+    };
+    uint64_t e[U];
+    bool ok[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         const uint64_t j = j0 + (uint64_t)u * js;
         ok[u] = j < len;
         e[u] = ok[u] ? j : j0;
     }
-    A x[kUnroll];
-    T b0[kUnroll], b1[kUnroll];
-    const T* r1 = row(1);
-    const T* r2 = row(2);
+    A x[U];
+    T b0[U], b1[U];
+    const T* r1 = next_row();
+    const T* r2 = next_row();
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
         x[u] = E::widen(r1[e[u]]);
         b0[u] = r2[e[u]];
     }
     if (R == 2) {
-        scalar_step<E, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, U, false, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
         return;
     }
     // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
-    scalar_step<E, RED, false, true, false>(x, b0, b1, acc, fin, row(3), e, ok, fr);
+    scalar_step<E, RED, U, false, true, false>(x, b0, b1, acc, fin, next_row(), e, ok, fr);
     int s = 1;  // the next step; its input is in b1
     for (; s + 1 <= R - 3; s += 2) {
-        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 3), e, ok, fr);
-        scalar_step<E, RED, true, true, false>(x, b0, b1, acc, fin, row(s + 4), e, ok, fr);
+        scalar_step<E, RED, U, true, true, false>(x, b1, b0, acc, fin, next_row(), e, ok, fr);
+        scalar_step<E, RED, U, true, true, false>(x, b0, b1, acc, fin, next_row(), e, ok, fr);
     }
     if (s == R - 3) {
-        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, row(s + 3), e, ok, fr);
-        scalar_step<E, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, U, true, true, false>(x, b1, b0, acc, fin, next_row(), e, ok, fr);
+        scalar_step<E, RED, U, true, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
     } else {
-        scalar_step<E, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, U, true, false, true>(x, b1, b0, acc, fin, nullptr, e, ok, fr);
     }
 }
 
-template <class E>
+template <class E, int U>
 __device__ inline void fused_reduce_scalar_op(const RingArgs& a, int c, uint64_t lo, uint64_t len,
                                               uint64_t j0, uint64_t js)
 {
     switch (a.redop) {
     case AR_MAX:
-        fused_reduce_scalar<E, AR_MAX>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_MAX, U>(a, c, lo, len, j0, js);
         break;
     case AR_MIN:
-        fused_reduce_scalar<E, AR_MIN>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_MIN, U>(a, c, lo, len, j0, js);
         break;
     case AR_AVG:
-        fused_reduce_scalar<E, AR_AVG>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_AVG, U>(a, c, lo, len, j0, js);
         break;
     default:
-        fused_reduce_scalar<E, AR_SUM>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_SUM, U>(a, c, lo, len, j0, js);
         break;
+    }
+}
+
+// The copy steps of a tile on the scalar path: U elements per thread (the
+// same ones the reduce steps took), loads first and unconditional, then the
+// stores.
+template <class E, int U>
+__device__ inline void copy_scalar(const typename E::T* __restrict__ src,
+                                   typename E::T* __restrict__ dst, uint64_t len, uint64_t j0,
+                                   uint64_t js)
+{
+    typename E::T r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * js;
+        r[u] = src[j < len ? j : j0];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t j = j0 + (uint64_t)u * js;
+        if (U == 1 || j < len)
+            dst[j] = r[u];
+    }
+}
+
+// One tile's whole chain on the scalar path with U slots per thread.
+template <class E, int OP, int U>
+__device__ inline void fused_tile_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t len,
+                                         uint64_t j0, uint64_t js)
+{
+    using T = typename E::T;
+    T* out = static_cast<T*>(a.out);
+    const int R = a.R, m = a.m;
+    if constexpr (OP != kOpAllGather)
+        fused_reduce_scalar_op<E, U>(a, c, lo, len, j0, js);
+    if constexpr (OP != kOpReduceScatter) {
+        if constexpr (OP == kOpAllGather) {
+            const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
+                           (lo - (uint64_t)c * a.S);
+            copy_scalar<E, U>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
+            step_boundary();
+        }
+        int p = c;
+        for (int s = 0; s <= R - 2; ++s) {
+            int q = p + m;
+            if (q >= R)
+                q -= R;
+            copy_scalar<E, U>(out + (uint64_t)p * a.out_row + lo, out + (uint64_t)q * a.out_row + lo,
+                              len, j0, js);
+            step_boundary();
+            p = q;
+        }
     }
 }
 
@@ -273,13 +332,9 @@ template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
 {
     using E = Elem<DT>;
-    using T = typename E::T;
-    const int R = a.R;
     const uint64_t tile_slots = a.tile_slots;
     const uint64_t tiles_per_seg = (a.sub_len + tile_slots - 1) / tile_slots;
-    const uint64_t ntiles = tiles_per_seg * (uint64_t)R;
-    const int m = a.m;
-    T* out = static_cast<T*>(a.out);
+    const uint64_t ntiles = tiles_per_seg * (uint64_t)a.R;
 
     // with xcd_pack = n only every n-th workgroup works: workgroups are
     // dispatched to the XCDs round-robin, so the working ones share an XCD
@@ -296,26 +351,13 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
         if (!active)
             continue;  // this thread has no element in a part-filled tile
 
-        if constexpr (OP != kOpAllGather)
-            fused_reduce_scalar_op<E>(a, c, lo, len, j0, js);
-        if constexpr (OP != kOpReduceScatter) {
-            if constexpr (OP == kOpAllGather) {
-                const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
-                               (lo - (uint64_t)c * a.S);
-                copy_slots<E, 1>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
-                step_boundary();
-            }
-            int p = c;
-            for (int s = 0; s <= R - 2; ++s) {
-                int q = p + m;
-                if (q >= R)
-                    q -= R;
-                copy_slots<E, 1>(out + (uint64_t)p * a.out_row + lo, out + (uint64_t)q * a.out_row + lo,
-                                 len, j0, js);
-                step_boundary();
-                p = q;
-            }
-        }
+        // a tile whose stride covers all its elements (at most one per
+        // thread: scalar_tile spreads a part-filled tile one per thread)
+        // takes the one-slot chain
+        if (js >= len - (j0 - threadIdx.x))
+            fused_tile_scalar<E, OP, 1>(a, c, lo, len, j0, js);
+        else
+            fused_tile_scalar<E, OP, kUnroll>(a, c, lo, len, j0, js);
     }
 }
 
