@@ -317,7 +317,8 @@ __device__ inline bool scalar_tile(const RingArgs& a, uint64_t t, int* c, uint64
     *len = hi - *lo;
     const uint64_t first = k * tile_slots;
     const uint64_t n = *len > first ? *len - first : 0;
-    uint64_t stride = tile_slots / kUnroll;
+    // a tile of at most kBlock slots has one per thread, a larger one kUnroll
+    uint64_t stride = tile_slots <= (uint64_t)kBlock ? tile_slots : tile_slots / kUnroll;
     if (n < tile_slots)
         stride = n < (uint64_t)kBlock ? n : (uint64_t)kBlock;
     *js = stride;
@@ -351,10 +352,11 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
         if (!active)
             continue;  // this thread has no element in a part-filled tile
 
-        // a tile whose stride covers all its elements (at most one per
-        // thread: scalar_tile spreads a part-filled tile one per thread)
+        // a tile whose stride covers all its elements (one per thread)
         // takes the one-slot chain
-        if (js >= len - (j0 - threadIdx.x))
+        const uint64_t first = j0 - threadIdx.x;
+        const uint64_t nt = len - first < tile_slots ? len - first : tile_slots;
+        if (js >= nt)
             fused_tile_scalar<E, OP, 1>(a, c, lo, len, j0, js);
         else
             fused_tile_scalar<E, OP, kUnroll>(a, c, lo, len, j0, js);
