@@ -195,11 +195,11 @@ int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, voi
  * the library holds on every GPU it runs on until the process ends.  The
  * launch then takes at most as many waves as the array holds staging slots
  * (2,048 for bfloat16, 4,096 for 32-bit types), so every count up to the
- * comm's capacity runs.  Limit: when the buffers are not 16-byte aligned
- * row by row (or segments are shorter than 2 KiB) the call takes the scalar
- * path, which keeps one float32 per element in the array; there, with the
- * running value staged, count * 4 must not exceed 8 MiB, and a larger count
- * returns AR_ERR_INVALID_ARG without launching anything.  Nothing in the
+ * comm's capacity runs.  Small counts take the scalar path, which keeps one
+ * float32 per element in the array (they fit); a staged call whose count * 4
+ * exceeds 8 MiB takes the vector path when the buffers are 16-byte aligned
+ * row by row, and returns AR_ERR_INVALID_ARG without launching anything when
+ * they are not (or when segments are shorter than 2 KiB).  Nothing in the
  * array needs clearing (a call writes every slot before reading it).  All
  * calls on one GPU share its array: two of them in flight at once on one GPU
  * (on different streams, or from different comms) race and give wrong
