@@ -222,6 +222,73 @@ def test_scalar_vector_switch_boundary(env, launch, dtype, R):
         assert comm.check() == api.AR_SUCCESS
 
 
+def _ncu(env):
+    import torch
+    return torch.cuda.get_device_properties(env["dev"]).multi_processor_count
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [3, 8, 16])
+@pytest.mark.parametrize("channels", [1, 2])
+def test_fused_scalar_tiles_up_to_one_per_cu(env, dtype, R, channels):
+    """The fused form keeps its scalar path (tiles of 256 elements, one per
+    thread) while those tiles number at most one per CU, and takes the vector
+    path beyond: 16-byte aligned segments just under, at and just over the
+    switch (so both sides run), whole and ragged (a ragged count is not
+    aligned and stays scalar), out of place and in place, and reduce-scatter
+    then all-gather, bit-exact against the oracle."""
+    api, orc = env["api"], env["orc"]
+    ncu = _ncu(env)
+    per_seg = max(1, ncu // R) * 256 * channels  # elements per segment at the switch
+    for S in (per_seg - 8, per_seg, per_seg + 8):
+        for N in (R * S, R * S - 3):
+            x = rand_input(env, dtype, R, N, seed=17 * S + N + R)
+            comm = api.Comm(R, N, dtype, device=env["dev"], launch="fused", channels=channels)
+            strides = [api.ar_ring_channel_stride(comm.handle, k) for k in range(channels)]
+            ref = orc.ring_allreduce(x, dtype, strides=strides)
+            send = to_dev(env, x, dtype)
+            recv = poisoned(env, (R, N), dtype)
+            comm.allreduce(send, recv)
+            assert from_dev(env, recv, dtype).tobytes() == ref.tobytes(), (S, N)
+            comm.allreduce(send, send)  # in place: the hand-off goes through the workspace
+            assert from_dev(env, send, dtype).tobytes() == ref.tobytes(), (S, N, "in place")
+            assert comm.check() == api.AR_SUCCESS
+        comm = api.Comm(R, R * S, dtype, device=env["dev"], launch="fused", channels=channels)
+        strides = [api.ar_ring_channel_stride(comm.handle, k) for k in range(channels)]
+        x = rand_input(env, dtype, R, R * S, seed=5 * S + R)
+        shard = poisoned(env, (R, S), dtype)
+        comm.reduce_scatter(to_dev(env, x, dtype), shard)
+        rs = from_dev(env, shard, dtype)
+        assert rs.tobytes() == orc.ring_reduce_scatter(x, dtype, strides=strides).tobytes(), S
+        full = poisoned(env, (R, R * S), dtype)
+        comm.all_gather(shard, full)
+        assert from_dev(env, full, dtype).tobytes() == \
+            orc.ring_all_gather(rs, dtype, strides=strides).tobytes(), S
+        assert comm.check() == api.AR_SUCCESS
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+@pytest.mark.parametrize("R", [3, 8])
+def test_ll_one_line_per_thread_switch(env, dtype, R):
+    """The LL kernels take one line per thread while every workgroup has at
+    most one 256-line sub-block, four above: ring + LL and the tree at counts
+    on both sides of that switch, bit-exact against the oracle."""
+    orc = env["orc"]
+    ncu = _ncu(env)
+    # ring + LL: sub-blocks per segment up to the workgroups per rank (ncu / R)
+    s_ring = max(1, ncu // R) * 256
+    # tree: lines per tree half up to the workgroups per (tree, rank) (ncu / 2R)
+    h_tree = max(1, ncu // (2 * R)) * 256
+    for N in (R * s_ring, R * s_ring + R, R * (s_ring + 256) + 1):
+        x = rand_input(env, dtype, R, N, seed=N + R)
+        (y,) = run_allreduce(env, x, dtype, launch="ll")
+        assert y.tobytes() == orc.ring_allreduce(x, dtype).tobytes(), ("ring-LL", N)
+    for N in (2 * h_tree, 2 * h_tree + 2, 2 * (h_tree + 256) + 1):
+        x = rand_input(env, dtype, R, N, seed=3 * N + R)
+        (y,) = run_allreduce(env, x, dtype, "tree", "ll")
+        assert y.tobytes() == orc.tree_allreduce(x, dtype).tobytes(), ("tree", N)
+
+
 # ---------------------------------------------------------------- config 4: tree + LL
 
 def test_cfg4_tree_ll_sizes(env):
