@@ -478,22 +478,13 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
         grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(g, 1u << 20));
         e = launch_ring_fused_vec(c->dtype, a, grid, st);
     } else if (launch == AR_LAUNCH_FUSED) {
-        const uint64_t V = 1;
         // tiles of kBlock elements, one per thread: a tile's chain of 2(R-1)
-        // steps is latency-bound, and one slot per thread keeps each step to
-        // the fewest instructions
-        uint64_t tile = (uint64_t)kBlock;
-        const uint64_t seg_slots = (a.sub_len + V - 1) / V;
-        a.tile_slots = tile;
-        const uint64_t tiles = (seg_slots + tile - 1) / tile * (uint64_t)a.R;
-        // One workgroup per CU by default for all-reduce and all-gather: with
-        // more tiles in flight per XCD the rows of the copy chain are evicted
-        // from the XCD's L2 before the next step re-reads them (R = 8 fp32
-        // 64 MiB/rank: 0.22 ms at 256 workgroups, 0.24 at 512, 0.26 at
-        // 2048).  Reduce-scatter alone does better with 8 per CU (R = 16 bf16
-        // 25 MiB buckets: 173-178 against 182-184 us at 256).
-        const int64_t dflt = (a.op == kOpReduceScatter) ? 8 * (int64_t)c->ncu : (int64_t)c->ncu;
-        const int64_t want = c->grid > 0 ? c->grid : dflt;
+        // steps is latency-bound, and one element per thread keeps each step
+        // to the fewest instructions.  Up to 8 workgroups per CU, so that a
+        // large call on rows that are not 16-byte aligned still has enough
+        // chains in flight to stream.
+        const uint64_t tiles = (a.sub_len + kBlock - 1) / kBlock * (uint64_t)a.R;
+        const int64_t want = c->grid > 0 ? c->grid : 8 * (int64_t)c->ncu;
         grid = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)tiles, want, 1 << 20}));
         // On the scalar path (segments shorter than a cache line, so lines are
         // shared between the tiles of different segments) the tiles stay on one

@@ -73,8 +73,6 @@ struct RingArgs {
     uint64_t unit;    // pipelined ring: elements per flagged chunk (a multiple of the slot)
     uint64_t nunits;  // pipelined ring: chunks per segment, ceil(S / unit)
     uint64_t flag_stride; // pipelined ring: flags per segment in `flags`
-    uint64_t tile_slots; // fused form, scalar path: slots per tile (a multiple of kUnroll,
-                         //   <= kBlock * kUnroll)
     int xcd_pack;     // fused form, scalar path: only workgroups whose id is a multiple of
                       //   this take tiles (the others exit at once), so that they share one XCD
     uint64_t stage_wave; // fused form, vector path: accumulator elements of `part` per wave

@@ -114,62 +114,44 @@ __global__ __launch_bounds__(kBlock) void k_ring_placement(RingArgs a)
 
 // ---- fused: a tile runs every step ------------------------------------------
 
-// One reduce step of the scalar path (one element per slot; slot u of this
-// thread is element e[u], stored only if ok[u]).  The same structure as
+// One reduce step of the scalar path (one element per thread, element e).
+// The same structure as
 // fused_step: the hand-off is loaded after the previous step's store, the
 // next step's input is prefetched into `nxt`, and `own` was prefetched one
 // step earlier.  The empty asm takes the loaded hand-off values as operands,
 // so the compiler waits for them right there (leaving the prefetch in
 // flight) instead of moving each load into its store's branch and waiting
 // for everything outstanding.
-template <class E, int RED, int U, bool LOADX, bool PREFETCH, bool LAST>
-__device__ inline void scalar_step(typename E::A (&x)[U], const typename E::T (&own)[U],
-                                   typename E::T (&nxt)[U], typename E::A* acc,
-                                   typename E::T* fin, const typename E::T* next_row,
-                                   const uint64_t (&e)[U], const bool (&ok)[U], float R)
+template <class E, int RED, bool LOADX, bool PREFETCH, bool LAST>
+__device__ inline void scalar_step(typename E::A& x, const typename E::T& own,
+                                   typename E::T& nxt, typename E::A* acc, typename E::T* fin,
+                                   const typename E::T* next_row, uint64_t e, float R)
 {
     using A = typename E::A;
-    if constexpr (LOADX) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            x[u] = acc[e[u]];
+    if constexpr (LOADX)
+        x = acc[e];
+    if constexpr (PREFETCH)
+        nxt = next_row[e];
+    __asm__ __volatile__("" ::"v"(x));
+    A v = combine<E, RED>(x, E::widen(own));
+    if constexpr (LAST) {
+        v = finalize<E, RED>(v, R);
+        fin[e] = E::narrow(v);
+    } else {
+        acc[e] = v;
     }
-    if constexpr (PREFETCH) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            nxt[u] = next_row[e[u]];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        __asm__ __volatile__("" ::"v"(x[u]));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        A v = combine<E, RED>(x[u], E::widen(own[u]));
-        if constexpr (LAST)
-            v = finalize<E, RED>(v, R);
-        if (U == 1 || ok[u]) {  // with one slot per thread, every active thread's slot is in range
-            if constexpr (LAST)
-                fin[e[u]] = E::narrow(v);
-            else
-                acc[e[u]] = v;
-        }
-        x[u] = v;
-    }
+    x = v;
     step_boundary();
 }
 
-// The R-1 reduce steps of a tile on the scalar path (segments shorter than
-// one 128-byte line).  Each active thread has the U elements j0 + u*js of
-// segment c (U = 1 when the tile has at most one element per thread); one
-// past the end reads the thread's first element instead and stores nothing,
-// so every load is unconditional.  As on the vector path, the input of the
-// next step's rank is loaded before this step's store, into the other of two
-// register sets, so its HBM latency overlaps the hand-off instead of adding
-// to each step.  The rank whose row a step reads advances by m (no division:
+// The R-1 reduce steps of a tile on the scalar path: each active thread has
+// one element e of segment c.  As on the vector path, the input of the next
+// step's rank is loaded before this step's store, into the other of two
+// registers, so its HBM latency overlaps the hand-off instead of adding to
+// each step.  The rank whose row a step reads advances by m (no division:
 // each step is latency-bound, and its instruction count is part of it).
-template <class E, int RED, int U>
-__device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t len,
-                                           uint64_t j0, uint64_t js)
+template <class E, int RED>
+__device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t e)
 {
     using T = typename E::T;
     using A = typename E::A;
@@ -188,99 +170,60 @@ __device__ inline void fused_reduce_scalar(const RingArgs& a, int c, uint64_t lo
             rk -= R;
         return send + (uint64_t)rk * a.send_row;
     };
-    uint64_t e[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * js;
-        ok[u] = j < len;
-        e[u] = ok[u] ? j : j0;
-    }
-    A x[U];
-    T b0[U], b1[U];
-    const T* r1 = next_row();
-    const T* r2 = next_row();
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        x[u] = E::widen(r1[e[u]]);
-        b0[u] = r2[e[u]];
-    }
+    A x = E::widen(next_row()[e]);
+    T b0 = next_row()[e], b1;
     if (R == 2) {
-        scalar_step<E, RED, U, false, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, false, false, true>(x, b0, b1, acc, fin, nullptr, e, fr);
         return;
     }
     // R >= 3: steps 0 .. R-3 hand off, step R-2 is the owner's
-    scalar_step<E, RED, U, false, true, false>(x, b0, b1, acc, fin, next_row(), e, ok, fr);
+    scalar_step<E, RED, false, true, false>(x, b0, b1, acc, fin, next_row(), e, fr);
     int s = 1;  // the next step; its input is in b1
     for (; s + 1 <= R - 3; s += 2) {
-        scalar_step<E, RED, U, true, true, false>(x, b1, b0, acc, fin, next_row(), e, ok, fr);
-        scalar_step<E, RED, U, true, true, false>(x, b0, b1, acc, fin, next_row(), e, ok, fr);
+        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, next_row(), e, fr);
+        scalar_step<E, RED, true, true, false>(x, b0, b1, acc, fin, next_row(), e, fr);
     }
     if (s == R - 3) {
-        scalar_step<E, RED, U, true, true, false>(x, b1, b0, acc, fin, next_row(), e, ok, fr);
-        scalar_step<E, RED, U, true, false, true>(x, b0, b1, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, true, true, false>(x, b1, b0, acc, fin, next_row(), e, fr);
+        scalar_step<E, RED, true, false, true>(x, b0, b1, acc, fin, nullptr, e, fr);
     } else {
-        scalar_step<E, RED, U, true, false, true>(x, b1, b0, acc, fin, nullptr, e, ok, fr);
+        scalar_step<E, RED, true, false, true>(x, b1, b0, acc, fin, nullptr, e, fr);
     }
 }
 
-template <class E, int U>
-__device__ inline void fused_reduce_scalar_op(const RingArgs& a, int c, uint64_t lo, uint64_t len,
-                                              uint64_t j0, uint64_t js)
+template <class E>
+__device__ inline void fused_reduce_scalar_op(const RingArgs& a, int c, uint64_t lo, uint64_t e)
 {
     switch (a.redop) {
     case AR_MAX:
-        fused_reduce_scalar<E, AR_MAX, U>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_MAX>(a, c, lo, e);
         break;
     case AR_MIN:
-        fused_reduce_scalar<E, AR_MIN, U>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_MIN>(a, c, lo, e);
         break;
     case AR_AVG:
-        fused_reduce_scalar<E, AR_AVG, U>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_AVG>(a, c, lo, e);
         break;
     default:
-        fused_reduce_scalar<E, AR_SUM, U>(a, c, lo, len, j0, js);
+        fused_reduce_scalar<E, AR_SUM>(a, c, lo, e);
         break;
     }
 }
 
-// The copy steps of a tile on the scalar path: U elements per thread (the
-// same ones the reduce steps took), loads first and unconditional, then the
-// stores.
-template <class E, int U>
-__device__ inline void copy_scalar(const typename E::T* __restrict__ src,
-                                   typename E::T* __restrict__ dst, uint64_t len, uint64_t j0,
-                                   uint64_t js)
-{
-    typename E::T r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * js;
-        r[u] = src[j < len ? j : j0];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint64_t j = j0 + (uint64_t)u * js;
-        if (U == 1 || j < len)
-            dst[j] = r[u];
-    }
-}
-
-// One tile's whole chain on the scalar path with U slots per thread.
-template <class E, int OP, int U>
-__device__ inline void fused_tile_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t len,
-                                         uint64_t j0, uint64_t js)
+// One tile's whole chain on the scalar path: element e of segment c.
+template <class E, int OP>
+__device__ inline void fused_tile_scalar(const RingArgs& a, int c, uint64_t lo, uint64_t e)
 {
     using T = typename E::T;
     T* out = static_cast<T*>(a.out);
     const int R = a.R, m = a.m;
     if constexpr (OP != kOpAllGather)
-        fused_reduce_scalar_op<E, U>(a, c, lo, len, j0, js);
+        fused_reduce_scalar_op<E>(a, c, lo, e);
     if constexpr (OP != kOpReduceScatter) {
         if constexpr (OP == kOpAllGather) {
             const T* src = static_cast<const T*>(a.send) + (uint64_t)c * a.send_row +
                            (lo - (uint64_t)c * a.S);
-            copy_scalar<E, U>(src, out + (uint64_t)c * a.out_row + lo, len, j0, js);
+            out[(uint64_t)c * a.out_row + lo + e] = src[e];
             step_boundary();
         }
         int p = c;
@@ -288,53 +231,39 @@ __device__ inline void fused_tile_scalar(const RingArgs& a, int c, uint64_t lo, 
             int q = p + m;
             if (q >= R)
                 q -= R;
-            copy_scalar<E, U>(out + (uint64_t)p * a.out_row + lo, out + (uint64_t)q * a.out_row + lo,
-                              len, j0, js);
+            out[(uint64_t)q * a.out_row + lo + e] = out[(uint64_t)p * a.out_row + lo + e];
             step_boundary();
             p = q;
         }
     }
 }
 
-// Tile t of a fused launch on the scalar path (segments shorter than
-// AR_SCALAR_SEG_BYTES, one element per slot): segment c, its range [lo, lo +
-// len) of a full row, and this thread's first element j0 (elements j0 + u*js).
-// False for an empty tile of a short trailing segment (uniform per
-// workgroup).  Tiles are numbered segment by segment.  A tile the segment
-// fills only in part puts one element on each thread (up to kBlock threads),
-// so that a wave's elements are adjacent and each step stores them with one
-// instruction (four elements of one thread in one cache line took four
-// stores: 8.5 against 6 us a call).
-__device__ inline bool scalar_tile(const RingArgs& a, uint64_t t, int* c, uint64_t* lo,
-                                   uint64_t* len, uint64_t* j0, uint64_t* js, bool* active)
+// Tile t of a fused launch on the scalar path: kBlock elements of one
+// segment, one per thread (tiles are numbered segment by segment).  Sets the
+// segment c, its range start lo in a full row, and this thread's element e
+// within the segment; false when the thread has no element (past the end of
+// a part-filled tile, or an empty tile of a short trailing segment).
+__device__ inline bool scalar_tile(const RingArgs& a, uint64_t tiles_per_seg, uint64_t t, int* c,
+                                   uint64_t* lo, uint64_t* e)
 {
-    const uint64_t tile_slots = a.tile_slots;
-    const uint64_t tiles_per_seg = (a.sub_len + tile_slots - 1) / tile_slots;
     *c = (int)(t / tiles_per_seg);
     const uint64_t k = t % tiles_per_seg;
     uint64_t hi;
     seg_range(a.N, a.S, *c, a.sub_lo, a.sub_len, lo, &hi);
-    *len = hi - *lo;
-    const uint64_t first = k * tile_slots;
-    const uint64_t n = *len > first ? *len - first : 0;
-    // a tile of at most kBlock slots has one per thread, a larger one kUnroll
-    uint64_t stride = tile_slots <= (uint64_t)kBlock ? tile_slots : tile_slots / kUnroll;
-    if (n < tile_slots)
-        stride = n < (uint64_t)kBlock ? n : (uint64_t)kBlock;
-    *js = stride;
-    *active = threadIdx.x < stride;
-    *j0 = first + threadIdx.x;
-    return first < *len;
+    *e = k * (uint64_t)kBlock + threadIdx.x;
+    return *e < hi - *lo;
 }
 
-// The fused form on the scalar path: a workgroup takes a tile of a segment
-// through all 2(R-1) steps (the vector path is k_ring_fused_vec).
+// The fused form on the scalar path (the vector path is k_ring_fused_vec): a
+// workgroup takes a tile of kBlock elements, one per thread, through all
+// 2(R-1) steps.  Each step of a tile's chain is latency-bound (a store, then
+// the next step's load of the same address), so one element per thread
+// keeps the step to the fewest instructions.
 template <int DT, int OP>
 __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
 {
     using E = Elem<DT>;
-    const uint64_t tile_slots = a.tile_slots;
-    const uint64_t tiles_per_seg = (a.sub_len + tile_slots - 1) / tile_slots;
+    const uint64_t tiles_per_seg = (a.sub_len + kBlock - 1) / kBlock;
     const uint64_t ntiles = tiles_per_seg * (uint64_t)a.R;
 
     // with xcd_pack = n only every n-th workgroup works: workgroups are
@@ -345,21 +274,9 @@ __global__ __launch_bounds__(kBlock) void k_ring_fused(RingArgs a)
     const uint64_t wg = blockIdx.x / pack, nwg = gridDim.x / pack;
     for (uint64_t t = wg; t < ntiles; t += nwg) {
         int c;
-        uint64_t lo, len, j0, js;
-        bool active;
-        if (!scalar_tile(a, t, &c, &lo, &len, &j0, &js, &active))
-            continue;  // empty tile of a short trailing segment (uniform per workgroup)
-        if (!active)
-            continue;  // this thread has no element in a part-filled tile
-
-        // a tile whose stride covers all its elements (one per thread)
-        // takes the one-slot chain
-        const uint64_t first = j0 - threadIdx.x;
-        const uint64_t nt = len - first < tile_slots ? len - first : tile_slots;
-        if (js >= nt)
-            fused_tile_scalar<E, OP, 1>(a, c, lo, len, j0, js);
-        else
-            fused_tile_scalar<E, OP, kUnroll>(a, c, lo, len, j0, js);
+        uint64_t lo, e;
+        if (scalar_tile(a, tiles_per_seg, t, &c, &lo, &e))
+            fused_tile_scalar<E, OP>(a, c, lo, e);
     }
 }
 
