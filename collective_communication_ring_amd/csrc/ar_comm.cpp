@@ -259,14 +259,12 @@ int resolve_algo(const ar_comm* c, size_t count)
 }
 
 // Do the 16-byte vector kernels apply?  Every row start and every segment
-// start must be 16-byte aligned in both T and accumulator units.  Segments
-// shorter than one 128-byte cache line take the scalar path: measured faster
-// there (R = 8 fp32, 128-512 B per rank: 8.7 against 9.5 us fused).
-// Segments shorter than this take the scalar path (one element per lane)
-// in every ring form.  Its tiles put one element on each lane and, in the
-// fused form, stay on one XCD, so a short segment's few loads and stores per
-// step are single instructions; 16-byte slots only pay once a segment has
-// enough of them (R = 8 fp32, fused, graph-replayed: 1-8 KiB per rank 6.0 /
+// start must be 16-byte aligned in both T and accumulator units, and a
+// segment must be at least AR_SCALAR_SEG_BYTES long.  Shorter segments take
+// the scalar path (one element per lane) in every ring form: a short
+// segment's few loads and stores per step are then single instructions, and
+// 16-byte slots only pay once a segment has enough of them (R = 8 fp32,
+// fused, graph-replayed: 1-8 KiB per rank 6.0 /
 // 6.1 / 5.8 / 5.9 us with the vector path from 128-byte segments, 5.3 / 5.2
 // / 5.3 / 5.5 us with this threshold; the step form 30 -> 27.5 us there; a
 // 8 KiB threshold was slower at 32 KiB per rank and at R = 4, 16 KiB).

@@ -474,6 +474,52 @@ def test_unaligned_views_use_the_scalar_path(env):
         assert from_dev(env, recv, "float32").tobytes() == orc.ring_allreduce(x).tobytes()
 
 
+def _offset_view(env, shape, dtype, off):
+    """A contiguous [rows, cols] view starting `off` elements into an
+    allocation of 0xFF bytes, so that its rows are not 16-byte aligned."""
+    torch = env["torch"]
+    tdt = {"int32": torch.int32, "float32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    base = torch.empty(shape[0] * shape[1] + off, dtype=tdt, device=env["dev"])
+    base.view(torch.uint8).fill_(0xFF)
+    return base[off:].view(*shape)
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
+def test_unaligned_views_with_more_tiles_than_the_grid(env, dtype):
+    """Rows that are not 16-byte aligned take the fused form's scalar path at
+    any size.  Its default grid is 8 workgroups per CU; here the segments hold
+    more 256-element tiles than that, so each workgroup loops over several,
+    with a ragged last segment; then a small call with a grid of 3.
+    All-reduce, reduce-scatter and all-gather, bit-exact."""
+    api, orc = env["api"], env["orc"]
+    R = 8
+    S = 256 * _ncu(env) + 300  # ceil(S / 256) * R tiles > 8 per CU
+    for N, grid in ((R * S - 3, None), (R * 700 - 5, 3)):
+        opts = {} if grid is None else {"grid": grid}
+        comm = api.Comm(R, N, dtype, device=env["dev"], launch="fused", **opts)
+        x = rand_input(env, dtype, R, N, seed=N)
+        send = _offset_view(env, (R, N), dtype, 1)
+        send.copy_(to_dev(env, x, dtype))
+        recv = _offset_view(env, (R, N), dtype, 3)
+        comm.allreduce(send, recv)
+        assert from_dev(env, recv, dtype).tobytes() == orc.ring_allreduce(x, dtype).tobytes(), \
+            (N, grid, "ar")
+        n = N // R
+        xs = np.ascontiguousarray(x[:, :R * n])
+        rsend = _offset_view(env, (R, R * n), dtype, 1)
+        rsend.copy_(to_dev(env, xs, dtype))
+        shard = _offset_view(env, (R, n), dtype, 3)
+        comm.reduce_scatter(rsend, shard)
+        rs = orc.ring_reduce_scatter(xs, dtype)
+        assert from_dev(env, shard, dtype).tobytes() == rs.tobytes(), (N, grid, "rs")
+        full = _offset_view(env, (R, R * n), dtype, 1)
+        comm.all_gather(shard, full)
+        assert from_dev(env, full, dtype).tobytes() == orc.ring_all_gather(rs, dtype).tobytes(), \
+            (N, grid, "ag")
+        assert comm.check() == api.AR_SUCCESS
+        comm.close()
+
+
 def test_argument_errors(env):
     torch, api = env["torch"], env["api"]
     comm = api.Comm(4, 64, "float32", device=env["dev"])
