@@ -17,15 +17,15 @@ hand-offs stay in the XCD's L2).  One step = one all-reduce of the whole
   hop_rate_GBps = 5 (R-1) N s / time: every hop's load and store counted,
            most of them served by L2 in the fused form (not an HBM rate).
 
-The same line carries, unless --no-extras: the config 3 sweep (8 B .. 1 GiB
-per rank) with its alpha-beta fit; config 4 (tree + LL against the ring
-forms, 8 B .. 256 KiB) with the crossovers and AR_AUTO's choices; a few
-config 5 gradient buckets (R = 16 bf16 reduce-scatter, all-gather, checked
-against the oracle); the pipelined ring (simple protocol, 512 KiB chunks)
+The same line carries, unless --no-extras: the message-size sweep (R = 8
+fp32, 8 B .. 1 GiB per rank) with its alpha-beta fit; tree + LL against the
+ring forms (R = 8 fp32, 8 B .. 256 KiB) with the crossovers and AR_AUTO's
+choices; a few 25 MiB gradient buckets (R = 16 bf16 reduce-scatter,
+all-gather, all-reduce, checked against the oracle); the pipelined ring (simple protocol, 512 KiB chunks)
 on the headline workload; and a 512 MiB copy as the streaming ceiling.
 cpu_baseline times the oracle on one thread and on all host cores.
 
-Other modes (--mode): config1 (R = 4 int32, 4096 per rank, every form), matrix
+Other modes (--mode): r4-int32 (R = 4 int32, 4096 per rank, every form), matrix
 (fused, 64 MiB per rank, R = 2..16, every dtype),
 sweep (8 B .. 1 GiB per rank, alpha-beta fit), tree-vs-ring (8 B .. 256 KiB),
 buckets (R = 16 bf16 reduce-scatter then all-gather, 40 x 25 MiB), stream
@@ -121,7 +121,7 @@ def time_graph(fn, calls, torch, reps=1, warmup=5):
     """`warmup` eager calls, then `calls` back-to-back calls captured in one
     HIP graph; one untimed replay, then `reps` timed replays.  Returns ms per
     call.  Removes the host's enqueue pacing from small-message timings
-    (config 3: 5 warm-up, then 20 timed calls)."""
+    (the sweep: 5 warm-up, then 20 timed calls)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -409,7 +409,7 @@ def timed_point(fn, torch, eager):
 
 
 def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused", eager=False):
-    """Config 3: R = 8 fp32 N(0,1), 8 B .. 1 GiB per rank (28 sizes), 5
+    """The message-size sweep: R = 8 fp32 N(0,1), 8 B .. 1 GiB per rank (28 sizes), 5
     warm-up then 20 timed calls each (one graph replay), fit T = a + b n."""
     R, s = 8, 4
     dev = torch.device("cuda:0")
@@ -464,7 +464,7 @@ TVR_VARIANTS = [("tree-ll", dict(algo="tree", proto="ll")),
 
 
 def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eager=False):
-    """Config 4: R = 8 fp32 U[-1,1), 8 B .. 256 KiB per rank (16 sizes): the
+    """Tree against ring: R = 8 fp32 U[-1,1), 8 B .. 256 KiB per rank (16 sizes): the
     double binary tree with LL against every ring form (5 warm-up + 20 timed
     calls per size, one graph replay); an alpha-beta fit per variant, the
     crossover of the tree with each ring form (measured and from the fits),
@@ -559,7 +559,7 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
 
 
 def buckets_few(torch, api, measure, inputs, np, nb=4):
-    """Config 5 on its first `nb` buckets: R = 16 bf16 N(0,0.02), 13,107,200
+    """The gradient buckets, the first `nb`: R = 16 bf16 N(0,0.02), 13,107,200
     elements (25 MiB) per rank each; reduce-scatter, then all-gather, then
     all-reduce of every bucket in turn, timed per bucket (5 warm-up passes
     over the buckets, then 20 timed).  Every bucket is checked: the
@@ -579,20 +579,33 @@ def buckets_few(torch, api, measure, inputs, np, nb=4):
     def each(fn):
         return lambda: [fn(b) for b in range(nb)]
 
-    out = {}
-    for name, fn, hbm in (
+    out, t_of = {}, {}
+    for name, fn, hbm, hop in (
             ("reduce_scatter", each(lambda b: comm.reduce_scatter(xs[b], shards[b])),
-             measure.reduce_scatter_hbm_bytes(R, N, s)),
+             measure.reduce_scatter_hbm_bytes(R, N, s), measure.reduce_scatter_alg_bytes(R, N, s)),
             ("all_gather", each(lambda b: comm.all_gather(shards[b], fulls[b])),
-             measure.all_gather_hbm_bytes(R, N, s)),
+             measure.all_gather_hbm_bytes(R, N, s), measure.all_gather_alg_bytes(R, N, s)),
             ("allreduce", each(lambda b: comm.allreduce(xs[b], ars[b])),
-             measure.allreduce_hbm_bytes(R, N, s))):
+             measure.allreduce_hbm_bytes(R, N, s), measure.allreduce_alg_bytes(R, N, s, acc=4))):
         _, total_ms, _ = time_calls(fn, 20, 5, torch)
-        t = total_ms / 20 / nb / 1e3
+        t = t_of[name] = total_ms / 20 / nb / 1e3
+        algbw = N * s / t / 1e9
         f = measure.busbw_factor("allreduce" if name == "allreduce" else "rs", R)
-        out[name] = dict(us_per_bucket=round(t * 1e6, 2), busbw_GBps=round(N * s / t / 1e9 * f, 1),
+        # counter bytes of the same kernel (fused form), while its sources match
+        meas = measured_traffic("bucket_bf16_r16_25MiB_%s_fused" % name)
+        out[name] = dict(us_per_bucket=round(t * 1e6, 2), algbw_GBps=round(algbw, 1),
+                         busbw_GBps=round(algbw * f, 1),
                          hbm_GBps=round(hbm / t / 1e9, 1),
-                         hbm_frac_of_peak=round(hbm / t / 1e9 / PEAK_HBM_GBPS, 4))
+                         hbm_frac_of_peak=round(hbm / t / 1e9 / PEAK_HBM_GBPS, 4),
+                         hbm_measured_GBps=round(meas / t / 1e9, 1) if meas else None,
+                         hbm_measured_frac_of_peak=(round(meas / t / 1e9 / PEAK_HBM_GBPS, 4)
+                                                    if meas else None),
+                         hop_rate_GBps=round(hop / t / 1e9, 1))
+    # the pair the buckets run: reduce-scatter then all-gather, an all-reduce
+    t2 = t_of["reduce_scatter"] + t_of["all_gather"]
+    out["rs_then_ag"] = dict(us_per_bucket=round(t2 * 1e6, 2), algbw_GBps=round(N * s / t2 / 1e9, 1),
+                             busbw_GBps=round(N * s / t2 / 1e9 *
+                                              measure.busbw_factor("allreduce", R), 1))
     ok = comm.check() == api.AR_SUCCESS
     threads = cpu_info()["threads"]
     bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -612,7 +625,7 @@ def buckets_few(torch, api, measure, inputs, np, nb=4):
 
 
 def mode_sweep(args):
-    """Config 3 alone: ring all-reduce, R = 8, fp32, 8 B .. --max-bytes per
+    """The message-size sweep alone: ring all-reduce, R = 8, fp32, 8 B .. --max-bytes per
     rank in powers of two, 5 warm-up + 20 timed calls each; alpha-beta fit."""
     import numpy as np
     import torch
@@ -647,7 +660,7 @@ def ll_hop_latency_us(torch, iters=20000):
 
 
 def mode_tree_vs_ring(args):
-    """Config 4 alone (up to --tvr-max-bytes per rank): tree + LL against every
+    """Tree against ring alone (up to --tvr-max-bytes per rank): tree + LL against every
     ring form, fits, crossovers and AR_AUTO's choices."""
     import numpy as np
     import torch
@@ -658,7 +671,7 @@ def mode_tree_vs_ring(args):
 
 
 def mode_buckets(args):
-    """Config 5: R = 16 bf16 N(0, 0.02), 40 buckets x 13,107,200 elements per
+    """The gradient buckets: R = 16 bf16 N(0, 0.02), 40 buckets x 13,107,200 elements per
     rank, reduce-scatter then all-gather per bucket (and all-reduce)."""
     import torch
     from collective_communication_ring_amd import api, inputs, measure
@@ -847,7 +860,7 @@ def mode_counters(args):
     known size (the calibration) and the headline's row pattern without hops
     (ar_stream_rows), then 3 all-reduces of the headline workload
     in each launch form, then 3 small tree-LL all-reduces, then 3 reduce-
-    scatters, all-gathers and all-reduces of one config 5 bucket."""
+    scatters, all-gathers and all-reduces of one 25 MiB gradient bucket."""
     import torch
     from collective_communication_ring_amd import api, inputs
     dev = torch.device("cuda:0")
@@ -878,7 +891,7 @@ def mode_counters(args):
         comm.allreduce(small, out)
     torch.cuda.synchronize()
     del send, recv, small, out
-    # one gradient bucket of config 5: reduce-scatter, all-gather, all-reduce
+    # one 25 MiB gradient bucket (R = 16 bf16): reduce-scatter, all-gather, all-reduce
     w = inputs.WORKLOADS["buckets_bf16_r16"]
     Rb, Nb = w["R"], w["count"]
     xb = inputs.device_bucket_bf16(Rb, Nb, w["seed"], 0, dev)
@@ -897,8 +910,8 @@ def mode_counters(args):
     return 0
 
 
-def mode_config1(args):
-    """Config 1: ring all-reduce (sum), R = 4, int32, 4096 elements per rank,
+def mode_r4_int32(args):
+    """Ring all-reduce (sum), R = 4, int32, 4096 elements per rank,
     chunk = count / R; time per call (graph-replayed) in every form, each
     result checked bit for bit against the oracle and the int64 sum."""
     import numpy as np
@@ -921,9 +934,9 @@ def mode_config1(args):
         ok = comm.check() == api.AR_SUCCESS and (got == exact[None, :]).all() and (
             name == "tree-ll" or got.tobytes() == ref.tobytes())
         res[name] = dict(t_us=round(t_us, 3), exact=bool(ok))
-        log("config 1 %-10s %8.2f us  exact=%s" % (name, t_us, ok))
+        log("r4-int32 %-10s %8.2f us  exact=%s" % (name, t_us, ok))
         comm.close()
-    print(json.dumps(dict(mode="config1", R=R, count_per_rank=N, dtype="int32", results=res,
+    print(json.dumps(dict(mode="r4-int32", R=R, count_per_rank=N, dtype="int32", results=res,
                           cpu_baseline=dict(kind="oracle", cores=1, t_us=t_or * 1e6,
                                             sample="%d calls" % n_or))), flush=True)
     return 0 if all(r["exact"] for r in res.values()) else 1
@@ -1021,11 +1034,11 @@ def main():
                     help="ring launch form; 'll' = the ring with the LL protocol")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
-                    choices=["headline", "config1", "matrix", "sweep", "tree-vs-ring",
+                    choices=["headline", "r4-int32", "matrix", "sweep", "tree-vs-ring",
                              "buckets", "stream", "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--tvr-max-bytes", type=int, default=256 * 1024,
-                    help="tree-vs-ring: largest per-rank size (config 4 stops at 256 KiB)")
+                    help="tree-vs-ring: largest per-rank size (the default stops at 256 KiB)")
     ap.add_argument("--buckets", type=int, default=0)
     ap.add_argument("--out", default=None)
     ap.add_argument("--grids", default="256,512,768,1024,1280,1536,1792,2048")
@@ -1038,7 +1051,7 @@ def main():
                     help="headline: only the headline workload (no sweep, tree-vs-ring, buckets, "
                          "pipelined ring or copy ceiling)")
     ap.add_argument("--extra-buckets", type=int, default=4,
-                    help="headline: config 5 buckets timed and checked in the extras")
+                    help="headline: 25 MiB gradient buckets timed and checked in the extras")
     ap.add_argument("--channels", type=int, default=1,
                     help="ring channels (each its own ring stride over a sub-range of "
                          "every segment)")
@@ -1051,7 +1064,7 @@ def main():
               "MI355X's HBM, so --gpus must be 1 (got --gpus %d, WORLD_SIZE %d)."
               % (args.gpus, world), file=sys.stderr)
         return 2
-    fn = {"headline": headline, "config1": mode_config1, "matrix": mode_matrix,
+    fn = {"headline": headline, "r4-int32": mode_r4_int32, "matrix": mode_matrix,
           "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
           "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
           "tune": mode_tune, "overlap": mode_overlap}[args.mode]

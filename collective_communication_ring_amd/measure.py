@@ -26,9 +26,10 @@ latency floor, beta the reciprocal bandwidth).
 import numpy as np
 
 
-def allreduce_alg_bytes(R, N, s):
-    """Hop bytes of one ring all-reduce."""
-    return 5 * (R - 1) * N * s
+def allreduce_alg_bytes(R, N, s, acc=None):
+    """Hop bytes of one ring all-reduce: the reduce-scatter's, then R-1 copy
+    steps (5 (R-1) N s when the partials are in T itself, acc = s)."""
+    return reduce_scatter_alg_bytes(R, N, s, s if acc is None else acc) + 2 * (R - 1) * N * s
 
 
 def allreduce_hbm_bytes(R, N, s):

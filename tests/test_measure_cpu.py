@@ -34,6 +34,13 @@ def test_byte_counts():
     # float32 reduce-scatter: every step reads 8 and writes 4 bytes
     assert measure.reduce_scatter_alg_bytes(8, 1024, 4) == 7 * 12 * 1024
     assert measure.reduce_scatter_alg_bytes(2, 1024, 4) == 12 * 1024
+    # bf16 all-reduce with float32 partials: the reduce-scatter's (10R - 14) N,
+    # then R - 1 copy steps of 2 bf16 each; with partials in T (acc = s) the
+    # same count is 5 (R - 1) N s at every R
+    assert measure.allreduce_alg_bytes(16, N, 2, acc=4) == (10 * 16 - 14) * N + 4 * 15 * N
+    for R in (2, 3, 8, 16):
+        assert measure.allreduce_alg_bytes(R, 1000, 2) == 5 * (R - 1) * 1000 * 2
+        assert measure.allreduce_alg_bytes(R, 1000, 4, acc=4) == 5 * (R - 1) * 1000 * 4
     assert abs(measure.busbw_factor("allreduce", 8) - 1.75) < 1e-12
     assert abs(measure.busbw_factor("rs", 16) - 15 / 16) < 1e-12
 

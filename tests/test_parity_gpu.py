@@ -95,10 +95,10 @@ def run_allreduce(env, x, dtype, algo="ring", proto="simple", launch=None, reps=
     return outs
 
 
-# ---------------------------------------------------------------- config 1
+# ---------------------------------------------------------------- R = 4 int32, 4096 per rank
 
 @pytest.mark.parametrize("launch", LAUNCHES)
-def test_cfg1_ring_int32_r4(env, launch):
+def test_ring_int32_r4_4096(env, launch):
     x = env["inputs"].host_inputs("ring_int32_r4")
     R, N = x.shape
     (y,) = run_allreduce(env, x, "int32", launch=launch, chunk_bytes=(N // R) * 4)
@@ -107,10 +107,10 @@ def test_cfg1_ring_int32_r4(env, launch):
     assert (y == want[None, :]).all()
 
 
-# ---------------------------------------------------------------- config 2
+# ---------------------------------------------------------------- R = 8 fp32, 64 MiB per rank
 
 @pytest.mark.parametrize("launch", LAUNCHES)
-def test_cfg2_ring_f32_r8_64MiB(env, launch):
+def test_ring_f32_r8_64MiB(env, launch):
     x = env["inputs"].host_inputs("ring_f32_r8_64MiB")
     (y,) = run_allreduce(env, x, "float32", launch=launch, chunk_bytes=512 * 1024)
     ref = env["orc"].ring_allreduce(x)
@@ -289,9 +289,9 @@ def test_ll_one_line_per_thread_switch(env, dtype, R):
         assert y.tobytes() == orc.tree_allreduce(x, dtype).tobytes(), ("tree", N)
 
 
-# ---------------------------------------------------------------- config 4: tree + LL
+# ---------------------------------------------------------------- tree + LL, R = 8, 8 B .. 256 KiB per rank
 
-def test_cfg4_tree_ll_sizes(env):
+def test_tree_ll_r8_8B_to_256KiB(env):
     orc, inputs = env["orc"], env["inputs"]
     for nbytes in [2 ** k for k in range(3, 19)]:
         N = nbytes // 4
@@ -414,9 +414,9 @@ def test_fused_staging_with_any_grid(env, grid):
     assert y.tobytes() == orc.ring_allreduce(x, "bf16").tobytes()
 
 
-# ---------------------------------------------------------------- config 5
+# ---------------------------------------------------------------- gradient buckets, R = 16 bf16, 40 x 25 MiB
 
-def test_cfg5_gradient_buckets_bf16_r16(env):
+def test_gradient_buckets_bf16_r16_40x25MiB(env):
     """40 buckets x 13,107,200 bf16 per rank, R = 16: reduce-scatter then
     all-gather equals all-reduce bit for bit on every bucket.  Every bucket is
     also compared with the oracle: 64 sampled elements of each segment (the
@@ -593,7 +593,7 @@ def test_graph_replay_matches_eager(env, variant):
     assert comm.check() == api.AR_SUCCESS
 
 
-# ---------------------------------------------------------------- config 3 at full size
+# ---------------------------------------------------------------- the sweep's largest size, 1 GiB per rank
 
 def _segment_samples(rng, N, R, m):
     """m element indices from each ring segment of an N-element row, in
@@ -611,7 +611,7 @@ def _segment_samples(rng, N, R, m):
 
 
 @pytest.mark.parametrize("launch", ["auto", "step", "pipelined", "ll"])
-def test_cfg3_largest_size_sampled(env, launch):
+def test_ring_f32_r8_1GiB_sampled(env, launch):
     """R = 8, fp32, 1 GiB per rank (the sweep's largest size) in the launch form
     the benchmark times: sampled outputs against the oracle.  The ring's fold
     for an element depends only on its segment, so m samples from each

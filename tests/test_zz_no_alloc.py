@@ -42,7 +42,7 @@ def _bits(env, t):
 
 
 @pytest.mark.parametrize("dtype,R,sizes,in_place", [
-    ("bf16", 16, (13_107_200, 1_048_576 + 16 * 8), False),  # a config 5 bucket, then a smaller one
+    ("bf16", 16, (13_107_200, 1_048_576 + 16 * 8), False),  # a 25 MiB gradient bucket, then a smaller one
     ("float32", 8, (16_777_216, 65_536 * 8 + 8), True),     # the headline, in place
     ("float32", 8, (16_777_216, 4096 * 8), False),
     ("int32", 4, (1 << 20, 4096), False),
