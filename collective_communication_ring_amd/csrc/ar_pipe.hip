@@ -118,39 +118,57 @@ __device__ inline void cstore_t(rsrc_t r, uint32_t elem, const typename E::A (&v
     }
 }
 
+// A chunk's accumulators (4 bytes per element): slot j of V elements keeps
+// its V/4 16-byte halves in runs of their own, half h of slot j at
+// (h * nfull + j) * 16 bytes for the chunk's nfull whole slots, so one
+// 16-byte-per-lane instruction covers whole lines.  For 32-bit T (V = 4)
+// and on the scalar path (V = 1) this is plain element order.  The ragged
+// end's elements follow at 4 bytes each, in element order.  Producer and
+// consumer of a chunk have the same length, so they agree on the layout.
 template <class E, int V, int POL>
-__device__ inline void cload_a(rsrc_t r, uint32_t elem, typename E::A (&o)[V])
+__device__ inline void cload_a(rsrc_t r, uint32_t j, uint32_t nfull, typename E::A (&o)[V])
 {
-    const uint32_t off = elem * 4u;
     if constexpr (V == 1) {
-        o[0] = E::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL));
-    } else {
+        o[0] = E::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, j * 4u, 0, POL));
+        return;
+    }
 #pragma unroll
-        for (int h = 0; h < V / 4; ++h) {
-            u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16u * h, 0, POL);
+    for (int h = 0; h < V / 4; ++h) {
+        u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)h * nfull + j) * 16u, 0, POL);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[4 * h + i] = E::from_bits(w[i]);
-        }
+        for (int i = 0; i < 4; ++i)
+            o[4 * h + i] = E::from_bits(w[i]);
     }
 }
 
 template <class E, int V, int POL>
-__device__ inline void cstore_a(rsrc_t r, uint32_t elem, const typename E::A (&v)[V])
+__device__ inline void cstore_a(rsrc_t r, uint32_t j, uint32_t nfull, const typename E::A (&v)[V])
 {
-    const uint32_t off = elem * 4u;
     if constexpr (V == 1) {
-        __builtin_amdgcn_raw_buffer_store_b32(E::to_bits(v[0]), r, off, 0, POL);
-    } else {
-#pragma unroll
-        for (int h = 0; h < V / 4; ++h) {
-            u32x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[i] = E::to_bits(v[4 * h + i]);
-            __builtin_amdgcn_raw_buffer_store_b128(w, r, off + 16u * h, 0, POL);
-        }
+        __builtin_amdgcn_raw_buffer_store_b32(E::to_bits(v[0]), r, j * 4u, 0, POL);
+        return;
     }
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = E::to_bits(v[4 * h + i]);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, ((uint32_t)h * nfull + j) * 16u, 0, POL);
+    }
+}
+
+// One accumulator at element e (the scalar path and the ragged end).
+template <class E, int POL>
+__device__ inline typename E::A cload_a1(rsrc_t r, uint32_t e)
+{
+    return E::from_bits(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4u, 0, POL));
+}
+
+template <class E, int POL>
+__device__ inline void cstore_a1(rsrc_t r, uint32_t e, typename E::A v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(E::to_bits(v), r, e * 4u, 0, POL);
 }
 
 // Reduce one chunk of ulen elements: dst = prev + own.  prev is the
@@ -172,7 +190,7 @@ __device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_
                 if constexpr (FIRST)
                     cload_t<E, V, PREV_POL>(prev, j * V, x[u]);
                 else
-                    cload_a<E, V, PREV_POL>(prev, j * V, x[u]);
+                    cload_a<E, V, PREV_POL>(prev, j, nfull, x[u]);
                 cload_t<E, V, kPlain>(own, j * V, y[u]);
             }
         }
@@ -189,7 +207,7 @@ __device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_
                 if constexpr (LAST)
                     cstore_t<E, V, kCoherent>(dst, j * V, x[u]);
                 else
-                    cstore_a<E, V, kCoherent>(dst, j * V, x[u]);
+                    cstore_a<E, V, kCoherent>(dst, j, nfull, x[u]);
             }
         }
     }
@@ -199,14 +217,14 @@ __device__ inline void chunk_reduce(rsrc_t prev, rsrc_t own, rsrc_t dst, uint64_
         if constexpr (FIRST)
             cload_t<E, 1, PREV_POL>(prev, e, x);
         else
-            cload_a<E, 1, PREV_POL>(prev, e, x);
+            x[0] = cload_a1<E, PREV_POL>(prev, e);
         cload_t<E, 1, kPlain>(own, e, y);
         x[0] = combine<E, RED>(x[0], y[0]);
         if constexpr (LAST) {
             x[0] = finalize<E, RED>(x[0], R);
             cstore_t<E, 1, kCoherent>(dst, e, x);
         } else {
-            cstore_a<E, 1, kCoherent>(dst, e, x);
+            cstore_a1<E, kCoherent>(dst, e, x[0]);
         }
     }
 }
