@@ -222,6 +222,30 @@ def test_scalar_vector_switch_boundary(env, launch, dtype, R):
         assert comm.check() == api.AR_SUCCESS
 
 
+@pytest.mark.parametrize("chunk_bytes", [16384, 49152, 524288])
+@pytest.mark.parametrize("R", [3, 8, 16])
+def test_pipelined_bf16_chunk_layouts(env, chunk_bytes, R):
+    """The pipelined ring keeps a bf16 chunk's float32 partials as one run
+    per 16-byte half, laid out by the chunk's number of whole slots: chunks
+    of three sizes (two workgroups per rank, so no chunk is cut finer), each
+    segment two whole chunks and a ragged third (125 whole 8-element slots
+    and 3 elements).  All-reduce and reduce-scatter, bit-exact."""
+    api, orc = env["api"], env["orc"]
+    U = chunk_bytes // 2
+    S = 2 * U + 1003
+    N = R * S
+    x = rand_input(env, "bf16", R, N, seed=R * 7 + chunk_bytes)
+    (y,) = run_allreduce(env, x, "bf16", launch="pipelined", chunk_bytes=chunk_bytes, grid=2 * R)
+    assert y.tobytes() == orc.ring_allreduce(x, "bf16").tobytes()
+    comm = api.Comm(R, N, "bf16", device=env["dev"], launch="pipelined", chunk_bytes=chunk_bytes,
+                    grid=2 * R)
+    shard = poisoned(env, (R, S), "bf16")
+    comm.reduce_scatter(to_dev(env, x, "bf16"), shard)
+    assert from_dev(env, shard, "bf16").tobytes() == orc.ring_reduce_scatter(x, "bf16").tobytes()
+    assert comm.check() == api.AR_SUCCESS
+    comm.close()
+
+
 def _ncu(env):
     import torch
     return torch.cuda.get_device_properties(env["dev"]).multi_processor_count
