@@ -468,7 +468,9 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
     double binary tree with LL against every ring form (5 warm-up + 20 timed
     calls per size, one graph replay); an alpha-beta fit per variant, the
     crossover of the tree with each ring form (measured and from the fits),
-    and AR_AUTO's choice before and after loading the fitted lines."""
+    and AR_AUTO's choice before and after loading the fitted lines (for the
+    hand-off forms also with AR_PROTO_AUTO: tree + LL, ring + LL or the
+    simple protocol)."""
     R, s = 8, 4
     dev = torch.device("cuda:0")
     counts = inputs.sweep_counts(8, max_bytes, s)
@@ -532,7 +534,28 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
                              of=len(counts))
         return out
 
+    def proto_auto():
+        # with AR_PROTO_AUTO a hand-off form's call runs tree + LL, ring + LL
+        # or its simple protocol; how often that is the fastest of the three
+        out = {}
+        for name in ("ring-pipelined", "ring-step"):
+            probe.set_option(api.AR_OPT_LAUNCH, forms[name]["launch"])
+            probe.set_option(api.AR_OPT_PROTO, api.AR_PROTO_AUTO)
+            picks = []
+            for n in counts:
+                a, p, _ = probe.plan(n)
+                picks.append("tree-ll" if a == api.AR_TREE else "ring-ll" if p == api.AR_LL
+                             else name)
+            best = [min(("tree-ll", "ring-ll", name), key=lambda v: res[v][i])
+                    for i in range(len(counts))]
+            out[name] = dict(matches_measured=sum(p == b for p, b in zip(picks, best)),
+                             of=len(counts),
+                             picks={v: picks.count(v) for v in ("tree-ll", "ring-ll", name)})
+        probe.set_option(api.AR_OPT_PROTO, api.AR_SIMPLE)
+        return out
+
     auto["default_lines"] = choices()
+    auto["default_lines_protocol_auto"] = proto_auto()
     for name, f in fits.items():
         # a line that barely rises over this range fits a huge (or negative)
         # bandwidth: cap it at 1e6 GB/s, which adds < 1 ns at 256 KiB
@@ -540,6 +563,7 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
         bw = 1e6 if not (0 < bw < 1e6) else bw
         api.ar_set_cost(probe.handle, api.COST_FORMS[name], max(0.0, f["alpha_us"]), bw)
     auto["fitted_lines"] = choices()
+    auto["fitted_lines_protocol_auto"] = proto_auto()
     probe.close()
     hop = ll_hop_latency_us(torch)
     # the stream is looked up at each call: under capture it is the graph's

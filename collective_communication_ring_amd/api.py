@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libar.so")
 # ---- constants mirrored from include/ar.h --------------------------------
 AR_INT32, AR_FLOAT32, AR_BF16 = 0, 1, 2
 AR_RING, AR_TREE, AR_AUTO = 0, 1, 2
-AR_SIMPLE, AR_LL = 0, 1
+AR_SIMPLE, AR_LL, AR_PROTO_AUTO = 0, 1, 2
 AR_SUCCESS, AR_ERR_INVALID_ARG, AR_ERR_INVALID_USAGE, AR_ERR_UNSUPPORTED = 0, 1, 2, 3
 AR_ERR_HIP, AR_ERR_TIMEOUT, AR_ERR_INTERNAL = 4, 5, 6
 AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 3
@@ -34,7 +34,7 @@ REDOPS = {"sum": AR_SUM, "max": AR_MAX, "min": AR_MIN, "avg": AR_AVG}
 
 DTYPES = {"int32": AR_INT32, "float32": AR_FLOAT32, "bf16": AR_BF16}
 ALGOS = {"ring": AR_RING, "tree": AR_TREE, "auto": AR_AUTO}
-PROTOS = {"simple": AR_SIMPLE, "ll": AR_LL}
+PROTOS = {"simple": AR_SIMPLE, "ll": AR_LL, "auto": AR_PROTO_AUTO}
 LAUNCHES = {"auto": AR_LAUNCH_AUTO, "step": AR_LAUNCH_STEP, "fused": AR_LAUNCH_FUSED,
             "pipelined": AR_LAUNCH_PIPELINED}
 ELEM_SIZE = {AR_INT32: 4, AR_FLOAT32: 4, AR_BF16: 2}

@@ -32,6 +32,10 @@ constexpr int64_t kDefaultTimeoutUs = 2000000;      // 2 s bounded waits
 // ~640 KB/rank against the pipelined ring, ~460 KB against ring + LL and
 // ~1 MB against the step ring (measured: the tree is faster than each of them
 // up to 512 KiB and slower from 1 MiB), and none against the fused ring.
+// With AR_PROTO_AUTO the ring goes by LL where its line is below the simple
+// form's: up to ~830 KB/rank against the pipelined ring and ~1.7 MB against
+// the step ring (so with AR_AUTO: tree up to ~460 KB, then ring + LL, then
+// the simple form), and at no size against the fused ring.
 struct CostLine {
     double alpha_us;
     double bw_gbps;
@@ -223,11 +227,9 @@ int resolve_launch(const ar_comm* c)
     return AR_LAUNCH_FUSED;
 }
 
-// The cost-model line of the ring as this comm would run it.
-int ring_cost_form(const ar_comm* c)
+// The cost-model line of the ring's simple-protocol launch form.
+int simple_ring_form(const ar_comm* c)
 {
-    if (c->proto == AR_LL)
-        return AR_COST_RING_LL;
     switch (resolve_launch(c)) {
     case AR_LAUNCH_STEP:
         return AR_COST_RING_STEP;
@@ -240,23 +242,89 @@ int ring_cost_form(const ar_comm* c)
 
 double cost_us(const CostLine& l, double bytes) { return l.alpha_us + bytes / (l.bw_gbps * 1e3); }
 
+// The ring's protocol for `bytes` per rank: the comm's, or with
+// AR_PROTO_AUTO, LL where the ring + LL line is strictly below the
+// simple-protocol form's.
+int ring_proto(const ar_comm* c, double bytes)
+{
+    if (c->proto != AR_PROTO_AUTO)
+        return c->proto;
+    return cost_us(c->cost[AR_COST_RING_LL], bytes) <
+                   cost_us(c->cost[simple_ring_form(c)], bytes)
+               ? AR_LL
+               : AR_SIMPLE;
+}
+
+// Bytes per rank the cost model weighs for a call over rows of `count`.
+double call_bytes(const ar_comm* c, size_t count) { return (double)count * elem_size(c->dtype); }
+
 // AR_AUTO: tree for small messages, ring for large ones, chosen by size
 // ("NCCL and NVSHMEM -- two GPU communication models, side by side": the
 // tree for latency at small sizes, the ring for bandwidth at large ones, and
 // NCCL picks automatically).  The choice is whichever line of the cost model
-// is lower at this size: the tree's, or that of the ring form the call would
-// use.  A fixed threshold (AR_OPT_TREE_MAX_BYTES >= 0) overrides the model.
+// is lower at this size: the tree's, or that of the ring as the call would
+// run it (its protocol, then its launch form).  A fixed threshold
+// (AR_OPT_TREE_MAX_BYTES >= 0) overrides the model.
 int resolve_algo(const ar_comm* c, size_t count)
 {
     if (c->algo != AR_AUTO)
         return c->algo;
-    const double bytes = (double)count * elem_size(c->dtype);
+    const double bytes = call_bytes(c, count);
     if (c->tree_max_bytes >= 0)
         return bytes <= (double)c->tree_max_bytes ? AR_TREE : AR_RING;
-    return cost_us(c->cost[AR_COST_TREE_LL], bytes) < cost_us(c->cost[ring_cost_form(c)], bytes)
-               ? AR_TREE
-               : AR_RING;
+    const int form = ring_proto(c, bytes) == AR_LL ? AR_COST_RING_LL : simple_ring_form(c);
+    return cost_us(c->cost[AR_COST_TREE_LL], bytes) < cost_us(c->cost[form], bytes) ? AR_TREE
+                                                                                     : AR_RING;
 }
+
+// The protocol of a call whose algorithm is `algo` (the tree's lines are LL).
+int resolve_proto(const ar_comm* c, size_t count, int algo)
+{
+    return algo == AR_TREE ? AR_LL : ring_proto(c, call_bytes(c, count));
+}
+
+// The per-rank sizes n >= 0 (bytes) at which line a is strictly below line
+// b, as an integer range [lo, hi] (lo > hi: none; hi = INT64_MAX: no upper
+// end).  Two lines meet once at most, so the range is empty, everything, a
+// prefix [0, hi] or a suffix [lo, INT64_MAX].  The meeting point is found in
+// floating point, then the ends are stepped (a few steps at most) to the
+// exact integers at which the same comparison resolve_algo makes changes.
+struct Span {
+    int64_t lo, hi;
+};
+
+Span below(const CostLine& a, const CostLine& b)
+{
+    constexpr double kBig = 4e15;  // integers are exact in a double far beyond this
+    auto lt = [&](int64_t n) { return cost_us(a, (double)n) < cost_us(b, (double)n); };
+    const double da = a.alpha_us - b.alpha_us;
+    const double ds = 1.0 / (a.bw_gbps * 1e3) - 1.0 / (b.bw_gbps * 1e3);
+    if (ds == 0.0)
+        return da < 0.0 ? Span{0, INT64_MAX} : Span{1, 0};
+    const double x = -da / ds;  // where the lines meet
+    if (ds > 0.0) {
+        // a rises faster: below b up to the meeting point
+        if (x >= kBig)
+            return Span{0, INT64_MAX};
+        int64_t hi = x <= 0.0 ? 0 : (int64_t)x;
+        for (int i = 0; i < 64 && hi > 0 && !lt(hi); ++i)
+            --hi;
+        for (int i = 0; i < 64 && lt(hi + 1); ++i)
+            ++hi;
+        return lt(hi) ? Span{0, hi} : Span{1, 0};
+    }
+    // a rises more slowly: below b from the meeting point on
+    if (x >= kBig)
+        return Span{1, 0};
+    int64_t lo = x <= 0.0 ? 0 : (int64_t)x;
+    for (int i = 0; i < 64 && lo > 0 && lt(lo - 1); ++i)
+        --lo;
+    for (int i = 0; i < 64 && !lt(lo); ++i)
+        ++lo;
+    return Span{lo, INT64_MAX};
+}
+
+Span intersect(Span a, Span b) { return Span{std::max(a.lo, b.lo), std::min(a.hi, b.hi)}; }
 
 // Do the 16-byte vector kernels apply?  Every row start and every segment
 // start must be 16-byte aligned in both T and accumulator units, and a
@@ -388,6 +456,7 @@ struct RunOpts {
     const void* stage = nullptr;  // the region a.part points at when staging is allowed
     size_t stage_bytes = 0;
     bool fused_only = false;
+    int proto = AR_SIMPLE;        // the call's ring protocol (resolve_proto)
 };
 
 int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o);
@@ -416,7 +485,7 @@ int run_ring(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
 
 int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
 {
-    if (c->proto == AR_LL && !o.fused_only)
+    if (o.proto == AR_LL && !o.fused_only)
         return run_ring_ll(c, a, st);
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
@@ -602,12 +671,14 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     return AR_SUCCESS;
 }
 
-// The workspace's hand-off region, where the collectives stage hand-offs.
-RunOpts ws_opts(const ar_comm* c)
+// A call's run options: the workspace's hand-off region, where the
+// collectives stage hand-offs, and the ring protocol for rows of `count`.
+RunOpts ws_opts(const ar_comm* c, size_t count)
 {
     RunOpts o;
     o.stage = c->ws + c->off_part;
     o.stage_bytes = c->part_bytes;
+    o.proto = resolve_proto(c, count, AR_RING);
     return o;
 }
 
@@ -646,7 +717,7 @@ int ar_init(ar_comm_t* out, int R, size_t count, ar_dtype_t dtype, ar_algo_t alg
         return AR_ERR_INVALID_ARG;
     if (algo != AR_RING && algo != AR_TREE && algo != AR_AUTO)
         return AR_ERR_INVALID_ARG;
-    if (proto != AR_SIMPLE && proto != AR_LL)
+    if (proto != AR_SIMPLE && proto != AR_LL && proto != AR_PROTO_AUTO)
         return AR_ERR_INVALID_ARG;
     if (count > ((size_t)1 << 40))
         return AR_ERR_INVALID_ARG;
@@ -794,7 +865,7 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
     a.R = c->R;
     a.op = kOpAllReduce;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st, ws_opts(c));
+    return run_ring(c, a, st, ws_opts(c, count));
 }
 
 int ar_allreduce_noalloc(ar_comm_t c, const void* send, void* recv, size_t count, void* stream)
@@ -882,7 +953,7 @@ int ar_reduce_scatter(ar_comm_t c, const void* send, void* recv, size_t recvcoun
     a.R = c->R;
     a.op = kOpReduceScatter;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st, ws_opts(c));
+    return run_ring(c, a, st, ws_opts(c, N));
 }
 
 int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, void* stream)
@@ -915,7 +986,7 @@ int ar_all_gather(ar_comm_t c, const void* send, void* recv, size_t sendcount, v
     a.R = c->R;
     a.op = kOpAllGather;
     a.timeout_ticks = timeout_ticks(c);
-    return run_ring(c, a, st, ws_opts(c));
+    return run_ring(c, a, st, ws_opts(c, N));
 }
 
 int ar_check(ar_comm_t c)
@@ -975,7 +1046,7 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
         c->algo = (int)v;
         return AR_SUCCESS;
     case AR_OPT_PROTO:
-        if (v != AR_SIMPLE && v != AR_LL)
+        if (v != AR_SIMPLE && v != AR_LL && v != AR_PROTO_AUTO)
             return AR_ERR_INVALID_ARG;
         c->proto = (int)v;
         return AR_SUCCESS;
@@ -1028,7 +1099,7 @@ int ar_plan(ar_comm_t c, size_t count, int* algo, int* proto, int* launch)
     if (!c || !algo || !proto || !launch)
         return AR_ERR_INVALID_ARG;
     *algo = resolve_algo(c, count);
-    *proto = (*algo == AR_TREE) ? AR_LL : c->proto;
+    *proto = resolve_proto(c, count, *algo);
     *launch = (*algo == AR_TREE || *proto == AR_LL) ? AR_LAUNCH_AUTO : resolve_launch(c);
     return AR_SUCCESS;
 }
@@ -1058,23 +1129,18 @@ int64_t ar_auto_tree_max_bytes(ar_comm_t c)
         return -1;
     if (c->tree_max_bytes >= 0)
         return c->tree_max_bytes;
-    // the lines cross once at most: the tree is cheaper below the crossing
-    const CostLine t = c->cost[AR_COST_TREE_LL], r = c->cost[ring_cost_form(c)];
-    const double bt = 1.0 / (t.bw_gbps * 1e3), br = 1.0 / (r.bw_gbps * 1e3);  // us per byte
-    if (t.alpha_us >= r.alpha_us && bt >= br)
-        return 0;  // the ring is never slower
-    if (t.alpha_us < r.alpha_us && bt <= br)
-        return INT64_MAX;  // the tree is never slower
-    const double n = (r.alpha_us - t.alpha_us) / (bt - br);
-    if (n <= 0.0)
-        return 0;
-    if (n >= 9e18)
-        return INT64_MAX;
-    // the largest size the tree still takes (resolve_algo's strict <)
-    int64_t b = (int64_t)n;
-    while (b > 0 && !(cost_us(t, (double)b) < cost_us(r, (double)b)))
-        --b;
-    return b;
+    // the sizes at which the tree's line is below the ring's as calls would
+    // run it: below the simple form's and, for ring + LL or AR_PROTO_AUTO
+    // (the ring then costs the lower of its two lines), below ring + LL's
+    const CostLine t = c->cost[AR_COST_TREE_LL];
+    const Span simple = below(t, c->cost[simple_ring_form(c)]);
+    const Span ll = below(t, c->cost[AR_COST_RING_LL]);
+    const Span s = c->proto == AR_SIMPLE ? simple : c->proto == AR_LL ? ll : intersect(simple, ll);
+    if (s.lo > s.hi)
+        return 0;  // never by tree
+    if (s.lo == 0)
+        return s.hi;  // every size up to s.hi by tree (INT64_MAX: every size)
+    return -2;  // only sizes from s.lo on by tree
 }
 
 int ar_ring_segment(ar_comm_t c, size_t count, int seg, size_t* lo, size_t* hi)

@@ -65,8 +65,18 @@ typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
 /* AR_SIMPLE: bulk data, then a release, then a ready flag (or a kernel
  * boundary between steps).  AR_LL: data and its arrival flag packed in one
  * 8-byte store -- 4 bytes of data, 4 bytes of flag -- that the consumer polls
- * ("Demystifying NVSHMEM ..." summary, paragraph on collectives). */
-typedef enum { AR_SIMPLE = 0, AR_LL = 1 } ar_proto_t;
+ * ("Demystifying NVSHMEM ..." summary, paragraph on collectives).
+ * AR_PROTO_AUTO: chosen per call from the same cost model as AR_AUTO
+ * (ar_set_cost): the ring runs with AR_LL where the ring + LL line is
+ * strictly below the line of the comm's simple-protocol launch form at the
+ * call's size, else with AR_SIMPLE; the tree always moves LL lines.  With
+ * AR_AUTO the tree is then weighed against that cheaper ring.  The pages
+ * pick the algorithm by size ("NCCL and NVSHMEM -- two GPU communication
+ * models, side by side", ring vs tree); picking the protocol by the same
+ * model is this library's extension.  With the default fused ring the model
+ * keeps AR_SIMPLE at every size (its line is below ring + LL's); with
+ * AR_LAUNCH_PIPELINED or AR_LAUNCH_STEP mid-size messages go by ring + LL. */
+typedef enum { AR_SIMPLE = 0, AR_LL = 1, AR_PROTO_AUTO = 2 } ar_proto_t;
 
 /* Reduction operator (ar_set_option(AR_OPT_REDOP, ...)); the default is the
  * sum.  Ranks reduce with sum, min or max; an average is the sum divided by
@@ -235,7 +245,10 @@ int ar_set_option(ar_comm_t comm, int option, int64_t value);
 int ar_get_option(ar_comm_t comm, int option, int64_t* value);
 
 /* Resolved algorithm, protocol and launch that a call with `count` elements
- * per rank would use (values of ar_algo_t, ar_proto_t, ar_launch_t). */
+ * per rank would use (values of ar_algo_t, ar_proto_t, ar_launch_t; never
+ * AR_AUTO or AR_PROTO_AUTO; the launch is AR_LAUNCH_AUTO for the tree and
+ * for ring + LL, which have one form each).  For reduce-scatter and
+ * all-gather the model's size is the full row per rank (R times the shard). */
 int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
 
 /* The cost model behind AR_AUTO: for each algorithm and ring launch form a
@@ -248,9 +261,12 @@ int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
  * own measurements (other R, dtype or machine) sets them here.
  * ar_set_cost: AR_ERR_INVALID_ARG for an unknown form, alpha_us < 0,
  *   bw_gbps <= 0 or a NaN.
- * ar_auto_tree_max_bytes: the largest per-rank message AR_AUTO sends by tree
- *   under the comm's current options (0: none; INT64_MAX: every size); -1
- *   for a NULL comm. */
+ * ar_auto_tree_max_bytes: under the comm's current options, the largest
+ *   per-rank message AR_AUTO sends by tree when it sends every message up to
+ *   that size by tree and none above (0: none; INT64_MAX: every size); -2
+ *   when it sends some larger messages by tree but not the smallest (lines
+ *   set to cross the other way), so that no such size exists; -1 for a NULL
+ *   comm. */
 typedef enum {
     AR_COST_TREE_LL = 0,
     AR_COST_RING_FUSED = 1,

@@ -131,6 +131,103 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
         api.ar_destroy(c)
 
 
+def _line_cross(a, b):
+    """Bytes per rank where two cost lines (alpha_us, GB/s) meet."""
+    return (b[0] - a[0]) / (1e-3 / a[1] - 1e-3 / b[1])
+
+
+def _cost(line, n):
+    return line[0] + n / (line[1] * 1e3)
+
+
+def test_plan_protocol_auto(api):
+    """AR_PROTO_AUTO takes ring + LL where its line is strictly below the
+    simple form's, and AR_AUTO weighs the tree against that cheaper ring."""
+    c = api.ar_init(8, 1 << 24, api.AR_FLOAT32, api.AR_AUTO, api.AR_PROTO_AUTO)
+    try:
+        assert api.ar_get_option(c, api.AR_OPT_PROTO) == api.AR_PROTO_AUTO
+        tree = api.ar_get_cost(c, api.AR_COST_TREE_LL)
+        ll = api.ar_get_cost(c, api.AR_COST_RING_LL)
+        # the default fused ring: simple protocol and ring at every size
+        for n in (1, 1000, 1 << 20, 1 << 24):
+            assert api.ar_plan(c, n) == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+        assert api.ar_auto_tree_max_bytes(c) == 0
+        for launch, form in ((api.AR_LAUNCH_PIPELINED, api.AR_COST_RING_PIPELINED),
+                             (api.AR_LAUNCH_STEP, api.AR_COST_RING_STEP)):
+            api.ar_set_option(c, api.AR_OPT_LAUNCH, launch)
+            simple = api.ar_get_cost(c, form)
+            t_max = api.ar_auto_tree_max_bytes(c)
+            # the tree goes up to the lower of its two crossings (with ring + LL here)
+            assert abs(t_max - min(_line_cross(tree, ll), _line_cross(tree, simple))) < 2
+            ll_max = _line_cross(ll, simple)  # ring + LL below the simple form up to here
+            assert t_max < ll_max
+            assert api.ar_plan(c, 1) == (api.AR_TREE, api.AR_LL, api.AR_LAUNCH_AUTO)
+            assert api.ar_plan(c, t_max // 4) == (api.AR_TREE, api.AR_LL, api.AR_LAUNCH_AUTO)
+            assert api.ar_plan(c, t_max // 4 + 1) == (api.AR_RING, api.AR_LL, api.AR_LAUNCH_AUTO)
+            # the switch to the simple form sits where the two ring lines cross
+            k = int(ll_max) // 4
+            for n in range(k - 2, k + 3):
+                want = api.AR_LL if _cost(ll, 4 * n) < _cost(simple, 4 * n) else api.AR_SIMPLE
+                got = api.ar_plan(c, n)
+                assert got[:2] == (api.AR_RING, want), (launch, n, got)
+            assert api.ar_plan(c, 1 << 22) == (api.AR_RING, api.AR_SIMPLE, launch)
+            # a ring-only comm keeps the same protocol choice
+            api.ar_set_option(c, api.AR_OPT_ALGO, api.AR_RING)
+            assert api.ar_plan(c, 1) == (api.AR_RING, api.AR_LL, api.AR_LAUNCH_AUTO)
+            assert api.ar_plan(c, 1 << 22) == (api.AR_RING, api.AR_SIMPLE, launch)
+            api.ar_set_option(c, api.AR_OPT_ALGO, api.AR_AUTO)
+        # a fixed protocol still wins over the model (step form, 1.2 MB per
+        # rank: above the tree's crossing, below ring + LL's)
+        assert api.ar_plan(c, 1_200_000 // 4)[:2] == (api.AR_RING, api.AR_LL)
+        api.ar_set_option(c, api.AR_OPT_PROTO, api.AR_SIMPLE)
+        assert api.ar_plan(c, 1_200_000 // 4) == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_STEP)
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, api.AR_OPT_PROTO, 3)
+    finally:
+        api.ar_destroy(c)
+    with pytest.raises(api.ArError):
+        api.ar_init(8, 1024, api.AR_FLOAT32, api.AR_AUTO, 3)
+
+
+def test_auto_tree_max_bytes_for_any_lines(api):
+    """ar_auto_tree_max_bytes for lines a caller may set: a prefix of sizes
+    by tree, none, all, or (lines crossing the other way) -2; answers at once
+    even where the lines meet far out."""
+    c = api.ar_init(8, 1024, api.AR_FLOAT32, api.AR_AUTO, api.AR_SIMPLE)
+    try:
+        api.ar_set_option(c, api.AR_OPT_LAUNCH, api.AR_LAUNCH_PIPELINED)
+        P, T = api.AR_COST_RING_PIPELINED, api.AR_COST_TREE_LL
+        # the tree cheaper only for large messages
+        api.ar_set_cost(c, T, 100.0, 1000.0)
+        api.ar_set_cost(c, P, 10.0, 100.0)
+        assert api.ar_auto_tree_max_bytes(c) == -2
+        assert api.ar_plan(c, 1)[0] == api.AR_RING
+        assert api.ar_plan(c, 1 << 30)[0] == api.AR_TREE
+        # never, always, and equal lines (strictly below: never)
+        api.ar_set_cost(c, T, 20.0, 100.0)
+        assert api.ar_auto_tree_max_bytes(c) == 0
+        api.ar_set_cost(c, T, 1.0, 1000.0)
+        assert api.ar_auto_tree_max_bytes(c) == 2 ** 63 - 1
+        api.ar_set_cost(c, T, 10.0, 100.0)
+        assert api.ar_auto_tree_max_bytes(c) == 0
+        # meeting points far out: ~5e8 bytes (a prefix), ~1e9 bytes (a suffix)
+        api.ar_set_cost(c, T, 0.0, 1e-3)
+        api.ar_set_cost(c, P, 5e8, 1e8)
+        b = api.ar_auto_tree_max_bytes(c)
+        assert abs(b - _line_cross((0.0, 1e-3), (5e8, 1e8))) < 2
+        assert api.ar_plan(c, b // 4)[0] == api.AR_TREE
+        assert api.ar_plan(c, b // 4 + 1)[0] == api.AR_RING
+        api.ar_set_cost(c, T, 1e8, 1e8)
+        api.ar_set_cost(c, P, 0.0, 1e-2)
+        assert api.ar_auto_tree_max_bytes(c) == -2
+        # lines that meet beyond any size: the side that wins at n = 0 everywhere
+        api.ar_set_cost(c, T, 0.0, 1e8)
+        api.ar_set_cost(c, P, 1e8, 1e8 * 0.999999)
+        assert api.ar_auto_tree_max_bytes(c) == 2 ** 63 - 1
+    finally:
+        api.ar_destroy(c)
+
+
 @pytest.mark.parametrize("R", [2, 3, 4, 5, 7, 8, 16, 64])
 def test_library_schedule_matches_oracle(api, orc, R):
     """The library's host scheduler and the oracle are separate code; their

@@ -380,6 +380,55 @@ def test_auto_selects_tree_then_ring(env):
         assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
 
 
+@pytest.mark.parametrize("launch", ["pipelined", "step"])
+def test_protocol_auto_runs_the_planned_protocol(env, capfd, launch):
+    """With AR_PROTO_AUTO each call runs the algorithm and protocol ar_plan
+    reports (the library's debug line names the kernels it launched):
+    tree + LL, ring + LL or the simple-protocol ring by size; all-reduce,
+    and reduce-scatter + all-gather weighed by the full row, bit-exact."""
+    api, orc = env["api"], env["orc"]
+    R, Nmax = 8, 1 << 20
+    x = env["inputs"].draw("normal", R, Nmax, seed=13)
+    comm = api.Comm(R, Nmax, "float32", "auto", "auto", device=env["dev"], launch=launch, debug=1)
+    tree_max = api.ar_auto_tree_max_bytes(comm.handle)
+    assert 0 < tree_max < 600_000 // 4 * 4
+    seen = set()
+    # 4 KiB (tree), 600 KB (ring + LL), 4 MiB (the simple form) per rank
+    for N in (1024, 150_000, Nmax):
+        algo, proto, _ = comm.plan(N)
+        kind = "tree" if algo == api.AR_TREE else "ring-ll" if proto == api.AR_LL else "simple"
+        seen.add(kind)
+        xs = np.ascontiguousarray(x[:, :N])
+        send = to_dev(env, xs, "float32")
+        recv = poisoned(env, (R, N), "float32")
+        capfd.readouterr()
+        comm.allreduce(send, recv)
+        got = from_dev(env, recv, "float32")
+        err = capfd.readouterr().err
+        ref = orc.tree_allreduce(xs) if kind == "tree" else orc.ring_allreduce(xs)
+        assert got.tobytes() == ref.tobytes(), (N, kind)
+        assert ("ar: tree-LL" in err) == (kind == "tree"), (N, kind, err)
+        assert ("ar: ring-LL" in err) == (kind == "ring-ll"), (N, kind, err)
+        assert ("launch=" + launch in err) == (kind == "simple"), (N, kind, err)
+    assert seen == {"tree", "ring-ll", "simple"}
+    # reduce-scatter and all-gather are ring only; their size is the full row
+    for N in (150_000 // R * R, Nmax):
+        proto = comm.plan(N)[1] if comm.plan(N)[0] == api.AR_RING else api.AR_LL
+        xs = np.ascontiguousarray(x[:, :N])
+        shard = poisoned(env, (R, N // R), "float32")
+        full = poisoned(env, (R, N), "float32")
+        capfd.readouterr()
+        comm.reduce_scatter(to_dev(env, xs, "float32"), shard)
+        comm.all_gather(shard, full)
+        rs = from_dev(env, shard, "float32")
+        err = capfd.readouterr().err
+        assert rs.tobytes() == orc.ring_reduce_scatter(xs).tobytes()
+        assert from_dev(env, full, "float32").tobytes() == orc.ring_all_gather(rs).tobytes()
+        assert ("ar: ring-LL" in err) == (proto == api.AR_LL), (N, err)
+    assert comm.check() == api.AR_SUCCESS
+    comm.close()
+
+
 # ---------------------------------------------------------------- wave tiles
 
 # 16-byte slots per lane of the fused form's wave tile (kWaveSlots): a tile is
