@@ -578,9 +578,10 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
         const uint64_t tile = (uint64_t)kBlock * kUnroll * V;  // elements per workgroup pass
         const uint64_t es = (uint64_t)elem_size(c->dtype);
         uint64_t unit = c->chunk_bytes > 0 ? (uint64_t)c->chunk_bytes / es : a.sub_len;
-        // a chunk is addressed through one buffer resource (byte offsets below
-        // 2 GiB): cap it at 1 GiB
-        unit = std::min<uint64_t>(unit, kMaxChunkBytes / es);
+        // a chunk's elements and its 4-byte accumulators are each addressed
+        // through one buffer resource (byte offsets below 2 GiB): cap both at
+        // 1 GiB, i.e. the chunk at kMaxChunkBytes / 4 elements whatever T
+        unit = std::min<uint64_t>(unit, kMaxChunkBytes / 4);
         unit = std::max<uint64_t>(tile, unit / tile * tile);
         uint64_t nunits = (a.sub_len + unit - 1) / unit;
         // the chunk is the pipelining unit; cut it finer when a segment has

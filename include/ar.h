@@ -127,7 +127,9 @@ typedef enum {
 /* Tunables for ar_set_option / ar_get_option. */
 typedef enum {
     AR_OPT_CHUNK_BYTES = 0,   /* pipelined ring: slice ("chunk") size in bytes of T; 0 = whole
-                                 segment; at most 1 GiB is used (larger values are cut) */
+                                 segment; at most 2^28 elements are used (1 GiB of 32-bit T,
+                                 512 MiB of bf16, whose float32 partials take 1 GiB); larger
+                                 values are cut */
     AR_OPT_LAUNCH = 1,        /* an ar_launch_t */
     AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default */
     AR_OPT_TIMEOUT_US = 3,    /* microseconds before a kernel's bounded wait gives up */

@@ -246,6 +246,41 @@ def test_pipelined_bf16_chunk_layouts(env, chunk_bytes, R):
     comm.close()
 
 
+def test_pipelined_bf16_largest_chunk(env):
+    """The largest pipelined chunk: R = 3 bf16, segments of 2^29 + 512
+    elements, whole-segment chunks (chunk size 0) and two workgroups per rank,
+    so chunks stay as large as the library allows.  A chunk's float32
+    partials take 4 bytes per element and must stay addressable by one buffer
+    resource (below 2 GiB).  Sampled outputs -- each segment's ends and the
+    elements around 2^28 and 2^29 into it -- against the oracle, and no
+    output element left unwritten."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R = 3
+    S = (1 << 29) + 512
+    N = R * S
+    g = torch.Generator(device=env["dev"])
+    g.manual_seed(29)
+    send = torch.randn((R, N), generator=g, device=env["dev"], dtype=torch.bfloat16)
+    recv = torch.full_like(send, float("nan"))
+    comm = api.Comm(R, N, "bf16", device=env["dev"], launch="pipelined", chunk_bytes=0,
+                    grid=2 * R, timeout_us=30_000_000)
+    comm.allreduce(send, recv)
+    torch.cuda.synchronize()
+    assert comm.check() == api.AR_SUCCESS
+    offs = sorted({0, 1, 2, 3, S - 4, S - 3, S - 2, S - 1}
+                  | {b + d for b in (1 << 28, 1 << 29) for d in range(-8, 8)})
+    idx = np.array([c * S + o for c in range(R) for o in offs], dtype=np.int64)
+    ti = torch.from_numpy(idx).to(env["dev"])
+    xs = send[:, ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    ys = recv[:, ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    # segment c's samples sit in columns [c*m, (c+1)*m) of [R, R*m]: the same fold
+    assert ys.tobytes() == orc.ring_allreduce(np.ascontiguousarray(xs), "bf16").tobytes()
+    assert not torch.isnan(recv).any().item()
+    comm.close()
+    del send, recv, comm
+    torch.cuda.empty_cache()
+
+
 def _ncu(env):
     import torch
     return torch.cuda.get_device_properties(env["dev"]).multi_processor_count
