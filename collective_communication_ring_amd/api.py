@@ -23,7 +23,7 @@ AR_ERR_HIP, AR_ERR_TIMEOUT, AR_ERR_INTERNAL = 4, 5, 6
 AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 3
 (AR_OPT_CHUNK_BYTES, AR_OPT_LAUNCH, AR_OPT_GRID, AR_OPT_TIMEOUT_US, AR_OPT_DEBUG,
  AR_OPT_ALGO, AR_OPT_PROTO, AR_OPT_TREE_MAX_BYTES, AR_OPT_DEBUG_MUTE_RANK, AR_OPT_REDOP,
- AR_OPT_CHANNELS) = range(11)
+ AR_OPT_CHANNELS, AR_OPT_DEBUG_LL_LAUNCHES) = range(12)
 AR_SUM, AR_MAX, AR_MIN, AR_AVG = 0, 1, 2, 3
 (AR_COST_TREE_LL, AR_COST_RING_FUSED, AR_COST_RING_PIPELINED, AR_COST_RING_STEP,
  AR_COST_RING_LL) = range(5)

@@ -49,6 +49,11 @@ constexpr CostLine kDefaultCost[AR_COST_FORMS] = {
 };
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
 constexpr uint64_t kMaxChunkBytes = 1ull << 30;      // pipelined ring: largest chunk
+// LL flags are 32-bit epochs advanced once per launch (ring + LL: 2e and
+// 2e + 1; the tree: a group's epoch + 1): after this many tree and ring-LL
+// launches the lines and epochs are cleared again, so no flag wraps around
+// to a value that a stale line may still hold.
+constexpr uint64_t kLLResetLaunches = 1ull << 30;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -168,6 +173,7 @@ struct ar_comm {
     int resident_tree[3] = {};
     int resident_rll[3] = {};
     // last call
+    uint64_t ll_launches = 0;  // tree and ring-LL launches since their lines were cleared
     hipStream_t last_stream = nullptr;
     int last_hip = 0;
 };
@@ -399,6 +405,29 @@ uint64_t ll_grid_per_rank(uint64_t lines, int groups, int ncu, int ept, int64_t 
     return std::max<uint64_t>(1, std::min<uint64_t>(g, (uint64_t)cap));
 }
 
+// Before each tree or ring-LL launch: once kLLResetLaunches of them have run
+// since the lines were cleared, clear the tree's lines and group epochs, the
+// ring-LL lines and the ring-LL epoch word on the stream, so the launch
+// starts again from epoch 1.  The error word and the pipelined ring's 64-bit
+// flags are left alone.
+int ll_launch_guard(ar_comm* c, hipStream_t st)
+{
+    if (c->ll_launches >= kLLResetLaunches) {
+        hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,
+                                       (c->off_flags - c->off_up) / sizeof(uint64_t), st);
+        if (e == hipSuccess)
+            e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_rll), 0ull,
+                                (c->ws_need - c->off_rll) / sizeof(uint64_t), st);
+        if (e == hipSuccess)
+            e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws) + kCtrlRingLLEpoch, 0u, 1, st);
+        if (e != hipSuccess)
+            return fail_hip(c, e);
+        c->ll_launches = 0;
+    }
+    ++c->ll_launches;
+    return AR_SUCCESS;
+}
+
 // Ring with the LL protocol: one launch per piece of the segments.
 int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
 {
@@ -437,6 +466,9 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
         if (ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > c->resident_rll[c->dtype])
             a.xcd_sets = 1;
         const int64_t grid = ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R);
+        const int rc = ll_launch_guard(c, st);
+        if (rc)
+            return rc;
         hipError_t e = launch_ring_ll(c->dtype, a, (int)grid, st);
         if (e != hipSuccess)
             return fail_hip(c, e);
@@ -660,6 +692,9 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
         const int grid = (int)ll_grid_for_sets(2 * (int64_t)a.blocks_per_rank, a.xcd_sets, c->R);
         if (grid > res)
             return AR_ERR_INTERNAL;
+        const int rc = ll_launch_guard(c, st);
+        if (rc)
+            return rc;
         hipError_t e = launch_tree_ll(c->dtype, a, grid, st);
         if (e != hipSuccess)
             return fail_hip(c, e);
@@ -818,6 +853,7 @@ int ar_set_workspace(ar_comm_t c, void* dev, size_t bytes, void* stream)
         c->ws = nullptr;
         return fail_hip(c, e);
     }
+    c->ll_launches = 0;
     c->last_stream = st;
     return AR_SUCCESS;
 }
@@ -1071,6 +1107,11 @@ int ar_set_option(ar_comm_t c, int option, int64_t v)
             return AR_ERR_INVALID_ARG;
         c->channels = v;
         return AR_SUCCESS;
+    case AR_OPT_DEBUG_LL_LAUNCHES:
+        if (v < 0 || (uint64_t)v > kLLResetLaunches)
+            return AR_ERR_INVALID_ARG;
+        c->ll_launches = (uint64_t)v;
+        return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }
@@ -1091,6 +1132,7 @@ int ar_get_option(ar_comm_t c, int option, int64_t* v)
     case AR_OPT_DEBUG_MUTE_RANK: *v = c->mute_rank; return AR_SUCCESS;
     case AR_OPT_REDOP: *v = c->redop; return AR_SUCCESS;
     case AR_OPT_CHANNELS: *v = c->channels; return AR_SUCCESS;
+    case AR_OPT_DEBUG_LL_LAUNCHES: *v = (int64_t)c->ll_launches; return AR_SUCCESS;
     }
     return AR_ERR_INVALID_ARG;
 }

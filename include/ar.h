@@ -142,11 +142,13 @@ typedef enum {
                                    skip publishing (LL lines, ready flags), so its consumers'
                                    bounded waits expire; -1 (default) = none */
     AR_OPT_REDOP = 9,           /* an ar_redop_t for ar_allreduce / ar_reduce_scatter */
-    AR_OPT_CHANNELS = 10        /* ring channels K (default 1): every segment is cut into K
+    AR_OPT_CHANNELS = 10,       /* ring channels K (default 1): every segment is cut into K
                                    sub-ranges of Sk = ceil(ceil(S/K)/8)*8 elements, and
                                    channel k runs its own ring q -> q + m_k over sub-range k
                                    (strides from ar_ring_channel_stride); the multi-rail /
                                    channels idea ("GPU MODE lecture 68 notes", section 06) */
+    AR_OPT_DEBUG_LL_LAUNCHES = 11 /* testing only: tree and ring + LL launches counted since
+                                   their lines were last cleared (see ar_set_workspace) */
 } ar_option_t;
 
 /* Create a communicator for R logical ranks (2 <= R <= 64) and up to
@@ -178,9 +180,18 @@ size_t ar_workspace_bytes(ar_comm_t comm);
  * LL lines (enqueued on `stream`; ordered before any later call on the same
  * stream).  No page defines this call: it is this library's own boundary
  * design; the stream argument lets the clearing be ordered with the caller's
- * own work instead of synchronizing the device.  The memory stays owned by the caller and must outlive every
- * collective issued on this comm.  Returns AR_ERR_INVALID_ARG when `bytes`
- * is smaller than ar_workspace_bytes or `dev` is NULL or misaligned. */
+ * own work instead of synchronizing the device.  The memory stays owned by
+ * the caller and must outlive every collective issued on this comm.  Returns
+ * AR_ERR_INVALID_ARG when `bytes` is smaller than ar_workspace_bytes or
+ * `dev` is NULL or misaligned.
+ * LL flags are 32-bit epochs that grow by one per launch.  Every 2^30 tree
+ * or ring + LL launches the library clears the lines and epochs again, on
+ * the call's stream, before the next such launch, so a flag never wraps
+ * around to a value a stale line may hold.  The library counts the launches
+ * it enqueues; replays of a captured HIP graph advance the epochs without
+ * it: a caller that replays a graph holding tree or ring + LL calls more
+ * than 2^30 times calls ar_set_workspace again (outside the graph) before
+ * that many replays. */
 int ar_set_workspace(ar_comm_t comm, void* dev, size_t bytes, void* stream);
 
 /* All-reduce (sum, or the comm's AR_OPT_REDOP).  send and recv are

@@ -71,7 +71,8 @@ def test_options_round_trip(api):
                          (api.AR_OPT_GRID, 512), (api.AR_OPT_TIMEOUT_US, 1000),
                          (api.AR_OPT_ALGO, api.AR_TREE), (api.AR_OPT_PROTO, api.AR_LL),
                          (api.AR_OPT_TREE_MAX_BYTES, 1 << 20), (api.AR_OPT_DEBUG_MUTE_RANK, 2),
-                         (api.AR_OPT_DEBUG_MUTE_RANK, -1)):
+                         (api.AR_OPT_DEBUG_MUTE_RANK, -1), (api.AR_OPT_DEBUG_LL_LAUNCHES, 1 << 30),
+                         (api.AR_OPT_DEBUG_LL_LAUNCHES, 0)):
             api.ar_set_option(c, opt, val)
             assert api.ar_get_option(c, opt) == val
         with pytest.raises(api.ArError):
@@ -80,6 +81,8 @@ def test_options_round_trip(api):
             api.ar_set_option(c, 1234, 1)
         with pytest.raises(api.ArError):
             api.ar_set_option(c, api.AR_OPT_DEBUG_MUTE_RANK, 4)  # R = 4
+        with pytest.raises(api.ArError):
+            api.ar_set_option(c, api.AR_OPT_DEBUG_LL_LAUNCHES, (1 << 30) + 1)
     finally:
         api.ar_destroy(c)
 

@@ -281,6 +281,43 @@ def test_pipelined_bf16_largest_chunk(env):
     torch.cuda.empty_cache()
 
 
+def test_ll_epochs_restart_before_they_wrap(env):
+    """LL flags are 32-bit epochs advanced once per launch; every 2^30 tree or
+    ring + LL launches the library clears the lines and epochs on the stream
+    before the next such launch.  Forced from the host: the ring + LL epoch
+    word (control word 4 of the workspace) set to 2^31 - 1, where the next
+    launch's reduce flag 2 * epoch would wrap to 0 -- the value of every line
+    not written since the clear -- and the launch count set to the reset
+    point.  The next call, over more lines than any before, must match the
+    oracle, and the count restarts; the tree likewise."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R = 4
+    comm = api.Comm(R, 1 << 16, "float32", "ring", "ll", device=env["dev"])
+    for N, reset in ((1000, False), (1 << 16, True)):
+        x = rand_input(env, "float32", R, N, seed=N)
+        if reset:
+            comm.workspace[:256].view(torch.int32)[4] = 2 ** 31 - 1
+            comm.set_option(api.AR_OPT_DEBUG_LL_LAUNCHES, 1 << 30)
+        recv = poisoned(env, (R, N), "float32")
+        comm.allreduce(to_dev(env, x, "float32"), recv)
+        assert from_dev(env, recv, "float32").tobytes() == orc.ring_allreduce(x).tobytes(), N
+        assert comm.check() == api.AR_SUCCESS
+    launches = comm.get_option(api.AR_OPT_DEBUG_LL_LAUNCHES)
+    assert 1 <= launches < 100  # counted again from the reset
+    assert int(comm.workspace[:256].view(torch.int32)[4].item()) == launches
+    comm.close()
+    tree = api.Comm(R, 1 << 16, "float32", "tree", "ll", device=env["dev"])
+    for N in (1000, 1 << 16):
+        x = rand_input(env, "float32", R, N, seed=N + 1)
+        tree.set_option(api.AR_OPT_DEBUG_LL_LAUNCHES, 1 << 30)
+        recv = poisoned(env, (R, N), "float32")
+        tree.allreduce(to_dev(env, x, "float32"), recv)
+        assert from_dev(env, recv, "float32").tobytes() == orc.tree_allreduce(x).tobytes(), N
+        assert 1 <= tree.get_option(api.AR_OPT_DEBUG_LL_LAUNCHES) < 100
+    assert tree.check() == api.AR_SUCCESS
+    tree.close()
+
+
 def _ncu(env):
     import torch
     return torch.cuda.get_device_properties(env["dev"]).multi_processor_count
