@@ -449,7 +449,11 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
     a.mute_rank = (int)c->mute_rank;
     a.redop = (int)c->redop;
     a.timeout_ticks = r.timeout_ticks;
-    const int64_t gmax = c->resident_rll[c->dtype] / a.R;
+    // every workgroup must be resident: at most the occupancy limit, and at
+    // most AR_OPT_GRID (a stream held to fewer CUs holds fewer workgroups)
+    const int64_t res = c->grid > 0 ? std::min<int64_t>(c->resident_rll[c->dtype], c->grid)
+                                    : (int64_t)c->resident_rll[c->dtype];
+    const int64_t gmax = res / a.R;
     if (gmax < 1)
         return AR_ERR_UNSUPPORTED;
     int launches = 0;
@@ -460,10 +464,9 @@ int run_ring_ll(ar_comm* c, const RingArgs& r, hipStream_t st)
         // sets of R workgroups on one XCD each, the grid rounded up to whole
         // rows of sets; every workgroup must still be resident
         a.xcd_sets = c->nxcd;
-        while (a.per_rank_wg > 1 &&
-               ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > c->resident_rll[c->dtype])
+        while (a.per_rank_wg > 1 && ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > res)
             --a.per_rank_wg;
-        if (ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > c->resident_rll[c->dtype])
+        if (ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R) > res)
             a.xcd_sets = 1;
         const int64_t grid = ll_grid_for_sets(a.per_rank_wg, a.xcd_sets, a.R);
         const int rc = ll_launch_guard(c, st);
@@ -668,8 +671,10 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
             a.node[t][r] = tree_node_word(c->tt.parent[t][r], c->tt.nchild[t][r],
                                           c->tt.child[t][r][0], c->tt.child[t][r][1]);
     // every workgroup must be resident at once: at most res / (2R) per
-    // (tree, rank); a workgroup loops over its sub-blocks of kBlock lines
-    const int64_t res = c->resident_tree[c->dtype];
+    // (tree, rank), res being the occupancy limit capped by AR_OPT_GRID; a
+    // workgroup loops over its sub-blocks of kBlock lines
+    const int64_t res = c->grid > 0 ? std::min<int64_t>(c->resident_tree[c->dtype], c->grid)
+                                    : (int64_t)c->resident_tree[c->dtype];
     const int64_t bpr_max = res / (2 * c->R);
     if (bpr_max < 1)
         return AR_ERR_UNSUPPORTED;

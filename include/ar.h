@@ -113,7 +113,8 @@ typedef enum {
  * AR_LAUNCH_AUTO: the library's choice (the default).
  * The pipelined ring, the ring with AR_LL and the tree need every workgroup
  * of a launch resident at once (the library sizes their grids to the
- * device's occupancy).  Two such launches running at the same time on
+ * device's occupancy, capped by AR_OPT_GRID; on a stream held to fewer CUs
+ * the caller sets AR_OPT_GRID, else the waits expire: AR_ERR_TIMEOUT).  Two such launches running at the same time on
  * different streams can each hold part of the device and wait for each
  * other until their bounded waits expire (AR_ERR_TIMEOUT): do not overlap
  * them with each other.  The step and fused forms have no such waits. */
@@ -131,7 +132,12 @@ typedef enum {
                                  512 MiB of bf16, whose float32 partials take 1 GiB); larger
                                  values are cut */
     AR_OPT_LAUNCH = 1,        /* an ar_launch_t */
-    AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default */
+    AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default.  For the
+                                 pipelined ring, ring + LL and the tree, whose workgroups
+                                 must all be resident at once, a cap: on a stream held to
+                                 some CUs (ar_stream_create_cu_masked) set it to at most the
+                                 workgroups those CUs hold (one per CU is always safe); it
+                                 must be at least R (2R for the tree) */
     AR_OPT_TIMEOUT_US = 3,    /* microseconds before a kernel's bounded wait gives up */
     AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */

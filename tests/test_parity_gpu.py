@@ -978,23 +978,31 @@ def test_two_comms_on_two_streams(env, pair):
         assert c.check() == api.AR_SUCCESS
 
 
-def test_comm_on_a_cu_masked_stream_then_teardown(env):
-    """A comm used on a caller-owned CU-masked stream: exact, and closing the
-    comm before destroying the stream releases the workspace cleanly (the
-    workspace is recorded on every stream the comm ran on)."""
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+def test_comm_on_a_cu_masked_stream_then_teardown(env, variant):
+    """A comm used on a caller-owned stream held to 32 CUs, with AR_OPT_GRID
+    at one workgroup per CU (the forms whose workgroups must all be resident
+    fit those CUs): exact in every form, and closing the comm before
+    destroying the stream releases the workspace cleanly (the workspace is
+    recorded on every stream the comm ran on)."""
     torch, api, orc = env["torch"], env["api"], env["orc"]
     ncu = torch.cuda.get_device_properties(env["dev"]).multi_processor_count
     raw = api.ar_stream_create_cu_masked(range(32), ncu)
     try:
         st = torch.cuda.ExternalStream(raw, device=env["dev"])
         x = env["inputs"].draw("normal", 8, 1 << 16, seed=61)
-        comm = api.Comm(8, 1 << 16, "float32", device=env["dev"], launch="fused", grid=32)
+        if variant == "tree":
+            comm = api.Comm(8, 1 << 16, "float32", "tree", "ll", device=env["dev"], grid=32)
+            ref = orc.tree_allreduce(x)
+        else:
+            comm = api.Comm(8, 1 << 16, "float32", device=env["dev"], grid=32, **ring_opts(variant))
+            ref = orc.ring_allreduce(x)
         send = to_dev(env, x, "float32")
         recv = poisoned(env, x.shape, "float32")
         st.wait_stream(torch.cuda.current_stream())
         comm.allreduce(send, recv, stream=st)
         torch.cuda.synchronize()
-        assert from_dev(env, recv, "float32").tobytes() == orc.ring_allreduce(x).tobytes()
+        assert from_dev(env, recv, "float32").tobytes() == ref.tobytes()
         assert comm.check() == api.AR_SUCCESS
         comm.close()
         del comm
