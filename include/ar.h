@@ -20,7 +20,9 @@
  *  - One collective in flight per communicator: two calls on the same comm
  *    must be ordered on one stream (a team's internal resources cannot be
  *    shared by two concurrent collectives -- "Demystifying NVSHMEM ..."
- *    summary, paragraph on fence/quiet and teams).  All ranks of the comm take
+ *    summary, paragraph on fence/quiet and teams), and made from one host
+ *    thread at a time (a communicator's host state is not locked; different
+ *    communicators may be used from different threads).  All ranks of the comm take
  *    part in every call with the same count and dtype ("NCCL, NIXL, and
  *    Distributed GPU Communication", section on communication types).
  *  - Create a communicator once and reuse it; creation is the expensive part
@@ -114,10 +116,11 @@ typedef enum {
  * The pipelined ring, the ring with AR_LL and the tree need every workgroup
  * of a launch resident at once (the library sizes their grids to the
  * device's occupancy, capped by AR_OPT_GRID; on a stream held to fewer CUs
- * the caller sets AR_OPT_GRID, else the waits expire: AR_ERR_TIMEOUT).  Two such launches running at the same time on
- * different streams can each hold part of the device and wait for each
- * other until their bounded waits expire (AR_ERR_TIMEOUT): do not overlap
- * them with each other.  The step and fused forms have no such waits. */
+ * the caller sets AR_OPT_GRID, else the waits expire: AR_ERR_TIMEOUT).  Two
+ * such launches running at the same time on different streams can each hold
+ * part of the device and wait for each other until their bounded waits
+ * expire (AR_ERR_TIMEOUT): do not overlap them with each other.  The step
+ * and fused forms have no such waits. */
 typedef enum {
     AR_LAUNCH_AUTO = 0,
     AR_LAUNCH_STEP = 1,
