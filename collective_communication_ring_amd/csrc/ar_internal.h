@@ -156,7 +156,7 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t v, size_t n, hipStream_t s);
 
 // Last HIP error of the utility calls (ar_stream_*, ar_ll_pingpong).
-extern int g_util_hip_error;
+extern thread_local int g_util_hip_error;  // per host thread
 
 // The allocation-free all-reduce's device array (ar_noalloc.hip): 8 MiB per
 // GPU, the hand-off staging of 2,048 waves for bfloat16 (4,096 for 32-bit

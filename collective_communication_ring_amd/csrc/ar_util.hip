@@ -256,7 +256,7 @@ extern "C" int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int 
 // ---- CU-masked streams -------------------------------------------------------
 
 namespace ar {
-int g_util_hip_error = 0;  // last HIP error of the utility calls
+thread_local int g_util_hip_error = 0;  // last HIP error of this thread's utility calls
 }
 
 extern "C" int ar_stream_create_cu_masked(void** stream, uint32_t mask_words, const uint32_t* mask)

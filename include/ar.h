@@ -362,7 +362,8 @@ int ar_ll_pingpong(void* lines, uint32_t* result_dev, int iters, int xcd_apart,
 const char* ar_status_string(int status);
 
 /* Last hipError_t seen by this comm (0 if none); with comm == NULL, the last
- * one seen by the utility calls (ar_stream_*, ar_ll_pingpong). */
+ * one seen by the calling thread's utility calls (ar_stream_*,
+ * ar_ll_pingpong). */
 int ar_last_hip_error(ar_comm_t comm);
 
 #ifdef __cplusplus
