@@ -1186,6 +1186,45 @@ def test_concurrent_with_compute_on_another_stream(env, launch):
 
 # ---------------------------------------------------------------- random combinations
 
+def test_random_automatic_choices_match_oracle(env):
+    """60 seeded draws with the algorithm and the protocol both chosen by the
+    library (AR_AUTO, AR_PROTO_AUTO) over a random ring launch form, ranks,
+    dtype, operator, channels and sizes up to 2 MB per rank, so tree + LL,
+    ring + LL and the simple-protocol ring all run: each result bit-exact
+    against the oracle's replay of the schedule ar_plan reports."""
+    api, orc = env["api"], env["orc"]
+    rng = np.random.default_rng(20261204)
+    kinds = set()
+    for case in range(60):
+        R = int(rng.integers(2, 17))
+        dtype = ["int32", "float32", "bf16"][int(rng.integers(3))]
+        launch = ["pipelined", "step", "fused"][int(rng.integers(3))]
+        ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
+        op = ops[int(rng.integers(len(ops)))]
+        K = 1 if R == 2 else int(rng.integers(1, 3))
+        es = 2 if dtype == "bf16" else 4
+        # bytes per rank: half log-uniform over 8 B .. 2 MB, half uniform over
+        # 300 KB .. 2 MB, where ring + LL lies between the tree and the simple form
+        nbytes = np.exp(rng.uniform(np.log(8), np.log(2e6))) if case % 2 else rng.uniform(3e5, 2e6)
+        N = max(1, int(nbytes) // es)
+        what = (case, R, dtype, launch, op, K, N)
+        x = rand_input(env, dtype, R, N, seed=1000 + case)
+        comm = api.Comm(R, N, dtype, "auto", "auto", device=env["dev"], launch=launch, redop=op,
+                        channels=K)
+        algo, proto, _ = comm.plan(N)
+        kinds.add("tree" if algo == api.AR_TREE else "ring-ll" if proto == api.AR_LL else "simple")
+        if algo == api.AR_TREE:
+            ref = orc.tree_allreduce(x, dtype, op=op)
+        else:
+            ref = orc.ring_allreduce(x, dtype, op=op, strides=comm.channel_strides())
+        recv = poisoned(env, (R, N), dtype)
+        comm.allreduce(to_dev(env, x, dtype), recv)
+        assert from_dev(env, recv, dtype).tobytes() == ref.tobytes(), what
+        assert comm.check() == api.AR_SUCCESS, what
+        comm.close()
+    assert kinds == {"tree", "ring-ll", "simple"}, kinds
+
+
 def test_random_configurations_match_oracle(env):
     """200 seeded draws over the option space at once: ranks, ragged sizes,
     dtype, launch form (and the tree), ring channels, reduction operator, in
