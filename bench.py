@@ -291,6 +291,10 @@ def headline(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        # per-call event times of the same timed calls (back to back, so each
+        # also holds the gap before the next launch)
+        "ms_per_call_median": round(sorted(per)[len(per) // 2], 6),
+        "ms_per_call_min": round(min(per), 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
