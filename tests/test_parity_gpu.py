@@ -755,6 +755,40 @@ def _segment_samples(rng, N, R, m):
     return np.array(idx, dtype=np.int64)
 
 
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+def test_counts_beyond_2_32_elements_sampled(env, variant):
+    """R = 2 bf16 with 2^32 + 1000 elements (8 GiB) per rank, so element
+    indices pass both 2^31 and 2^32: every form, sampled outputs -- each
+    segment's ends and the elements around 2^31 and 2^32 -- against the
+    oracle (with two ranks the fold is one float32 addition, the same in
+    every order and layout), and no output element left unwritten."""
+    torch, api, orc = env["torch"], env["api"], env["orc"]
+    R, N = 2, (1 << 32) + 1000
+    g = torch.Generator(device=env["dev"])
+    g.manual_seed(32)
+    send = torch.randn((R, N), generator=g, device=env["dev"], dtype=torch.bfloat16)
+    recv = torch.full_like(send, float("nan"))
+    if variant == "tree":
+        comm = api.Comm(R, N, "bf16", "tree", "ll", device=env["dev"])
+    else:
+        comm = api.Comm(R, N, "bf16", device=env["dev"], **ring_opts(variant))
+    comm.allreduce(send, recv)
+    torch.cuda.synchronize()
+    assert comm.check() == api.AR_SUCCESS
+    S = -(-N // R)
+    picks = {0, 1, S - 1, S, S + 1, N - 2, N - 1}
+    picks |= {b + d for b in (1 << 31, 1 << 32) for d in range(-4, 4)}
+    idx = np.array(sorted(picks), dtype=np.int64)
+    ti = torch.from_numpy(idx).to(env["dev"])
+    xs = send[:, ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    ys = recv[:, ti].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert ys.tobytes() == orc.ring_allreduce(np.ascontiguousarray(xs), "bf16").tobytes()
+    assert not torch.isnan(recv).any().item()
+    comm.close()
+    del send, recv, comm
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("launch", ["auto", "step", "pipelined", "ll"])
 def test_ring_f32_r8_1GiB_sampled(env, launch):
     """R = 8, fp32, 1 GiB per rank (the sweep's largest size) in the launch form
