@@ -891,11 +891,10 @@ def test_measurement_utilities(env):
 # ---------------------------------------------------------------- operators, in place
 
 @pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
-@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
-@pytest.mark.parametrize("op", ["max", "min", "avg"])
+@pytest.mark.parametrize("dtype,op", [(d, o) for d in ("int32", "float32", "bf16")
+                                      for o in ("max", "min", "avg")
+                                      if not (d == "int32" and o == "avg")])  # refused: see below
 def test_reduction_operators(env, variant, dtype, op):
-    if op == "avg" and dtype == "int32":
-        pytest.skip("no integer average")
     api, orc = env["api"], env["orc"]
     for R, N in ((3, 1001), (8, 8 * 4096 + 24), (16, 16 * 5)):
         x = rand_input(env, dtype, R, N, seed=R * 7 + N)
