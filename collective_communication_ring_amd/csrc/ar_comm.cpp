@@ -410,19 +410,26 @@ uint64_t ll_grid_per_rank(uint64_t lines, int groups, int ncu, int ept, int64_t 
 // ring-LL lines and the ring-LL epoch word on the stream, so the launch
 // starts again from epoch 1.  The error word and the pipelined ring's 64-bit
 // flags are left alone.
+hipError_t ll_clear(ar_comm* c, hipStream_t st)
+{
+    hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,
+                                   (c->off_flags - c->off_up) / sizeof(uint64_t), st);
+    if (e == hipSuccess)
+        e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_rll), 0ull,
+                            (c->ws_need - c->off_rll) / sizeof(uint64_t), st);
+    if (e == hipSuccess)
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws) + kCtrlRingLLEpoch, 0u, 1, st);
+    if (e == hipSuccess)
+        c->ll_launches = 0;
+    return e;
+}
+
 int ll_launch_guard(ar_comm* c, hipStream_t st)
 {
     if (c->ll_launches >= kLLResetLaunches) {
-        hipError_t e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_up), 0ull,
-                                       (c->off_flags - c->off_up) / sizeof(uint64_t), st);
-        if (e == hipSuccess)
-            e = launch_fill_u64(reinterpret_cast<uint64_t*>(c->ws + c->off_rll), 0ull,
-                                (c->ws_need - c->off_rll) / sizeof(uint64_t), st);
-        if (e == hipSuccess)
-            e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws) + kCtrlRingLLEpoch, 0u, 1, st);
+        hipError_t e = ll_clear(c, st);
         if (e != hipSuccess)
             return fail_hip(c, e);
-        c->ll_launches = 0;
     }
     ++c->ll_launches;
     return AR_SUCCESS;
@@ -1046,7 +1053,13 @@ int ar_check(ar_comm_t c)
         return fail_hip(c, e);
     if (word == 0)
         return AR_SUCCESS;
+    // A bounded wait expired.  The tree's root advances a group's epoch even
+    // then, and a workgroup that started after that could have stored lines
+    // with the next launch's flag: clear the LL lines and epochs too, so the
+    // next calls start from clean state.
     e = launch_fill_u32(reinterpret_cast<uint32_t*>(c->ws) + kCtrlError, 0u, 1, c->last_stream);
+    if (e == hipSuccess)
+        e = ll_clear(c, c->last_stream);
     if (e == hipSuccess)
         e = hipStreamSynchronize(c->last_stream);
     if (e != hipSuccess)

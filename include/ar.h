@@ -257,8 +257,12 @@ int ar_all_gather(ar_comm_t comm, const void* send, void* recv, size_t sendcount
 
 /* Synchronize the comm's last stream and report its device error word:
  * AR_ERR_TIMEOUT when a bounded wait expired in an earlier call, else
- * AR_SUCCESS.  Clears the word.  No page defines this call: it is this
- * library's own boundary design (the kernels' bounded waits report here). */
+ * AR_SUCCESS.  Clears the word, and on AR_ERR_TIMEOUT also clears the
+ * comm's LL lines and epochs, so that later calls start from clean state.
+ * After a timeout the results of every call enqueued since the previous
+ * ar_check are not valid; call ar_check before relying on later ones.  No
+ * page defines this call: it is this library's own boundary design (the
+ * kernels' bounded waits report here). */
 int ar_check(ar_comm_t comm);
 
 /* Set / read one tunable (ar_option_t).  Unknown options or out-of-range

@@ -825,7 +825,8 @@ def test_ring_f32_r8_1GiB_sampled(env, launch):
 def test_watchdog_reports_timeout_and_recovers(env, variant, mute):
     """Forced from the host: one logical rank skips publishing, so its
     consumers' bounded waits (5 ms here) expire.  The kernel still finishes,
-    ar_check reports AR_ERR_TIMEOUT once, and the next call is correct.  Rank
+    ar_check reports AR_ERR_TIMEOUT once (clearing the LL lines and epochs
+    too), and the next call is correct.  Rank
     0 is tree A's root: muted, it sends nothing down, but must still advance
     its line groups' epochs so that the next call uses fresh flags."""
     import time
@@ -849,6 +850,9 @@ def test_watchdog_reports_timeout_and_recovers(env, variant, mute):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     assert comm.check() == api.AR_ERR_TIMEOUT
+    if variant in ("tree", "ll"):
+        # the LL lines and epochs were cleared with the error word
+        assert comm.get_option(api.AR_OPT_DEBUG_LL_LAUNCHES) == 0
     assert comm.check() == api.AR_SUCCESS  # the error word was cleared
     assert dt < 1.0, dt
     comm.set_option(api.AR_OPT_DEBUG_MUTE_RANK, -1)
