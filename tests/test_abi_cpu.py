@@ -41,6 +41,21 @@ def test_every_declared_symbol_is_exported(api):
     assert not missing, missing
 
 
+def test_python_constants_match_the_header(api):
+    """Every enumerator ar.h defines has the same value in the Python binding."""
+    src = open(os.path.join(ROOT, "include", "ar.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    vals = {}
+    for body in re.findall(r"typedef enum\s*\{(.*?)\}", src, flags=re.S):
+        for name, v in re.findall(r"(AR_[A-Z0-9_]+)\s*=\s*(-?\d+)", body):
+            vals[name] = int(v)
+    assert len(vals) > 30
+    missing = [n for n in vals if n != "AR_COST_FORMS" and not hasattr(api, n)]
+    assert not missing, missing
+    wrong = {n: (v, getattr(api, n)) for n, v in vals.items() if hasattr(api, n) and getattr(api, n) != v}
+    assert not wrong, wrong
+
+
 def test_init_argument_checks(api):
     import ctypes
     L = api.lib()
