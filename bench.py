@@ -18,9 +18,9 @@ hand-offs stay in the XCD's L2).  One step = one all-reduce of the whole
            most of them served by L2 in the fused form (not an HBM rate).
 
 The same line carries, unless --no-extras: the message-size sweep (R = 8
-fp32, 8 B .. 1 GiB per rank) with its alpha-beta fit; tree + LL against the
-ring forms (R = 8 fp32, 8 B .. 256 KiB) with the crossovers and AR_AUTO's
-choices; a few 25 MiB gradient buckets (R = 16 bf16 reduce-scatter,
+fp32, 8 B .. 1 GiB per rank) with its alpha-beta fit; the trees (fused, and
+with LL) against the ring forms (R = 8 fp32, 8 B .. 256 KiB) with the
+crossovers and AR_AUTO's choices; a few 25 MiB gradient buckets (R = 16 bf16 reduce-scatter,
 all-gather, all-reduce, checked against the oracle); the pipelined ring (simple protocol, 512 KiB chunks)
 on the headline workload; and a 512 MiB copy as the streaming ceiling.
 cpu_baseline times the oracle on one thread and on all host cores.
@@ -461,6 +461,7 @@ def sweep_fit(torch, api, measure, inputs, np, max_bytes=1 << 30, launch="fused"
 
 
 TVR_VARIANTS = [("tree-ll", dict(algo="tree", proto="ll")),
+                ("tree-fused", dict(algo="tree", proto="simple", launch="fused")),
                 ("ring-fused", dict(algo="ring", proto="simple", launch="fused")),
                 ("ring-pipelined", dict(algo="ring", proto="simple", launch="pipelined")),
                 ("ring-ll", dict(algo="ring", proto="ll")),
@@ -469,9 +470,10 @@ TVR_VARIANTS = [("tree-ll", dict(algo="tree", proto="ll")),
 
 def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eager=False):
     """Tree against ring: R = 8 fp32 U[-1,1), 8 B .. 256 KiB per rank (16 sizes): the
-    double binary tree with LL against every ring form (5 warm-up + 20 timed
-    calls per size, one graph replay); an alpha-beta fit per variant, the
-    crossover of the tree with each ring form (measured and from the fits),
+    double binary tree (fused, and with LL) against every ring form (5 warm-up
+    + 20 timed calls per size, one graph replay); an alpha-beta fit per
+    variant, the crossover of each ring form with its tree (the fused tree for
+    the fused ring, the LL tree for the others; measured and from the fits),
     and AR_AUTO's choice before and after loading the fitted lines (for the
     hand-off forms also with AR_PROTO_AUTO: tree + LL, ring + LL or the
     simple protocol)."""
@@ -495,7 +497,7 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
             res[name].append(round(timed_point(lambda: c.allreduce(sv, rv), torch, eager) * 1e3, 3))
             if N in (counts[0], counts[len(counts) // 2], counts[-1]):
                 ref, _, _, _ = cpu_baseline_leg(
-                    (lambda o: o.tree_allreduce(xs)) if name == "tree-ll"
+                    (lambda o: o.tree_allreduce(xs)) if name.startswith("tree")
                     else (lambda o: o.ring_allreduce(xs)), 0.0, 1, threads=threads)
                 exact &= rv.cpu().numpy().tobytes() == ref.tobytes()
     for c in comms.values():
@@ -503,16 +505,22 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
         c.close()
     sizes = [n * s for n in counts]
     fits = {name: measure.fit_alpha_beta(sizes, [t / 1e6 for t in ts]) for name, ts in res.items()}
+    # the tree AR_AUTO weighs against each ring form: the fused tree beside
+    # the fused ring, the LL tree beside the forms that hand off between ranks
+    tree_of = lambda name: "tree-fused" if name == "ring-fused" else "tree-ll"
     crossover = {}
-    for name, _ in TVR_VARIANTS[1:]:
-        # the smallest size from which this ring form is faster than the tree
+    for name, _ in TVR_VARIANTS:
+        if name.startswith("tree"):
+            continue
+        # the smallest size from which this ring form is faster than its tree
         # at every larger size of the range
+        tr = tree_of(name)
         meas = None
         for i in range(len(sizes)):
-            if all(res[name][j] < res["tree-ll"][j] for j in range(i, len(sizes))):
+            if all(res[name][j] < res[tr][j] for j in range(i, len(sizes))):
                 meas = sizes[i]
                 break
-        fitted = measure.crossover_bytes(fits["tree-ll"], fits[name])
+        fitted = measure.crossover_bytes(fits[tr], fits[name])
         crossover[name] = dict(measured_bytes=meas,
                                fit_bytes=round(fitted) if fitted is not None else None)
     # AR_AUTO's choice for each ring form: with the library's default lines,
@@ -531,7 +539,7 @@ def tree_vs_ring_fit(torch, api, measure, inputs, np, max_bytes=256 * 1024, eage
             probe.set_option(api.AR_OPT_LAUNCH, f["launch"])
             probe.set_option(api.AR_OPT_PROTO, f["proto"])
             plan = [probe.plan(n)[0] for n in counts]
-            faster = [api.AR_TREE if res["tree-ll"][i] < res[name][i] else api.AR_RING
+            faster = [api.AR_TREE if res[tree_of(name)][i] < res[name][i] else api.AR_RING
                       for i in range(len(counts))]
             out[name] = dict(tree_max_bytes=api.ar_auto_tree_max_bytes(probe.handle),
                              matches_measured=sum(p == q for p, q in zip(plan, faster)),

@@ -26,10 +26,10 @@ AR_LAUNCH_AUTO, AR_LAUNCH_STEP, AR_LAUNCH_FUSED, AR_LAUNCH_PIPELINED = 0, 1, 2, 
  AR_OPT_CHANNELS, AR_OPT_DEBUG_LL_LAUNCHES) = range(12)
 AR_SUM, AR_MAX, AR_MIN, AR_AVG = 0, 1, 2, 3
 (AR_COST_TREE_LL, AR_COST_RING_FUSED, AR_COST_RING_PIPELINED, AR_COST_RING_STEP,
- AR_COST_RING_LL) = range(5)
+ AR_COST_RING_LL, AR_COST_TREE_FUSED) = range(6)
 COST_FORMS = {"tree-ll": AR_COST_TREE_LL, "ring-fused": AR_COST_RING_FUSED,
               "ring-pipelined": AR_COST_RING_PIPELINED, "ring-step": AR_COST_RING_STEP,
-              "ring-ll": AR_COST_RING_LL}
+              "ring-ll": AR_COST_RING_LL, "tree-fused": AR_COST_TREE_FUSED}
 REDOPS = {"sum": AR_SUM, "max": AR_MAX, "min": AR_MIN, "avg": AR_AVG}
 
 DTYPES = {"int32": AR_INT32, "float32": AR_FLOAT32, "bf16": AR_BF16}

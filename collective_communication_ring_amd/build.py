@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libar.so")
 SOURCES = ["ar_comm.cpp", "ar_ring.hip", "ar_fused.hip", "ar_pipe.hip", "ar_ring_ll.hip", "ar_tree.hip",
-           "ar_util.hip", "ar_noalloc.hip"]
+           "ar_tree_fused.hip", "ar_util.hip", "ar_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -16,6 +16,7 @@
 
 #include "ar.h"
 #include "ar_internal.h"
+#include "ar_tree_fused.h"
 
 using namespace ar;
 
@@ -46,6 +47,7 @@ constexpr CostLine kDefaultCost[AR_COST_FORMS] = {
     {21.7, 278.0},  // ring, pipelined (simple protocol: ready flags)
     {28.9, 179.0},  // ring, one launch per step
     {11.6, 63.2},   // ring + LL
+    {2.8, 316.0},   // tree, fused
 };
 constexpr uint64_t kTreeLinesCap = 1u << 16;         // LL lines per (tree, rank) per launch
 constexpr uint64_t kMaxChunkBytes = 1ull << 30;      // pipelined ring: largest chunk
@@ -144,7 +146,7 @@ struct ar_comm {
     int64_t debug = 0;
     int64_t tree_max_bytes = -1;  // AR_AUTO: -1 = by the cost model, else a fixed threshold
     CostLine cost[AR_COST_FORMS] = {kDefaultCost[0], kDefaultCost[1], kDefaultCost[2],
-                                    kDefaultCost[3], kDefaultCost[4]};
+                                    kDefaultCost[3], kDefaultCost[4], kDefaultCost[5]};
     int64_t mute_rank = -1;  // testing the watchdog only
     int64_t redop = AR_SUM;
     int64_t channels = 1;
@@ -248,6 +250,23 @@ int simple_ring_form(const ar_comm* c)
 
 double cost_us(const CostLine& l, double bytes) { return l.alpha_us + bytes / (l.bw_gbps * 1e3); }
 
+// Does a tree call take the fused form (one launch, hops through the nodes'
+// output rows) rather than the LL form?  With the fused launch, a protocol
+// other than LL, a 32-bit type (a bfloat16 row cannot hold a float32
+// partial) and at most kTreeFusedMaxRanks ranks (the kernel is compiled for
+// each R).
+bool tree_fused_ok(const ar_comm* c)
+{
+    return c->proto != AR_LL && resolve_launch(c) == AR_LAUNCH_FUSED && c->dtype != AR_BF16 &&
+           c->R <= kTreeFusedMaxRanks;
+}
+
+// The cost-model line of the tree as this comm would run it.
+int tree_cost_form(const ar_comm* c)
+{
+    return tree_fused_ok(c) ? AR_COST_TREE_FUSED : AR_COST_TREE_LL;
+}
+
 // The ring's protocol for `bytes` per rank: the comm's, or with
 // AR_PROTO_AUTO, LL where the ring + LL line is strictly below the
 // simple-protocol form's.
@@ -279,14 +298,18 @@ int resolve_algo(const ar_comm* c, size_t count)
     if (c->tree_max_bytes >= 0)
         return bytes <= (double)c->tree_max_bytes ? AR_TREE : AR_RING;
     const int form = ring_proto(c, bytes) == AR_LL ? AR_COST_RING_LL : simple_ring_form(c);
-    return cost_us(c->cost[AR_COST_TREE_LL], bytes) < cost_us(c->cost[form], bytes) ? AR_TREE
-                                                                                     : AR_RING;
+    return cost_us(c->cost[tree_cost_form(c)], bytes) < cost_us(c->cost[form], bytes) ? AR_TREE
+                                                                                        : AR_RING;
 }
 
-// The protocol of a call whose algorithm is `algo` (the tree's lines are LL).
+// The protocol of a call whose algorithm is `algo` (the LL tree moves LL
+// lines; the fused tree, like the fused ring, has no protocol of its own and
+// reports AR_SIMPLE).
 int resolve_proto(const ar_comm* c, size_t count, int algo)
 {
-    return algo == AR_TREE ? AR_LL : ring_proto(c, call_bytes(c, count));
+    if (algo == AR_TREE)
+        return tree_fused_ok(c) ? AR_SIMPLE : AR_LL;
+    return ring_proto(c, call_bytes(c, count));
 }
 
 // The per-rank sizes n >= 0 (bytes) at which line a is strictly below line
@@ -719,6 +742,36 @@ int run_tree(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t s
     return AR_SUCCESS;
 }
 
+// The fused tree: one launch, tree A's elements on the first workgroups and
+// tree B's on the rest, one element per thread (each a grid-stride loop).
+int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStream_t st)
+{
+    TreeFusedArgs a{};
+    a.send = send;
+    a.out = recv;
+    a.N = N;
+    a.H = (N + 1) / 2;
+    a.redop = (int)c->redop;
+    // up to 4 workgroups per CU in all (or AR_OPT_GRID), shared by the two
+    // halves in proportion, at least one for a half that has elements
+    const int64_t total = c->grid > 0 ? c->grid : 4 * (int64_t)c->ncu;
+    const uint64_t ha = a.H, hb = N - a.H;
+    const uint64_t need_a = (ha + kBlock - 1) / kBlock, need_b = (hb + kBlock - 1) / kBlock;
+    const uint64_t cap_a = std::max<uint64_t>(1, (uint64_t)total / 2);
+    const uint64_t ga = std::min<uint64_t>(need_a, cap_a);
+    const uint64_t gb = hb ? std::min<uint64_t>(need_b, std::max<uint64_t>(1, (uint64_t)total - ga))
+                           : 0;
+    a.blocks_a = (int)ga;
+    const int grid = (int)(ga + gb);
+    hipError_t e = launch_tree_fused(c->dtype, c->R, a, grid, st);
+    if (c->debug)
+        std::fprintf(stderr, "ar: tree-fused R=%d N=%llu dtype=%s grid=%d\n", c->R,
+                     (unsigned long long)N, dtype_name(c->dtype), grid);
+    if (e != hipSuccess)
+        return fail_hip(c, e);
+    return AR_SUCCESS;
+}
+
 // A call's run options: the workspace's hand-off region, where the
 // collectives stage hand-offs, and the ring protocol for rows of `count`.
 RunOpts ws_opts(const ar_comm* c, size_t count)
@@ -891,7 +944,8 @@ int ar_allreduce(ar_comm_t c, const void* send, void* recv, size_t count, void* 
         return AR_SUCCESS;
     const int algo = resolve_algo(c, count);
     if (algo == AR_TREE)
-        return run_tree(c, send, recv, count, st);
+        return tree_fused_ok(c) ? run_tree_fused(c, send, recv, count, st)
+                                : run_tree(c, send, recv, count, st);
     RingArgs a{};
     a.send = send;
     // A segment's running value lives in its owner's output row when the
@@ -1161,7 +1215,10 @@ int ar_plan(ar_comm_t c, size_t count, int* algo, int* proto, int* launch)
         return AR_ERR_INVALID_ARG;
     *algo = resolve_algo(c, count);
     *proto = resolve_proto(c, count, *algo);
-    *launch = (*algo == AR_TREE || *proto == AR_LL) ? AR_LAUNCH_AUTO : resolve_launch(c);
+    if (*algo == AR_TREE)
+        *launch = tree_fused_ok(c) ? AR_LAUNCH_FUSED : AR_LAUNCH_AUTO;
+    else
+        *launch = *proto == AR_LL ? AR_LAUNCH_AUTO : resolve_launch(c);
     return AR_SUCCESS;
 }
 
@@ -1193,7 +1250,7 @@ int64_t ar_auto_tree_max_bytes(ar_comm_t c)
     // the sizes at which the tree's line is below the ring's as calls would
     // run it: below the simple form's and, for ring + LL or AR_PROTO_AUTO
     // (the ring then costs the lower of its two lines), below ring + LL's
-    const CostLine t = c->cost[AR_COST_TREE_LL];
+    const CostLine t = c->cost[tree_cost_form(c)];
     const Span simple = below(t, c->cost[simple_ring_form(c)]);
     const Span ll = below(t, c->cost[AR_COST_RING_LL]);
     const Span s = c->proto == AR_SIMPLE ? simple : c->proto == AR_LL ? ll : intersect(simple, ll);

@@ -1,0 +1,32 @@
+// ar_tree_fused.h -- arguments of the fused double binary tree, shared by the
+// host (ar_comm.cpp) and the kernel (ar_tree_fused.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar_internal.h"
+
+namespace ar {
+
+// The fused tree is compiled for R = 2 .. kTreeFusedMaxRanks, each R with its
+// trees fixed at compile time.
+constexpr int kTreeFusedMaxRanks = 16;
+
+// One launch covers the whole collective.  Workgroups [0, blocks_a) take the
+// elements [0, H) of tree A, the others [H, N) of tree B, one element per
+// thread (a grid-stride loop on each half).
+struct TreeFusedArgs {
+    const void* send;
+    void* out;
+    uint64_t N;
+    uint64_t H;
+    int redop;
+    int blocks_a;  // workgroups on tree A's half
+};
+
+// hipErrorInvalidValue for a dtype other than int32/float32, an R outside
+// 2 .. kTreeFusedMaxRanks, or an integer AR_AVG.
+hipError_t launch_tree_fused(int dtype, int R, const TreeFusedArgs& a, int grid, hipStream_t st);
+
+}  // namespace ar

@@ -54,14 +54,21 @@ typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
  * AR_TREE: double binary tree -- two complementary binary trees working at
  * once, each reducing and broadcasting half of the elements ("NCCL and
  * NVSHMEM -- two GPU communication models, side by side", section "double
- * binary tree").  AR_AUTO picks by message size: tree for small messages,
- * ring for large ones (same page: tree for small messages, ring for large,
- * chosen automatically).  The choice compares two lines of a cost model
- * (ar_set_cost): the tree's and the one of the ring launch form the call
- * would use.  With the default fused ring, whose latency floor is below the
- * tree's on one GPU, the model keeps the ring at every size; with a form in
+ * binary tree").  It runs in one of two forms with the same fold order (so
+ * the same bits): fused -- one launch, each thread carrying an element up
+ * and down its tree through the nodes' output rows -- when the launch is
+ * fused (AR_LAUNCH_AUTO is), the protocol is not AR_LL, the type is 32-bit
+ * and R <= 16; else with LL lines between the nodes' workgroups.
+ * AR_AUTO picks by message size: tree for small messages, ring for large ones
+ * (same page: tree for small messages, ring for large, chosen
+ * automatically).  The choice compares two lines of a cost model
+ * (ar_set_cost): that of the tree in the form the call would run and that of
+ * the ring launch form the call would use.  With the defaults (fused forms,
+ * R = 8, float32) the tree takes messages up to about 3 MB per rank; a
+ * bfloat16 comm, or one of more than 16 ranks, has only the LL tree, whose
+ * line is above the fused ring's: the ring at every size.  With a form in
  * which every step is a hand-off between ranks (AR_LAUNCH_STEP,
- * AR_LAUNCH_PIPELINED, AR_LL) it sends small messages by tree. */
+ * AR_LAUNCH_PIPELINED, AR_LL) the LL tree takes small messages. */
 typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
 
 /* AR_SIMPLE: bulk data, then a release, then a ready flag (or a kernel
@@ -71,8 +78,9 @@ typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
  * AR_PROTO_AUTO: chosen per call from the same cost model as AR_AUTO
  * (ar_set_cost): the ring runs with AR_LL where the ring + LL line is
  * strictly below the line of the comm's simple-protocol launch form at the
- * call's size, else with AR_SIMPLE; the tree always moves LL lines.  With
- * AR_AUTO the tree is then weighed against that cheaper ring.  The pages
+ * call's size, else with AR_SIMPLE; the tree takes its fused form where it
+ * can (see AR_TREE), else LL lines.  With AR_AUTO the tree is then weighed
+ * against that cheaper ring.  The pages
  * pick the algorithm by size ("NCCL and NVSHMEM -- two GPU communication
  * models, side by side", ring vs tree); picking the protocol by the same
  * model is this library's extension.  With the default fused ring the model
@@ -113,14 +121,16 @@ typedef enum {
  *   the consumer polls the flag, then reads coherently) -- the simple
  *   protocol.
  * AR_LAUNCH_AUTO: the library's choice (the default).
- * The pipelined ring, the ring with AR_LL and the tree need every workgroup
+ * A tree call takes its fused form with AR_LAUNCH_FUSED or AR_LAUNCH_AUTO
+ * (see AR_TREE), its LL form with the others.
+ * The pipelined ring, the ring with AR_LL and the LL tree need every workgroup
  * of a launch resident at once (the library sizes their grids to the
  * device's occupancy, capped by AR_OPT_GRID; on a stream held to fewer CUs
  * the caller sets AR_OPT_GRID, else the waits expire: AR_ERR_TIMEOUT).  Two
  * such launches running at the same time on different streams can each hold
  * part of the device and wait for each other until their bounded waits
  * expire (AR_ERR_TIMEOUT): do not overlap them with each other.  The step
- * and fused forms have no such waits. */
+ * and fused forms (ring and tree) have no such waits. */
 typedef enum {
     AR_LAUNCH_AUTO = 0,
     AR_LAUNCH_STEP = 1,
@@ -272,8 +282,9 @@ int ar_get_option(ar_comm_t comm, int option, int64_t* value);
 
 /* Resolved algorithm, protocol and launch that a call with `count` elements
  * per rank would use (values of ar_algo_t, ar_proto_t, ar_launch_t; never
- * AR_AUTO or AR_PROTO_AUTO; the launch is AR_LAUNCH_AUTO for the tree and
- * for ring + LL, which have one form each).  For reduce-scatter and
+ * AR_AUTO or AR_PROTO_AUTO; the launch is AR_LAUNCH_AUTO for the LL tree
+ * and for ring + LL, which have one form each; the fused tree reports
+ * AR_SIMPLE and AR_LAUNCH_FUSED).  For reduce-scatter and
  * all-gather the model's size is the full row per rank (R times the shard). */
 int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
 
@@ -281,10 +292,14 @@ int ar_plan(ar_comm_t comm, size_t count, int* algo, int* proto, int* launch);
  * line T(n) = alpha_us + n / (bw_gbps * 1e3) microseconds, n = bytes per
  * rank -- the alpha-beta model ("NCCL and NVSHMEM -- two GPU communication
  * models, side by side", cost-model paragraph: alpha is the latency floor,
- * beta the reciprocal bandwidth).  AR_AUTO takes the tree where the tree's
- * line is strictly below the line of the ring form the call would use.  The
- * defaults are fits measured on MI355X at R = 8, float32; a caller with its
- * own measurements (other R, dtype or machine) sets them here.
+ * beta the reciprocal bandwidth).  AR_AUTO takes the tree where the line of
+ * the tree's form (AR_COST_TREE_FUSED or AR_COST_TREE_LL) is strictly below
+ * the line of the ring form the call would use.  The defaults are fits
+ * measured on MI355X at R = 8, float32 (the fused tree's set so that its
+ * crossing with the fused ring lies where the measured times cross, between
+ * 2 and 4 MiB per rank: its time is flat to 512 KiB, which no one line
+ * follows); a caller with its own measurements (other R, dtype or machine)
+ * sets them here.
  * ar_set_cost: AR_ERR_INVALID_ARG for an unknown form, alpha_us < 0,
  *   bw_gbps <= 0 or a NaN.
  * ar_auto_tree_max_bytes: under the comm's current options, the largest
@@ -299,7 +314,8 @@ typedef enum {
     AR_COST_RING_PIPELINED = 2,
     AR_COST_RING_STEP = 3,
     AR_COST_RING_LL = 4,
-    AR_COST_FORMS = 5
+    AR_COST_TREE_FUSED = 5,
+    AR_COST_FORMS = 6
 } ar_cost_form_t;
 int ar_set_cost(ar_comm_t comm, int form, double alpha_us, double bw_gbps);
 int ar_get_cost(ar_comm_t comm, int form, double* alpha_us, double* bw_gbps);

@@ -106,12 +106,28 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
     c = api.ar_init(8, 1 << 22, api.AR_FLOAT32, api.AR_AUTO)
     try:
         assert api.ar_get_option(c, api.AR_OPT_TREE_MAX_BYTES) == -1  # by the cost model
-        # the default fused ring's line is below the tree's at every size
-        ta, tb = api.ar_get_cost(c, api.AR_COST_TREE_LL)
+        # the default launch: the fused tree's line against the fused ring's,
+        # crossing between 2 and 4 MiB per rank
+        ua, ub = api.ar_get_cost(c, api.AR_COST_TREE_FUSED)
         fa, fb = api.ar_get_cost(c, api.AR_COST_RING_FUSED)
+        n = api.ar_auto_tree_max_bytes(c)
+        cross = (fa - ua) / (1e-3 / ub - 1e-3 / fb)
+        assert 2 << 20 < n <= cross < n + 2 and cross < 4 << 20
+        assert api.ar_plan(c, 1)[:3] == (api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+        assert api.ar_plan(c, n // 4)[0] == api.AR_TREE
+        assert api.ar_plan(c, n // 4 + 1)[:3] == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+        # the LL tree's line is above the fused ring's at every size, so where
+        # the tree cannot be fused (bfloat16, or more than 16 ranks) AUTO keeps
+        # the ring
+        ta, tb = api.ar_get_cost(c, api.AR_COST_TREE_LL)
         assert fa < ta and fb > tb
-        assert api.ar_auto_tree_max_bytes(c) == 0
-        assert api.ar_plan(c, 1)[0] == api.AR_RING and api.ar_plan(c, 1 << 22)[0] == api.AR_RING
+        for R, dt in ((8, api.AR_BF16), (17, api.AR_FLOAT32)):
+            d = api.ar_init(R, 1 << 22, dt, api.AR_AUTO)
+            try:
+                assert api.ar_auto_tree_max_bytes(d) == 0
+                assert api.ar_plan(d, 1)[0] == api.AR_RING
+            finally:
+                api.ar_destroy(d)
         # with the pipelined ring the lines cross: tree below, ring above
         api.ar_set_option(c, api.AR_OPT_LAUNCH, api.AR_LAUNCH_PIPELINED)
         n = api.ar_auto_tree_max_bytes(c)
@@ -139,7 +155,7 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
         api.ar_set_option(c, api.AR_OPT_TREE_MAX_BYTES, -1)
         assert api.ar_auto_tree_max_bytes(c) < n
         # bad models are refused
-        for form, a, b in ((5, 1.0, 1.0), (-1, 1.0, 1.0), (0, -1.0, 1.0), (0, 1.0, 0.0),
+        for form, a, b in ((6, 1.0, 1.0), (-1, 1.0, 1.0), (0, -1.0, 1.0), (0, 1.0, 0.0),
                            (0, float("nan"), 1.0), (0, 1.0, float("nan"))):
             with pytest.raises(api.ArError):
                 api.ar_set_cost(c, form, a, b)
@@ -166,10 +182,16 @@ def test_plan_protocol_auto(api):
         assert api.ar_get_option(c, api.AR_OPT_PROTO) == api.AR_PROTO_AUTO
         tree = api.ar_get_cost(c, api.AR_COST_TREE_LL)
         ll = api.ar_get_cost(c, api.AR_COST_RING_LL)
-        # the default fused ring: simple protocol and ring at every size
-        for n in (1, 1000, 1 << 20, 1 << 24):
+        # the default fused launch: ring + LL never beats the fused ring, so
+        # the fused tree below its crossing with the fused ring, the fused ring
+        # above
+        fused = (api.ar_get_cost(c, api.AR_COST_TREE_FUSED), api.ar_get_cost(c, api.AR_COST_RING_FUSED))
+        t_max = api.ar_auto_tree_max_bytes(c)
+        assert abs(t_max - _line_cross(*fused)) < 2
+        for n in (1, 1000, t_max // 4):
+            assert api.ar_plan(c, n) == (api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+        for n in (t_max // 4 + 1, 1 << 20, 1 << 24):
             assert api.ar_plan(c, n) == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
-        assert api.ar_auto_tree_max_bytes(c) == 0
         for launch, form in ((api.AR_LAUNCH_PIPELINED, api.AR_COST_RING_PIPELINED),
                              (api.AR_LAUNCH_STEP, api.AR_COST_RING_STEP)):
             api.ar_set_option(c, api.AR_OPT_LAUNCH, launch)

@@ -3,6 +3,8 @@ inputs.  The oracle replays the same ring/tree order, so every dtype is
 expected bit-exact; float32 is also held to the stated tolerance against the
 float64 sum (1e-6 relative + 1e-6*R absolute), bfloat16 to 1e-2 relative.
 """
+import re
+
 import numpy as np
 import pytest
 
@@ -409,6 +411,46 @@ def test_tree_ll_ragged(env, dtype, R):
         ref = orc.tree_allreduce(x, dtype)
         for y in outs:
             assert y.tobytes() == ref.tobytes(), (R, N)
+
+
+@pytest.mark.parametrize("dtype", ["int32", "float32"])
+@pytest.mark.parametrize("R", list(range(2, 17)) + [17, 64])
+def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
+    """The fused tree (a tree call with the fused launch and a protocol other
+    than LL, 32-bit types, R <= 16, the trees compiled in for each R): the LL
+    tree's fold order, so bit-exact against the oracle's tree -- every
+    operator, ragged sizes, in place, and a grid of 3 workgroups that loops
+    over the elements -- and the library's debug line shows the fused kernel
+    ran.  Beyond 16 ranks the same call takes the LL tree."""
+    api, orc = env["api"], env["orc"]
+    fused = R <= 16
+    ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
+    Nmax = 4 * 4096 + 37
+    # (a grid of 3 for the fused form only: the LL tree needs 2R resident
+    # workgroups and refuses a smaller grid)
+    for op, grid in [(op, None) for op in ops] + ([("sum", 3)] if fused else []):
+        opts = {} if grid is None else {"grid": grid}
+        comm = api.Comm(R, Nmax, dtype, "tree", "simple", device=env["dev"], launch="fused",
+                        redop=op, debug=1, **opts)
+        want = ((api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED) if fused
+                else (api.AR_TREE, api.AR_LL, api.AR_LAUNCH_AUTO))
+        assert comm.plan(Nmax)[:3] == want
+        for N in (1, 2, 7, 1000, 4097, Nmax):
+            x = rand_input(env, dtype, R, N, seed=R * 131 + N + len(op))
+            ref = orc.tree_allreduce(x, dtype, op=op)
+            capfd.readouterr()
+            send = to_dev(env, x, dtype)
+            recv = poisoned(env, (R, N), dtype)
+            comm.allreduce(send, recv)
+            assert from_dev(env, recv, dtype).tobytes() == ref.tobytes(), (op, grid, N)
+            err = capfd.readouterr().err
+            assert ("ar: tree-fused" in err) == fused and ("ar: tree-LL" in err) != fused, err
+            if fused and grid is not None:
+                assert int(re.search(r"tree-fused .* grid=(\d+)", err).group(1)) <= grid, err
+            comm.allreduce(send, send)  # in place
+            assert from_dev(env, send, dtype).tobytes() == ref.tobytes(), (op, grid, N, "in place")
+        assert comm.check() == api.AR_SUCCESS
+        comm.close()
 
 
 def test_tree_epochs_across_sizes(env):
@@ -1226,9 +1268,10 @@ def test_concurrent_with_compute_on_another_stream(env, launch):
 def test_random_automatic_choices_match_oracle(env):
     """60 seeded draws with the algorithm and the protocol both chosen by the
     library (AR_AUTO, AR_PROTO_AUTO) over a random ring launch form, ranks,
-    dtype, operator, channels and sizes up to 2 MB per rank, so tree + LL,
-    ring + LL and the simple-protocol ring all run: each result bit-exact
-    against the oracle's replay of the schedule ar_plan reports."""
+    dtype, operator, channels and sizes up to 2 MB per rank, so the fused
+    tree, tree + LL, ring + LL and the simple-protocol ring all run: each
+    result bit-exact against the oracle's replay of the schedule ar_plan
+    reports."""
     api, orc = env["api"], env["orc"]
     rng = np.random.default_rng(20261204)
     kinds = set()
@@ -1248,8 +1291,9 @@ def test_random_automatic_choices_match_oracle(env):
         x = rand_input(env, dtype, R, N, seed=1000 + case)
         comm = api.Comm(R, N, dtype, "auto", "auto", device=env["dev"], launch=launch, redop=op,
                         channels=K)
-        algo, proto, _ = comm.plan(N)
-        kinds.add("tree" if algo == api.AR_TREE else "ring-ll" if proto == api.AR_LL else "simple")
+        algo, proto, plaunch = comm.plan(N)
+        kinds.add(("tree-fused" if plaunch == api.AR_LAUNCH_FUSED else "tree") if algo == api.AR_TREE
+                  else "ring-ll" if proto == api.AR_LL else "simple")
         if algo == api.AR_TREE:
             ref = orc.tree_allreduce(x, dtype, op=op)
         else:
@@ -1259,30 +1303,34 @@ def test_random_automatic_choices_match_oracle(env):
         assert from_dev(env, recv, dtype).tobytes() == ref.tobytes(), what
         assert comm.check() == api.AR_SUCCESS, what
         comm.close()
-    assert kinds == {"tree", "ring-ll", "simple"}, kinds
+    assert kinds == {"tree", "tree-fused", "ring-ll", "simple"}, kinds
 
 
 def test_random_configurations_match_oracle(env):
     """200 seeded draws over the option space at once: ranks, ragged sizes,
-    dtype, launch form (and the tree), ring channels, reduction operator, in
-    place, and all-reduce or reduce-scatter then all-gather; each result
-    bit-exact against the oracle's replay of the same schedule."""
+    dtype, launch form (and the LL or fused tree), ring channels, reduction
+    operator, in place, and all-reduce or reduce-scatter then all-gather; each
+    result bit-exact against the oracle's replay of the same schedule."""
     api, orc = env["api"], env["orc"]
     rng = np.random.default_rng(20261203)
     for case in range(200):
         R = int(rng.integers(2, 17))
         dtype = ["int32", "float32", "bf16"][int(rng.integers(3))]
-        variant = (LAUNCHES + ["tree"])[int(rng.integers(len(LAUNCHES) + 1))]
+        variant = (LAUNCHES + ["tree", "tree-fused"])[int(rng.integers(len(LAUNCHES) + 2))]
         ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
         op = ops[int(rng.integers(len(ops)))]
-        coll = "ar" if variant == "tree" else ["ar", "rs_ag"][int(rng.integers(2))]
-        K = 1 if variant == "tree" or R == 2 else int(rng.integers(1, 3))  # R = 2 has one stride
+        tree = variant.startswith("tree")
+        coll = "ar" if tree else ["ar", "rs_ag"][int(rng.integers(2))]
+        K = 1 if tree or R == 2 else int(rng.integers(1, 3))  # R = 2 has one stride
         what = (case, R, dtype, variant, op, coll, K)
         if coll == "ar":
             N = int(np.exp(rng.uniform(0, np.log(300000))))
             x = rand_input(env, dtype, R, N, seed=case)
-            if variant == "tree":
-                comm = api.Comm(R, N, dtype, "tree", "ll", device=env["dev"], redop=op)
+            if tree:
+                # the fused tree for 32-bit types and R <= 16, else the LL tree
+                tree_opts = (dict(proto="simple", launch="fused") if variant == "tree-fused"
+                             else dict(proto="ll"))
+                comm = api.Comm(R, N, dtype, "tree", device=env["dev"], redop=op, **tree_opts)
                 ref = orc.tree_allreduce(x, dtype, op=op)
             else:
                 comm = api.Comm(R, N, dtype, device=env["dev"], redop=op, channels=K,
