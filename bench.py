@@ -25,9 +25,11 @@ all-gather, all-reduce, checked against the oracle); the pipelined ring (simple 
 on the headline workload; and a 512 MiB copy as the streaming ceiling.
 cpu_baseline times the oracle on one thread and on all host cores.
 
-Other modes (--mode): r4-int32 (R = 4 int32, 4096 per rank, every form), matrix
+Other modes (--mode): r4-int32 (R = 4 int32, 4096 per rank, every form and both
+trees), matrix
 (fused, 64 MiB per rank, R = 2..16, every dtype),
 sweep (8 B .. 1 GiB per rank, alpha-beta fit), tree-vs-ring (8 B .. 256 KiB),
+tree-large (both trees beside the fused ring at 4 .. 64 MiB per rank),
 buckets (R = 16 bf16 reduce-scatter then all-gather, 40 x 25 MiB), stream
 (c = a + b and copy reference kernels), counters (a short program for
 rocprofv3 --pmc runs), tune (grid sizes), overlap (buckets beside GEMMs on
@@ -948,8 +950,9 @@ def mode_counters(args):
 
 def mode_r4_int32(args):
     """Ring all-reduce (sum), R = 4, int32, 4096 elements per rank,
-    chunk = count / R; time per call (graph-replayed) in every form, each
-    result checked bit for bit against the oracle and the int64 sum."""
+    chunk = count / R; time per call (graph-replayed) in every form and both
+    tree forms, each result checked bit for bit against the int64 sum (and
+    the rings against the oracle's ring)."""
     import numpy as np
     import torch
     from collective_communication_ring_amd import api, inputs
@@ -963,12 +966,13 @@ def mode_r4_int32(args):
     res = {}
     for name, kw in (("fused", ring_kw("fused")), ("step", ring_kw("step")),
                      ("pipelined", ring_kw("pipelined")), ("ll", ring_kw("ll")),
-                     ("tree-ll", dict(algo="tree", proto="ll"))):
+                     ("tree-ll", dict(algo="tree", proto="ll")),
+                     ("tree-fused", dict(algo="tree", proto="simple", launch="fused"))):
         comm = api.Comm(R, N, "int32", device=dev, chunk_bytes=(N // R) * 4, **kw)
         t_us = time_graph(lambda: comm.allreduce(send, recv), 20, torch) * 1e3
         got = recv.cpu().numpy()
         ok = comm.check() == api.AR_SUCCESS and (got == exact[None, :]).all() and (
-            name == "tree-ll" or got.tobytes() == ref.tobytes())
+            name.startswith("tree") or got.tobytes() == ref.tobytes())
         res[name] = dict(t_us=round(t_us, 3), exact=bool(ok))
         log("r4-int32 %-10s %8.2f us  exact=%s" % (name, t_us, ok))
         comm.close()
@@ -976,6 +980,58 @@ def mode_r4_int32(args):
                           cpu_baseline=dict(kind="oracle", cores=1, t_us=t_or * 1e6,
                                             sample="%d calls" % n_or))), flush=True)
     return 0 if all(r["exact"] for r in res.values()) else 1
+
+
+def mode_tree_large(args):
+    """The two tree forms beside the fused ring on the 64 MiB-per-rank inputs
+    (R = 8 fp32, N(0,1) seed 2) and on their first 4 and 16 MiB per rank:
+    after ~20 ms of untimed calls, event-timed 5 warm-up + 20 calls per
+    point (host-enqueued), the 2 R N s
+    compulsory bytes' HBM rate, and every 64 MiB result checked bit for bit
+    against the oracle's tree or ring."""
+    import torch
+    from collective_communication_ring_amd import api, inputs, measure
+    dev = torch.device("cuda:0")
+    x = inputs.host_inputs("ring_f32_r8_64MiB")
+    R, N = x.shape
+    s = 4
+    send = torch.from_numpy(x).to(dev)
+    recv = torch.empty_like(send)
+    forms = (("tree-fused", dict(algo="tree", proto="simple", launch="fused")),
+             ("tree-ll", dict(algo="tree", proto="ll")),
+             ("ring-fused", dict(algo="ring", proto="simple", launch="fused")))
+    threads = cpu_info()["threads"]
+    res, exact = {}, True
+    # ~20 ms of untimed calls first: the first point follows a 512 MiB upload,
+    # and 5 warm-up calls of ~20 us each are too short for it otherwise
+    comm = api.Comm(R, N, "float32", device=dev, **dict(forms[2][1]))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.02:
+        comm.allreduce(send, recv)
+        torch.cuda.synchronize()
+    comm.close()
+    for n in (N // 16, N // 4, N):
+        sv = send.reshape(-1)[:R * n].view(R, n)
+        rv = recv.reshape(-1)[:R * n].view(R, n)
+        for name, kw in forms:
+            comm = api.Comm(R, n, "float32", device=dev, **kw)
+            per, total_ms, _ = time_calls(lambda: comm.allreduce(sv, rv), 20, 5, torch)
+            us = total_ms / 20 * 1e3
+            ok = comm.check() == api.AR_SUCCESS
+            if n == N:
+                ref, _, _, _ = cpu_baseline_leg(
+                    (lambda o: o.tree_allreduce(x)) if name.startswith("tree")
+                    else (lambda o: o.ring_allreduce(x)), 0.0, 1, threads=threads)
+                ok &= rv.cpu().numpy().tobytes() == ref.tobytes()
+            exact &= bool(ok)
+            hbm = measure.allreduce_hbm_bytes(R, n, s) / (us / 1e6) / 1e9
+            res.setdefault(str(n * s), {})[name] = dict(us=round(us, 2), hbm_GBps=round(hbm, 1),
+                                                       hbm_frac=round(hbm / PEAK_HBM_GBPS, 4))
+            log("tree-large %9d B/rank %-10s %9.2f us  %7.1f GB/s" % (n * s, name, us, hbm))
+            comm.close()
+    print(json.dumps(dict(mode="tree_large", R=R, dtype="f32", exact=exact, results=res)),
+          flush=True)
+    return 0 if exact else 1
 
 
 def mode_matrix(args):
@@ -1071,7 +1127,7 @@ def main():
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: library default)")
     ap.add_argument("--mode", default="headline",
                     choices=["headline", "r4-int32", "matrix", "sweep", "tree-vs-ring",
-                             "buckets", "stream", "counters", "tune", "overlap"])
+                             "tree-large", "buckets", "stream", "counters", "tune", "overlap"])
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--tvr-max-bytes", type=int, default=256 * 1024,
                     help="tree-vs-ring: largest per-rank size (the default stops at 256 KiB)")
@@ -1101,7 +1157,7 @@ def main():
               % (args.gpus, world), file=sys.stderr)
         return 2
     fn = {"headline": headline, "r4-int32": mode_r4_int32, "matrix": mode_matrix,
-          "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring,
+          "sweep": mode_sweep, "tree-vs-ring": mode_tree_vs_ring, "tree-large": mode_tree_large,
           "buckets": mode_buckets, "stream": mode_stream, "counters": mode_counters,
           "tune": mode_tune, "overlap": mode_overlap}[args.mode]
     return fn(args)

@@ -755,8 +755,18 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     // up to 4 workgroups per CU in all (or AR_OPT_GRID), shared by the two
     // halves in proportion, at least one for a half that has elements
     const int64_t total = c->grid > 0 ? c->grid : 4 * (int64_t)c->ncu;
+    // 16-byte packs of 4 elements when one element per thread would take
+    // more than one pass of the grid and every half and row starts on 16
+    // bytes.  (Small calls keep one element per thread: the chain is latency
+    // bound there, and more waves carry it sooner.  Large ones move 16 bytes
+    // per access, which also keeps their speed when send and recv sit a large
+    // power of two apart: one element per thread slowed by ~1.6x there.)
+    a.vec = (N > (uint64_t)total * kBlock && N % 8 == 0 && aligned16(send) && aligned16(recv))
+                ? 1 : 0;
+    const uint64_t per_block = (uint64_t)kBlock * (a.vec ? 4 : 1);
     const uint64_t ha = a.H, hb = N - a.H;
-    const uint64_t need_a = (ha + kBlock - 1) / kBlock, need_b = (hb + kBlock - 1) / kBlock;
+    const uint64_t need_a = (ha + per_block - 1) / per_block;
+    const uint64_t need_b = (hb + per_block - 1) / per_block;
     const uint64_t cap_a = std::max<uint64_t>(1, (uint64_t)total / 2);
     const uint64_t ga = std::min<uint64_t>(need_a, cap_a);
     const uint64_t gb = hb ? std::min<uint64_t>(need_b, std::max<uint64_t>(1, (uint64_t)total - ga))
@@ -765,8 +775,8 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     const int grid = (int)(ga + gb);
     hipError_t e = launch_tree_fused(c->dtype, c->R, a, grid, st);
     if (c->debug)
-        std::fprintf(stderr, "ar: tree-fused R=%d N=%llu dtype=%s grid=%d\n", c->R,
-                     (unsigned long long)N, dtype_name(c->dtype), grid);
+        std::fprintf(stderr, "ar: tree-fused R=%d N=%llu dtype=%s vec=%d grid=%d\n", c->R,
+                     (unsigned long long)N, dtype_name(c->dtype), a.vec ? 4 : 1, grid);
     if (e != hipSuccess)
         return fail_hip(c, e);
     return AR_SUCCESS;

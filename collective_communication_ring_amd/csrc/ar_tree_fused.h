@@ -14,8 +14,11 @@ namespace ar {
 constexpr int kTreeFusedMaxRanks = 16;
 
 // One launch covers the whole collective.  Workgroups [0, blocks_a) take the
-// elements [0, H) of tree A, the others [H, N) of tree B, one element per
-// thread (a grid-stride loop on each half).
+// elements [0, H) of tree A, the others [H, N) of tree B, V elements per
+// thread (a grid-stride loop on each half): V = 4 (16-byte accesses) when
+// vec is set, which the host does only for N above the grid's threads, a
+// multiple of 8, with both buffers 16-byte aligned (so every half and row
+// starts on 16 bytes and each half is whole packs), else V = 1.
 struct TreeFusedArgs {
     const void* send;
     void* out;
@@ -23,6 +26,7 @@ struct TreeFusedArgs {
     uint64_t H;
     int redop;
     int blocks_a;  // workgroups on tree A's half
+    int vec;
 };
 
 // hipErrorInvalidValue for a dtype other than int32/float32, an R outside

@@ -108,57 +108,133 @@ constexpr FusedShape<R> fused_shape()
     return s;
 }
 
-// One element's whole tree TT (0: A, 1: B), every row index a constant.
-template <class E, int RED, int R, int TT>
+// V consecutive elements of one row: V = 4 (one 16-byte access) where the
+// halves and rows are 16-byte aligned, else V = 1.
+template <class E, int V>
+struct Pack {
+    typename E::A v[V];
+};
+
+template <class E, int V>
+__device__ inline Pack<E, V> load_pack(const typename E::T* p)
+{
+    Pack<E, V> r;
+    if constexpr (V == 1) {
+        r.v[0] = E::widen(*p);
+    } else {
+        static_assert(V == 4 && sizeof(typename E::T) == 4, "16 bytes of 32-bit elements");
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r.v[k] = E::from_bits(u[k]);
+    }
+    return r;
+}
+
+template <class E, int V>
+__device__ inline void store_pack(typename E::T* p, const Pack<E, V>& r)
+{
+    if constexpr (V == 1) {
+        *p = E::narrow(r.v[0]);
+    } else {
+        u32x4 u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            u[k] = E::t_bits(E::narrow(r.v[k]));
+        *reinterpret_cast<u32x4*>(p) = u;
+    }
+}
+
+// The raw T bits of V elements, for the broadcast (no arithmetic).
+template <int V>
+struct Raw {
+    uint32_t v[V];
+};
+
+template <class E, int V>
+__device__ inline Raw<V> load_raw(const typename E::T* p)
+{
+    Raw<V> r;
+    if constexpr (V == 1) {
+        r.v[0] = E::t_bits(*p);
+    } else {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r.v[k] = u[k];
+    }
+    return r;
+}
+
+template <class E, int V>
+__device__ inline void store_raw(typename E::T* p, const Raw<V>& r)
+{
+    if constexpr (V == 1) {
+        *p = E::t_from_bits(r.v[0]);
+    } else {
+        u32x4 u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            u[k] = r.v[k];
+        *reinterpret_cast<u32x4*>(p) = u;
+    }
+}
+
+// Elements e .. e+V-1 through the whole tree TT (0: A, 1: B), every row
+// index a constant; each of the V elements folds on its own, in the same
+// order.
+template <class E, int RED, int R, int TT, int V>
 __device__ inline void tree_fused_elem(const typename E::T* x, typename E::T* y, uint64_t N,
                                        uint64_t e, float fr)
 {
-    using T = typename E::T;
-    using A = typename E::A;
     constexpr FusedShape<R> S = fused_shape<R>();
-    A xin[R];  // own inputs, by breadth-first position, all loaded at once
+    Pack<E, V> xin[R];  // own inputs, by breadth-first position, all loaded at once
 #pragma unroll
     for (int i = 0; i < R; ++i)
-        xin[i] = E::widen(x[(uint64_t)S.bfs[TT][i] * N + e]);
+        xin[i] = load_pack<E, V>(x + (uint64_t)S.bfs[TT][i] * N + e);
     // up, deepest level first
 #pragma unroll
     for (int L = S.nlev[TT] - 1; L >= 0; --L) {
-        A cv[R][2];
+        Pack<E, V> cv[R][2];
 #pragma unroll
         for (int i = S.lvl[TT][L]; i < S.lvl[TT][L + 1]; ++i) {
             const int v = S.bfs[TT][i];
 #pragma unroll
             for (int k = 0; k < S.nch[TT][v]; ++k)
-                cv[i][k] = E::widen(y[(uint64_t)S.ch[TT][v][k] * N + e]);
+                cv[i][k] = load_pack<E, V>(y + (uint64_t)S.ch[TT][v][k] * N + e);
         }
 #pragma unroll
         for (int i = S.lvl[TT][L]; i < S.lvl[TT][L + 1]; ++i) {
             const int v = S.bfs[TT][i];
-            A acc = xin[i];
+            Pack<E, V> acc = xin[i];
 #pragma unroll
             for (int k = 0; k < S.nch[TT][v]; ++k)
-                acc = combine<E, RED>(acc, cv[i][k]);
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    acc.v[j] = combine<E, RED>(acc.v[j], cv[i][k].v[j]);
             if (S.parent[TT][v] < 0)
-                acc = finalize<E, RED>(acc, fr);
-            y[(uint64_t)v * N + e] = E::narrow(acc);
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    acc.v[j] = finalize<E, RED>(acc.v[j], fr);
+            store_pack<E, V>(y + (uint64_t)v * N + e, acc);
         }
         step_boundary();
     }
     // down, from the root's children
 #pragma unroll
     for (int L = 1; L < S.nlev[TT]; ++L) {
-        T val[R];
+        Raw<V> val[R];
 #pragma unroll
         for (int i = S.lvl[TT][L]; i < S.lvl[TT][L + 1]; ++i)
-            val[i] = y[(uint64_t)S.parent[TT][S.bfs[TT][i]] * N + e];
+            val[i] = load_raw<E, V>(y + (uint64_t)S.parent[TT][S.bfs[TT][i]] * N + e);
 #pragma unroll
         for (int i = S.lvl[TT][L]; i < S.lvl[TT][L + 1]; ++i)
-            y[(uint64_t)S.bfs[TT][i] * N + e] = val[i];
+            store_raw<E, V>(y + (uint64_t)S.bfs[TT][i] * N + e, val[i]);
         step_boundary();
     }
 }
 
-template <int DT, int RED, int R>
+template <int DT, int RED, int R, int V>
 __global__ __launch_bounds__(kBlock) void k_tree_fused_r(TreeFusedArgs a)
 {
     using E = Elem<DT>;
@@ -171,11 +247,12 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused_r(TreeFusedArgs a)
     const uint64_t lo = tb ? a.H : 0, hi = tb ? N : a.H;
     const uint64_t b = tb ? blockIdx.x - a.blocks_a : blockIdx.x;
     const uint64_t nb = tb ? gridDim.x - a.blocks_a : a.blocks_a;
-    for (uint64_t e = lo + b * kBlock + threadIdx.x; e < hi; e += nb * kBlock) {
+    // (with V = 4 the host guarantees that both halves are whole packs)
+    for (uint64_t e = lo + (b * kBlock + threadIdx.x) * V; e < hi; e += nb * kBlock * V) {
         if (tb)
-            tree_fused_elem<E, RED, R, 1>(x, y, N, e, fr);
+            tree_fused_elem<E, RED, R, 1, V>(x, y, N, e, fr);
         else
-            tree_fused_elem<E, RED, R, 0>(x, y, N, e, fr);
+            tree_fused_elem<E, RED, R, 0, V>(x, y, N, e, fr);
     }
 }
 
@@ -183,10 +260,12 @@ template <int DT, int RED, int R>
 void tree_fused_launch_r(int r, const TreeFusedArgs& a, int grid, hipStream_t st)
 {
     if constexpr (R <= kTreeFusedMaxRanks) {
-        if (r == R)
-            hipLaunchKernelGGL((k_tree_fused_r<DT, RED, R>), dim3(grid), dim3(kBlock), 0, st, a);
-        else
+        if (r != R)
             tree_fused_launch_r<DT, RED, R + 1>(r, a, grid, st);
+        else if (a.vec)
+            hipLaunchKernelGGL((k_tree_fused_r<DT, RED, R, 4>), dim3(grid), dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_tree_fused_r<DT, RED, R, 1>), dim3(grid), dim3(kBlock), 0, st, a);
     }
 }
 

@@ -120,6 +120,56 @@ def test_ring_f32_r8_64MiB(env, launch):
     check_tolerance(env, y, x, "float32")
 
 
+@pytest.mark.parametrize("form", ["fused", "ll"])
+def test_tree_f32_r8_64MiB(env, form):
+    """Both tree forms on the same 64 MiB-per-rank inputs (the fused tree in
+    16-byte packs, its default grid looping over each half 16 times; the LL
+    tree runs 128 pieces): bit-exact against the oracle's tree, and within
+    the float32 tolerance of the exact sum."""
+    x = env["inputs"].host_inputs("ring_f32_r8_64MiB")
+    kw = dict(proto="simple", launch="fused") if form == "fused" else dict(proto="ll")
+    (y,) = run_allreduce(env, x, "float32", algo="tree", **kw)
+    assert y.tobytes() == env["orc"].tree_allreduce(x).tobytes()
+    check_tolerance(env, y, x, "float32")
+
+
+def test_tree_fused_unaligned_views_take_single_elements(env, capfd):
+    """Rows of a view that starts 4 bytes into its allocation are not 16-byte
+    aligned: the fused tree takes one element per thread there even where
+    the grid (here 4 workgroups) would take 16-byte packs, bit-exact."""
+    api, orc = env["api"], env["orc"]
+    R, N = 8, 4096
+    x = rand_input(env, "float32", R, N, seed=77)
+    base = to_dev(env, np.zeros((R * N + 1,), np.float32), "float32")
+    send = base[1:].view(R, N)
+    send.copy_(to_dev(env, x, "float32"))
+    out = poisoned(env, (R * N + 1,), "float32")[1:].view(R, N)
+    comm = api.Comm(R, N, "float32", "tree", "simple", device=env["dev"], launch="fused", debug=1,
+                    grid=4)
+    capfd.readouterr()
+    comm.allreduce(send, out)
+    assert "vec=1" in capfd.readouterr().err
+    aligned = poisoned(env, (R, N), "float32")
+    capfd.readouterr()
+    comm.allreduce(to_dev(env, x, "float32"), aligned)  # the same call, aligned: packs
+    assert "vec=4" in capfd.readouterr().err
+    assert from_dev(env, aligned, "float32").tobytes() == orc.tree_allreduce(x).tobytes()
+    assert from_dev(env, out, "float32").tobytes() == orc.tree_allreduce(x).tobytes()
+    assert comm.check() == api.AR_SUCCESS
+
+
+def test_tree_fused_int32_r16_large_ragged(env):
+    """The fused tree at R = 16 on 4 Mi + 3 int32 per rank (odd N: one
+    element per thread, looping over each half ~16 times, and tree A's half
+    one element longer), against the oracle's tree and the exact int64
+    sum."""
+    R, N = 16, (1 << 22) + 3
+    x = rand_input(env, "int32", R, N, seed=1603)
+    (y,) = run_allreduce(env, x, "int32", algo="tree", launch="fused")
+    assert y.tobytes() == env["orc"].tree_allreduce(x, "int32").tobytes()
+    assert (y == x.astype(np.int64).sum(axis=0).astype(np.int32)[None, :]).all()
+
+
 # ---------------------------------------------------------------- ragged sizes
 
 @pytest.mark.parametrize("launch", LAUNCHES)
@@ -419,9 +469,10 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
     """The fused tree (a tree call with the fused launch and a protocol other
     than LL, 32-bit types, R <= 16, the trees compiled in for each R): the LL
     tree's fold order, so bit-exact against the oracle's tree -- every
-    operator, ragged sizes, in place, and a grid of 3 workgroups that loops
-    over the elements -- and the library's debug line shows the fused kernel
-    ran.  Beyond 16 ranks the same call takes the LL tree."""
+    operator, ragged sizes and sizes taking 16-byte packs, in place, and a
+    grid of 3 workgroups that loops over the elements -- and the library's
+    debug line shows the fused kernel ran, and in which width.  Beyond 16
+    ranks the same call takes the LL tree."""
     api, orc = env["api"], env["orc"]
     fused = R <= 16
     ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
@@ -435,7 +486,9 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
         want = ((api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED) if fused
                 else (api.AR_TREE, api.AR_LL, api.AR_LAUNCH_AUTO))
         assert comm.plan(Nmax)[:3] == want
-        for N in (1, 2, 7, 1000, 4097, Nmax):
+        # N a multiple of 8 above the grid's threads takes 16-byte packs (4
+        # elements per thread): here with the grid of 3 (768 threads)
+        for N in (1, 2, 7, 8, 1000, 4097, 4 * 4096, Nmax):
             x = rand_input(env, dtype, R, N, seed=R * 131 + N + len(op))
             ref = orc.tree_allreduce(x, dtype, op=op)
             capfd.readouterr()
@@ -445,6 +498,9 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
             assert from_dev(env, recv, dtype).tobytes() == ref.tobytes(), (op, grid, N)
             err = capfd.readouterr().err
             assert ("ar: tree-fused" in err) == fused and ("ar: tree-LL" in err) != fused, err
+            if fused:
+                vec = grid is not None and N % 8 == 0 and N > grid * 256
+                assert ("vec=4" if vec else "vec=1") in err, err
             if fused and grid is not None:
                 assert int(re.search(r"tree-fused .* grid=(\d+)", err).group(1)) <= grid, err
             comm.allreduce(send, send)  # in place
