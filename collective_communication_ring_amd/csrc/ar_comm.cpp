@@ -252,13 +252,11 @@ double cost_us(const CostLine& l, double bytes) { return l.alpha_us + bytes / (l
 
 // Does a tree call take the fused form (one launch, hops through the nodes'
 // output rows) rather than the LL form?  With the fused launch, a protocol
-// other than LL, a 32-bit type (a bfloat16 row cannot hold a float32
-// partial) and at most kTreeFusedMaxRanks ranks (the kernel is compiled for
-// each R).
+// other than LL and at most kTreeFusedMaxRanks ranks (the kernel is compiled
+// for each R).
 bool tree_fused_ok(const ar_comm* c)
 {
-    return c->proto != AR_LL && resolve_launch(c) == AR_LAUNCH_FUSED && c->dtype != AR_BF16 &&
-           c->R <= kTreeFusedMaxRanks;
+    return c->proto != AR_LL && resolve_launch(c) == AR_LAUNCH_FUSED && c->R <= kTreeFusedMaxRanks;
 }
 
 // The cost-model line of the tree as this comm would run it.
@@ -761,9 +759,11 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     // bound there, and more waves carry it sooner.  Large ones move 16 bytes
     // per access, which also keeps their speed when send and recv sit a large
     // power of two apart: one element per thread slowed by ~1.6x there.)
-    a.vec = (N > (uint64_t)total * kBlock && N % 8 == 0 && aligned16(send) && aligned16(recv))
+    const uint64_t pack = 16 / elem_size(c->dtype);  // elements in 16 bytes
+    a.vec = (N > (uint64_t)total * kBlock && N % (2 * pack) == 0 && aligned16(send) &&
+             aligned16(recv))
                 ? 1 : 0;
-    const uint64_t per_block = (uint64_t)kBlock * (a.vec ? 4 : 1);
+    const uint64_t per_block = (uint64_t)kBlock * (a.vec ? pack : 1);
     const uint64_t ha = a.H, hb = N - a.H;
     const uint64_t need_a = (ha + per_block - 1) / per_block;
     const uint64_t need_b = (hb + per_block - 1) / per_block;
@@ -776,7 +776,7 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     hipError_t e = launch_tree_fused(c->dtype, c->R, a, grid, st);
     if (c->debug)
         std::fprintf(stderr, "ar: tree-fused R=%d N=%llu dtype=%s vec=%d grid=%d\n", c->R,
-                     (unsigned long long)N, dtype_name(c->dtype), a.vec ? 4 : 1, grid);
+                     (unsigned long long)N, dtype_name(c->dtype), a.vec ? (int)pack : 1, grid);
     if (e != hipSuccess)
         return fail_hip(c, e);
     return AR_SUCCESS;

@@ -15,10 +15,11 @@ constexpr int kTreeFusedMaxRanks = 16;
 
 // One launch covers the whole collective.  Workgroups [0, blocks_a) take the
 // elements [0, H) of tree A, the others [H, N) of tree B, V elements per
-// thread (a grid-stride loop on each half): V = 4 (16-byte accesses) when
-// vec is set, which the host does only for N above the grid's threads, a
-// multiple of 8, with both buffers 16-byte aligned (so every half and row
-// starts on 16 bytes and each half is whole packs), else V = 1.
+// thread (a grid-stride loop on each half): V = 16 bytes of T (4 for 32-bit
+// T, 8 for bfloat16) when vec is set, which the host does only for N above
+// the grid's threads, a multiple of 2V, with both buffers 16-byte aligned (so
+// every half and row starts on 16 bytes and each half is whole packs), else
+// V = 1.
 struct TreeFusedArgs {
     const void* send;
     void* out;
@@ -29,7 +30,7 @@ struct TreeFusedArgs {
     int vec;
 };
 
-// hipErrorInvalidValue for a dtype other than int32/float32, an R outside
+// hipErrorInvalidValue for an unknown dtype, an R outside
 // 2 .. kTreeFusedMaxRanks, or an integer AR_AVG.
 hipError_t launch_tree_fused(int dtype, int R, const TreeFusedArgs& a, int grid, hipStream_t st);
 

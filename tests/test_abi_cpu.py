@@ -117,11 +117,15 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
         assert api.ar_plan(c, n // 4)[0] == api.AR_TREE
         assert api.ar_plan(c, n // 4 + 1)[:3] == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
         # the LL tree's line is above the fused ring's at every size, so where
-        # the tree cannot be fused (bfloat16, or more than 16 ranks) AUTO keeps
-        # the ring
+        # the tree cannot be fused (more than 16 ranks) AUTO keeps the ring
         ta, tb = api.ar_get_cost(c, api.AR_COST_TREE_LL)
         assert fa < ta and fb > tb
-        for R, dt in ((8, api.AR_BF16), (17, api.AR_FLOAT32)):
+        b = api.ar_init(16, 1 << 22, api.AR_BF16, api.AR_AUTO)
+        try:  # a bfloat16 comm of 16 ranks has the fused tree
+            assert api.ar_plan(b, 1)[:3] == (api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+        finally:
+            api.ar_destroy(b)
+        for R, dt in ((17, api.AR_BF16), (17, api.AR_FLOAT32)):
             d = api.ar_init(R, 1 << 22, dt, api.AR_AUTO)
             try:
                 assert api.ar_auto_tree_max_bytes(d) == 0

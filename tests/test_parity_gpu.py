@@ -158,6 +158,19 @@ def test_tree_fused_unaligned_views_take_single_elements(env, capfd):
     assert comm.check() == api.AR_SUCCESS
 
 
+def test_tree_fused_bf16_r16_gradient_bucket(env, capfd):
+    """The fused tree on one gradient bucket's shape (R = 16 bfloat16,
+    13,107,200 elements per rank, N(0,0.02)): 16-byte packs of 8 elements,
+    float32 partials in two halves, bit-exact against the oracle's tree."""
+    api, orc = env["api"], env["orc"]
+    R, N = 16, 13_107_200
+    x = rand_input(env, "bf16", R, N, seed=1605)
+    (y,) = run_allreduce(env, x, "bf16", algo="tree", launch="fused", debug=1)
+    assert "vec=8" in capfd.readouterr().err
+    assert y.tobytes() == orc.tree_allreduce(x, "bf16").tobytes()
+    check_tolerance(env, y, x, "bf16")
+
+
 def test_tree_fused_int32_r16_large_ragged(env):
     """The fused tree at R = 16 on 4 Mi + 3 int32 per rank (odd N: one
     element per thread, looping over each half ~16 times, and tree A's half
@@ -463,12 +476,13 @@ def test_tree_ll_ragged(env, dtype, R):
             assert y.tobytes() == ref.tobytes(), (R, N)
 
 
-@pytest.mark.parametrize("dtype", ["int32", "float32"])
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
 @pytest.mark.parametrize("R", list(range(2, 17)) + [17, 64])
 def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
     """The fused tree (a tree call with the fused launch and a protocol other
-    than LL, 32-bit types, R <= 16, the trees compiled in for each R): the LL
-    tree's fold order, so bit-exact against the oracle's tree -- every
+    than LL, R <= 16, the trees compiled in for each R; bfloat16 partials in
+    two 16-bit halves): the LL tree's fold order, so bit-exact against the
+    oracle's tree -- every
     operator, ragged sizes and sizes taking 16-byte packs, in place, and a
     grid of 3 workgroups that loops over the elements -- and the library's
     debug line shows the fused kernel ran, and in which width.  Beyond 16
@@ -486,8 +500,9 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
         want = ((api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED) if fused
                 else (api.AR_TREE, api.AR_LL, api.AR_LAUNCH_AUTO))
         assert comm.plan(Nmax)[:3] == want
-        # N a multiple of 8 above the grid's threads takes 16-byte packs (4
-        # elements per thread): here with the grid of 3 (768 threads)
+        # N a multiple of two packs above the grid's threads takes 16-byte
+        # packs (4 or 8 elements per thread): here with the grid of 3 (768
+        # threads)
         for N in (1, 2, 7, 8, 1000, 4097, 4 * 4096, Nmax):
             x = rand_input(env, dtype, R, N, seed=R * 131 + N + len(op))
             ref = orc.tree_allreduce(x, dtype, op=op)
@@ -499,8 +514,9 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
             err = capfd.readouterr().err
             assert ("ar: tree-fused" in err) == fused and ("ar: tree-LL" in err) != fused, err
             if fused:
-                vec = grid is not None and N % 8 == 0 and N > grid * 256
-                assert ("vec=4" if vec else "vec=1") in err, err
+                pack = 8 if dtype == "bf16" else 4
+                vec = grid is not None and N % (2 * pack) == 0 and N > grid * 256
+                assert ("vec=%d" % (pack if vec else 1)) in err, err
             if fused and grid is not None:
                 assert int(re.search(r"tree-fused .* grid=(\d+)", err).group(1)) <= grid, err
             comm.allreduce(send, send)  # in place
@@ -1184,28 +1200,34 @@ def _assert_same_special(y, ref, dtype, what):
     assert y[~nan].tobytes() == ref[~nan].tobytes(), what
 
 
-@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree", "tree-fused"])
 @pytest.mark.parametrize("dtype", ["float32", "bf16"])
 @pytest.mark.parametrize("op", ["sum", "max", "min", "avg"])
 def test_special_values(env, variant, dtype, op):
     """Denormals, signed zeros, infinities and NaNs go through every form and
     operator exactly as the oracle folds them (no flush to zero, no fused or
-    reassociated adds, max/min by the same strict comparison)."""
+    reassociated adds, max/min by the same strict comparison); the fused
+    tree also with a grid of 16, so that 32,816 elements take 16-byte
+    packs."""
     orc = env["orc"]
-    for R, N in ((8, 8 * 4096 + 40), (5, 1003)):
+    for R, N in ((8, 8 * 4096 + 48), (5, 1003)):
         x = _special_f32(R, N, seed=R * 131 + N)
         if dtype == "bf16":
             x = orc.bf16_from_f32(x)
         if variant == "tree":
-            (y,) = run_allreduce(env, x, dtype, "tree", "ll", redop=op)
-            ref = orc.tree_allreduce(x, dtype, op=op)
+            runs = [dict(algo="tree", proto="ll")]
+        elif variant == "tree-fused":
+            runs = [dict(algo="tree", launch="fused"), dict(algo="tree", launch="fused", grid=16)]
         else:
-            (y,) = run_allreduce(env, x, dtype, launch=variant, redop=op)
-            ref = orc.ring_allreduce(x, dtype, op=op)
-        _assert_same_special(y, ref, dtype, (variant, dtype, op, R, N))
+            runs = [dict(launch=variant)]
+        for kw in runs:
+            (y,) = run_allreduce(env, x, dtype, redop=op, **kw)
+            ref = (orc.tree_allreduce(x, dtype, op=op) if variant.startswith("tree")
+                   else orc.ring_allreduce(x, dtype, op=op))
+            _assert_same_special(y, ref, dtype, (variant, dtype, op, R, N, kw))
 
 
-@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree", "tree-fused"])
 def test_int32_sum_wraps(env, variant):
     """int32 sums wrap modulo 2^32 in every form, as in the oracle and as
     numpy's int64 sum reduced modulo 2^32."""
@@ -1214,8 +1236,9 @@ def test_int32_sum_wraps(env, variant):
     rng = np.random.default_rng(77)
     x = rng.integers(-2 ** 31, 2 ** 31, size=(R, N), dtype=np.int64).astype(np.int32)
     want = (x.astype(np.int64).sum(axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
-    if variant == "tree":
-        (y,) = run_allreduce(env, x, "int32", "tree", "ll")
+    if variant.startswith("tree"):
+        kw = dict(proto="ll") if variant == "tree" else dict(launch="fused")
+        (y,) = run_allreduce(env, x, "int32", "tree", **kw)
         assert y.tobytes() == orc.tree_allreduce(x).tobytes()
     else:
         (y,) = run_allreduce(env, x, "int32", launch=variant)
@@ -1383,7 +1406,7 @@ def test_random_configurations_match_oracle(env):
             N = int(np.exp(rng.uniform(0, np.log(300000))))
             x = rand_input(env, dtype, R, N, seed=case)
             if tree:
-                # the fused tree for 32-bit types and R <= 16, else the LL tree
+                # the fused tree for R <= 16, else the LL tree
                 tree_opts = (dict(proto="simple", launch="fused") if variant == "tree-fused"
                              else dict(proto="ll"))
                 comm = api.Comm(R, N, dtype, "tree", device=env["dev"], redop=op, **tree_opts)
