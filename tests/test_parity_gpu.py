@@ -812,7 +812,7 @@ def test_repeat_runs_bit_identical(env, launch):
 
 # ---------------------------------------------------------------- graphs
 
-@pytest.mark.parametrize("variant", ["fused", "step", "pipelined", "ll", "tree"])
+@pytest.mark.parametrize("variant", ["fused", "step", "pipelined", "ll", "tree", "tree-fused"])
 def test_graph_replay_matches_eager(env, variant):
     """Capture one call in a HIP graph and replay it several times with eager
     calls and synchronizations in between; every replay must equal the eager
@@ -821,8 +821,9 @@ def test_graph_replay_matches_eager(env, variant):
     torch, api = env["torch"], env["api"]
     R, N = 8, 40_000
     x = env["inputs"].draw("normal", R, N, seed=17)
-    if variant == "tree":
-        comm = api.Comm(R, N, "float32", "tree", "ll", device=env["dev"])
+    if variant.startswith("tree"):
+        kw = dict(proto="ll") if variant == "tree" else dict(proto="simple", launch="fused")
+        comm = api.Comm(R, N, "float32", "tree", device=env["dev"], **kw)
         ref = env["orc"].tree_allreduce(x)
     else:
         comm = api.Comm(R, N, "float32", device=env["dev"], **ring_opts(variant))
@@ -1316,15 +1317,19 @@ def test_multi_channel_full_size_order_differs_from_one_channel(env):
     check_tolerance(env, y4, x, "float32")
 
 
-@pytest.mark.parametrize("launch", ["fused", "step"])
+@pytest.mark.parametrize("launch", ["fused", "step", "tree-fused"])
 def test_concurrent_with_compute_on_another_stream(env, launch):
-    """A ring all-reduce on a second stream while GEMMs run on the first
-    (the overlap pattern) stays exact."""
+    """A ring (or fused tree) all-reduce on a second stream while GEMMs run
+    on the first (the overlap pattern) stays exact."""
     torch, api, orc = env["torch"], env["api"], env["orc"]
     R, N = 8, 1 << 20
     x = env["inputs"].draw("normal", R, N, seed=44)
-    ref = orc.ring_allreduce(x)
-    comm = api.Comm(R, N, "float32", device=env["dev"], launch=launch)
+    if launch == "tree-fused":
+        ref = orc.tree_allreduce(x)
+        comm = api.Comm(R, N, "float32", "tree", device=env["dev"], launch="fused")
+    else:
+        ref = orc.ring_allreduce(x)
+        comm = api.Comm(R, N, "float32", device=env["dev"], launch=launch)
     send = to_dev(env, x, "float32")
     recv = poisoned(env, (R, N), "float32")
     a = torch.randn((2048, 2048), device=env["dev"])
