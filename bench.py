@@ -917,9 +917,10 @@ def mode_overlap(args):
 def mode_counters(args):
     """A short program for byte-counter runs (rocprofv3 --pmc): a copy of a
     known size (the calibration) and the headline's row pattern without hops
-    (ar_stream_rows), then 3 all-reduces of the headline workload
-    in each launch form, then 3 small tree-LL all-reduces, then 3 reduce-
-    scatters, all-gathers and all-reduces of one 25 MiB gradient bucket."""
+    (ar_stream_rows), then 3 all-reduces of the headline workload in each
+    ring launch form and by the fused tree, then 3 small all-reduces by each
+    tree form, then 3 reduce-scatters, all-gathers and all-reduces (ring,
+    then fused tree) of one 25 MiB gradient bucket."""
     import torch
     from collective_communication_ring_amd import api, inputs
     dev = torch.device("cuda:0")
@@ -943,11 +944,17 @@ def mode_counters(args):
         for _ in range(3):
             comm.allreduce(send, recv)
         torch.cuda.synchronize()
-    comm = api.Comm(R, 65536, "float32", "tree", "ll", device=dev)
+    # the fused tree on the same workload (16-byte packs)
+    comm = api.Comm(R, N, "float32", "tree", "simple", device=dev, launch="fused")
+    for _ in range(3):
+        comm.allreduce(send, recv)
+    torch.cuda.synchronize()
     small = send[:, :65536].contiguous()
     out = torch.empty_like(small)
-    for _ in range(3):
-        comm.allreduce(small, out)
+    for proto, launch in (("ll", None), ("simple", "fused")):
+        comm = api.Comm(R, 65536, "float32", "tree", proto, device=dev, launch=launch)
+        for _ in range(3):
+            comm.allreduce(small, out)
     torch.cuda.synchronize()
     del send, recv, small, out
     # one 25 MiB gradient bucket (R = 16 bf16): reduce-scatter, all-gather, all-reduce
@@ -961,6 +968,9 @@ def mode_counters(args):
         comm.reduce_scatter(xb, shard)
     for _ in range(3):
         comm.all_gather(shard, full)
+    for _ in range(3):
+        comm.allreduce(xb, full)
+    comm = api.Comm(Rb, Nb, "bf16", "tree", "simple", device=dev, launch="fused")
     for _ in range(3):
         comm.allreduce(xb, full)
     torch.cuda.synchronize()

@@ -753,7 +753,7 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     // up to 4 workgroups per CU in all (or AR_OPT_GRID), shared by the two
     // halves in proportion, at least one for a half that has elements
     const int64_t total = c->grid > 0 ? c->grid : 4 * (int64_t)c->ncu;
-    // 16-byte packs of 4 elements when one element per thread would take
+    // 16-byte packs (4 or 8 elements) when one element per thread would take
     // more than one pass of the grid and every half and row starts on 16
     // bytes.  (Small calls keep one element per thread: the chain is latency
     // bound there, and more waves carry it sooner.  Large ones move 16 bytes
@@ -763,13 +763,25 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     a.vec = (N > (uint64_t)total * kBlock && N % (2 * pack) == 0 && aligned16(send) &&
              aligned16(recv))
                 ? 1 : 0;
+    // The packed form keeps each non-root output line in L2 from its partial
+    // to its final value only while few waves are in flight: by default 2
+    // workgroups per CU while the call's rows (2 R N s) fit in half the
+    // 256 MB Infinity Cache, else 1 (at 4 waves per CU each XCD's waves hold
+    // ~4 MiB of dirty lines, its L2's size, and the partials reached HBM:
+    // 1.8x the compulsory writes at R = 8 fp32 64 MiB per rank).
+    int64_t grid_total = total;
+    if (a.vec && c->grid <= 0) {
+        const double rows = 2.0 * c->R * (double)N * elem_size(c->dtype);
+        grid_total = (rows <= 128.0 * (1 << 20) ? 2 : 1) * (int64_t)c->ncu;
+    }
     const uint64_t per_block = (uint64_t)kBlock * (a.vec ? pack : 1);
     const uint64_t ha = a.H, hb = N - a.H;
     const uint64_t need_a = (ha + per_block - 1) / per_block;
     const uint64_t need_b = (hb + per_block - 1) / per_block;
-    const uint64_t cap_a = std::max<uint64_t>(1, (uint64_t)total / 2);
+    const uint64_t cap_a = std::max<uint64_t>(1, (uint64_t)grid_total / 2);
     const uint64_t ga = std::min<uint64_t>(need_a, cap_a);
-    const uint64_t gb = hb ? std::min<uint64_t>(need_b, std::max<uint64_t>(1, (uint64_t)total - ga))
+    const uint64_t gb = hb ? std::min<uint64_t>(need_b,
+                                                std::max<uint64_t>(1, (uint64_t)grid_total - ga))
                            : 0;
     a.blocks_a = (int)ga;
     const int grid = (int)(ga + gb);
