@@ -147,11 +147,14 @@ typedef enum {
                                  values are cut */
     AR_OPT_LAUNCH = 1,        /* an ar_launch_t */
     AR_OPT_GRID = 2,          /* workgroups per launch; 0 = library default.  For the
-                                 pipelined ring, ring + LL and the tree, whose workgroups
+                                 pipelined ring, ring + LL and the LL tree, whose workgroups
                                  must all be resident at once, a cap: on a stream held to
                                  some CUs (ar_stream_create_cu_masked) set it to at most the
                                  workgroups those CUs hold (one per CU is always safe); it
-                                 must be at least R (2R for the tree) */
+                                 must be at least R (2R for the LL tree).  The fused ring and
+                                 the fused tree take it as their grid (the fused ring caps it
+                                 at the waves its staging holds); their workgroups never wait
+                                 for each other */
     AR_OPT_TIMEOUT_US = 3,    /* microseconds before a kernel's bounded wait gives up */
     AR_OPT_DEBUG = 4,         /* 1: print algorithm/protocol/launch per call to stderr */
     AR_OPT_ALGO = 5,          /* an ar_algo_t, overriding the one given to ar_init */
@@ -167,8 +170,9 @@ typedef enum {
                                    channel k runs its own ring q -> q + m_k over sub-range k
                                    (strides from ar_ring_channel_stride); the multi-rail /
                                    channels idea ("GPU MODE lecture 68 notes", section 06) */
-    AR_OPT_DEBUG_LL_LAUNCHES = 11 /* testing only: tree and ring + LL launches counted since
-                                   their lines were last cleared (see ar_set_workspace) */
+    AR_OPT_DEBUG_LL_LAUNCHES = 11 /* testing only: LL tree and ring + LL launches counted
+                                   since their lines were last cleared (see
+                                   ar_set_workspace) */
 } ar_option_t;
 
 /* Create a communicator for R logical ranks (2 <= R <= 64) and up to
