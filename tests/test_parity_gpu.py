@@ -870,21 +870,25 @@ def _segment_samples(rng, N, R, m):
     return np.array(idx, dtype=np.int64)
 
 
-@pytest.mark.parametrize("variant", LAUNCHES + ["tree"])
+@pytest.mark.parametrize("variant", LAUNCHES + ["tree", "tree-fused", "tree-fused-packed"])
 def test_counts_beyond_2_32_elements_sampled(env, variant):
     """R = 2 bf16 with 2^32 + 1000 elements (8 GiB) per rank, so element
     indices pass both 2^31 and 2^32: every form, sampled outputs -- each
     segment's ends and the elements around 2^31 and 2^32 -- against the
     oracle (with two ranks the fold is one float32 addition, the same in
-    every order and layout), and no output element left unwritten."""
+    every order and layout), and no output element left unwritten.  The
+    fused tree runs one element per thread there, and 16-byte packs at
+    2^32 + 1008 (a multiple of two packs)."""
     torch, api, orc = env["torch"], env["api"], env["orc"]
-    R, N = 2, (1 << 32) + 1000
+    R, N = 2, (1 << 32) + (1008 if variant == "tree-fused-packed" else 1000)
     g = torch.Generator(device=env["dev"])
     g.manual_seed(32)
     send = torch.randn((R, N), generator=g, device=env["dev"], dtype=torch.bfloat16)
     recv = torch.full_like(send, float("nan"))
     if variant == "tree":
         comm = api.Comm(R, N, "bf16", "tree", "ll", device=env["dev"])
+    elif variant.startswith("tree-fused"):
+        comm = api.Comm(R, N, "bf16", "tree", device=env["dev"], launch="fused")
     else:
         comm = api.Comm(R, N, "bf16", device=env["dev"], **ring_opts(variant))
     comm.allreduce(send, recv)
