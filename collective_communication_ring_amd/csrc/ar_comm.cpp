@@ -252,11 +252,10 @@ double cost_us(const CostLine& l, double bytes) { return l.alpha_us + bytes / (l
 
 // Does a tree call take the fused form (one launch, hops through the nodes'
 // output rows) rather than the LL form?  With the fused launch, a protocol
-// other than LL and at most kTreeFusedMaxRanks ranks (the kernel is compiled
-// for each R).
+// other than LL and an R the kernel is compiled for (2 .. 16, 32, 64).
 bool tree_fused_ok(const ar_comm* c)
 {
-    return c->proto != AR_LL && resolve_launch(c) == AR_LAUNCH_FUSED && c->R <= kTreeFusedMaxRanks;
+    return c->proto != AR_LL && resolve_launch(c) == AR_LAUNCH_FUSED && tree_fused_compiled(c->R);
 }
 
 // The cost-model line of the tree as this comm would run it.
@@ -754,14 +753,15 @@ int run_tree_fused(ar_comm* c, const void* send, void* recv, uint64_t N, hipStre
     // halves in proportion, at least one for a half that has elements
     const int64_t total = c->grid > 0 ? c->grid : 4 * (int64_t)c->ncu;
     // 16-byte packs (4 or 8 elements) when one element per thread would take
-    // more than one pass of the grid and every half and row starts on 16
-    // bytes.  (Small calls keep one element per thread: the chain is latency
+    // more than one pass of the grid, every half and row starts on 16 bytes
+    // and R <= kTreeFusedMaxRanks (at 32 and 64 ranks a pack per node would
+    // not fit in registers).  (Small calls keep one element per thread: the chain is latency
     // bound there, and more waves carry it sooner.  Large ones move 16 bytes
     // per access, which also keeps their speed when send and recv sit a large
     // power of two apart: one element per thread slowed by ~1.6x there.)
     const uint64_t pack = 16 / elem_size(c->dtype);  // elements in 16 bytes
-    a.vec = (N > (uint64_t)total * kBlock && N % (2 * pack) == 0 && aligned16(send) &&
-             aligned16(recv))
+    a.vec = (c->R <= kTreeFusedMaxRanks && N > (uint64_t)total * kBlock && N % (2 * pack) == 0 &&
+             aligned16(send) && aligned16(recv))
                 ? 1 : 0;
     // The packed form keeps each non-root output line in L2 from its partial
     // to its final value only while few waves are in flight: by default 2

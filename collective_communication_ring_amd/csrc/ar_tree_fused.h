@@ -9,9 +9,14 @@
 
 namespace ar {
 
-// The fused tree is compiled for R = 2 .. kTreeFusedMaxRanks, each R with its
-// trees fixed at compile time.
+// The fused tree is compiled for R = 2 .. kTreeFusedMaxRanks and for 32 and
+// 64, each R with its trees fixed at compile time; 16-byte packs up to
+// kTreeFusedMaxRanks (at 32 and 64 ranks one element per thread).
 constexpr int kTreeFusedMaxRanks = 16;
+inline bool tree_fused_compiled(int R)
+{
+    return (R >= 2 && R <= kTreeFusedMaxRanks) || R == 32 || R == 64;
+}
 
 // One launch covers the whole collective.  Workgroups [0, blocks_a) take the
 // elements [0, H) of tree A, the others [H, N) of tree B, V elements per
@@ -30,8 +35,9 @@ struct TreeFusedArgs {
     int vec;
 };
 
-// hipErrorInvalidValue for an unknown dtype, an R outside
-// 2 .. kTreeFusedMaxRanks, or an integer AR_AVG.
+// hipErrorInvalidValue for an unknown dtype, an R not compiled
+// (tree_fused_compiled), vec at more than kTreeFusedMaxRanks ranks, or an
+// integer AR_AVG.
 hipError_t launch_tree_fused(int dtype, int R, const TreeFusedArgs& a, int grid, hipStream_t st);
 
 }  // namespace ar

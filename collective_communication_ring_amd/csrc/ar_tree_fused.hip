@@ -23,8 +23,8 @@
 // used, so a hop costs one round trip per level, not per node -- 2(depth)
 // round trips in all (6 at R = 8), against the ring's 2(R-1).  Every own
 // input is read before the first row is written, so in place works.  The
-// kernel is compiled for each R up to kTreeFusedMaxRanks; the host takes the
-// LL tree beyond that.
+// kernel is compiled for each R up to kTreeFusedMaxRanks and for 32 and 64
+// (tree_fused_compiled); the host takes the LL tree for other R.
 #include "ar_elem.h"
 #include "ar_tree_fused.h"
 
@@ -63,7 +63,8 @@ constexpr int shape_parent(int R, int t, int r)
     return p < 0 ? -1 : (p + 1) % R;
 }
 
-// Levels of a tree on at most kTreeFusedMaxRanks ranks (depth <= 5 at 16).
+// Most levels of a compiled tree (7 at R = 64; a deeper shape would fail to
+// compile: constant evaluation checks bounds).
 constexpr int kTreeMaxLevels = 8;
 
 template <int R>
@@ -325,6 +326,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_fused_r(TreeFusedArgs a)
 template <int DT, int RED, int R>
 void tree_fused_launch_r(int r, const TreeFusedArgs& a, int grid, hipStream_t st)
 {
+    if (r == 32 || r == 64) {  // one element per thread (the host never sets vec here)
+        if (r == 32)
+            hipLaunchKernelGGL((k_tree_fused_r<DT, RED, 32, 1>), dim3(grid), dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((k_tree_fused_r<DT, RED, 64, 1>), dim3(grid), dim3(kBlock), 0, st, a);
+        return;
+    }
     if constexpr (R <= kTreeFusedMaxRanks) {
         constexpr int kVec = 16 / (int)sizeof(typename Elem<DT>::T);
         if (r != R)
@@ -365,7 +373,7 @@ hipError_t tree_fused_dt(int R, const TreeFusedArgs& a, int grid, hipStream_t st
 
 hipError_t launch_tree_fused(int dtype, int R, const TreeFusedArgs& a, int grid, hipStream_t st)
 {
-    if (R < 2 || R > kTreeFusedMaxRanks)
+    if (!tree_fused_compiled(R) || (a.vec && R > kTreeFusedMaxRanks))
         return hipErrorInvalidValue;
     switch (dtype) {
     case AR_INT32:

@@ -117,15 +117,17 @@ def test_plan_picks_tree_for_small_and_ring_for_large(api):
         assert api.ar_plan(c, n // 4)[0] == api.AR_TREE
         assert api.ar_plan(c, n // 4 + 1)[:3] == (api.AR_RING, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
         # the LL tree's line is above the fused ring's at every size, so where
-        # the tree cannot be fused (more than 16 ranks) AUTO keeps the ring
+        # the tree cannot be fused (R of 17 .. 63 other than 32) AUTO keeps the
+        # ring
         ta, tb = api.ar_get_cost(c, api.AR_COST_TREE_LL)
         assert fa < ta and fb > tb
-        b = api.ar_init(16, 1 << 22, api.AR_BF16, api.AR_AUTO)
-        try:  # a bfloat16 comm of 16 ranks has the fused tree
-            assert api.ar_plan(b, 1)[:3] == (api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
-        finally:
-            api.ar_destroy(b)
-        for R, dt in ((17, api.AR_BF16), (17, api.AR_FLOAT32)):
+        for R, dt in ((16, api.AR_BF16), (32, api.AR_FLOAT32), (64, api.AR_INT32)):
+            b = api.ar_init(R, 1 << 22, dt, api.AR_AUTO)
+            try:  # R = 2..16, 32 and 64 have the fused tree, every dtype
+                assert api.ar_plan(b, 1)[:3] == (api.AR_TREE, api.AR_SIMPLE, api.AR_LAUNCH_FUSED)
+            finally:
+                api.ar_destroy(b)
+        for R, dt in ((17, api.AR_BF16), (17, api.AR_FLOAT32), (48, api.AR_FLOAT32)):
             d = api.ar_init(R, 1 << 22, dt, api.AR_AUTO)
             try:
                 assert api.ar_auto_tree_max_bytes(d) == 0

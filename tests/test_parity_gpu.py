@@ -477,18 +477,18 @@ def test_tree_ll_ragged(env, dtype, R):
 
 
 @pytest.mark.parametrize("dtype", ["int32", "float32", "bf16"])
-@pytest.mark.parametrize("R", list(range(2, 17)) + [17, 64])
+@pytest.mark.parametrize("R", list(range(2, 18)) + [32, 33, 64])
 def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
     """The fused tree (a tree call with the fused launch and a protocol other
-    than LL, R <= 16, the trees compiled in for each R; bfloat16 partials in
-    two 16-bit halves): the LL tree's fold order, so bit-exact against the
-    oracle's tree -- every
+    than LL, R <= 16 or R = 32 or 64, the trees compiled in for each R;
+    bfloat16 partials in two 16-bit halves): the LL tree's fold order, so
+    bit-exact against the oracle's tree -- every
     operator, ragged sizes and sizes taking 16-byte packs, in place, and a
     grid of 3 workgroups that loops over the elements -- and the library's
-    debug line shows the fused kernel ran, and in which width.  Beyond 16
-    ranks the same call takes the LL tree."""
+    debug line shows the fused kernel ran, and in which width.  At other R
+    the same call takes the LL tree."""
     api, orc = env["api"], env["orc"]
-    fused = R <= 16
+    fused = R <= 16 or R in (32, 64)
     ops = ["sum", "max", "min"] + ([] if dtype == "int32" else ["avg"])
     Nmax = 4 * 4096 + 37
     # (a grid of 3 for the fused form only: the LL tree needs 2R resident
@@ -515,7 +515,7 @@ def test_tree_fused_matches_the_tree_order(env, capfd, dtype, R):
             assert ("ar: tree-fused" in err) == fused and ("ar: tree-LL" in err) != fused, err
             if fused:
                 pack = 8 if dtype == "bf16" else 4
-                vec = grid is not None and N % (2 * pack) == 0 and N > grid * 256
+                vec = grid is not None and N % (2 * pack) == 0 and N > grid * 256 and R <= 16
                 assert ("vec=%d" % (pack if vec else 1)) in err, err
             if fused and grid is not None:
                 assert int(re.search(r"tree-fused .* grid=(\d+)", err).group(1)) <= grid, err
