@@ -57,7 +57,7 @@ typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
  * binary tree").  It runs in one of two forms with the same fold order (so
  * the same bits): fused -- one launch, each thread carrying an element up
  * and down its tree through the nodes' output rows -- when the launch is
- * fused (AR_LAUNCH_AUTO is), the protocol is not AR_LL and R <= 16 (a
+ * fused (AR_LAUNCH_AUTO is), the protocol is not AR_LL and R <= 16, 32 or 64 (a
  * bfloat16 node's float32 partial travels in two 16-bit halves); else with
  * LL lines between the nodes' workgroups.
  * AR_AUTO picks by message size: tree for small messages, ring for large ones
@@ -66,8 +66,8 @@ typedef enum { AR_INT32 = 0, AR_FLOAT32 = 1, AR_BF16 = 2 } ar_dtype_t;
  * (ar_set_cost): that of the tree in the form the call would run and that of
  * the ring launch form the call would use.  With the defaults (fused forms,
  * R = 8, float32) the tree takes messages up to about 3 MB per rank; a comm
- * of more than 16 ranks has only the LL tree, whose line is above the fused
- * ring's: the ring at every size.  With a form in
+ * of 17 .. 63 ranks other than 32 has only the LL tree, whose line is above
+ * the fused ring's: the ring at every size.  With a form in
  * which every step is a hand-off between ranks (AR_LAUNCH_STEP,
  * AR_LAUNCH_PIPELINED, AR_LL) the LL tree takes small messages. */
 typedef enum { AR_RING = 0, AR_TREE = 1, AR_AUTO = 2 } ar_algo_t;
