@@ -1019,7 +1019,8 @@ def mode_tree_large(args):
     after ~20 ms of untimed calls, event-timed 5 warm-up + 20 calls per
     point (host-enqueued), the 2 R N s
     compulsory bytes' HBM rate, and every 64 MiB result checked bit for bit
-    against the oracle's tree or ring."""
+    against the oracle's tree or ring; then the fused tree and the fused ring
+    on one gradient bucket (R = 16 bf16, 25 MiB per rank), also checked."""
     import torch
     from collective_communication_ring_amd import api, inputs, measure
     dev = torch.device("cuda:0")
@@ -1060,8 +1061,31 @@ def mode_tree_large(args):
                                                        hbm_frac=round(hbm / PEAK_HBM_GBPS, 4))
             log("tree-large %9d B/rank %-10s %9.2f us  %7.1f GB/s" % (n * s, name, us, hbm))
             comm.close()
-    print(json.dumps(dict(mode="tree_large", R=R, dtype="f32", exact=exact, results=res)),
-          flush=True)
+    del send, recv
+    torch.cuda.empty_cache()
+    # one gradient bucket (R = 16 bf16, 25 MiB per rank): fused tree and fused ring
+    w = inputs.WORKLOADS["buckets_bf16_r16"]
+    Rb, Nb = w["R"], w["count"]
+    xb = inputs.device_bucket_bf16(Rb, Nb, w["seed"], 0, dev)
+    full = torch.empty_like(xb)
+    xh = xb.view(torch.int16).cpu().numpy().view("uint16")
+    bucket = {}
+    for name, kw in forms[::2]:
+        comm = api.Comm(Rb, Nb, "bf16", device=dev, **kw)
+        per, total_ms, _ = time_calls(lambda: comm.allreduce(xb, full), 20, 5, torch)
+        us = total_ms / 20 * 1e3
+        ref, _, _, _ = cpu_baseline_leg(
+            (lambda o: o.tree_allreduce(xh, "bf16")) if name.startswith("tree")
+            else (lambda o: o.ring_allreduce(xh, "bf16")), 0.0, 1, threads=threads)
+        ok = comm.check() == api.AR_SUCCESS and \
+            full.view(torch.int16).cpu().numpy().view("uint16").tobytes() == ref.tobytes()
+        exact &= bool(ok)
+        hbm = measure.allreduce_hbm_bytes(Rb, Nb, 2) / (us / 1e6) / 1e9
+        bucket[name] = dict(us=round(us, 2), hbm_GBps=round(hbm, 1))
+        log("tree-large bucket R=16 bf16 %-10s %9.2f us" % (name, us))
+        comm.close()
+    print(json.dumps(dict(mode="tree_large", R=R, dtype="f32", exact=exact, results=res,
+                          bucket_r16_bf16_25MiB=bucket)), flush=True)
     return 0 if exact else 1
 
 
