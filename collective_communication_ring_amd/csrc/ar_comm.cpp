@@ -594,6 +594,13 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
         }
         a.stage_wave = 0;
         a.max_units = 0xffffffffu;
+        // reduce steps hand off through LDS for every reduce-scatter and every
+        // all-reduce whose rows total at most 512 MiB (measured crossover: LDS
+        // 7-13% faster up to 32 MiB per rank at R = 8 float32, level at 64 MiB,
+        // ~7% slower from 128 MiB, where the owner's output row takes it)
+        a.hand_lds = (a.op == kOpReduceScatter ||
+                      2.0 * a.R * (double)a.N * elem_size(c->dtype) <= 512.0 * (1 << 20))
+                         ? 1 : 0;
         if (a.op != kOpAllGather && o.stage && a.part == o.stage) {
             // the hand-off goes through each wave's staging slot in the hand-off
             // region: at most as many waves as it holds slots take tiles

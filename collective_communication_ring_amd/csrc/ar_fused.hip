@@ -27,15 +27,18 @@
 //
 // Where a reduce step's running value is handed on: in the wave's own region
 // of LDS (16 KiB per workgroup), a store and a load by the same lane as
-// through L2 but at a fraction of the round trip.  (Earlier it went through
-// memory: the owner's output
-// row when the accumulator is T, else a per-wave staging slot of the
-// workspace or, for a bfloat16 all-reduce, the lines of output rows c+m and
-// c+2m.  With LDS: R = 16 bfloat16 buckets, reduce-scatter 117 -> 74 us and
-// all-reduce 198 -> 170 us; R = 8 float32 64 MiB per rank, reduce-scatter
-// 144 -> 95 us; the all-reduce, bound by its 16 rows in HBM, unchanged.)
-// Tiles cut short by a segment's end (the checked path) still stage in
-// memory.  A float32 value sits in LDS as two runs of 16-byte halves.
+// through L2 but at a fraction of the round trip -- for every reduce-scatter,
+// every call that would otherwise stage it in memory (bfloat16, in place) and
+// an all-reduce whose rows (2 R N s) total at most 512 MiB (RingArgs::
+// hand_lds).  A larger all-reduce with the accumulator type T hands it on in
+// the owner's output row, where the final value lands: from 128 MiB per rank
+// at R = 8 float32 that was ~7% faster than LDS, up to 32 MiB 7-13% slower,
+// level at 64 MiB.  (With LDS: R = 16 bfloat16 buckets, reduce-scatter 117 ->
+// 74 us and all-reduce 198 -> 170 us, against a per-wave staging slot in the
+// workspace or the lines of two output rows; R = 8 float32 64 MiB per rank,
+// reduce-scatter 144 -> 95 us.)  Tiles cut short by a segment's end (the
+// checked path) still stage in memory.  A float32 value sits in LDS as two
+// runs of 16-byte halves.
 //
 // Every access goes through a buffer resource that spans exactly the tile it
 // addresses: an offset past the tile is dropped by the hardware.
@@ -114,6 +117,37 @@ __device__ inline void a_store(const Hand& r, uint32_t lane, int u, const typena
         for (int i = 0; i < 4; ++i)
             q[i] = E::to_bits(v[4 * h + i]);
         r.h[h][(uint32_t)u * 64u + lane] = q;
+    }
+}
+
+// The same hand-off through memory: half h of every accumulator slot in the
+// run behind h[h] (the owner's output row), each kTileSlots * 16 bytes.
+struct HandMem {
+    rsrc_t h[2];
+};
+
+template <class E, int V>
+__device__ inline void a_load(const HandMem& r, uint32_t lane, int u, typename E::A (&o)[V])
+{
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const u32x4 q = bload<kPolPlain>(r.h[h], t_off(u, lane));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o[4 * h + i] = E::from_bits(q[i]);
+    }
+}
+
+template <class E, int V>
+__device__ inline void a_store(const HandMem& r, uint32_t lane, int u, const typename E::A (&v)[V])
+{
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        u32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            q[i] = E::to_bits(v[4 * h + i]);
+        bstore<kPolPlain>(r.h[h], t_off(u, lane), q);
     }
 }
 
@@ -367,8 +401,9 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
     const uint64_t ntiles = tps * (uint64_t)a.R;
     // this wave's staging slot, or the running value in part at c*part_seg + e
     A* stage = a.stage_wave ? static_cast<A*>(a.part) + (uint64_t)unit * a.stage_wave : nullptr;
-    // every whole tile hands its running value on through this wave's LDS
-    // region (the staging slot or part then serves ragged tiles only)
+    // a whole tile hands its running value on through this wave's LDS region
+    // where the host asks for it (and wherever it would stage in memory); the
+    // staging slot then serves ragged tiles only
     __shared__ u32x4 lds_hand[kWaves][2][kTileSlots];
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int c = (int)(unit / tps);
@@ -390,10 +425,20 @@ __device__ inline void wt_run(const RingArgs& a, uint32_t unit, uint32_t nunits,
                     T* fin = static_cast<T*>(a.out) + (uint64_t)c * a.out_row +
                              (OP == kOpReduceScatter ? tl.lo - (uint64_t)c * a.S : tl.lo) +
                              tl.first * V;
-                    Hand hand;
-                    hand.h[0] = lds_hand[wave][0];
-                    hand.h[1] = lds_hand[wave][1];
-                    wt_reduce<E, V, RED, FP>(a, tl, hand, tile_rsrc(fin, kTileSlots * 16u));
+                    if (stage || a.hand_lds) {
+                        Hand hand;
+                        hand.h[0] = lds_hand[wave][0];
+                        hand.h[1] = lds_hand[wave][1];
+                        wt_reduce<E, V, RED, FP>(a, tl, hand, tile_rsrc(fin, kTileSlots * 16u));
+                    } else {
+                        // the owner's output row (the accumulator is T)
+                        HandMem hm;
+                        constexpr uint32_t half = kTileSlots * 16u;
+                        const char* b = reinterpret_cast<const char*>(acc + tl.first * V);
+                        hm.h[0] = tile_rsrc(b, half);
+                        hm.h[1] = tile_rsrc(b + half, half);
+                        wt_reduce<E, V, RED, FP>(a, tl, hm, tile_rsrc(fin, kTileSlots * 16u));
+                    }
                 }
                 if constexpr (OP != kOpReduceScatter)
                     wt_copy<E, V, OP>(a, tl);

@@ -82,6 +82,8 @@ struct RingArgs {
     uint32_t max_units;  // fused form, vector path: waves that take tiles (the staging holds
                          //   this many); waves of the grid past it exit
     int ragged;          // fused form, vector path: some segment ends inside a wave tile
+    int hand_lds;        // fused form, vector path: whole tiles hand the running value on
+                         //   through LDS even where a row could take it
     uint64_t sub_lo;  // this channel's sub-range of every segment: [c*S + sub_lo,
     uint64_t sub_len; //   c*S + sub_lo + sub_len), clipped to the segment
     int m;            // this channel's ring stride: rank q receives from q - m
