@@ -602,8 +602,9 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
                       2.0 * a.R * (double)a.N * elem_size(c->dtype) <= 512.0 * (1 << 20))
                          ? 1 : 0;
         if (a.op != kOpAllGather && o.stage && a.part == o.stage) {
-            // the hand-off goes through each wave's staging slot in the hand-off
-            // region: at most as many waves as it holds slots take tiles
+            // whole tiles hand off through LDS, tiles cut short by a segment's end
+            // through each wave's staging slot in the hand-off region: at most as
+            // many waves as it holds slots take tiles
             a.stage_wave = (uint64_t)kWaveTileSlots * V;
             const uint64_t slots = o.stage_bytes / (a.stage_wave * 4);
             if (slots < 1)

@@ -76,9 +76,10 @@ struct RingArgs {
     int xcd_pack;     // fused form, scalar path: only workgroups whose id is a multiple of
                       //   this take tiles (the others exit at once), so that they share one XCD
     uint64_t stage_wave; // fused form, vector path: accumulator elements of `part` per wave
-                         //   (each wave's own hand-off staging slot, reused for every tile it
-                         //   takes); 0: the running value of element e of segment c sits at
-                         //   part[c * part_seg + e]
+                         //   (each wave's own staging slot, reused for every tile it takes:
+                         //   whole tiles hand off through LDS, tiles cut short by a segment's
+                         //   end through this slot); 0: the running value of element e of
+                         //   segment c sits at part[c * part_seg + e]
     uint32_t max_units;  // fused form, vector path: waves that take tiles (the staging holds
                          //   this many); waves of the grid past it exit
     int ragged;          // fused form, vector path: some segment ends inside a wave tile

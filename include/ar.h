@@ -238,8 +238,10 @@ int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, voi
  * fused ring (the comm's algorithm, protocol and launch options are not
  * consulted) and needs no workspace: ar_set_workspace is not required.
  * Where ar_allreduce stages the float32 running value in the workspace
- * (bfloat16, or send == recv), this call uses a device array of 8 MiB that
- * the library holds on every GPU it runs on until the process ends.  The
+ * (bfloat16, or send == recv: for the scalar path and for wave tiles cut
+ * short by a segment's end; whole tiles hand off through LDS), this call
+ * uses a device array of 8 MiB that the library holds on every GPU it runs
+ * on until the process ends.  The
  * launch then takes at most as many waves as the array holds staging slots
  * (2,048 for bfloat16, 4,096 for 32-bit types), so every count up to the
  * comm's capacity runs.  Small counts take the scalar path, which keeps one
