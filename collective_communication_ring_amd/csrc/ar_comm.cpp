@@ -380,17 +380,17 @@ bool vector_ok(const ar_comm* c, const void* send, const void* part, const void*
 // Does the fused form take its 16-byte vector path for a channel whose
 // segments are sub_len long?  Its scalar path runs tiles of kBlock elements,
 // one per thread, each tile's 2(R-1)-step chain a latency-bound run by lone
-// waves; while all of them fit one pass over the CUs (one workgroup each) it
-// is the faster one (R = 8, graph-replayed: fp32 16-256 KiB per rank
-// 4.65-4.99 -> 4.13-4.35 us, bf16 16-128 KiB 5.9-6.1 -> 4.2-4.3 us; with
-// twice the tiles, bf16 at 256 KiB, 6.1 against 6.6 us on the vector path).
+// waves; while its tiles number at most two per CU it is the faster one (its
+// reduce steps hand off through LDS; R = 8, graph-replayed: fp32 512 KiB per
+// rank 4.4-4.5 against 4.7 us, bf16 256 KiB 4.3 against 5.6 us on the vector
+// path; at four per CU, fp32 1 MiB, 6.4 against 5.2 us).
 bool fused_vector(const ar_comm* c, const void* send, const void* part, const void* out,
                   uint64_t N, uint64_t S, uint64_t send_row, uint64_t out_row, uint64_t sub_len)
 {
     if (!vector_ok(c, send, part, out, N, S, send_row, out_row))
         return false;
     const uint64_t tiles = (sub_len + kBlock - 1) / kBlock * (uint64_t)c->R;
-    return tiles > (uint64_t)c->ncu;
+    return tiles > 2 * (uint64_t)c->ncu;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
@@ -570,10 +570,7 @@ int run_ring_channel(ar_comm* c, RingArgs& a, hipStream_t st, const RunOpts& o)
             e = launch_ring_step(c->dtype, vec, a, gx, st);
         }
     } else if (launch == AR_LAUNCH_FUSED && vec &&
-               (fused_vector(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row, a.sub_len) ||
-                // the scalar path keeps one accumulator per element: a staging
-                // region that cannot hold them all takes the vector path
-                (o.stage && a.part == o.stage && a.N * 4 > o.stage_bytes))) {
+               fused_vector(c, a.send, a.part, a.out, a.N, a.S, a.send_row, a.out_row, a.sub_len)) {
         // wave tiles of kWaveTileSlots 16-byte slots; two workgroups (8 waves)
         // per CU by default
         const uint64_t V = c->dtype == AR_BF16 ? 8 : 4;
@@ -1036,14 +1033,9 @@ int ar_allreduce_noalloc(ar_comm_t c, const void* send, void* recv, size_t count
     a.out_row = count;
     a.R = c->R;
     a.op = kOpAllReduce;
-    // the vector path stages per wave (the launch takes as many waves as the
-    // array holds slots); the scalar path keeps one accumulator per element,
-    // which must fit.  (Aligned rows take the scalar path only while its tiles
-    // fit one pass over the CUs, i.e. for counts of at most kBlock * ncu per
-    // channel: far below the array.)
-    if (staged && !vector_ok(c, send, a.part, recv, a.N, a.S, a.send_row, a.out_row) &&
-        count * 4 > scratch_bytes)
-        return AR_ERR_INVALID_ARG;
+    // the vector path stages its cut-short tiles per wave (the launch takes as
+    // many waves as the array holds slots); the scalar path hands off through
+    // LDS and needs none of it, so every count runs
     RunOpts o;
     o.stage = scratch;
     o.stage_bytes = scratch_bytes;

@@ -238,17 +238,15 @@ int ar_allreduce(ar_comm_t comm, const void* send, void* recv, size_t count, voi
  * fused ring (the comm's algorithm, protocol and launch options are not
  * consulted) and needs no workspace: ar_set_workspace is not required.
  * Where ar_allreduce stages the float32 running value in the workspace
- * (bfloat16, or send == recv: for the scalar path and for wave tiles cut
- * short by a segment's end; whole tiles hand off through LDS), this call
- * uses a device array of 8 MiB that the library holds on every GPU it runs
- * on until the process ends.  The
+ * (bfloat16, or send == recv: for wave tiles cut short by a segment's end;
+ * whole tiles and the scalar path hand off through LDS), this call uses a
+ * device array of 8 MiB that the library holds on every GPU it runs on until
+ * the process ends.  The
  * launch then takes at most as many waves as the array holds staging slots
  * (2,048 for bfloat16, 4,096 for 32-bit types), so every count up to the
- * comm's capacity runs.  Small counts take the scalar path, which keeps one
- * float32 per element in the array (they fit); a staged call whose count * 4
- * exceeds 8 MiB takes the vector path when the buffers are 16-byte aligned
- * row by row, and returns AR_ERR_INVALID_ARG without launching anything when
- * they are not (or when segments are shorter than 2 KiB).  Nothing in the
+ * comm's capacity runs, whatever the alignment of the buffers (the scalar
+ * path, taken by small counts and rows not 16-byte aligned, uses none of the
+ * array).  Nothing in the
  * array needs clearing (a call writes every slot before reading it).  All
  * calls on one GPU share its array: two of them in flight at once on one GPU
  * (on different streams, or from different comms) race and give wrong

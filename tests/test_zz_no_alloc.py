@@ -4,11 +4,11 @@ It is called through the C ABI with device pointers.  Its output must equal
 ar_allreduce's on the same inputs, bit for bit.  Each case runs two calls in
 a row, the second with a smaller input: the device array keeps the last
 call's contents and must not leak them into the next call.  The cases cover:
-- bfloat16 and in-place float32, which stage the float32 running value in
-  the library's device array;
-- out-of-place float32 and int32, whose running value lives in the owner's
-  row;
-- the scalar path.
+- bfloat16 and in-place float32, whose wave tiles cut short by a segment's
+  end stage the float32 running value in the library's device array (whole
+  tiles hand it on through LDS);
+- out-of-place float32 and int32;
+- the scalar path, which hands off through LDS, at any count.
 """
 import numpy as np
 import pytest
@@ -66,21 +66,26 @@ def test_noalloc_matches_allreduce(env, dtype, R, sizes, in_place):
     comm.close()
 
 
-def test_noalloc_refuses_a_scalar_path_call_too_large_for_its_array(env):
-    """Odd bf16 rows (not 16-byte aligned) take the scalar path, which keeps
-    one float32 per element in the 8 MiB array: above 2,097,152 elements the
-    call is refused on the host, before anything is launched."""
+def test_noalloc_runs_a_scalar_path_call_of_any_size(env):
+    """Odd bf16 rows (not 16-byte aligned) take the scalar path, which hands
+    its running value on through LDS and uses none of the 8 MiB array: a
+    count above what the array could hold as one float32 per element
+    (2,097,152) runs, on two calls in a row, and equals ar_allreduce."""
     torch, api = env["torch"], env["api"]
-    R, N = 2, (8 << 20) // 4 + 1
+    R, N = 2, (8 << 20) // 4 + 1001
     comm = api.Comm(R, N, "bf16", "ring", device=env["dev"])
-    x = torch.zeros((R, N), dtype=torch.bfloat16, device=env["dev"])
-    y = torch.empty_like(x)
+    g = torch.Generator(device=env["dev"])
+    g.manual_seed(71)
+    x = torch.randn((R, N), generator=g, device=env["dev"]).to(torch.bfloat16)
     L = api.lib()
     st = torch.cuda.current_stream().cuda_stream
-    assert L.ar_allreduce_noalloc(comm.handle, x.data_ptr(), y.data_ptr(), N, st) == \
-        api.AR_ERR_INVALID_ARG
-    # an odd count just under the limit (still the scalar path) runs
-    assert L.ar_allreduce_noalloc(comm.handle, x.data_ptr(), y.data_ptr(), N - 2, st) == \
-        api.AR_SUCCESS
-    torch.cuda.synchronize()
+    for n in (N, N - 2000):
+        xs = x[:, :n].contiguous()
+        y = torch.full_like(xs, float("nan"))
+        assert L.ar_allreduce_noalloc(comm.handle, xs.data_ptr(), y.data_ptr(), n, st) == \
+            api.AR_SUCCESS
+        ref = torch.full_like(xs, float("nan"))
+        comm.allreduce(xs, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), n
     comm.close()
