@@ -15,7 +15,8 @@ hand-offs stay in the XCD's L2).  One step = one all-reduce of the whole
            5 (R-1) N s for the forms whose every hop goes through memory;
            roofline.traffic = the bytes rocprofv3's counters saw per launch.
   hop_rate_GBps = 5 (R-1) N s / time: every hop's load and store counted,
-           most of them served by L2 in the fused form (not an HBM rate).
+           served by L2, or by LDS for the reduce steps of smaller or bf16
+           calls, in the fused form (not an HBM rate).
 
 The same line carries, unless --no-extras: the message-size sweep (R = 8
 fp32, 8 B .. 1 GiB per rank) with its alpha-beta fit; the trees (fused, and
